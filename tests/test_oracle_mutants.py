@@ -1,0 +1,80 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of oracle.c (on the CPU), builds it with the
+oracle's flags, points the oracle module at it, and runs the pin tests: at least one pin
+must fail.  The planted copies live in a temporary directory and are never used elsewhere.
+"""
+import pytest
+
+import oracle
+from tests import test_oracle_ef as T_ef
+from tests import test_oracle_quant as T_q
+from tests import test_oracle_ratio as T_r
+from tests import test_oracle_select as T_s
+
+MUTANTS = {
+    "tie_rule_higher_index_wins": ("return a->pos < b->pos ? -1 : 1;",
+                                   "return a->pos > b->pos ? -1 : 1;"),
+    "signed_key_order": ("return bits_of(x) & 0x7FFFFFFFu;", "return bits_of(x) ^ 0x80000000u;"),
+    "fused_momentum": ("float mu = m * u[i];\n            u[i] = mu + x;",
+                       "u[i] = fmaf(m, u[i], x);"),
+    "dropped_residual_term": ("e[i] = e[i] + x;", "e[i] = x;"),
+    "negative_zero_residual": ("e[sel[j]] = 0.0f;", "e[sel[j]] = -0.0f;"),
+    "output_in_rank_order": ("qsort(sel, (size_t)k, sizeof *sel, by_pos);", ""),
+    "off_by_one_selection": ("for (int64_t j = 0; j < k; ++j) sel[j] = rec[j].pos;",
+                             "for (int64_t j = 0; j < k; ++j) sel[j] = rec[j + (j + 1 < n)].pos;"),
+    "philox_no_key_bump": ("k0 += weyl0;", ""),
+    "philox_swapped_words": ("uint32_t n1 = lo1;", "uint32_t n1 = lo0;"),
+    "sr_round_to_nearest": ("q = (int)f + (((float)u24 < frac * 16777216.0f) ? 1 : 0);",
+                            "q = (int)f + (frac >= 0.5f ? 1 : 0);"),
+    "scale_over_128": ("float scale = absmax / 127.0f;", "float scale = absmax / 128.0f;"),
+    "quant_error_not_fed_back": ("e_seg[idx[j]] = v - deq;", "e_seg[idx[j]] = v;"),
+    "k_floor_not_ceil": ("__int128 num = (__int128)n * ppb + 999999999;",
+                         "__int128 num = (__int128)n * ppb;"),
+    "decompress_ignores_scale": ("(float)codes[out + j] * scales[s]", "(float)codes[out + j]"),
+}
+
+
+def _pins(orc):
+    yield lambda: T_s.test_hand_examples(orc)
+    yield lambda: [T_s.test_brute_force_tiny(orc, s) for s in range(12)]
+    yield lambda: T_s.test_numpy_lexsort(orc, 1, 5000, 37)
+    yield lambda: T_s.test_signed_zero_and_inf_order(orc)
+    yield lambda: T_ef.test_ef_add_is_ieee_fp32(orc)
+    yield lambda: T_ef.test_momentum_is_two_roundings(orc)
+    yield lambda: T_ef.test_split_is_exact(orc, 57)
+    yield lambda: T_q.test_philox_known_answers(orc)
+    yield lambda: T_q.test_sr_toy_from_pages(orc)
+    yield lambda: T_q.test_int8_closed_forms(orc)
+    yield lambda: T_q.test_int8_zero_segment_and_error_feedback(orc)
+    yield lambda: T_q.test_decompress_reconstructs(orc, False)
+    yield lambda: T_r.test_k_from_ratio(orc)
+
+
+def _failures():
+    n = 0
+    for pin in _pins(oracle):
+        try:
+            pin()
+        except Exception:          # noqa: BLE001 - any failing pin counts
+            n += 1
+    return n
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = oracle.source()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = oracle.compile_variant(src.replace(old, new), str(tmp_path / f"{name}.so"))
+    saved = oracle._lib
+    try:
+        oracle._lib = oracle.load(path)
+        assert _failures() >= 1, f"no pin caught the planted mistake {name}"
+    finally:
+        oracle._lib = saved
+
+
+def test_unplanted_oracle_passes_every_pin():
+    oracle.lib()
+    assert _failures() == 0
