@@ -1,0 +1,284 @@
+"""Throughput of the error-feedback Top-k compress step on one MI355X.
+
+One step = one pass of the whole hot path over one gradient: (momentum,) EF add, exact
+per-segment Top-k select, ordered compaction into (value, index), residual write (and, for
+the hybrid workload, the int8 stage).  Inputs are seeded synthetic gradients resident in
+HBM before the timed region; a pool of four gradient buffers cycles so that every step sees a fresh
+gradient.  Prints one JSON line.
+
+value = GB/s of fp32 input gradient (4 N bytes per step / step time), whole job.
+roofline = the streaming EF pass (the dominant kernel): algorithmic bytes per launch
+(12 N: read g, read e, write e; 20 N with momentum) / its average HIP-event duration,
+against the 8 TB/s HBM3E peak.
+cpu_baseline = the CPU oracle on one transformer layer's segments of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "EF-Top-k compress GB/s of fp32 gradient (1 GPU) and % of HBM peak"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "c5p_llama2_7b_plain"
+# HBM bytes per launch of the streaming pass, from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+# scaled by the same counters on the copy kernel (written by hand from profiles/)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-momentum-variant", action="store_true")
+    return ap.parse_args()
+
+
+def bytes_per_element(wl):
+    return 20 if wl.momentum is not None else 12
+
+
+def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup):
+    import torch
+    vals, idx, codes, scales = outs
+    m = wl.momentum or 0.0
+
+    def step(t):
+        plan.compress(gbufs[t % len(gbufs)], e, vals, idx, u=u, momentum=m)
+        if wl.int8:
+            plan.quant_int8(vals, idx, codes, scales, e=e, seed=0, step=t)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    plan.timing()                       # drop the warm-up events
+    plan.set_timing(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for t in range(warmup, warmup + steps):
+        step(t)
+    stop.record()
+    torch.cuda.synchronize()
+    plan.set_timing(False)
+    total_ms = start.elapsed_time(stop)
+    k1_ms, launches = plan.timing()
+    return total_ms / steps, k1_ms / max(launches, 1), launches
+
+
+def setup(wl, n_gbufs=4):
+    import torch
+    import gradient_compression_amd as gca
+    from synth import gen
+    plan = gca.Plan(wl.offsets(), ratio=wl.ratio)
+    dev = torch.device("cuda")
+    gbufs = []
+    for t in range(n_gbufs):
+        g = torch.empty(wl.n, dtype=torch.float32, device=dev)
+        gen.fill_gradient(g, wl, t)
+        gbufs.append(g)
+    e = torch.zeros(wl.n, dtype=torch.float32, device=dev)
+    u = torch.zeros(wl.n, dtype=torch.float32, device=dev) if wl.momentum is not None else None
+    vals = torch.empty(plan.total_k, dtype=torch.float32, device=dev)
+    idx = torch.empty(plan.total_k, dtype=torch.int32, device=dev)
+    codes = torch.empty(plan.total_k, dtype=torch.int8, device=dev) if wl.int8 else None
+    scales = torch.empty(wl.n_seg, dtype=torch.float32, device=dev) if wl.int8 else None
+    torch.cuda.synchronize()
+    return plan, gbufs, e, u, (vals, idx, codes, scales)
+
+
+def copy_ceiling(n_bytes=8 << 30):
+    """Reference: the library's dwordx4 copy kernel, GB/s of read + write."""
+    import torch
+    import gradient_compression_amd as gca
+    n = n_bytes // 4
+    a = torch.zeros(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        gca.copy_f32(a, b)
+    torch.cuda.synchronize()
+    s, t = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(10):
+        gca.copy_f32(a, b)
+    t.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(t) / 10
+    del a, b
+    return 2 * n * 4 / ms / 1e6
+
+
+def cpu_baseline(plan, wl, gbuf, e, u):
+    """Time the CPU oracle on one transformer layer's segments (the first 'layer0' ones, or
+    the first segments up to ~200M elements), in a thread pool over segments; check its
+    output against the GPU's on the same inputs."""
+    import concurrent.futures as cf
+    import torch
+    import oracle
+    off = wl.offsets()
+    segs = [s for s in range(wl.n_seg) if 1 <= s <= 9] if wl.n_seg > 9 else [0]
+    budget = 250_000_000
+    total = 0
+    pick = []
+    for s in segs:
+        n = int(off[s + 1] - off[s])
+        if total + n > budget and pick:
+            break
+        pick.append(s)
+        total += n
+    host = {}
+    for s in pick:
+        a, b = int(off[s]), int(off[s + 1])
+        host[s] = dict(g=gbuf[a:b].cpu().numpy(), e=e[a:b].cpu().numpy(),
+                       u=u[a:b].cpu().numpy() if u is not None else None)
+    # the GPU step on the same state, for a parity spot check
+    vals = torch.empty(plan.total_k, dtype=torch.float32, device="cuda")
+    idx = torch.empty(plan.total_k, dtype=torch.int32, device="cuda")
+    plan.compress(gbuf, e, vals, idx, u=u, momentum=wl.momentum or 0.0)
+    torch.cuda.synchronize()
+    threads = max(1, min(len(pick), len(os.sched_getaffinity(0)), 16))
+    oracle.lib()
+
+    def run(s):
+        h = host[s]
+        return s, oracle.topk_ef_segment(h["g"], h["e"], int(plan.k[s]), u=h["u"],
+                                         momentum=wl.momentum or 0.0)
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        res = dict(ex.map(run, pick))
+    dt = time.perf_counter() - t0
+    ok = True
+    for s in pick:
+        ka, kb = int(plan.out_off[s]), int(plan.out_off[s + 1])
+        a, b = int(off[s]), int(off[s + 1])
+        hv, hi = res[s]
+        ok &= vals[ka:kb].cpu().numpy().tobytes() == hv.tobytes()
+        ok &= np.array_equal(idx[ka:kb].cpu().numpy(), hi)
+        ok &= e[a:b].cpu().numpy().tobytes() == host[s]["e"].tobytes()
+    return {
+        "value": round(4.0 * total / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one EF-Top-k step of segments {pick[0]}..{pick[-1]} ({len(pick)} tensors, "
+                   f"{total} fp32 elements) of {wl.name}, full sort per segment, "
+                   f"{dt:.2f} s wall on {threads} threads"),
+        "parity_with_gpu_on_sample": bool(ok),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+              "requested). Compression is worker-local; run one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gradient_compression_amd as gca
+    from synth import workload
+    gca.lib()  # fails loudly when the HIP library is not built
+    wl = workload(args.workload)
+    log(f"[bench] workload {wl.name}: N={wl.n} segments={wl.n_seg} ratio={wl.ratio}")
+    plan, gbufs, e, u, outs = setup(wl)
+    log(f"[bench] inputs resident ({len(gbufs)} gradient buffers); warmup {args.warmup}, "
+        f"timing {args.steps} steps")
+    ms, k1_ms, launches = time_steps(plan, wl, gbufs, e, u, outs, args.steps, args.warmup)
+    st = plan.last_stats()
+    bpe = bytes_per_element(wl)
+    value = 4.0 * wl.n / ms / 1e6                     # GB/s of fp32 gradient
+    eff = bpe * wl.n / ms / 1e6
+    k1_ach = bpe * wl.n / k1_ms / 1e6
+    log(f"[bench] {ms:.3f} ms/step, {value:.1f} GB/s gradient, effective {eff:.1f} GB/s "
+        f"({eff / HBM_PEAK_GBPS:.1%} of peak); EF pass {k1_ms:.3f} ms ({k1_ach:.1f} GB/s)")
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f).get(wl.name)
+        traffic = tr.get("bytes_per_launch") if tr else None
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "n_elements": wl.n,
+            "segments": wl.n_seg,
+            "k_ratio": wl.ratio,
+            "total_k": int(plan.total_k),
+            "momentum": wl.momentum,
+            "int8": wl.int8,
+            "gradient_dist": f"{wl.scale} * Student-t({wl.df})" if wl.dist == "t" else wl.dist,
+        },
+        "elements_per_s": round(wl.n / ms * 1e3, 1),
+        "effective_GBps": round(eff, 1),
+        "hbm_peak_frac_effective": round(eff / HBM_PEAK_GBPS, 4),
+        "candidates_per_k": round(float(st["candidates"].sum()) / max(plan.total_k, 1), 3),
+        "full_path_segments_last_step": int((st["mode"] == gca.MODE_FULL).sum()),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_ef_capture (EF add + key + candidate capture)",
+            "achieved": round(k1_ach, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(k1_ach / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_element": bpe,
+            "avg_launch_ms": round(k1_ms, 4),
+            "launches": launches,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline: oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(plan, wl, gbufs[0], e, u)
+    del gbufs, e, u, outs
+    plan.close()
+    torch.cuda.empty_cache()
+    try:
+        result["copy_ceiling_GBps"] = round(copy_ceiling(), 1)
+    except Exception as ex:  # noqa: BLE001 - context figure only
+        log(f"[bench] copy ceiling skipped: {ex}")
+    if not args.no_momentum_variant and wl.name == DEFAULT_WORKLOAD:
+        # the same shape with momentum correction (u = 0.9 u + g), as the 7B workload states
+        wm = workload("c5_llama2_7b")
+        plan_m, gb_m, e_m, u_m, outs_m = setup(wm)
+        ms_m, k1m, _ = time_steps(plan_m, wm, gb_m, e_m, u_m, outs_m, max(args.steps // 2, 3),
+                                  args.warmup)
+        result["momentum_variant"] = {
+            "workload": wm.name, "ms_per_step": round(ms_m, 4),
+            "GBps_gradient": round(4.0 * wm.n / ms_m / 1e6, 2),
+            "hbm_peak_frac_12B": round(12.0 * wm.n / ms_m / 1e6 / HBM_PEAK_GBPS, 4),
+            "hbm_peak_frac_20B": round(20.0 * wm.n / ms_m / 1e6 / HBM_PEAK_GBPS, 4),
+            "ef_pass_ms": round(k1m, 4),
+        }
+        log(f"[bench] momentum variant: {ms_m:.3f} ms/step")
+        plan_m.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+"""MI355X-native error-feedback Top-k gradient compression.
+
+A thin Python binding over the C ABI of ``libgc.so`` (``include/gc.h``): argument
+marshalling only, every step of the path runs in the library's HIP kernels.  PyTorch is used
+for device memory and streams.  The package fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgc.so")
+
+GC_OK = 0
+GC_ERR_INVALID_ARG = -1
+GC_ERR_OOM = -2
+GC_ERR_HIP = -3
+GC_ERR_UNSUPPORTED = -4
+GC_MOMENTUM_MASK = 0x1
+GC_DEBUG_FORCE_FALLBACK = 0x100
+GC_DEBUG_NO_ESTIMATE = 0x200
+
+MODE_SKIP, MODE_CANDIDATES, MODE_FULL, MODE_RECAPTURED = 0, 1, 2, 3
+
+EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layout",
+           "gc_topk_ef_compress", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
+           "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32",
+           "gc_status_string")
+
+_lib = None
+
+
+class GCError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgc.so (built by ``__graft_entry__.build()``); raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                          "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u32, u64, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                   ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float)
+    sig = {
+        "gc_plan_create": [vp, i32, vp, vp, u32, vp],
+        "gc_plan_destroy": [vp],
+        "gc_plan_total_k": [vp, vp],
+        "gc_plan_layout": [vp, vp, vp],
+        "gc_topk_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp],
+        "gc_quant_int8": [vp, vp, vp, vp, u64, u64, vp, vp, vp],
+        "gc_decompress": [vp, vp, vp, vp, vp, vp, ctypes.c_int, vp],
+        "gc_plan_reset_estimate": [vp, vp],
+        "gc_plan_last_stats": [vp, vp, vp, vp, vp, vp],
+        "gc_plan_set_timing": [vp, ctypes.c_int],
+        "gc_plan_timing": [vp, vp, vp],
+        "gc_copy_f32": [vp, vp, i64, vp],
+        "gc_status_string": [ctypes.c_int],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "gc_status_string" else ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().gc_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != GC_OK:
+        raise GCError(rc, what)
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev_ptr(t, dtype, name, numel=None):
+    """Device pointer of a contiguous CUDA/HIP tensor of the given dtype (None -> NULL)."""
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Plan:
+    """A compression plan over a segmented buffer (one segment per parameter tensor).
+
+    ``seg_off``: int64[n_seg + 1] segment offsets; give per-segment ``k`` or ``ratio``.
+    """
+
+    def __init__(self, seg_off, k=None, ratio=None, flags: int = 0):
+        L = lib()
+        self._h = ctypes.c_void_p()
+        off = np.ascontiguousarray(seg_off, dtype=np.int64)
+        self.n_seg = int(off.size - 1)
+        if self.n_seg < 0:
+            raise ValueError("seg_off needs at least one entry")
+        kp = rp = None
+        if k is not None:
+            self._k_in = np.ascontiguousarray(np.broadcast_to(np.asarray(k, np.int64), (self.n_seg,)))
+            kp = _np_ptr(self._k_in)
+        if ratio is not None:
+            self._r_in = np.ascontiguousarray(np.broadcast_to(np.asarray(ratio, np.float64),
+                                                              (self.n_seg,)))
+            rp = _np_ptr(self._r_in)
+        _check(L.gc_plan_create(_np_ptr(off), self.n_seg, kp, rp, int(flags),
+                                ctypes.byref(self._h)), "gc_plan_create")
+        self.seg_off = off.copy()
+        self.n = int(off[-1])
+        self.flags = int(flags)
+        tk = ctypes.c_int64()
+        _check(L.gc_plan_total_k(self._h, ctypes.byref(tk)), "gc_plan_total_k")
+        self.total_k = tk.value
+        self.k = np.zeros(self.n_seg, np.int64)
+        self.out_off = np.zeros(self.n_seg + 1, np.int64)
+        _check(L.gc_plan_layout(self._h, _np_ptr(self.k), _np_ptr(self.out_off)),
+               "gc_plan_layout")
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            lib().gc_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # ---------------------------------------------------------------- entry points
+    def compress(self, g, e, out_vals, out_idx, u=None, momentum: float = 0.0, stream=None):
+        """g^ = TopK(g + e) per segment into (out_vals, out_idx); e <- the residual.
+
+        With ``u`` (velocity): u <- momentum*u + g first, and acc = e + u.
+        """
+        import torch
+        n = self.n
+        rc = lib().gc_topk_ef_compress(
+            self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
+            _dev_ptr(u, torch.float32, "u", n), float(momentum),
+            _dev_ptr(out_vals, torch.float32, "out_vals", self.total_k),
+            _dev_ptr(out_idx, torch.int32, "out_idx", self.total_k), _stream(stream))
+        _check(rc, "gc_topk_ef_compress")
+
+    def quant_int8(self, vals, idx, out_codes, out_scales, e=None, seed: int = 0, step: int = 0,
+                   stream=None):
+        """int8 codes and per-segment scales of the kept values (stochastic rounding);
+        with ``e`` the quantisation error is fed back into the residual."""
+        import torch
+        rc = lib().gc_quant_int8(
+            self._h, _dev_ptr(vals, torch.float32, "vals", self.total_k),
+            _dev_ptr(idx, torch.int32, "idx", self.total_k), _dev_ptr(e, torch.float32, "e", self.n),
+            int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1),
+            _dev_ptr(out_codes, torch.int8, "out_codes", self.total_k),
+            _dev_ptr(out_scales, torch.float32, "out_scales", self.n_seg), _stream(stream))
+        _check(rc, "gc_quant_int8")
+
+    def decompress(self, idx, dense, vals=None, codes=None, scales=None, accumulate=False,
+                   stream=None):
+        import torch
+        rc = lib().gc_decompress(
+            self._h, _dev_ptr(vals, torch.float32, "vals", self.total_k),
+            _dev_ptr(codes, torch.int8, "codes", self.total_k),
+            _dev_ptr(scales, torch.float32, "scales", self.n_seg),
+            _dev_ptr(idx, torch.int32, "idx", self.total_k),
+            _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
+            _stream(stream))
+        _check(rc, "gc_decompress")
+
+    def reset_estimate(self, stream=None):
+        _check(lib().gc_plan_reset_estimate(self._h, _stream(stream)), "gc_plan_reset_estimate")
+
+    def last_stats(self, stream=None) -> dict:
+        """Per-segment mode, candidate count, k-th key and ties of the last call (syncs)."""
+        out = {name: np.zeros(self.n_seg, np.uint32)
+               for name in ("mode", "candidates", "kth_key", "ties")}
+        rc = lib().gc_plan_last_stats(self._h, _np_ptr(out["mode"]), _np_ptr(out["candidates"]),
+                                      _np_ptr(out["kth_key"]), _np_ptr(out["ties"]),
+                                      _stream(stream))
+        _check(rc, "gc_plan_last_stats")
+        return out
+
+    def set_timing(self, enable: bool = True):
+        _check(lib().gc_plan_set_timing(self._h, int(bool(enable))), "gc_plan_set_timing")
+
+    def timing(self):
+        """(milliseconds, launches) of the streaming pass since the last query."""
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        _check(lib().gc_plan_timing(self._h, ctypes.byref(ms), ctypes.byref(n)), "gc_plan_timing")
+        return ms.value, n.value
+
+
+def copy_f32(src, dst, stream=None):
+    """Reference streaming copy (16-byte loads and stores) for bandwidth calibration."""
+    import torch
+    n = src.numel()
+    _check(lib().gc_copy_f32(_dev_ptr(src, torch.float32, "src"),
+                             _dev_ptr(dst, torch.float32, "dst", n), n, _stream(stream)),
+           "gc_copy_f32")
+
+
+__all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "EXPORTS",
+           "GC_MOMENTUM_MASK", "GC_DEBUG_FORCE_FALLBACK", "GC_DEBUG_NO_ESTIMATE", "MODE_SKIP",
+           "MODE_CANDIDATES", "MODE_FULL", "MODE_RECAPTURED"]

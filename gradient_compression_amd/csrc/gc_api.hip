@@ -1,0 +1,437 @@
+// gc_api.hip -- host side of the C ABI declared in include/gc.h: plan construction (segment,
+// tile and chunk tables, candidate capacities, device workspace), argument checks, and the
+// launch sequence of each entry point.  No call except gc_plan_create allocates device memory.
+#include "gc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "gc_internal.h"
+
+namespace {
+
+// Segments at most this long capture every element (their select runs on the candidates).
+constexpr int64_t kSmallSegment = 65536;
+// Candidate capacity of a larger segment, in multiples of its k (at least kMinCapacity).
+constexpr int64_t kCapacityFactor = 16;
+constexpr int64_t kMinCapacity = 65536;
+// First margin of the threshold estimate (next threshold = beta * |k-th largest|).
+constexpr float kInitialBeta = 0.9f;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// k = min(n, ceil(n * ratio)) with the ratio in exact parts per billion; -1 if invalid.
+int64_t k_from_ratio(int64_t n, double ratio) {
+  if (!(ratio >= 0.0 && ratio <= 1.0)) return -1;
+  if (n <= 0) return 0;
+  const int64_t ppb = std::llround(ratio * 1e9);
+  const __int128 num = (__int128)n * ppb + 999999999;
+  const int64_t k = (int64_t)(num / 1000000000);
+  return std::min(k, n);
+}
+
+struct Carver {  // sub-allocates one device block, 256-byte aligned pieces
+  size_t off = 0;
+  std::vector<std::pair<void**, size_t>> req;
+  template <typename T>
+  void add(T** p, int64_t count) {
+    req.emplace_back(reinterpret_cast<void**>(p), (size_t)std::max<int64_t>(count, 1) * sizeof(T));
+  }
+  size_t total() const {
+    size_t t = 0;
+    for (auto& r : req) t += (r.second + 255) & ~(size_t)255;
+    return t;
+  }
+  void place(char* base) {
+    size_t o = 0;
+    for (auto& r : req) {
+      *r.first = base + o;
+      o += (r.second + 255) & ~(size_t)255;
+    }
+  }
+};
+
+}  // namespace
+
+struct gc_plan {
+  int device = 0;
+  int32_t n_seg = 0;
+  uint32_t flags = 0;
+  std::vector<int64_t> seg_off, k, out_off;
+  int64_t total_k = 0;
+  gc::DevPlan dp{};
+  gc::OutPlan op{};
+  void* mem = nullptr;
+  bool timing = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending, spare;
+};
+
+namespace {
+
+int check_device(const gc_plan* p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GC_ERR_HIP;
+  return dev == p->device ? GC_OK : GC_ERR_INVALID_ARG;
+}
+
+template <typename T>
+hipError_t upload(T* dst, const std::vector<T>& src) {
+  if (src.empty()) return hipSuccess;
+  return hipMemcpy(dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gc_status_string(int status) {
+  switch (status) {
+    case GC_OK: return "success";
+    case GC_ERR_INVALID_ARG: return "invalid argument";
+    case GC_ERR_OOM: return "out of device memory";
+    case GC_ERR_HIP: return "HIP runtime error";
+    case GC_ERR_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
+                   uint32_t flags, gc_plan** out) {
+  if (!out) return GC_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (n_seg < 0 || !seg_off) return GC_ERR_INVALID_ARG;
+  if (n_seg > 0 && (k == nullptr) == (ratio == nullptr)) return GC_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)(GC_MOMENTUM_MASK | GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE))
+    return GC_ERR_INVALID_ARG;
+  if (seg_off[0] < 0) return GC_ERR_INVALID_ARG;
+  std::vector<int64_t> ks(n_seg);
+  for (int32_t s = 0; s < n_seg; ++s) {
+    const int64_t n = seg_off[s + 1] - seg_off[s];
+    if (n < 0 || n > INT32_MAX) return GC_ERR_INVALID_ARG;
+    ks[s] = k ? k[s] : k_from_ratio(n, ratio[s]);
+    if (ks[s] < 0 || ks[s] > n) return GC_ERR_INVALID_ARG;
+  }
+
+  gc_plan* p = new (std::nothrow) gc_plan();
+  if (!p) return GC_ERR_OOM;
+  if (hipGetDevice(&p->device) != hipSuccess) {
+    delete p;
+    return GC_ERR_HIP;
+  }
+  p->n_seg = n_seg;
+  p->flags = flags;
+  p->seg_off.assign(seg_off, seg_off + n_seg + 1);
+  p->k = ks;
+  p->out_off.assign(n_seg + 1, 0);
+  for (int32_t s = 0; s < n_seg; ++s) p->out_off[s + 1] = p->out_off[s] + ks[s];
+  p->total_k = p->out_off[n_seg];
+
+  // tables
+  std::vector<int64_t> tile_base(n_seg + 1, 0), chunk_base(n_seg + 1, 0), cand_base(n_seg, 0),
+      out_chunk_base(n_seg + 1, 0);
+  std::vector<uint32_t> kk(n_seg), cap(n_seg), thr_init(n_seg);
+  int64_t cand_total = 0;
+  for (int32_t s = 0; s < n_seg; ++s) {
+    const int64_t n = seg_off[s + 1] - seg_off[s];
+    tile_base[s + 1] = tile_base[s] + ceil_div(n, gc::kTile);
+    int64_t c = 0;
+    uint32_t thr = gc::kNoCapture;
+    if (ks[s] > 0) {
+      if (n <= kSmallSegment || ks[s] * kCapacityFactor >= n) {
+        c = n;
+        thr = 0;  // capture everything: the select then runs on the whole segment's copy
+      } else {
+        c = std::min(n, std::max(ks[s] * kCapacityFactor, kMinCapacity));
+      }
+      if (flags & (GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE)) thr = gc::kNoCapture;
+    }
+    kk[s] = (uint32_t)ks[s];
+    cap[s] = (uint32_t)c;
+    thr_init[s] = thr;
+    cand_base[s] = cand_total;
+    cand_total += round_up(c, 4);
+    chunk_base[s + 1] = chunk_base[s] + ceil_div(c, gc::kChunk);
+    out_chunk_base[s + 1] = out_chunk_base[s] + ceil_div(ks[s], gc::kOutChunk);
+  }
+  const int64_t n_tiles = tile_base[n_seg], n_chunks = chunk_base[n_seg];
+  const int64_t n_out_chunks = out_chunk_base[n_seg];
+  if (n_tiles > INT32_MAX || n_chunks + gc::kFullBlocks > INT32_MAX || n_out_chunks > INT32_MAX ||
+      cand_total > UINT32_MAX * 4ll) {
+    delete p;
+    return GC_ERR_UNSUPPORTED;
+  }
+  std::vector<int32_t> tile_seg(n_tiles), chunk_seg(n_chunks), out_chunk_seg(n_out_chunks);
+  for (int32_t s = 0; s < n_seg; ++s) {
+    for (int64_t t = tile_base[s]; t < tile_base[s + 1]; ++t) tile_seg[t] = s;
+    for (int64_t c = chunk_base[s]; c < chunk_base[s + 1]; ++c) chunk_seg[c] = s;
+    for (int64_t c = out_chunk_base[s]; c < out_chunk_base[s + 1]; ++c) out_chunk_seg[c] = s;
+  }
+
+  // device workspace
+  gc::DevPlan& d = p->dp;
+  d.n_seg = n_seg;
+  d.flags = (int32_t)flags;
+  d.n_tiles = n_tiles;
+  d.n_chunks = n_chunks;
+  int64_t *d_seg_off, *d_tile_base, *d_chunk_base, *d_out_off, *d_cand_base, *d_out_chunk_base;
+  int32_t *d_tile_seg, *d_chunk_seg, *d_out_chunk_seg;
+  uint32_t *d_k, *d_cap, *d_thr_init;
+  Carver cv;
+  cv.add(&d_seg_off, n_seg + 1);
+  cv.add(&d_tile_base, n_seg + 1);
+  cv.add(&d_tile_seg, n_tiles);
+  cv.add(&d_chunk_base, n_seg + 1);
+  cv.add(&d_chunk_seg, n_chunks);
+  cv.add(&d_k, n_seg);
+  cv.add(&d_out_off, n_seg + 1);
+  cv.add(&d_cand_base, n_seg);
+  cv.add(&d_cap, n_seg);
+  cv.add(&d_thr_init, n_seg);
+  cv.add(&d_out_chunk_seg, n_out_chunks);
+  cv.add(&d_out_chunk_base, n_seg + 1);
+  cv.add(&d.thr, n_seg);
+  cv.add(&d.cand_cnt, n_seg);
+  cv.add(&d.mode, n_seg);
+  cv.add(&d.prefix, n_seg);
+  cv.add(&d.kk, n_seg);
+  cv.add(&d.kth, n_seg);
+  cv.add(&d.ties, n_seg);
+  cv.add(&d.hist, (int64_t)n_seg * 3 * gc::kHistBins);
+  cv.add(&d.full_list, n_seg);
+  cv.add(&d.full_count, 1);
+  cv.add(&d.recap_list, n_seg);
+  cv.add(&d.recap_count, 1);
+  cv.add(&d.why, n_seg);
+  cv.add(&d.beta, n_seg);
+  cv.add(&d.err, 1);
+  cv.add(&d.run_off, n_tiles);
+  cv.add(&d.run_cnt, n_tiles);
+  cv.add(&d.run_dst, n_tiles);
+  cv.add(&d.tile_gt, n_tiles);
+  cv.add(&d.tile_eq, n_tiles);
+  cv.add(&d.tile_eq_base, n_tiles);
+  cv.add(&d.tile_sel_base, n_tiles);
+  cv.add(&d.chunk_gt, n_chunks);
+  cv.add(&d.chunk_eq, n_chunks);
+  cv.add(&d.chunk_eq_base, n_chunks);
+  cv.add(&d.chunk_sel_base, n_chunks);
+  cv.add(&d.cand_val, cand_total);
+  cv.add(&d.cand_idx, cand_total);
+  cv.add(&d.sort_val, cand_total);
+  cv.add(&d.sort_idx, cand_total);
+  if (hipMalloc(&p->mem, cv.total()) != hipSuccess) {
+    (void)hipGetLastError();
+    delete p;
+    return GC_ERR_OOM;
+  }
+  cv.place(static_cast<char*>(p->mem));
+  d.seg_off = d_seg_off;
+  d.tile_base = d_tile_base;
+  d.tile_seg = d_tile_seg;
+  d.chunk_base = d_chunk_base;
+  d.chunk_seg = d_chunk_seg;
+  d.k = d_k;
+  d.out_off = d_out_off;
+  d.cand_base = d_cand_base;
+  d.cand_cap = d_cap;
+  d.thr_init = d_thr_init;
+  gc::OutPlan& o = p->op;
+  o.n_seg = n_seg;
+  o.n_out_chunks = n_out_chunks;
+  o.seg_off = d_seg_off;
+  o.out_off = d_out_off;
+  o.out_chunk_seg = d_out_chunk_seg;
+  o.out_chunk_base = d_out_chunk_base;
+
+  hipError_t err = hipSuccess;
+  auto up = [&](hipError_t e) { if (err == hipSuccess) err = e; };
+  up(upload(d_seg_off, p->seg_off));
+  up(upload(d_tile_base, tile_base));
+  up(upload(d_tile_seg, tile_seg));
+  up(upload(d_chunk_base, chunk_base));
+  up(upload(d_chunk_seg, chunk_seg));
+  up(upload(d_k, kk));
+  up(upload(d_out_off, p->out_off));
+  up(upload(d_cand_base, cand_base));
+  up(upload(d_cap, cap));
+  up(upload(d_thr_init, thr_init));
+  up(upload(d_out_chunk_seg, out_chunk_seg));
+  up(upload(d_out_chunk_base, out_chunk_base));
+  up(upload(d.thr, thr_init));
+  up(upload(d.beta, std::vector<float>(n_seg, kInitialBeta)));
+  up(hipMemset(d.cand_cnt, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
+  up(hipMemset(d.mode, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
+  up(hipMemset(d.kth, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
+  up(hipMemset(d.ties, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
+  up(hipMemset(d.err, 0, sizeof(uint32_t)));
+  up(hipDeviceSynchronize());
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(p->mem);
+    delete p;
+    return GC_ERR_HIP;
+  }
+  *out = p;
+  return GC_OK;
+}
+
+int gc_plan_destroy(gc_plan* plan) {
+  if (!plan) return GC_OK;
+  int rc = GC_OK;
+  if (hipDeviceSynchronize() != hipSuccess) rc = GC_ERR_HIP;
+  for (auto& pr : plan->pending) {
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  for (auto& pr : plan->spare) {
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  if (plan->mem && hipFree(plan->mem) != hipSuccess) rc = GC_ERR_HIP;
+  delete plan;
+  return rc;
+}
+
+int gc_plan_total_k(const gc_plan* plan, int64_t* total_k) {
+  if (!plan || !total_k) return GC_ERR_INVALID_ARG;
+  *total_k = plan->total_k;
+  return GC_OK;
+}
+
+int gc_plan_layout(const gc_plan* plan, int64_t* k, int64_t* out_off) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  if (k && plan->n_seg) std::memcpy(k, plan->k.data(), sizeof(int64_t) * plan->n_seg);
+  if (out_off) std::memcpy(out_off, plan->out_off.data(), sizeof(int64_t) * (plan->n_seg + 1));
+  return GC_OK;
+}
+
+int gc_topk_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                        float* out_vals, int32_t* out_idx, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!g || !e || !aligned16(g) || !aligned16(e))) return GC_ERR_INVALID_ARG;
+  if (u && !aligned16(u)) return GC_ERR_INVALID_ARG;
+  if (plan->total_k > 0 && (!out_vals || !out_idx)) return GC_ERR_INVALID_ARG;
+  if (any && (g == e || (u && (g == u || e == u)))) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t b = nullptr, en = nullptr;
+  if (plan->timing) {
+    if (plan->spare.empty()) {
+      hipEvent_t x, y;
+      if (hipEventCreate(&x) != hipSuccess) return GC_ERR_HIP;
+      if (hipEventCreate(&y) != hipSuccess) {
+        (void)hipEventDestroy(x);
+        return GC_ERR_HIP;
+      }
+      plan->spare.emplace_back(x, y);
+    }
+    b = plan->spare.back().first;
+    en = plan->spare.back().second;
+    plan->pending.push_back(plan->spare.back());
+    plan->spare.pop_back();
+  }
+  const hipError_t err =
+      gc::launch_compress(plan->dp, g, e, u, momentum, out_vals, out_idx, st, b, en);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_quant_int8(gc_plan* plan, const float* vals, const int32_t* idx, float* e, uint64_t seed,
+                  uint64_t step, int8_t* out_codes, float* out_scales, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  if (plan->total_k > 0 && (!vals || !idx || !out_codes)) return GC_ERR_INVALID_ARG;
+  if (plan->n_seg > 0 && !out_scales) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  const hipError_t err = gc::launch_quant(plan->op, vals, idx, e, seed, step, out_codes,
+                                          out_scales, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_decompress(const gc_plan* plan, const float* vals, const int8_t* codes,
+                  const float* scales, const int32_t* idx, float* dense, int accumulate,
+                  void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  if ((vals == nullptr) == (codes == nullptr)) return GC_ERR_INVALID_ARG;
+  if (codes && !scales) return GC_ERR_INVALID_ARG;
+  if (plan->total_k > 0 && !idx) return GC_ERR_INVALID_ARG;
+  if (!dense && plan->seg_off[plan->n_seg] > plan->seg_off[0]) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (!accumulate) err = gc::launch_fill_zero(dense, plan->seg_off[0], plan->seg_off[plan->n_seg], st);
+  if (err == hipSuccess)
+    err = gc::launch_decompress(plan->op, vals, codes, scales, idx, dense, accumulate, st);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_plan_reset_estimate(gc_plan* plan, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  return gc::launch_reset(plan->dp, static_cast<hipStream_t>(stream)) == hipSuccess ? GC_OK
+                                                                                     : GC_ERR_HIP;
+}
+
+int gc_plan_last_stats(gc_plan* plan, uint32_t* mode, uint32_t* candidates, uint32_t* kth_key,
+                       uint32_t* ties_taken, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t bytes = sizeof(uint32_t) * plan->n_seg;
+  hipError_t err = hipSuccess;
+  auto cp = [&](uint32_t* dst, const uint32_t* src) {
+    if (dst && bytes && err == hipSuccess) err = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, st);
+  };
+  cp(mode, plan->dp.mode);
+  cp(candidates, plan->dp.cand_cnt);
+  cp(kth_key, plan->dp.kth);
+  cp(ties_taken, plan->dp.ties);
+  uint32_t flag = 0;
+  if (err == hipSuccess) err = hipMemcpyAsync(&flag, plan->dp.err, sizeof flag, hipMemcpyDeviceToHost, st);
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  if (err != hipSuccess) return GC_ERR_HIP;
+  return flag ? GC_ERR_HIP : GC_OK;
+}
+
+int gc_plan_set_timing(gc_plan* plan, int enable) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  plan->timing = enable != 0;
+  return GC_OK;
+}
+
+int gc_plan_timing(gc_plan* plan, double* ms, int64_t* launches) {
+  if (!plan || !ms || !launches) return GC_ERR_INVALID_ARG;
+  double sum = 0.0;
+  int64_t n = 0;
+  int rc = GC_OK;
+  for (auto& pr : plan->pending) {
+    float t = 0.0f;
+    if (hipEventSynchronize(pr.second) != hipSuccess ||
+        hipEventElapsedTime(&t, pr.first, pr.second) != hipSuccess)
+      rc = GC_ERR_HIP;
+    sum += t;
+    ++n;
+    plan->spare.push_back(pr);
+  }
+  plan->pending.clear();
+  *ms = sum;
+  *launches = n;
+  return rc;
+}
+
+int gc_copy_f32(const float* src, float* dst, int64_t n, void* stream) {
+  if (n < 0 || (n & 3) || (n && (!src || !dst || !aligned16(src) || !aligned16(dst))))
+    return GC_ERR_INVALID_ARG;
+  return gc::launch_copy(src, dst, n, static_cast<hipStream_t>(stream)) == hipSuccess ? GC_OK
+                                                                                      : GC_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// gc_internal.h -- shared definitions of the HIP kernels and the host plan (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gc {
+
+// Streaming layout: one workgroup of 4 wave64s per tile of 8192 elements.  Wave w owns the
+// contiguous range [w*2048, (w+1)*2048) of its tile; inside it, slot v (0..7) of lane l holds
+// the 4 consecutive elements starting at w*2048 + v*256 + l*4.  Element order in the tile is
+// therefore (w, v, l, c), which is index order: every ordered rank below follows it.
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kSlots = 8;
+constexpr int kWaveSpan = 64 * 4 * kSlots;         // 2048
+constexpr int kTile = kWaves * kWaveSpan;          // 8192
+// Candidate buffers are processed in chunks laid out exactly like tiles.
+constexpr int kChunk = kTile;
+// Workgroups that serve the exact full-segment path, striding over listed segments.
+constexpr int kFullBlocks = 1024;
+// Output chunks for the int8 and decompression kernels.
+constexpr int kOutChunk = 4096;
+constexpr int kHistBins = 2048;
+
+constexpr uint32_t kNoCapture = 0xFFFFFFFFu;        // threshold above every key
+// Per-segment path of a call.  kModeCand: the candidates captured at the estimated threshold
+// hold the k largest.  kModeRecap: they did not, the segment's first-digit histogram was
+// taken and the candidates re-captured at the exact bucket floor.  kModeFull: the bucket is
+// larger than the capacity (or forced): radix select over the whole segment.
+enum : uint32_t { kModeSkip = 0, kModeCand = 1, kModeFull = 2, kModeRecap = 3, kModePending = 4 };
+// Why a segment left the estimate path (for the estimate's feedback).
+enum : uint32_t { kWhyNone = 0, kWhyCold = 1, kWhyMiss = 2, kWhyOverflow = 3 };
+// Plan flags seen by the kernels (same values as the public ones).
+constexpr int32_t kFlagMomentumMask = 0x1;
+constexpr int32_t kFlagForceFull = 0x100;
+constexpr int32_t kFlagNoEstimate = 0x200;
+
+// Device view of a plan, passed by value to every kernel.
+struct DevPlan {
+  int32_t n_seg;
+  int32_t flags;
+  int64_t n_tiles;
+  int64_t n_chunks;
+  // host-built tables
+  const int64_t* seg_off;      // [n_seg + 1]
+  const int64_t* tile_base;    // [n_seg + 1] first tile of each segment
+  const int32_t* tile_seg;     // [n_tiles]
+  const int64_t* chunk_base;   // [n_seg + 1] first candidate chunk of each segment
+  const int32_t* chunk_seg;    // [n_chunks]
+  const uint32_t* k;           // [n_seg]
+  const int64_t* out_off;      // [n_seg + 1]
+  const int64_t* cand_base;    // [n_seg] start of the segment's candidate region
+  const uint32_t* cand_cap;    // [n_seg] its capacity
+  const uint32_t* thr_init;    // [n_seg] threshold of a fresh plan
+  // per-segment state
+  uint32_t* thr;               // capture threshold of the next call
+  uint32_t* cand_cnt;          // candidates captured this call
+  uint32_t* mode;
+  uint32_t* prefix;            // radix-select prefix so far
+  uint32_t* kk;                // rank still to find inside the prefix
+  uint32_t* kth;               // k-th largest key
+  uint32_t* ties;              // entries taken at exactly kth
+  uint32_t* hist;              // [n_seg][3][kHistBins]
+  uint32_t* full_list;         // [n_seg] segments on the exact full-segment path
+  uint32_t* full_count;        // [1]
+  uint32_t* recap_list;        // [n_seg] segments whose candidates were not complete
+  uint32_t* recap_count;       // [1]
+  uint32_t* why;               // [n_seg] kWhy* of this call
+  float* beta;                 // [n_seg] threshold margin: next threshold = beta * |kth|
+  uint32_t* err;               // [1] internal consistency flag (0 = fine)
+  // per-tile state
+  uint32_t* run_off;           // [n_tiles] offset of the tile's run in its segment region
+  uint32_t* run_cnt;           // [n_tiles]
+  uint32_t* run_dst;           // [n_tiles] index-ordered position of the run
+  uint32_t* tile_gt;           // [n_tiles] (full-segment path) keys above kth
+  uint32_t* tile_eq;           // [n_tiles] keys equal to kth
+  uint32_t* tile_eq_base;      // [n_tiles] ties before the tile
+  uint32_t* tile_sel_base;     // [n_tiles] kept entries before the tile
+  // per-chunk state (candidate path)
+  uint32_t* chunk_gt;          // [n_chunks]
+  uint32_t* chunk_eq;
+  uint32_t* chunk_eq_base;
+  uint32_t* chunk_sel_base;
+  // candidate buffers, segment s at [cand_base[s], cand_base[s] + cand_cap[s])
+  float* cand_val;
+  int32_t* cand_idx;
+  float* sort_val;             // the same candidates in ascending index order
+  int32_t* sort_idx;
+};
+
+struct OutPlan {               // tables of the int8 and decompression kernels
+  int32_t n_seg;
+  int64_t n_out_chunks;
+  const int64_t* seg_off;
+  const int64_t* out_off;
+  const int32_t* out_chunk_seg;    // [n_out_chunks]
+  const int64_t* out_chunk_base;   // [n_seg + 1]
+};
+
+// Launchers (gc_kernels.hip).  Each returns the hipError_t of its launches.
+hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
+                           float* out_vals, int32_t* out_idx, hipStream_t st,
+                           hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_reset(const DevPlan& P, hipStream_t st);
+hipError_t launch_quant(const OutPlan& O, const float* vals, const int32_t* idx, float* e,
+                        uint64_t seed, uint64_t step, int8_t* codes, float* scales,
+                        hipStream_t st);
+hipError_t launch_decompress(const OutPlan& O, const float* vals, const int8_t* codes,
+                             const float* scales, const int32_t* idx, float* dense,
+                             int accumulate, hipStream_t st);
+hipError_t launch_fill_zero(float* dense, int64_t a, int64_t b, hipStream_t st);
+hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t st);
+
+}  // namespace gc

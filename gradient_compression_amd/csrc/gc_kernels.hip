@@ -1,0 +1,1006 @@
+// gc_kernels.hip -- gfx950 kernels of the error-feedback Top-k compressor.
+//
+// Per call (one stream, no host round trip):
+//   prep        zero the per-call counters
+//   ef_capture  the streaming pass over g, e (and u): momentum, EF add, write acc into e,
+//               and capture every (acc, index) whose magnitude key reaches the segment's
+//               threshold, as one index-ordered run per tile            [HBM-bound]
+//   select_init per segment: keep the candidates if they are complete (count in [k, cap]),
+//               else list the segment for the exact full-segment path
+//   hist/find   x3  radix select of the k-th largest key, digits of 11, 11 and 9 bits,
+//               LDS histograms; candidates or, on the full path, the whole segment
+//   scatter     candidates into ascending index order (runs placed by tile)
+//   count/scan/emit  order-preserving compaction: keys above the k-th, then the ties in
+//               index order; writes (value, index) and zeroes e (and u) where kept
+//   finalize    next threshold estimate = key(0.75 * kth)
+//
+// The method is the Top-K with error feedback of "Communication Optimization > Gradient
+// Compression" (Top-K section equations); momentum correction per the "Gradient
+// Sparsification" glossary; the int8 stage per the "Gradient Compression" glossary
+// (Top-k then 8-bit) with stochastic rounding (QSGD paragraph) and one scale per layer.
+#include "gc_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace gc {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef int i4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t mag_key(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// Number of set bits of m at lanes below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// First element (tile-relative) of this lane's slot 0.
+__device__ __forceinline__ int slot_base() { return wave_id() * kWaveSpan + lane_id() * 4; }
+
+// Exclusive scan of one uint32 per thread over a block of NT threads; *total gets the sum.
+// s_tmp: __shared__ uint32_t[NT / 64].  Contains barriers: call from every thread.
+template <int NT>
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+  const int lane = lane_id(), w = wave_id();
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_tmp[w] = x;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t t = s_tmp[i];
+    before += (i < w) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+// Sum over a block of NT threads (result valid in every thread).
+template <int NT>
+__device__ uint32_t block_sum(uint32_t v, uint32_t* s_tmp) {
+  uint32_t tot;
+  block_excl_scan<NT>(v, s_tmp, &tot);
+  return tot;
+}
+
+// Ordered ranks of the flagged elements of a tile laid out as (wave, slot, lane, element).
+// bits[v] holds the 4 flags of this lane's slot v.  On return woff[v] is the number of flagged
+// elements of the tile that come before this lane's slot v; the return value is the tile's
+// total.  Element c of slot v then has rank woff[v] + popcount(bits[v] & ((1 << c) - 1)).
+// s_w: __shared__ uint32_t[kWaves].  Contains barriers: call from every thread.
+__device__ uint32_t tile_rank(const uint32_t (&bits)[kSlots], uint32_t (&woff)[kSlots],
+                              uint32_t* s_w) {
+  uint32_t any = 0;
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) any |= bits[v];
+  uint32_t run = 0;
+  if (__ballot(any != 0)) {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const uint32_t b = bits[v];
+      const uint64_t m0 = __ballot(b & 1u), m1 = __ballot(b & 2u);
+      const uint64_t m2 = __ballot(b & 4u), m3 = __ballot(b & 8u);
+      woff[v] = run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+      run += __popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) woff[v] = 0;
+  }
+  if (lane_id() == 0) s_w[wave_id()] = run;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const uint32_t x = s_w[i];
+    before += (i < wave_id()) ? x : 0u;
+    total += x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) woff[v] += before;
+  return total;
+}
+
+// Load the len (<= kTile) elements at base into the tile layout; lanes past len get 0.
+// The vector path needs base 16-byte aligned and a whole tile.
+template <typename V, typename S>
+__device__ __forceinline__ void load_tile(const S* __restrict__ base, int len, V (&x)[kSlots]) {
+  const int pb = slot_base();
+  if (len == kTile && ((reinterpret_cast<uintptr_t>(base) & 15) == 0)) {
+    const V* b4 = reinterpret_cast<const V*>(base);
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) x[v] = b4[(pb + v * 256) >> 2];
+  } else {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = pb + v * 256 + c;
+        x[v][c] = p < len ? base[p] : S(0);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------ prep
+__global__ __launch_bounds__(kThreads) void k_prep(DevPlan P) {
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  if (s < P.n_seg) P.cand_cnt[s] = 0;
+  if (s == 0) {
+    *P.full_count = 0;
+    *P.recap_count = 0;
+    *P.err = 0;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_reset(DevPlan P) {
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  if (s < P.n_seg) P.thr[s] = P.thr_init[s];
+}
+
+// Tile t of segment s: first element and length.
+__device__ __forceinline__ void tile_range(const DevPlan& P, int s, int64_t t, int64_t* start,
+                                           int* len) {
+  const int64_t st = P.seg_off[s] + (t - P.tile_base[s]) * (int64_t)kTile;
+  const int64_t rem = P.seg_off[s + 1] - st;
+  *start = st;
+  *len = rem < kTile ? (int)rem : kTile;
+}
+
+// Capture, in index order, the elements of tile t (values acc in the tile layout) whose key
+// reaches thr: one atomic on the segment's counter reserves the tile's run; entries past the
+// capacity are counted but not stored (the segment then leaves the candidate path).
+__device__ __forceinline__ void capture_tile(const DevPlan& P, int s, int64_t t, int64_t start,
+                                             int len, const f4 (&acc)[kSlots], uint32_t thr,
+                                             uint32_t* s_w, uint32_t* s_base) {
+  const int pb = slot_base();
+  uint32_t bits[kSlots];
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    uint32_t b = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      b |= (pb + v * 256 + c < len && mag_key(acc[v][c]) >= thr) ? (1u << c) : 0u;
+    bits[v] = b;
+  }
+  uint32_t woff[kSlots];
+  const uint32_t total = tile_rank(bits, woff, s_w);
+  if (threadIdx.x == 0) {
+    const uint32_t base = total ? atomicAdd(&P.cand_cnt[s], total) : 0u;
+    P.run_off[t] = base;
+    P.run_cnt[t] = total;
+    *s_base = base;
+  }
+  __syncthreads();
+  if (total == 0) return;
+  const uint32_t base = *s_base, cap = P.cand_cap[s];
+  float* cv = P.cand_val + P.cand_base[s];
+  int32_t* ci = P.cand_idx + P.cand_base[s];
+  const int32_t lbase = (int32_t)(start - P.seg_off[s]) + pb;
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    const uint32_t b = bits[v];
+    if (!b) continue;
+    uint32_t q = base + woff[v];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if ((b >> c) & 1u) {
+        if (q < cap) {
+          cv[q] = acc[v][c];
+          ci[q] = lbase + v * 256 + c;
+        }
+        ++q;
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------------------- ef_capture
+// One tile per workgroup.  acc = e + (u = m*u + g | g) is written back into e; elements
+// whose key reaches the segment's threshold are captured (capture_tile).
+template <bool kMomentum>
+__global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float* __restrict__ g,
+                                                        float* __restrict__ e,
+                                                        float* __restrict__ u, float m) {
+  __shared__ uint32_t s_w[kWaves];
+  __shared__ uint32_t s_base;
+  const int64_t t = blockIdx.x;
+  const int s = P.tile_seg[t];
+  int64_t start;
+  int len;
+  tile_range(P, s, t, &start, &len);
+  const uint32_t thr = P.thr[s];
+  const int pb = slot_base();
+
+  f4 acc[kSlots];
+  if (len == kTile && (start & 3) == 0) {
+    const f4* g4 = reinterpret_cast<const f4*>(g + start);
+    f4* e4 = reinterpret_cast<f4*>(e + start);
+    f4* u4 = kMomentum ? reinterpret_cast<f4*>(u + start) : nullptr;
+    f4 gv[kSlots], uv[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      gv[v] = __builtin_nontemporal_load(g4 + q);
+      acc[v] = e4[q];
+      if (kMomentum) uv[v] = u4[q];
+    }
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      f4 x = gv[v];
+      if (kMomentum) {
+        const f4 mu = m * uv[v];
+        x = mu + x;
+        u4[q] = x;
+      }
+      acc[v] = acc[v] + x;
+      e4[q] = acc[v];
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = pb + v * 256 + c;
+        float a = 0.0f;
+        if (p < len) {
+          const int64_t i = start + p;
+          float x = g[i];
+          if (kMomentum) {
+            const float mu = m * u[i];
+            x = mu + x;
+            u[i] = x;
+          }
+          a = e[i] + x;
+          e[i] = a;
+        }
+        acc[v][c] = a;
+      }
+  }
+  if (thr == kNoCapture) return;  // uniform: this segment re-captures later
+  capture_tile(P, s, t, start, len, acc, thr, s_w, &s_base);
+}
+
+// ------------------------------------------------------------------------- select_init
+// Per segment: are the captured candidates complete?  Complete means at least k of them
+// and none lost to the capacity; then every key >= the k-th largest was captured.
+__global__ __launch_bounds__(kThreads) void k_select_init(DevPlan P) {
+  const int s = blockIdx.x;
+  const uint32_t k = P.k[s], thr = P.thr[s], c = P.cand_cnt[s], cap = P.cand_cap[s];
+  uint32_t mode, why = kWhyNone;
+  if (k == 0) {
+    mode = kModeSkip;
+  } else if (thr != kNoCapture && c >= k && c <= cap) {
+    mode = kModeCand;
+  } else {
+    mode = kModePending;
+    why = thr == kNoCapture ? kWhyCold : (c < k ? kWhyMiss : kWhyOverflow);
+  }
+  if (threadIdx.x == 0) {
+    P.mode[s] = mode;
+    P.why[s] = why;
+    P.prefix[s] = 0;
+    P.kk[s] = k;
+    P.kth[s] = 0;
+    P.ties[s] = 0;
+    if (mode == kModePending) P.recap_list[atomicAdd(P.recap_count, 1u)] = (uint32_t)s;
+  }
+  if (mode == kModeSkip) return;
+  uint32_t* h = P.hist + (size_t)s * 3 * kHistBins;
+  for (int i = threadIdx.x; i < 3 * kHistBins; i += kThreads) h[i] = 0;
+}
+
+__device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 9 : 0); }
+__device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 0x1FFu : 0x7FFu; }
+__device__ __forceinline__ uint32_t prefix_mask(int pass) {
+  return pass == 0 ? 0u : (pass == 1 ? 0x7FF00000u : 0x7FFFFE00u);
+}
+
+// Add the keys of one tile-shaped block of values into the LDS histogram.
+__device__ __forceinline__ void hist_add(uint32_t* h, const f4 (&x)[kSlots], int len,
+                                         uint32_t prefix, int pass) {
+  const int pb = slot_base(), sh = digit_shift(pass);
+  const uint32_t pm = prefix_mask(pass), dm = digit_mask(pass);
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t key = mag_key(x[v][c]);
+      if (pb + v * 256 + c < len && (key & pm) == prefix) atomicAdd(&h[(key >> sh) & dm], 1u);
+    }
+}
+
+__device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* gh) {
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) {
+    const uint32_t n = h[i];
+    if (n) atomicAdd(&gh[i], n);
+  }
+}
+
+// Histogram of one digit over every tile of the listed segments (values read from e).
+__device__ void hist_listed_tiles(const DevPlan& P, const float* __restrict__ e,
+                                  const uint32_t* list, uint32_t count, uint32_t want_mode,
+                                  int pass, int fb, uint32_t* h) {
+  for (uint32_t li = 0; li < count; ++li) {
+    const int s = (int)list[li];
+    if (P.mode[s] != want_mode) continue;
+    const uint32_t prefix = P.prefix[s];
+    uint32_t* gh = P.hist + ((size_t)s * 3 + pass) * kHistBins;
+    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
+      int64_t start;
+      int len;
+      tile_range(P, s, t, &start, &len);
+      for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+      f4 x[kSlots];
+      load_tile(e + start, len, x);
+      __syncthreads();
+      hist_add(h, x, len, prefix, pass);
+      __syncthreads();
+      hist_flush(h, gh);
+      __syncthreads();
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- recapture
+// First-digit histogram of the segments whose candidates were not complete.
+__global__ __launch_bounds__(kThreads) void k_recap_hist(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t h[kHistBins];
+  hist_listed_tiles(P, e, P.recap_list, *P.recap_count, kModePending, 0, blockIdx.x, h);
+}
+
+// Digit of the k-th largest key in a histogram (descending scan): d and the count above it.
+// s_tmp: __shared__ uint32_t[kWaves]; s_out: __shared__ uint32_t[2].  Contains barriers.
+__device__ bool find_digit(const uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
+                           uint32_t* d_out, uint32_t* above_out, uint32_t* bin_out) {
+  constexpr int kPer = kHistBins / kThreads;
+  uint32_t loc[kPer];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    loc[j] = gh[kHistBins - 1 - (threadIdx.x * kPer + j)];
+    sum += loc[j];
+  }
+  if (threadIdx.x == 0) {
+    s_out[0] = 0xFFFFFFFFu;
+    s_out[1] = 0;
+    s_out[2] = 0;
+  }
+  uint32_t tot;
+  uint32_t acc = block_excl_scan<kThreads>(sum, s_tmp, &tot);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (acc < kk && acc + loc[j] >= kk) {
+      s_out[0] = kHistBins - 1 - (threadIdx.x * kPer + j);
+      s_out[1] = acc;
+      s_out[2] = loc[j];
+    }
+    acc += loc[j];
+  }
+  __syncthreads();
+  *d_out = s_out[0];
+  *above_out = s_out[1];
+  *bin_out = s_out[2];
+  return s_out[0] != 0xFFFFFFFFu;
+}
+
+// Per pending segment: the first digit of the k-th largest key.  If the keys at or above
+// that bucket's floor fit the capacity, they are re-captured (kModeRecap); otherwise the
+// segment runs the radix select over all its elements (kModeFull).  Pass 0 is done here.
+__global__ __launch_bounds__(kThreads) void k_recap_decide(DevPlan P) {
+  __shared__ uint32_t s_tmp[kWaves];
+  __shared__ uint32_t s_out[3];
+  const int s = blockIdx.x;
+  if (P.mode[s] != kModePending) return;
+  const uint32_t k = P.k[s];
+  uint32_t d, above, bin;
+  const bool ok = find_digit(P.hist + (size_t)s * 3 * kHistBins, k, s_tmp, s_out, &d, &above,
+                             &bin);
+  if (threadIdx.x != 0) return;
+  if (!ok) {
+    atomicOr(P.err, 1u);
+    P.mode[s] = kModeSkip;
+    return;
+  }
+  P.prefix[s] = d << 20;
+  P.kk[s] = k - above;
+  if (!(P.flags & kFlagForceFull) && above + bin <= P.cand_cap[s]) {
+    P.mode[s] = kModeRecap;
+    P.thr[s] = d << 20;
+    P.cand_cnt[s] = 0;
+  } else {
+    P.mode[s] = kModeFull;
+    P.full_list[atomicAdd(P.full_count, 1u)] = (uint32_t)s;
+  }
+}
+
+// Re-capture from e (which holds acc) at the exact bucket floor.
+__global__ __launch_bounds__(kThreads) void k_recapture(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t s_w[kWaves];
+  __shared__ uint32_t s_base;
+  const uint32_t count = *P.recap_count;
+  for (uint32_t li = 0; li < count; ++li) {
+    const int s = (int)P.recap_list[li];
+    if (P.mode[s] != kModeRecap) continue;
+    const uint32_t thr = P.thr[s];
+    for (int64_t t = P.tile_base[s] + blockIdx.x; t < P.tile_base[s + 1]; t += kFullBlocks) {
+      int64_t start;
+      int len;
+      tile_range(P, s, t, &start, &len);
+      f4 x[kSlots];
+      load_tile(e + start, len, x);
+      capture_tile(P, s, t, start, len, x, thr, s_w, &s_base);
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ bool has_candidates(uint32_t mode) {
+  return mode == kModeCand || mode == kModeRecap;
+}
+
+// Per segment with candidates: index-ordered destination of every tile's run (exclusive
+// scan of the run sizes over the segment's tiles).
+__global__ __launch_bounds__(1024) void k_runs(DevPlan P) {
+  __shared__ uint32_t s_tmp[16];
+  const int s = blockIdx.x;
+  if (!has_candidates(P.mode[s])) return;
+  const int64_t t0 = P.tile_base[s], t1 = P.tile_base[s + 1];
+  uint32_t carry = 0;
+  for (int64_t tb = t0; tb < t1; tb += 1024) {
+    const int64_t t = tb + threadIdx.x;
+    const uint32_t n = t < t1 ? P.run_cnt[t] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<1024>(n, s_tmp, &tot);
+    if (t < t1) P.run_dst[t] = carry + ex;
+    carry += tot;
+  }
+}
+
+// ------------------------------------------------------------------------------ scatter
+// Candidates into ascending index order (tile t's run goes to run_dst[t]); on the estimate
+// path, also the first-digit histogram of the candidates.
+__global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
+  __shared__ uint32_t h[kHistBins];
+  const int64_t ch = blockIdx.x;
+  const int s = P.chunk_seg[ch];
+  const uint32_t mode = P.mode[s];
+  if (!has_candidates(mode)) return;
+  const int64_t c = P.cand_cnt[s];
+  const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+  if (j0 >= c) return;
+  const bool do_hist = mode == kModeCand;
+  if (do_hist)
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+  const int len = (int)min((int64_t)kChunk, c - j0);
+  const int64_t cb = P.cand_base[s], tb = P.tile_base[s];
+  constexpr int kPer = kChunk / kThreads;
+  int32_t ix[kPer];
+  float vx[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int p = r * kThreads + threadIdx.x;
+    ix[r] = p < len ? P.cand_idx[cb + j0 + p] : 0;
+    vx[r] = p < len ? P.cand_val[cb + j0 + p] : 0.0f;
+  }
+  if (do_hist) __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int p = r * kThreads + threadIdx.x;
+    if (p < len) {
+      const int64_t t = tb + ix[r] / kTile;
+      const uint32_t dst = P.run_dst[t] + ((uint32_t)(j0 + p) - P.run_off[t]);
+      if (ix[r] >= 0 && t < P.tile_base[s + 1] && dst < (uint32_t)c) {
+        P.sort_val[cb + dst] = vx[r];
+        P.sort_idx[cb + dst] = ix[r];
+      } else {
+        atomicOr(P.err, 8u);
+      }
+      if (do_hist) atomicAdd(&h[mag_key(vx[r]) >> 20], 1u);
+    }
+  }
+  if (do_hist) {
+    __syncthreads();
+    hist_flush(h, P.hist + (size_t)s * 3 * kHistBins);
+  }
+}
+
+// --------------------------------------------------------------------------------- hist
+// Passes 1 and 2.  Workgroups [0, n_chunks) histogram sorted candidate chunks; the last
+// kFullBlocks histogram the tiles of the segments on the full path.
+__global__ __launch_bounds__(kThreads) void k_hist(DevPlan P, const float* __restrict__ e,
+                                                   int pass) {
+  __shared__ uint32_t h[kHistBins];
+  if (blockIdx.x < P.n_chunks) {
+    const int64_t ch = blockIdx.x;
+    const int s = P.chunk_seg[ch];
+    if (!has_candidates(P.mode[s])) return;
+    const int64_t c = P.cand_cnt[s];
+    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+    if (j0 >= c) return;
+    const int len = (int)min((int64_t)kChunk, c - j0);
+    const uint32_t prefix = P.prefix[s];
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+    f4 x[kSlots];
+    load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
+    __syncthreads();
+    hist_add(h, x, len, prefix, pass);
+    __syncthreads();
+    hist_flush(h, P.hist + ((size_t)s * 3 + pass) * kHistBins);
+    return;
+  }
+  hist_listed_tiles(P, e, P.full_list, *P.full_count, kModeFull, pass,
+                    blockIdx.x - (int)P.n_chunks, h);
+}
+
+// --------------------------------------------------------------------------------- find
+// Per segment: the digit of this pass that holds the kk-th largest key of the prefix.
+// Pass 0 only for the estimate path (the others took it in k_recap_decide).
+__global__ __launch_bounds__(kThreads) void k_find(DevPlan P, int pass) {
+  __shared__ uint32_t s_tmp[kWaves];
+  __shared__ uint32_t s_out[3];
+  const int s = blockIdx.x;
+  const uint32_t mode = P.mode[s];
+  if (mode == kModeSkip || (pass == 0 && mode != kModeCand)) return;
+  const uint32_t kk = P.kk[s];
+  uint32_t d, above, bin;
+  const bool ok = find_digit(P.hist + ((size_t)s * 3 + pass) * kHistBins, kk, s_tmp, s_out, &d,
+                             &above, &bin);
+  if (threadIdx.x != 0) return;
+  if (!ok) {  // cannot happen when the histogram holds >= kk keys
+    atomicOr(P.err, 1u);
+    return;
+  }
+  const uint32_t prefix = P.prefix[s] | (d << digit_shift(pass));
+  const uint32_t nk = kk - above;
+  P.prefix[s] = prefix;
+  P.kk[s] = nk;
+  if (pass == 2) {
+    P.kth[s] = prefix;
+    P.ties[s] = nk;
+  }
+}
+
+// -------------------------------------------------------------------------------- count
+// Keys above and equal to the k-th, per candidate chunk (sorted) or per full-path tile.
+__device__ __forceinline__ void count_block(const f4 (&x)[kSlots], int len, uint32_t kth,
+                                            uint32_t* s_tmp, uint32_t* gt_out,
+                                            uint32_t* eq_out) {
+  const int pb = slot_base();
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t key = mag_key(x[v][c]);
+      const bool ok = pb + v * 256 + c < len;
+      gt += (ok && key > kth) ? 1u : 0u;
+      eq += (ok && key == kth) ? 1u : 0u;
+    }
+  const uint32_t tg = block_sum<kThreads>(gt, s_tmp);
+  const uint32_t te = block_sum<kThreads>(eq, s_tmp);
+  if (threadIdx.x == 0) {
+    *gt_out = tg;
+    *eq_out = te;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_count(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t s_tmp[kWaves];
+  if (blockIdx.x < P.n_chunks) {
+    const int64_t ch = blockIdx.x;
+    const int s = P.chunk_seg[ch];
+    if (!has_candidates(P.mode[s])) return;
+    const int64_t c = P.cand_cnt[s];
+    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+    if (j0 >= c) return;
+    const int len = (int)min((int64_t)kChunk, c - j0);
+    f4 x[kSlots];
+    load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
+    count_block(x, len, P.kth[s], s_tmp, &P.chunk_gt[ch], &P.chunk_eq[ch]);
+    return;
+  }
+  const int fb = blockIdx.x - (int)P.n_chunks;
+  const uint32_t nf = *P.full_count;
+  for (uint32_t li = 0; li < nf; ++li) {
+    const int s = (int)P.full_list[li];
+    const uint32_t kth = P.kth[s];
+    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
+      int64_t start;
+      int len;
+      tile_range(P, s, t, &start, &len);
+      f4 x[kSlots];
+      load_tile(e + start, len, x);
+      count_block(x, len, kth, s_tmp, &P.tile_gt[t], &P.tile_eq[t]);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------- scan
+// Per segment, over its chunks (candidates) or tiles (full path) in index order: ties
+// before each item, then kept entries before each item (ties taken: the first `ties`).
+__global__ __launch_bounds__(1024) void k_scan(DevPlan P) {
+  __shared__ uint32_t s_tmp[16];
+  const int s = blockIdx.x;
+  const uint32_t mode = P.mode[s];
+  if (mode == kModeSkip) return;
+  const uint32_t r = P.ties[s];
+  int64_t base, n;
+  const uint32_t *GT, *EQ;
+  uint32_t *EQB, *SELB;
+  if (has_candidates(mode)) {
+    base = P.chunk_base[s];
+    n = ((int64_t)P.cand_cnt[s] + kChunk - 1) / kChunk;
+    GT = P.chunk_gt; EQ = P.chunk_eq; EQB = P.chunk_eq_base; SELB = P.chunk_sel_base;
+  } else {
+    base = P.tile_base[s];
+    n = P.tile_base[s + 1] - base;
+    GT = P.tile_gt; EQ = P.tile_eq; EQB = P.tile_eq_base; SELB = P.tile_sel_base;
+  }
+  uint32_t carry_eq = 0, carry_sel = 0;
+  for (int64_t ib = 0; ib < n; ib += 1024) {
+    const int64_t i = ib + threadIdx.x;
+    const bool ok = i < n;
+    const uint32_t gt = ok ? GT[base + i] : 0u, eq = ok ? EQ[base + i] : 0u;
+    uint32_t tot_eq, tot_sel;
+    const uint32_t eqb = carry_eq + block_excl_scan<1024>(eq, s_tmp, &tot_eq);
+    const uint32_t take = eqb < r ? min(eq, r - eqb) : 0u;
+    const uint32_t selb = carry_sel + block_excl_scan<1024>(gt + take, s_tmp, &tot_sel);
+    if (ok) {
+      EQB[base + i] = eqb;
+      SELB[base + i] = selb;
+    }
+    carry_eq += tot_eq;
+    carry_sel += tot_sel;
+  }
+  if (threadIdx.x == 0 && carry_sel != P.k[s]) atomicOr(P.err, 2u);
+}
+
+// --------------------------------------------------------------------------------- emit
+// Ordered compaction of one tile-shaped block whose element p has value x and segment-local
+// index lidx(p): keep key > kth, and key == kth while the tie rank stays below r.
+template <typename IdxOf>
+__device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, IdxOf lidx,
+                                           uint32_t kth, uint32_t r, uint32_t eq_base,
+                                           int64_t out_pos, int64_t out_end, int64_t s0,
+                                           int32_t n_s, uint32_t* s_w, uint32_t* err,
+                                           float* __restrict__ e, float* __restrict__ u,
+                                           float* __restrict__ out_vals,
+                                           int32_t* __restrict__ out_idx) {
+  const int pb = slot_base();
+  uint32_t eqb[kSlots], gtb[kSlots], woff[kSlots];
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    uint32_t be = 0, bg = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t key = mag_key(x[v][c]);
+      const bool ok = pb + v * 256 + c < len;
+      be |= (ok && key == kth) ? (1u << c) : 0u;
+      bg |= (ok && key > kth) ? (1u << c) : 0u;
+    }
+    eqb[v] = be;
+    gtb[v] = bg;
+  }
+  tile_rank(eqb, woff, s_w);
+  uint32_t selb[kSlots];
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    uint32_t b = gtb[v];
+    uint32_t q = eq_base + woff[v];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((eqb[v] >> c) & 1u) {
+        b |= (q < r) ? (1u << c) : 0u;
+        ++q;
+      }
+    selb[v] = b;
+  }
+  tile_rank(selb, woff, s_w);
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    const uint32_t b = selb[v];
+    if (!b) continue;
+    int64_t q = out_pos + woff[v];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((b >> c) & 1u) {
+        const int32_t li = lidx(v, c);
+        if (q < out_end && li >= 0 && li < n_s) {
+          out_vals[q] = x[v][c];
+          out_idx[q] = li;
+          e[s0 + li] = 0.0f;
+          if (u) u[s0 + li] = 0.0f;
+        } else {
+          atomicOr(err, 4u);  // a rank outside the segment's output: never expected
+        }
+        ++q;
+      }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, float* __restrict__ e,
+                                                   float* __restrict__ u_mask,
+                                                   float* __restrict__ out_vals,
+                                                   int32_t* __restrict__ out_idx) {
+  __shared__ uint32_t s_w[kWaves];
+  if (blockIdx.x < P.n_chunks) {
+    const int64_t ch = blockIdx.x;
+    const int s = P.chunk_seg[ch];
+    if (!has_candidates(P.mode[s])) return;
+    const int64_t c = P.cand_cnt[s];
+    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+    if (j0 >= c) return;
+    const int len = (int)min((int64_t)kChunk, c - j0);
+    f4 x[kSlots];
+    i4 ix[kSlots];
+    load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
+    load_tile(P.sort_idx + P.cand_base[s] + j0, len, ix);
+    emit_block(x, len, [&](int v, int cc) { return (int32_t)ix[v][cc]; }, P.kth[s], P.ties[s],
+               P.chunk_eq_base[ch], P.out_off[s] + P.chunk_sel_base[ch], P.out_off[s + 1],
+               P.seg_off[s], (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, P.err, e, u_mask,
+               out_vals, out_idx);
+    return;
+  }
+  const int fb = blockIdx.x - (int)P.n_chunks;
+  const uint32_t nf = *P.full_count;
+  for (uint32_t li = 0; li < nf; ++li) {
+    const int s = (int)P.full_list[li];
+    const uint32_t kth = P.kth[s], r = P.ties[s];
+    const int64_t s0 = P.seg_off[s];
+    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
+      int64_t start;
+      int len;
+      tile_range(P, s, t, &start, &len);
+      f4 x[kSlots];
+      load_tile(e + start, len, x);
+      const int32_t lb = (int32_t)(start - s0) + slot_base();
+      emit_block(x, len, [&](int v, int cc) { return lb + v * 256 + cc; }, kth, r,
+                 P.tile_eq_base[t], P.out_off[s] + P.tile_sel_base[t], P.out_off[s + 1], s0,
+                 (int32_t)(P.seg_off[s + 1] - s0), s_w, P.err, e, u_mask, out_vals, out_idx);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- finalize
+// Threshold for the next call: beta * |kth|, where the margin beta follows the last calls:
+// lowered after too few candidates, raised after an overflow or far more than needed.
+// Segments that capture everything (small) or nothing (k = 0) keep their setting.
+__global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  if (s >= P.n_seg) return;
+  const uint32_t init = P.thr_init[s], mode = P.mode[s];
+  uint32_t next = init;
+  if (init == kNoCapture && mode != kModeSkip && !(P.flags & (kFlagForceFull | kFlagNoEstimate))) {
+    float b = P.beta[s];
+    const uint32_t why = P.why[s];
+    if (why == kWhyMiss) {
+      b = fmaxf(b * 0.85f, 0.25f);
+    } else if (why == kWhyOverflow) {
+      b = fminf(b * 1.05f, 0.98f);
+    } else if (mode == kModeCand) {
+      const float rho = (float)P.cand_cnt[s] / (float)P.k[s];
+      if (rho > 4.0f) b = fminf(b * 1.03f, 0.98f);
+      else if (rho < 1.5f) b = fmaxf(b * 0.97f, 0.25f);
+    }
+    P.beta[s] = b;
+    next = mag_key(b * __uint_as_float(P.kth[s]));
+  }
+  P.thr[s] = next;
+}
+
+// ------------------------------------------------------------------------------ int8 stage
+// Philox4x32-10 (Salmon et al., SC'11), word 0 of the output block.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t a = 0xD2511F53u, b = 0xCD9E8D57u;
+    const uint32_t hi0 = __umulhi(a, c0), lo0 = a * c0;
+    const uint32_t hi1 = __umulhi(b, c2), lo1 = b * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+// Per segment: scale = fl(max |v| / 127) over the kept values.
+__global__ __launch_bounds__(1024) void k_absmax(OutPlan O, const float* __restrict__ vals,
+                                                 float* __restrict__ scales) {
+  __shared__ uint32_t s_m[16];
+  const int s = blockIdx.x;
+  const int64_t a = O.out_off[s], b = O.out_off[s + 1];
+  uint32_t mx = 0;
+  for (int64_t j = a + threadIdx.x; j < b; j += 1024) mx = max(mx, mag_key(vals[j]));
+  for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, d, 64));
+  if (lane_id() == 0) s_m[wave_id()] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int i = 0; i < 16; ++i) m = max(m, s_m[i]);
+    scales[s] = __uint_as_float(m) / 127.0f;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant(OutPlan O, const float* __restrict__ vals,
+                                                    const int32_t* __restrict__ idx,
+                                                    float* __restrict__ e, uint32_t seed_lo,
+                                                    uint32_t seed_hi, uint32_t step_lo,
+                                                    int8_t* __restrict__ codes,
+                                                    const float* __restrict__ scales) {
+  const int64_t ch = blockIdx.x;
+  const int s = O.out_chunk_seg[ch];
+  const int64_t j0 = O.out_off[s] + (ch - O.out_chunk_base[s]) * (int64_t)kOutChunk;
+  const int64_t j1 = min(j0 + kOutChunk, O.out_off[s + 1]);
+  const float scale = scales[s];
+  const int64_t s0 = O.seg_off[s], n_s = O.seg_off[s + 1] - s0;
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += kThreads) {
+    const float v = vals[j];
+    const int32_t li = idx[j];
+    const int64_t gi = s0 + li;
+    int q = 0;
+    if (scale != 0.0f) {
+      float a = fabsf(v) / scale;
+      if (a > 127.0f) a = 127.0f;
+      const float f = floorf(a);
+      const float frac = a - f;
+      const uint32_t u24 = philox_word0((uint32_t)gi, (uint32_t)((uint64_t)gi >> 32), step_lo,
+                                        0x51u, seed_lo, seed_hi) >> 8;
+      q = (int)f + (((float)u24 < frac * 16777216.0f) ? 1 : 0);
+    }
+    const int code = signbit(v) ? -q : q;
+    codes[j] = (int8_t)code;
+    if (e && li >= 0 && li < n_s) {  // indices come from the compress call
+      const float deq = (float)code * scale;
+      e[gi] = v - deq;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- decompress
+__global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ d, int64_t a,
+                                                        int64_t b) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = a + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < b; i += stride)
+    d[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scatter_out(OutPlan O,
+                                                          const float* __restrict__ vals,
+                                                          const int8_t* __restrict__ codes,
+                                                          const float* __restrict__ scales,
+                                                          const int32_t* __restrict__ idx,
+                                                          float* __restrict__ dense,
+                                                          int accumulate) {
+  const int64_t ch = blockIdx.x;
+  const int s = O.out_chunk_seg[ch];
+  const int64_t j0 = O.out_off[s] + (ch - O.out_chunk_base[s]) * (int64_t)kOutChunk;
+  const int64_t j1 = min(j0 + kOutChunk, O.out_off[s + 1]);
+  const int64_t s0 = O.seg_off[s], n_s = O.seg_off[s + 1] - s0;
+  const float scale = vals ? 0.0f : scales[s];
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += kThreads) {
+    const float v = vals ? vals[j] : (float)codes[j] * scale;
+    const int32_t li = idx[j];
+    if (li < 0 || li >= n_s) continue;  // indices come from the compress call
+    float* d = dense + s0 + li;
+    *d = accumulate ? *d + v : v;
+  }
+}
+
+// --------------------------------------------------------------------------------- copy
+__global__ __launch_bounds__(kThreads) void k_copy(const f4* __restrict__ src,
+                                                   f4* __restrict__ dst, int64_t n4) {
+  const int64_t block = (int64_t)blockIdx.x * (kThreads * kSlots);
+  const int64_t base = block + threadIdx.x;
+  f4 x[kSlots];
+  if (block + kThreads * kSlots <= n4) {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) x[v] = __builtin_nontemporal_load(src + base + v * kThreads);
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) dst[base + v * kThreads] = x[v];
+    return;
+  }
+  for (int v = 0; v < kSlots; ++v) {
+    const int64_t i = base + v * kThreads;
+    if (i < n4) dst[i] = src[i];
+  }
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
+                           float* out_vals, int32_t* out_idx, hipStream_t st,
+                           hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (P.n_seg == 0) return hipSuccess;
+  k_prep<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
+  if (ev_begin) (void)hipEventRecord(ev_begin, st);
+  if (P.n_tiles > 0) {
+    if (u)
+      k_ef_capture<true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, u, m);
+    else
+      k_ef_capture<false><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, nullptr, m);
+  }
+  if (ev_end) (void)hipEventRecord(ev_end, st);
+  k_select_init<<<P.n_seg, kThreads, 0, st>>>(P);
+  k_recap_hist<<<kFullBlocks, kThreads, 0, st>>>(P, e);
+  k_recap_decide<<<P.n_seg, kThreads, 0, st>>>(P);
+  k_recapture<<<kFullBlocks, kThreads, 0, st>>>(P, e);
+  k_runs<<<P.n_seg, 1024, 0, st>>>(P);
+  if (P.n_chunks > 0) k_scatter<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
+  k_find<<<P.n_seg, kThreads, 0, st>>>(P, 0);
+  const unsigned mixed = (unsigned)(P.n_chunks + kFullBlocks);
+  for (int pass = 1; pass < 3; ++pass) {
+    k_hist<<<mixed, kThreads, 0, st>>>(P, e, pass);
+    k_find<<<P.n_seg, kThreads, 0, st>>>(P, pass);
+  }
+  k_count<<<mixed, kThreads, 0, st>>>(P, e);
+  k_scan<<<P.n_seg, 1024, 0, st>>>(P);
+  float* u_mask = (u && (P.flags & kFlagMomentumMask)) ? u : nullptr;
+  k_emit<<<mixed, kThreads, 0, st>>>(P, e, u_mask, out_vals, out_idx);
+  k_finalize<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(const DevPlan& P, hipStream_t st) {
+  if (P.n_seg == 0) return hipSuccess;
+  k_reset<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(const OutPlan& O, const float* vals, const int32_t* idx, float* e,
+                        uint64_t seed, uint64_t step, int8_t* codes, float* scales,
+                        hipStream_t st) {
+  if (O.n_seg == 0) return hipSuccess;
+  k_absmax<<<O.n_seg, 1024, 0, st>>>(O, vals, scales);
+  if (O.n_out_chunks > 0)
+    k_quant<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(
+        O, vals, idx, e, (uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)step, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_decompress(const OutPlan& O, const float* vals, const int8_t* codes,
+                             const float* scales, const int32_t* idx, float* dense,
+                             int accumulate, hipStream_t st) {
+  if (O.n_seg == 0) return hipSuccess;
+  if (O.n_out_chunks > 0)
+    k_scatter_out<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(O, vals, codes, scales, idx,
+                                                                 dense, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* dense, int64_t a, int64_t b, hipStream_t st) {
+  if (b <= a) return hipSuccess;
+  const int64_t want = (b - a + kThreads - 1) / kThreads;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  k_fill_zero<<<blocks, kThreads, 0, st>>>(dense, a, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  k_copy<<<blocks_for(n4, kThreads * kSlots), kThreads, 0, st>>>(
+      reinterpret_cast<const f4*>(src), reinterpret_cast<f4*>(dst), n4);
+  return hipGetLastError();
+}
+
+}  // namespace gc

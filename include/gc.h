@@ -1,0 +1,170 @@
+/*
+ * gc.h -- C ABI of the MI355X (gfx950) error-feedback Top-k gradient compressor.
+ *
+ * The operation, per segment (one parameter tensor) of a worker's flat fp32 gradient,
+ * is the error-feedback Top-k step of "Communication Optimization > Gradient Compression"
+ * (Top-K section, the two displayed equations):
+ *     acc = g + e_prev          (e_prev: the local residual of everything not yet sent)
+ *     g^  = TopK(acc)           (keep the k entries of largest |acc|, zero the rest)
+ *     e   = acc - g^            (the dropped mass stays local for the next step)
+ * with optional momentum correction first ("Gradient Sparsification" glossary, momentum
+ * sections: the velocity is updated with the dense local gradient before sparsification):
+ *     u = m*u + g ;  acc = e_prev + u
+ * The kept entries travel as an fp32 value plus a 32-bit index each (Top-K section,
+ * wire-format paragraph), optionally quantised to int8 with one scale per segment
+ * ("Gradient Compression" glossary: Top-k then 8-bit; "Communication Optimization >
+ * Gradient Compression": layer-wise scaling, stochastic rounding that keeps E[Q(x)] = x).
+ *
+ * Exact semantics (the results are unique and bit-exact):
+ *   - every fp32 operation is one IEEE binary32 operation, round to nearest even, no fused
+ *     multiply-add, denormals kept: u = fl(fl(m*u) + g), acc = fl(e + x);
+ *   - |acc| is ordered through the key bits(acc) & 0x7FFFFFFF (so -0 ties +0); among equal
+ *     magnitudes the lower index is kept first;
+ *   - the kept entries of a segment are written in ascending segment-local index order;
+ *   - the residual is +0.0 at a kept position and acc elsewhere.
+ *   - NaN inputs are outside the contract.
+ *
+ * All pointers are device pointers unless marked "host".  Calls are asynchronous on
+ * `stream` (a hipStream_t; NULL = the default stream): arguments are checked on the host
+ * before anything is launched, and errors of the launched work surface at the caller's
+ * next synchronisation.  No call allocates device memory except gc_plan_create.  A plan
+ * serves one stream at a time; calls on one plan must not overlap.  No exception crosses
+ * this interface; every function returns a gc_status (0 = success).
+ */
+#ifndef GC_H
+#define GC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GC_OK = 0,
+    GC_ERR_INVALID_ARG = -1,   /* a bad argument; nothing was launched */
+    GC_ERR_OOM = -2,           /* device memory for the plan could not be allocated */
+    GC_ERR_HIP = -3,           /* the HIP runtime reported an error (no device, launch failure) */
+    GC_ERR_UNSUPPORTED = -4    /* a valid request this build does not handle */
+} gc_status;
+
+/* Plan flags. */
+#define GC_MOMENTUM_MASK 0x1u         /* also zero the velocity u at the kept positions
+                                         (momentum factor masking, "Gradient
+                                         Sparsification" glossary, DGC section) */
+#define GC_DEBUG_FORCE_FALLBACK 0x100u /* every segment takes the exact radix select over
+                                          the whole segment (same results, slower; tests) */
+#define GC_DEBUG_NO_ESTIMATE 0x200u    /* keep no threshold between calls: every call
+                                          re-captures candidates from a histogram of the
+                                          whole segment (same results, slower; tests) */
+
+typedef struct gc_plan gc_plan;
+
+/*
+ * Build a plan for a segmented buffer and allocate its device workspace on the current
+ * device.
+ *   seg_off : host int64[n_seg + 1], non-decreasing, seg_off[0] >= 0; segment s covers
+ *             elements [seg_off[s], seg_off[s+1]) of g, e and u; each segment < 2^31 elements.
+ *   n_seg   : number of segments, >= 0.
+ *   k       : host int64[n_seg], 0 <= k[s] <= segment size; or NULL when ratio is given.
+ *   ratio   : host double[n_seg] in [0, 1]; k[s] = min(n_s, ceil(n_s * ratio[s])) computed in
+ *             exact parts-per-billion (0.1% of 2^20 gives 1049); or NULL when k is given.
+ *             Exactly one of k and ratio must be non-NULL.
+ *   flags   : GC_MOMENTUM_MASK | GC_DEBUG_FORCE_FALLBACK, or 0.
+ *   out     : receives the plan.
+ * The plan keeps a per-segment threshold estimate between calls; it only decides how much
+ * work a call does, never what it returns.
+ * Errors: GC_ERR_INVALID_ARG (any check above), GC_ERR_OOM, GC_ERR_HIP.
+ */
+int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
+                   uint32_t flags, gc_plan** out);
+
+/* Free the plan and its workspace (synchronises the device first).  NULL is accepted. */
+int gc_plan_destroy(gc_plan* plan);
+
+/* Sum of k over the segments: the length of vals, idx and codes. */
+int gc_plan_total_k(const gc_plan* plan, int64_t* total_k /* host */);
+
+/* Per-segment k (host int64[n_seg]) and the output offsets: out_off[s] is where segment s's
+ * kept entries start, out_off[n_seg] = total k (host int64[n_seg + 1]).  Either may be NULL. */
+int gc_plan_layout(const gc_plan* plan, int64_t* k /* host or NULL */,
+                   int64_t* out_off /* host or NULL */);
+
+/*
+ * The error-feedback Top-k step over every segment.
+ *   g        : float[N] fresh gradient, read only; must not alias e, u or the outputs.
+ *   e        : float[N] residual, read and rewritten in place.
+ *   u        : float[N] velocity, updated in place (u = fl(fl(momentum*u) + g)), or NULL for
+ *              plain error feedback (momentum is then ignored).
+ *   out_vals : float[total_k]; out_idx : int32[total_k] segment-local indices; segment s
+ *              writes [out_off[s], out_off[s+1]) in ascending index order.
+ * N = seg_off[n_seg]; elements outside the segments are not touched.  g, e and u must be
+ * 16-byte aligned.
+ * Errors: GC_ERR_INVALID_ARG (NULL or misaligned pointer), GC_ERR_HIP (launch failure).
+ */
+int gc_topk_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                        float* out_vals, int32_t* out_idx, void* stream);
+
+/*
+ * Quantise the kept values to int8, one scale per segment, with stochastic rounding:
+ *   scale_s = fl(absmax_s / 127) over the segment's kept values (0 when all are 0);
+ *   a = min(fl(|v| / scale_s), 127); q = floor(a) + [u24 < (a - floor(a)) * 2^24];
+ *   code = sign(v) * q  (0 when scale_s is 0)
+ * where u24 is the top 24 bits of word 0 of Philox4x32-10 (Salmon et al., SC'11) keyed by
+ * (seed low 32 bits, seed high 32 bits) at counter (global index low 32, global index high
+ * 32, step low 32, 0x51), global index = seg_off[s] + idx.
+ *   vals, idx : as written by gc_topk_ef_compress (total_k entries).
+ *   e         : float[N] residual or NULL; when given, the quantisation error is fed back:
+ *               e[seg_off[s] + idx] = fl(v - fl(code * scale_s)).
+ *   out_codes : int8[total_k]; out_scales : float[n_seg].
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_quant_int8(gc_plan* plan, const float* vals, const int32_t* idx, float* e, uint64_t seed,
+                  uint64_t step, int8_t* out_codes, float* out_scales, void* stream);
+
+/*
+ * Scatter kept entries back into a dense float[N] buffer: dense[seg_off[s] + idx] = v, with
+ * v = vals[j] when vals is given, else fl(codes[j] * scales[s]).  accumulate = 0 first sets
+ * dense to +0 over [seg_off[0], N); accumulate != 0 adds v instead of storing it.
+ * Exactly one of vals and codes must be non-NULL (scales with codes).
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_decompress(const gc_plan* plan, const float* vals, const int8_t* codes,
+                  const float* scales, const int32_t* idx, float* dense, int accumulate,
+                  void* stream);
+
+/* Forget the threshold estimates: the next compress call runs as on a fresh plan. */
+int gc_plan_reset_estimate(gc_plan* plan, void* stream);
+
+/*
+ * Diagnostics of the last compress call (synchronises `stream`).  Host arrays of n_seg, any
+ * may be NULL: mode[s] (0 = k is 0; 1 = selected among the candidates captured at the
+ * estimated threshold; 2 = exact radix select over the whole segment; 3 = candidates
+ * re-captured after a histogram of the whole segment), candidates[s] (entries captured),
+ * kth_key[s] (the k-th largest key bits(acc) & 0x7FFFFFFF), ties_taken[s] (entries kept
+ * at exactly that key).
+ */
+int gc_plan_last_stats(gc_plan* plan, uint32_t* mode, uint32_t* candidates, uint32_t* kth_key,
+                       uint32_t* ties_taken, void* stream);
+
+/*
+ * Timing of the streaming error-feedback pass: when enabled, every compress call records a
+ * HIP event pair around that kernel on its stream; gc_plan_timing returns the summed time
+ * in milliseconds and the number of launches since the last query (synchronising on the
+ * events) and resets both.
+ */
+int gc_plan_set_timing(gc_plan* plan, int enable);
+int gc_plan_timing(gc_plan* plan, double* ms /* host */, int64_t* launches /* host */);
+
+/* Reference streaming kernel for bandwidth calibration: dst[i] = src[i] for n floats with
+ * 16-byte loads and stores (n a multiple of 4, both pointers 16-byte aligned). */
+int gc_copy_f32(const float* src, float* dst, int64_t n, void* stream);
+
+/* Static text for a status code. */
+const char* gc_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GC_H */
