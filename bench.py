@@ -29,8 +29,28 @@ METRIC = "EF-Top-k compress GB/s of fp32 gradient (1 GPU) and % of HBM peak"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "c5p_llama2_7b_plain"
 # HBM bytes per launch of the streaming pass, from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
-# scaled by the same counters on the copy kernel (written by hand from profiles/)
+# scaled by the same counters on the copy kernel (see the summaries next to it)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    csrc = os.path.join(ROOT, "gradient_compression_amd", "csrc")
+    data = b"".join(open(os.path.join(csrc, f), "rb").read()
+                    for f in ("gc_kernels.hip", "gc_internal.h"))
+    return hashlib.sha256(data).hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of the streaming pass from the committed rocprofv3 counters, or
+    None when they are missing or were taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        tr = json.load(f).get(name)
+    if not tr or tr.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return tr["bytes_per_launch"]
 
 
 def log(msg):
@@ -206,11 +226,7 @@ def main():
     k1_ach = bpe * wl.n / k1_ms / 1e6
     log(f"[bench] {ms:.3f} ms/step, {value:.1f} GB/s gradient, effective {eff:.1f} GB/s "
         f"({eff / HBM_PEAK_GBPS:.1%} of peak); EF pass {k1_ms:.3f} ms ({k1_ach:.1f} GB/s)")
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f).get(wl.name)
-        traffic = tr.get("bytes_per_launch") if tr else None
+    traffic = measured_traffic(wl.name)
     result = {
         "metric": METRIC,
         "value": round(value, 2),

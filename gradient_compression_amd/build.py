@@ -35,9 +35,11 @@ def flags() -> list[str]:
             "-I", os.path.join(HERE, "csrc")]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *flags(), *SOURCES, "-o", tmp]
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile libgc.so; ``defines`` (e.g. "GC_TILE_SLOTS=4") override the compile-time
+    configuration of the streaming pass."""
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *flags(), *[f"-D{d}" for d in defines], *SOURCES, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
@@ -45,8 +47,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -170,8 +170,15 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
     return GC_ERR_UNSUPPORTED;
   }
   std::vector<int32_t> tile_seg(n_tiles), chunk_seg(n_chunks), out_chunk_seg(n_out_chunks);
+  std::vector<int4> tile_desc(n_tiles);
   for (int32_t s = 0; s < n_seg; ++s) {
-    for (int64_t t = tile_base[s]; t < tile_base[s + 1]; ++t) tile_seg[t] = s;
+    for (int64_t t = tile_base[s]; t < tile_base[s + 1]; ++t) {
+      tile_seg[t] = s;
+      const int64_t start = seg_off[s] + (t - tile_base[s]) * gc::kTile;
+      const int64_t len = std::min<int64_t>(gc::kTile, seg_off[s + 1] - start);
+      tile_desc[t] = make_int4((int)(uint32_t)start, (int)(uint32_t)((uint64_t)start >> 32),
+                               (int)len, s);
+    }
     for (int64_t c = chunk_base[s]; c < chunk_base[s + 1]; ++c) chunk_seg[c] = s;
     for (int64_t c = out_chunk_base[s]; c < out_chunk_base[s + 1]; ++c) out_chunk_seg[c] = s;
   }
@@ -184,11 +191,13 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   d.n_chunks = n_chunks;
   int64_t *d_seg_off, *d_tile_base, *d_chunk_base, *d_out_off, *d_cand_base, *d_out_chunk_base;
   int32_t *d_tile_seg, *d_chunk_seg, *d_out_chunk_seg;
+  int4* d_tile_desc;
   uint32_t *d_k, *d_cap, *d_thr_init;
   Carver cv;
   cv.add(&d_seg_off, n_seg + 1);
   cv.add(&d_tile_base, n_seg + 1);
   cv.add(&d_tile_seg, n_tiles);
+  cv.add(&d_tile_desc, n_tiles);
   cv.add(&d_chunk_base, n_seg + 1);
   cv.add(&d_chunk_seg, n_chunks);
   cv.add(&d_k, n_seg);
@@ -237,6 +246,7 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   d.seg_off = d_seg_off;
   d.tile_base = d_tile_base;
   d.tile_seg = d_tile_seg;
+  d.tile_desc = d_tile_desc;
   d.chunk_base = d_chunk_base;
   d.chunk_seg = d_chunk_seg;
   d.k = d_k;
@@ -257,6 +267,7 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   up(upload(d_seg_off, p->seg_off));
   up(upload(d_tile_base, tile_base));
   up(upload(d_tile_seg, tile_seg));
+  up(upload(d_tile_desc, tile_desc));
   up(upload(d_chunk_base, chunk_base));
   up(upload(d_chunk_seg, chunk_seg));
   up(upload(d_k, kk));

@@ -6,15 +6,31 @@
 
 namespace gc {
 
-// Streaming layout: one workgroup of 4 wave64s per tile of 8192 elements.  Wave w owns the
-// contiguous range [w*2048, (w+1)*2048) of its tile; inside it, slot v (0..7) of lane l holds
-// the 4 consecutive elements starting at w*2048 + v*256 + l*4.  Element order in the tile is
-// therefore (w, v, l, c), which is index order: every ordered rank below follows it.
-constexpr int kThreads = 256;
+// Streaming layout: one workgroup of kWaves wave64s per tile of kTile elements.  Wave w owns
+// the contiguous range [w*kWaveSpan, (w+1)*kWaveSpan) of its tile; inside it, slot v of lane l
+// holds the 4 consecutive elements starting at w*kWaveSpan + v*256 + l*4.  Element order in
+// the tile is therefore (w, v, l, c), which is index order: every ordered rank follows it.
+// Tile geometry and cache policy of the streaming pass (compile-time configuration).
+#ifndef GC_TILE_THREADS
+#define GC_TILE_THREADS 256
+#endif
+#ifndef GC_TILE_SLOTS
+#define GC_TILE_SLOTS 8
+#endif
+#ifndef GC_NT_LOAD_G        // gradient loads marked non-temporal
+#define GC_NT_LOAD_G 1
+#endif
+#ifndef GC_NT_LOAD_E        // residual (and velocity) loads marked non-temporal
+#define GC_NT_LOAD_E 1
+#endif
+#ifndef GC_NT_STORE_E       // residual (and velocity) stores marked non-temporal
+#define GC_NT_STORE_E 1
+#endif
+constexpr int kThreads = GC_TILE_THREADS;
 constexpr int kWaves = kThreads / 64;
-constexpr int kSlots = 8;
-constexpr int kWaveSpan = 64 * 4 * kSlots;         // 2048
-constexpr int kTile = kWaves * kWaveSpan;          // 8192
+constexpr int kSlots = GC_TILE_SLOTS;
+constexpr int kWaveSpan = 64 * 4 * kSlots;
+constexpr int kTile = kWaves * kWaveSpan;
 // Candidate buffers are processed in chunks laid out exactly like tiles.
 constexpr int kChunk = kTile;
 // Workgroups that serve the exact full-segment path, striding over listed segments.
@@ -46,6 +62,7 @@ struct DevPlan {
   const int64_t* seg_off;      // [n_seg + 1]
   const int64_t* tile_base;    // [n_seg + 1] first tile of each segment
   const int32_t* tile_seg;     // [n_tiles]
+  const int4* tile_desc;       // [n_tiles] {start low 32, start high 32, length, segment}
   const int64_t* chunk_base;   // [n_seg + 1] first candidate chunk of each segment
   const int32_t* chunk_seg;    // [n_chunks]
   const uint32_t* k;           // [n_seg]

@@ -216,11 +216,9 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
   __shared__ uint32_t s_w[kWaves];
   __shared__ uint32_t s_base;
   const int64_t t = blockIdx.x;
-  const int s = P.tile_seg[t];
-  int64_t start;
-  int len;
-  tile_range(P, s, t, &start, &len);
-  const uint32_t thr = P.thr[s];
+  const int4 desc = P.tile_desc[t];  // one load: no dependent lookups before the stream
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
   const int pb = slot_base();
 
   f4 acc[kSlots];
@@ -232,9 +230,9 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
 #pragma unroll
     for (int v = 0; v < kSlots; ++v) {
       const int q = (pb + v * 256) >> 2;
-      gv[v] = __builtin_nontemporal_load(g4 + q);
-      acc[v] = e4[q];
-      if (kMomentum) uv[v] = u4[q];
+      gv[v] = GC_NT_LOAD_G ? __builtin_nontemporal_load(g4 + q) : g4[q];
+      acc[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(e4 + q) : e4[q];
+      if (kMomentum) uv[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(u4 + q) : u4[q];
     }
 #pragma unroll
     for (int v = 0; v < kSlots; ++v) {
@@ -243,10 +241,10 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
       if (kMomentum) {
         const f4 mu = m * uv[v];
         x = mu + x;
-        u4[q] = x;
+        if (GC_NT_STORE_E) __builtin_nontemporal_store(x, u4 + q); else u4[q] = x;
       }
       acc[v] = acc[v] + x;
-      e4[q] = acc[v];
+      if (GC_NT_STORE_E) __builtin_nontemporal_store(acc[v], e4 + q); else e4[q] = acc[v];
     }
   } else {
 #pragma unroll
@@ -269,6 +267,7 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
         acc[v][c] = a;
       }
   }
+  const uint32_t thr = P.thr[s];
   if (thr == kNoCapture) return;  // uniform: this segment re-captures later
   capture_tile(P, s, t, start, len, acc, thr, s_w, &s_base);
 }
