@@ -26,6 +26,13 @@ namespace gc {
 #ifndef GC_NT_STORE_E       // residual (and velocity) stores marked non-temporal
 #define GC_NT_STORE_E 1
 #endif
+// Band of candidates-per-k that the threshold estimate steers toward (one step per call).
+#ifndef GC_RHO_LOW
+#define GC_RHO_LOW 1.5f
+#endif
+#ifndef GC_RHO_HIGH
+#define GC_RHO_HIGH 4.0f
+#endif
 constexpr int kThreads = GC_TILE_THREADS;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSlots = GC_TILE_SLOTS;

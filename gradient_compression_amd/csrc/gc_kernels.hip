@@ -596,27 +596,27 @@ __device__ __forceinline__ void count_block(const f4 (&x)[kSlots], int len, uint
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_count(DevPlan P, const float* __restrict__ e) {
+__global__ __launch_bounds__(kThreads) void k_count_cand(DevPlan P) {
   __shared__ uint32_t s_tmp[kWaves];
-  if (blockIdx.x < P.n_chunks) {
-    const int64_t ch = blockIdx.x;
-    const int s = P.chunk_seg[ch];
-    if (!has_candidates(P.mode[s])) return;
-    const int64_t c = P.cand_cnt[s];
-    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
-    if (j0 >= c) return;
-    const int len = (int)min((int64_t)kChunk, c - j0);
-    f4 x[kSlots];
-    load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
-    count_block(x, len, P.kth[s], s_tmp, &P.chunk_gt[ch], &P.chunk_eq[ch]);
-    return;
-  }
-  const int fb = blockIdx.x - (int)P.n_chunks;
+  const int64_t ch = blockIdx.x;
+  const int s = P.chunk_seg[ch];
+  if (!has_candidates(P.mode[s])) return;
+  const int64_t c = P.cand_cnt[s];
+  const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+  if (j0 >= c) return;
+  const int len = (int)min((int64_t)kChunk, c - j0);
+  f4 x[kSlots];
+  load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
+  count_block(x, len, P.kth[s], s_tmp, &P.chunk_gt[ch], &P.chunk_eq[ch]);
+}
+
+__global__ __launch_bounds__(kThreads) void k_count_full(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t s_tmp[kWaves];
   const uint32_t nf = *P.full_count;
   for (uint32_t li = 0; li < nf; ++li) {
     const int s = (int)P.full_list[li];
     const uint32_t kth = P.kth[s];
-    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
+    for (int64_t t = P.tile_base[s] + blockIdx.x; t < P.tile_base[s + 1]; t += kFullBlocks) {
       int64_t start;
       int len;
       tile_range(P, s, t, &start, &len);
@@ -668,55 +668,72 @@ __global__ __launch_bounds__(1024) void k_scan(DevPlan P) {
 }
 
 // --------------------------------------------------------------------------------- emit
-// Ordered compaction of one tile-shaped block whose element p has value x and segment-local
-// index lidx(p): keep key > kth, and key == kth while the tie rank stays below r.
-template <typename IdxOf>
-__device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, IdxOf lidx,
+// Ordered compaction of one tile-shaped block: keep key > kth, and key == kth while the tie
+// rank (eq_base + rank among the block's ties) stays below r.  slot_idx(v) gives the
+// segment-local indices of this lane's slot v (loaded only for slots that keep something).
+// A block whose ties are all kept or all dropped skips the tie ranking.
+template <typename SlotIdx>
+__device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotIdx slot_idx,
                                            uint32_t kth, uint32_t r, uint32_t eq_base,
-                                           int64_t out_pos, int64_t out_end, int64_t s0,
-                                           int32_t n_s, uint32_t* s_w, uint32_t* err,
-                                           float* __restrict__ e, float* __restrict__ u,
-                                           float* __restrict__ out_vals,
+                                           uint32_t eq_cnt, int64_t out_pos, int64_t out_end,
+                                           int64_t s0, int32_t n_s, uint32_t* s_w,
+                                           uint32_t* err, float* __restrict__ e,
+                                           float* __restrict__ u, float* __restrict__ out_vals,
                                            int32_t* __restrict__ out_idx) {
   const int pb = slot_base();
-  uint32_t eqb[kSlots], gtb[kSlots], woff[kSlots];
+  uint32_t selb[kSlots], woff[kSlots];
+  const bool ties_all = (uint64_t)eq_base + eq_cnt <= r;
+  const bool ties_none = eq_cnt == 0 || eq_base >= r;
+  if (ties_all || ties_none) {
 #pragma unroll
-  for (int v = 0; v < kSlots; ++v) {
-    uint32_t be = 0, bg = 0;
+    for (int v = 0; v < kSlots; ++v) {
+      uint32_t b = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t key = mag_key(x[v][c]);
-      const bool ok = pb + v * 256 + c < len;
-      be |= (ok && key == kth) ? (1u << c) : 0u;
-      bg |= (ok && key > kth) ? (1u << c) : 0u;
-    }
-    eqb[v] = be;
-    gtb[v] = bg;
-  }
-  tile_rank(eqb, woff, s_w);
-  uint32_t selb[kSlots];
-#pragma unroll
-  for (int v = 0; v < kSlots; ++v) {
-    uint32_t b = gtb[v];
-    uint32_t q = eq_base + woff[v];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if ((eqb[v] >> c) & 1u) {
-        b |= (q < r) ? (1u << c) : 0u;
-        ++q;
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t key = mag_key(x[v][c]);
+        const bool ok = pb + v * 256 + c < len;
+        b |= (ok && (key > kth || (ties_all && key == kth))) ? (1u << c) : 0u;
       }
-    selb[v] = b;
+      selb[v] = b;
+    }
+  } else {
+    uint32_t eqb[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      uint32_t be = 0, bg = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t key = mag_key(x[v][c]);
+        const bool ok = pb + v * 256 + c < len;
+        be |= (ok && key == kth) ? (1u << c) : 0u;
+        bg |= (ok && key > kth) ? (1u << c) : 0u;
+      }
+      eqb[v] = be;
+      selb[v] = bg;
+    }
+    tile_rank(eqb, woff, s_w);
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      uint32_t q = eq_base + woff[v];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((eqb[v] >> c) & 1u) {
+          selb[v] |= (q < r) ? (1u << c) : 0u;
+          ++q;
+        }
+    }
   }
   tile_rank(selb, woff, s_w);
 #pragma unroll
   for (int v = 0; v < kSlots; ++v) {
     const uint32_t b = selb[v];
-    if (!b) continue;
+    if (!__ballot(b != 0)) continue;   // uniform: nothing kept in this slot of the wave
+    const i4 li4 = slot_idx(v);
     int64_t q = out_pos + woff[v];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       if ((b >> c) & 1u) {
-        const int32_t li = lidx(v, c);
+        const int32_t li = li4[c];
         if (q < out_end && li >= 0 && li < n_s) {
           out_vals[q] = x[v][c];
           out_idx[q] = li;
@@ -730,44 +747,62 @@ __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, IdxOf
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, float* __restrict__ e,
-                                                   float* __restrict__ u_mask,
-                                                   float* __restrict__ out_vals,
-                                                   int32_t* __restrict__ out_idx) {
+__global__ __launch_bounds__(kThreads) void k_emit_cand(DevPlan P, float* __restrict__ e,
+                                                        float* __restrict__ u_mask,
+                                                        float* __restrict__ out_vals,
+                                                        int32_t* __restrict__ out_idx) {
   __shared__ uint32_t s_w[kWaves];
-  if (blockIdx.x < P.n_chunks) {
-    const int64_t ch = blockIdx.x;
-    const int s = P.chunk_seg[ch];
-    if (!has_candidates(P.mode[s])) return;
-    const int64_t c = P.cand_cnt[s];
-    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
-    if (j0 >= c) return;
-    const int len = (int)min((int64_t)kChunk, c - j0);
-    f4 x[kSlots];
-    i4 ix[kSlots];
-    load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
-    load_tile(P.sort_idx + P.cand_base[s] + j0, len, ix);
-    emit_block(x, len, [&](int v, int cc) { return (int32_t)ix[v][cc]; }, P.kth[s], P.ties[s],
-               P.chunk_eq_base[ch], P.out_off[s] + P.chunk_sel_base[ch], P.out_off[s + 1],
-               P.seg_off[s], (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, P.err, e, u_mask,
-               out_vals, out_idx);
-    return;
-  }
-  const int fb = blockIdx.x - (int)P.n_chunks;
+  const int64_t ch = blockIdx.x;
+  const int s = P.chunk_seg[ch];
+  if (!has_candidates(P.mode[s])) return;
+  const int64_t c = P.cand_cnt[s];
+  const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+  if (j0 >= c) return;
+  const int len = (int)min((int64_t)kChunk, c - j0);
+  const int64_t base = P.cand_base[s] + j0;
+  f4 x[kSlots];
+  load_tile(P.sort_val + base, len, x);
+  const int32_t* si = P.sort_idx + base;
+  const int pb = slot_base();
+  auto slot_idx = [&](int v) {
+    i4 r;
+    if (len == kTile) {
+      r = reinterpret_cast<const i4*>(si)[(pb + v * 256) >> 2];
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) r[cc] = pb + v * 256 + cc < len ? si[pb + v * 256 + cc] : 0;
+    }
+    return r;
+  };
+  emit_block(x, len, slot_idx, P.kth[s], P.ties[s], P.chunk_eq_base[ch], P.chunk_eq[ch],
+             P.out_off[s] + P.chunk_sel_base[ch], P.out_off[s + 1], P.seg_off[s],
+             (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, P.err, e, u_mask, out_vals,
+             out_idx);
+}
+
+__global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, float* __restrict__ e,
+                                                        float* __restrict__ u_mask,
+                                                        float* __restrict__ out_vals,
+                                                        int32_t* __restrict__ out_idx) {
+  __shared__ uint32_t s_w[kWaves];
   const uint32_t nf = *P.full_count;
   for (uint32_t li = 0; li < nf; ++li) {
     const int s = (int)P.full_list[li];
     const uint32_t kth = P.kth[s], r = P.ties[s];
     const int64_t s0 = P.seg_off[s];
-    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
+    for (int64_t t = P.tile_base[s] + blockIdx.x; t < P.tile_base[s + 1]; t += kFullBlocks) {
       int64_t start;
       int len;
       tile_range(P, s, t, &start, &len);
       f4 x[kSlots];
       load_tile(e + start, len, x);
       const int32_t lb = (int32_t)(start - s0) + slot_base();
-      emit_block(x, len, [&](int v, int cc) { return lb + v * 256 + cc; }, kth, r,
-                 P.tile_eq_base[t], P.out_off[s] + P.tile_sel_base[t], P.out_off[s + 1], s0,
+      auto slot_idx = [&](int v) {
+        const int32_t b0 = lb + v * 256;
+        return i4{b0, b0 + 1, b0 + 2, b0 + 3};
+      };
+      emit_block(x, len, slot_idx, kth, r, P.tile_eq_base[t], P.tile_eq[t],
+                 P.out_off[s] + P.tile_sel_base[t], P.out_off[s + 1], s0,
                  (int32_t)(P.seg_off[s + 1] - s0), s_w, P.err, e, u_mask, out_vals, out_idx);
     }
   }
@@ -791,8 +826,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
       b = fminf(b * 1.05f, 0.98f);
     } else if (mode == kModeCand) {
       const float rho = (float)P.cand_cnt[s] / (float)P.k[s];
-      if (rho > 4.0f) b = fminf(b * 1.03f, 0.98f);
-      else if (rho < 1.5f) b = fmaxf(b * 0.97f, 0.25f);
+      if (rho > GC_RHO_HIGH) b = fminf(b * 1.03f, 0.98f);
+      else if (rho < GC_RHO_LOW) b = fmaxf(b * 0.97f, 0.25f);
     }
     P.beta[s] = b;
     next = mag_key(b * __uint_as_float(P.kth[s]));
@@ -951,10 +986,13 @@ hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u,
     k_hist<<<mixed, kThreads, 0, st>>>(P, e, pass);
     k_find<<<P.n_seg, kThreads, 0, st>>>(P, pass);
   }
-  k_count<<<mixed, kThreads, 0, st>>>(P, e);
+  if (P.n_chunks > 0) k_count_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
+  k_count_full<<<kFullBlocks, kThreads, 0, st>>>(P, e);
   k_scan<<<P.n_seg, 1024, 0, st>>>(P);
   float* u_mask = (u && (P.flags & kFlagMomentumMask)) ? u : nullptr;
-  k_emit<<<mixed, kThreads, 0, st>>>(P, e, u_mask, out_vals, out_idx);
+  if (P.n_chunks > 0)
+    k_emit_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P, e, u_mask, out_vals, out_idx);
+  k_emit_full<<<kFullBlocks, kThreads, 0, st>>>(P, e, u_mask, out_vals, out_idx);
   k_finalize<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
   return hipGetLastError();
 }
