@@ -12,10 +12,10 @@ namespace gc {
 // the tile is therefore (w, v, l, c), which is index order: every ordered rank follows it.
 // Tile geometry and cache policy of the streaming pass (compile-time configuration).
 #ifndef GC_TILE_THREADS
-#define GC_TILE_THREADS 256
+#define GC_TILE_THREADS 1024
 #endif
 #ifndef GC_TILE_SLOTS
-#define GC_TILE_SLOTS 8
+#define GC_TILE_SLOTS 2
 #endif
 #ifndef GC_NT_LOAD_G        // gradient loads marked non-temporal
 #define GC_NT_LOAD_G 1
