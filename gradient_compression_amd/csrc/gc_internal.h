@@ -33,6 +33,12 @@ namespace gc {
 #ifndef GC_RHO_HIGH
 #define GC_RHO_HIGH 4.0f
 #endif
+#ifndef GC_NT_ZERO_E        // the scattered residual zeroing of kept entries non-temporal
+#define GC_NT_ZERO_E 1
+#endif
+#ifndef GC_BETA_MAX         // largest margin: next threshold <= GC_BETA_MAX * |k-th key|
+#define GC_BETA_MAX 0.98f
+#endif
 constexpr int kThreads = GC_TILE_THREADS;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSlots = GC_TILE_SLOTS;

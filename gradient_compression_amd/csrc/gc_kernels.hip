@@ -737,8 +737,13 @@ __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotI
         if (q < out_end && li >= 0 && li < n_s) {
           out_vals[q] = x[v][c];
           out_idx[q] = li;
-          e[s0 + li] = 0.0f;
-          if (u) u[s0 + li] = 0.0f;
+          if (GC_NT_ZERO_E) {
+            __builtin_nontemporal_store(0.0f, e + s0 + li);
+            if (u) __builtin_nontemporal_store(0.0f, u + s0 + li);
+          } else {
+            e[s0 + li] = 0.0f;
+            if (u) u[s0 + li] = 0.0f;
+          }
         } else {
           atomicOr(err, 4u);  // a rank outside the segment's output: never expected
         }
@@ -810,7 +815,8 @@ __global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, float* __rest
 
 // ----------------------------------------------------------------------------- finalize
 // Threshold for the next call: beta * |kth|, where the margin beta follows the last calls:
-// lowered after too few candidates, raised after an overflow or far more than needed.
+// lowered after too few candidates, raised after an overflow or far more than needed.  beta
+// may exceed 1: while the residual still grows, the next k-th key lies above the last one.
 // Segments that capture everything (small) or nothing (k = 0) keep their setting.
 __global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
   const int s = blockIdx.x * kThreads + threadIdx.x;
@@ -823,10 +829,10 @@ __global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
     if (why == kWhyMiss) {
       b = fmaxf(b * 0.85f, 0.25f);
     } else if (why == kWhyOverflow) {
-      b = fminf(b * 1.05f, 0.98f);
+      b = fminf(b * 1.05f, GC_BETA_MAX);
     } else if (mode == kModeCand) {
       const float rho = (float)P.cand_cnt[s] / (float)P.k[s];
-      if (rho > GC_RHO_HIGH) b = fminf(b * 1.03f, 0.98f);
+      if (rho > GC_RHO_HIGH) b = fminf(b * 1.03f, GC_BETA_MAX);
       else if (rho < GC_RHO_LOW) b = fmaxf(b * 0.97f, 0.25f);
     }
     P.beta[s] = b;

@@ -229,3 +229,70 @@ def test_argument_errors_on_gpu():
     plan.compress(g, e, v, i)
     torch.cuda.synchronize()
     plan.close()
+
+
+def test_checkpoint_resume_matches_straight_run():
+    """The error-feedback state is e (and u): five steps straight equal three steps, a
+    save and restore of e and u into fresh buffers (and a fresh plan), then two steps."""
+    sizes = [120000, 4096, 77777]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    grads = [torch.from_numpy(g).cuda() for g in t_grads(n, 5, scale=1e-4, seed=31)]
+
+    def run(plan, e, u, gs):
+        outs = []
+        for g in gs:
+            v = torch.empty(plan.total_k, device="cuda")
+            i = torch.empty(plan.total_k, dtype=torch.int32, device="cuda")
+            plan.compress(g, e, v, i, u=u, momentum=0.9)
+            outs.append((v.cpu().numpy(), i.cpu().numpy()))
+        return outs
+
+    p1 = gca.Plan(off, ratio=0.01)
+    e1, u1 = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    straight = run(p1, e1, u1, grads)
+    p2 = gca.Plan(off, ratio=0.01)
+    e2, u2 = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    first = run(p2, e2, u2, grads[:3])
+    saved = (e2.cpu().numpy().copy(), u2.cpu().numpy().copy())
+    p2.close()
+    p3 = gca.Plan(off, ratio=0.01)
+    e3, u3 = torch.from_numpy(saved[0]).cuda(), torch.from_numpy(saved[1]).cuda()
+    rest = run(p3, e3, u3, grads[3:])
+    for (a, b), (c, d) in zip(straight, first + rest):
+        assert a.tobytes() == c.tobytes() and b.tobytes() == d.tobytes()
+    assert e1.cpu().numpy().tobytes() == e3.cpu().numpy().tobytes()
+    assert u1.cpu().numpy().tobytes() == u3.cpu().numpy().tobytes()
+
+
+def test_side_stream_and_interleaved_plans():
+    """Calls run in order on the stream they are given; two plans over different segment
+    tables interleave without sharing state."""
+    import oracle
+    sizes_a, sizes_b = [100000, 3000], [50000, 50000, 7]
+    off_a = np.concatenate([[0], np.cumsum(sizes_a)]).astype(np.int64)
+    off_b = np.concatenate([[0], np.cumsum(sizes_b)]).astype(np.int64)
+    pa, pb = gca.Plan(off_a, ratio=0.01), gca.Plan(off_b, ratio=0.002)
+    ka = np.array([oracle.k_from_ratio(s, 0.01) for s in sizes_a], np.int64)
+    kb = np.array([oracle.k_from_ratio(s, 0.002) for s in sizes_b], np.int64)
+    ga = list(t_grads(int(off_a[-1]), 3, seed=41))
+    gb = list(t_grads(int(off_b[-1]), 3, seed=42))
+    side = torch.cuda.Stream()
+    ea, eb = torch.zeros(int(off_a[-1]), device="cuda"), torch.zeros(int(off_b[-1]), device="cuda")
+    ea_h, eb_h = np.zeros(int(off_a[-1]), np.float32), np.zeros(int(off_b[-1]), np.float32)
+    va, ia = torch.empty(pa.total_k, device="cuda"), torch.empty(pa.total_k, dtype=torch.int32, device="cuda")
+    vb, ib = torch.empty(pb.total_k, device="cuda"), torch.empty(pb.total_k, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for t in range(3):
+        with torch.cuda.stream(side):
+            gda = torch.from_numpy(ga[t]).to("cuda", non_blocking=False)
+            gdb = torch.from_numpy(gb[t]).to("cuda", non_blocking=False)
+            pa.compress(gda, ea, va, ia, stream=side)
+            pb.compress(gdb, eb, vb, ib, stream=side)
+        side.synchronize()
+        vo, io = oracle.topk_ef(ga[t], ea_h, off_a, ka)
+        assert va.cpu().numpy().tobytes() == vo.tobytes() and np.array_equal(ia.cpu().numpy(), io)
+        vo, io = oracle.topk_ef(gb[t], eb_h, off_b, kb)
+        assert vb.cpu().numpy().tobytes() == vo.tobytes() and np.array_equal(ib.cpu().numpy(), io)
+    assert ea.cpu().numpy().tobytes() == ea_h.tobytes()
+    assert eb.cpu().numpy().tobytes() == eb_h.tobytes()
