@@ -78,9 +78,11 @@ def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup):
     m = wl.momentum or 0.0
 
     def step(t):
-        plan.compress(gbufs[t % len(gbufs)], e, vals, idx, u=u, momentum=m)
-        if wl.int8:
-            plan.quant_int8(vals, idx, codes, scales, e=e, seed=0, step=t)
+        if wl.int8:   # compress and int8 (error feedback of the quantisation error) in one call
+            plan.compress_int8(gbufs[t % len(gbufs)], e, idx, codes, scales, out_vals=vals,
+                               u=u, momentum=m, seed=0, step=t)
+        else:
+            plan.compress(gbufs[t % len(gbufs)], e, vals, idx, u=u, momentum=m)
 
     for t in range(warmup):
         step(t)

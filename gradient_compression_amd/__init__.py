@@ -26,7 +26,7 @@ GC_DEBUG_NO_ESTIMATE = 0x200
 MODE_SKIP, MODE_CANDIDATES, MODE_FULL, MODE_RECAPTURED = 0, 1, 2, 3
 
 EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layout",
-           "gc_topk_ef_compress", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
+           "gc_topk_ef_compress", "gc_topk_ef_compress_int8", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
            "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32",
            "gc_status_string")
 
@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
         "gc_plan_total_k": [vp, vp],
         "gc_plan_layout": [vp, vp, vp],
         "gc_topk_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp],
+        "gc_topk_ef_compress_int8": [vp, vp, vp, vp, f32, u64, u64, vp, vp, vp, vp, vp],
         "gc_quant_int8": [vp, vp, vp, vp, u64, u64, vp, vp, vp],
         "gc_decompress": [vp, vp, vp, vp, vp, vp, ctypes.c_int, vp],
         "gc_plan_reset_estimate": [vp, vp],
@@ -175,6 +176,21 @@ class Plan:
             _dev_ptr(out_vals, torch.float32, "out_vals", self.total_k),
             _dev_ptr(out_idx, torch.int32, "out_idx", self.total_k), _stream(stream))
         _check(rc, "gc_topk_ef_compress")
+
+    def compress_int8(self, g, e, out_idx, out_codes, out_scales, out_vals=None, u=None,
+                      momentum: float = 0.0, seed: int = 0, step: int = 0, stream=None):
+        """compress then int8 in one call (the quantisation error goes back into e)."""
+        import torch
+        n = self.n
+        rc = lib().gc_topk_ef_compress_int8(
+            self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
+            _dev_ptr(u, torch.float32, "u", n), float(momentum), int(seed) & (2 ** 64 - 1),
+            int(step) & (2 ** 64 - 1),
+            _dev_ptr(out_vals, torch.float32, "out_vals", self.total_k),
+            _dev_ptr(out_idx, torch.int32, "out_idx", self.total_k),
+            _dev_ptr(out_codes, torch.int8, "out_codes", self.total_k),
+            _dev_ptr(out_scales, torch.float32, "out_scales", self.n_seg), _stream(stream))
+        _check(rc, "gc_topk_ef_compress_int8")
 
     def quant_int8(self, vals, idx, out_codes, out_scales, e=None, seed: int = 0, step: int = 0,
                    stream=None):

@@ -222,6 +222,7 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   cv.add(&d.why, n_seg);
   cv.add(&d.beta, n_seg);
   cv.add(&d.err, 1);
+
   cv.add(&d.run_off, n_tiles);
   cv.add(&d.run_cnt, n_tiles);
   cv.add(&d.run_dst, n_tiles);
@@ -233,6 +234,8 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   cv.add(&d.chunk_eq, n_chunks);
   cv.add(&d.chunk_eq_base, n_chunks);
   cv.add(&d.chunk_sel_base, n_chunks);
+  cv.add(&d.chunk_max, n_chunks);
+  cv.add(&d.tile_max, n_tiles);
   cv.add(&d.cand_val, cand_total);
   cv.add(&d.cand_idx, cand_total);
   cv.add(&d.sort_val, cand_total);
@@ -325,13 +328,16 @@ int gc_plan_layout(const gc_plan* plan, int64_t* k, int64_t* out_off) {
   return GC_OK;
 }
 
-int gc_topk_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
-                        float* out_vals, int32_t* out_idx, void* stream) {
+}  // extern "C"
+
+namespace {
+int compress_checked(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                     float* out_vals, int32_t* out_idx, const gc::Int8Args& q8, void* stream) {
   if (!plan) return GC_ERR_INVALID_ARG;
   const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
   if (any && (!g || !e || !aligned16(g) || !aligned16(e))) return GC_ERR_INVALID_ARG;
   if (u && !aligned16(u)) return GC_ERR_INVALID_ARG;
-  if (plan->total_k > 0 && (!out_vals || !out_idx)) return GC_ERR_INVALID_ARG;
+  if (plan->total_k > 0 && !out_idx) return GC_ERR_INVALID_ARG;
   if (any && (g == e || (u && (g == u || e == u)))) return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -352,8 +358,35 @@ int gc_topk_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float
     plan->spare.pop_back();
   }
   const hipError_t err =
-      gc::launch_compress(plan->dp, g, e, u, momentum, out_vals, out_idx, st, b, en);
+      gc::launch_compress(plan->dp, g, e, u, momentum, out_vals, out_idx, q8, st, b, en);
   return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gc_topk_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                        float* out_vals, int32_t* out_idx, void* stream) {
+  if (plan && plan->total_k > 0 && !out_vals) return GC_ERR_INVALID_ARG;
+  return compress_checked(plan, g, e, u, momentum, out_vals, out_idx, gc::Int8Args{}, stream);
+}
+
+int gc_topk_ef_compress_int8(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                             uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
+                             int8_t* out_codes, float* out_scales, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  if ((plan->total_k > 0 && !out_codes) || (plan->n_seg > 0 && !out_scales))
+    return GC_ERR_INVALID_ARG;
+  gc::Int8Args q8{};
+  q8.enabled = 1;
+  q8.codes = out_codes;
+  q8.scales = out_scales;
+  q8.seed_lo = (uint32_t)seed;
+  q8.seed_hi = (uint32_t)(seed >> 32);
+  q8.step_lo = (uint32_t)step;
+  if (plan->n_seg == 0) return GC_OK;
+  return compress_checked(plan, g, e, u, momentum, out_vals, out_idx, q8, stream);
 }
 
 int gc_quant_int8(gc_plan* plan, const float* vals, const int32_t* idx, float* e, uint64_t seed,

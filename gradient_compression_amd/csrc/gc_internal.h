@@ -99,6 +99,7 @@ struct DevPlan {
   uint32_t* why;               // [n_seg] kWhy* of this call
   float* beta;                 // [n_seg] threshold margin: next threshold = beta * |kth|
   uint32_t* err;               // [1] internal consistency flag (0 = fine)
+  uint32_t* tile_max;          // [n_tiles] largest key of a full-path tile (int8 absmax)
   // per-tile state
   uint32_t* run_off;           // [n_tiles] offset of the tile's run in its segment region
   uint32_t* run_cnt;           // [n_tiles]
@@ -112,6 +113,7 @@ struct DevPlan {
   uint32_t* chunk_eq;
   uint32_t* chunk_eq_base;
   uint32_t* chunk_sel_base;
+  uint32_t* chunk_max;         // [n_chunks] largest candidate key of the chunk (int8 absmax)
   // candidate buffers, segment s at [cand_base[s], cand_base[s] + cand_cap[s])
   float* cand_val;
   int32_t* cand_idx;
@@ -128,10 +130,18 @@ struct OutPlan {               // tables of the int8 and decompression kernels
   const int64_t* out_chunk_base;   // [n_seg + 1]
 };
 
+// Quantisation fused into the compress call (enabled == 0: plain compress).
+struct Int8Args {
+  int enabled;
+  int8_t* codes;
+  float* scales;
+  uint32_t seed_lo, seed_hi, step_lo;
+};
+
 // Launchers (gc_kernels.hip).  Each returns the hipError_t of its launches.
 hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
-                           float* out_vals, int32_t* out_idx, hipStream_t st,
-                           hipEvent_t ev_begin, hipEvent_t ev_end);
+                           float* out_vals, int32_t* out_idx, const Int8Args& q8,
+                           hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_reset(const DevPlan& P, hipStream_t st);
 hipError_t launch_quant(const OutPlan& O, const float* vals, const int32_t* idx, float* e,
                         uint64_t seed, uint64_t step, int8_t* codes, float* scales,

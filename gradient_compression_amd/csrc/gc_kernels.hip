@@ -41,6 +41,44 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // First element (tile-relative) of this lane's slot 0.
 __device__ __forceinline__ int slot_base() { return wave_id() * kWaveSpan + lane_id() * 4; }
 
+// Philox4x32-10 (Salmon et al., SC'11), word 0 of the output block.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t a = 0xD2511F53u, b = 0xCD9E8D57u;
+    const uint32_t hi0 = __umulhi(a, c0), lo0 = a * c0;
+    const uint32_t hi1 = __umulhi(b, c2), lo1 = b * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+// Stochastic int8 code of a kept value v (global index gi) at the segment's scale; returns
+// the code and writes the dequantised value fl(code * scale) to *deq.
+__device__ __forceinline__ int quant_code(float v, float scale, int64_t gi, uint32_t seed_lo,
+                                          uint32_t seed_hi, uint32_t step_lo, float* deq) {
+  int q = 0;
+  if (scale != 0.0f) {
+    float a = fabsf(v) / scale;
+    if (a > 127.0f) a = 127.0f;
+    const float f = floorf(a);
+    const float frac = a - f;
+    const uint32_t u24 = philox_word0((uint32_t)gi, (uint32_t)((uint64_t)gi >> 32), step_lo,
+                                      0x51u, seed_lo, seed_hi) >> 8;
+    q = (int)f + (((float)u24 < frac * 16777216.0f) ? 1 : 0);
+  }
+  const int code = signbit(v) ? -q : q;
+  *deq = (float)code * scale;
+  return code;
+}
+
 // Exclusive scan of one uint32 per thread over a block of NT threads; *total gets the sum.
 // s_tmp: __shared__ uint32_t[NT / 64].  Contains barriers: call from every thread.
 template <int NT>
@@ -64,6 +102,20 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total
   __syncthreads();
   *total = tot;
   return before + x - v;
+}
+
+// Largest value over a block of NT threads (valid in every thread).  s_tmp: [NT / 64].
+template <int NT>
+__device__ uint32_t block_max(uint32_t v, uint32_t* s_tmp) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
+  if (lane_id() == 0) s_tmp[wave_id()] = v;
+  __syncthreads();
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) m = max(m, s_tmp[i]);
+  __syncthreads();
+  return m;
 }
 
 // Sum over a block of NT threads (result valid in every thread).
@@ -510,6 +562,13 @@ __global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
       if (do_hist) atomicAdd(&h[mag_key(vx[r]) >> 20], 1u);
     }
   }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r)
+    if (r * kThreads + (int)threadIdx.x < len) mx = max(mx, mag_key(vx[r]));
+  __shared__ uint32_t s_m[kWaves];
+  mx = block_max<kThreads>(mx, s_m);
+  if (threadIdx.x == 0) P.chunk_max[ch] = mx;
   if (do_hist) {
     __syncthreads();
     hist_flush(h, P.hist + (size_t)s * 3 * kHistBins);
@@ -623,6 +682,15 @@ __global__ __launch_bounds__(kThreads) void k_count_full(DevPlan P, const float*
       f4 x[kSlots];
       load_tile(e + start, len, x);
       count_block(x, len, kth, s_tmp, &P.tile_gt[t], &P.tile_eq[t]);
+      uint32_t mx = 0;
+      const int pb = slot_base();
+#pragma unroll
+      for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (pb + v * 256 + c < len) mx = max(mx, mag_key(x[v][c]));
+      mx = block_max<kThreads>(mx, s_tmp);
+      if (threadIdx.x == 0) P.tile_max[t] = mx;
     }
   }
 }
@@ -630,29 +698,35 @@ __global__ __launch_bounds__(kThreads) void k_count_full(DevPlan P, const float*
 // --------------------------------------------------------------------------------- scan
 // Per segment, over its chunks (candidates) or tiles (full path) in index order: ties
 // before each item, then kept entries before each item (ties taken: the first `ties`).
-__global__ __launch_bounds__(1024) void k_scan(DevPlan P) {
+__global__ __launch_bounds__(1024) void k_scan(DevPlan P, float* __restrict__ scales) {
   __shared__ uint32_t s_tmp[16];
   const int s = blockIdx.x;
   const uint32_t mode = P.mode[s];
-  if (mode == kModeSkip) return;
+  if (mode == kModeSkip) {
+    if (scales && threadIdx.x == 0) scales[s] = 0.0f;  // fused int8: no kept values
+    return;
+  }
   const uint32_t r = P.ties[s];
   int64_t base, n;
-  const uint32_t *GT, *EQ;
+  const uint32_t *GT, *EQ, *MX;
   uint32_t *EQB, *SELB;
   if (has_candidates(mode)) {
     base = P.chunk_base[s];
     n = ((int64_t)P.cand_cnt[s] + kChunk - 1) / kChunk;
     GT = P.chunk_gt; EQ = P.chunk_eq; EQB = P.chunk_eq_base; SELB = P.chunk_sel_base;
+    MX = P.chunk_max;
   } else {
     base = P.tile_base[s];
     n = P.tile_base[s + 1] - base;
     GT = P.tile_gt; EQ = P.tile_eq; EQB = P.tile_eq_base; SELB = P.tile_sel_base;
+    MX = P.tile_max;
   }
-  uint32_t carry_eq = 0, carry_sel = 0;
+  uint32_t carry_eq = 0, carry_sel = 0, mx = 0;
   for (int64_t ib = 0; ib < n; ib += 1024) {
     const int64_t i = ib + threadIdx.x;
     const bool ok = i < n;
     const uint32_t gt = ok ? GT[base + i] : 0u, eq = ok ? EQ[base + i] : 0u;
+    if (scales && ok) mx = max(mx, MX[base + i]);
     uint32_t tot_eq, tot_sel;
     const uint32_t eqb = carry_eq + block_excl_scan<1024>(eq, s_tmp, &tot_eq);
     const uint32_t take = eqb < r ? min(eq, r - eqb) : 0u;
@@ -665,6 +739,10 @@ __global__ __launch_bounds__(1024) void k_scan(DevPlan P) {
     carry_sel += tot_sel;
   }
   if (threadIdx.x == 0 && carry_sel != P.k[s]) atomicOr(P.err, 2u);
+  if (scales) {  // fused int8: scale = fl(absmax / 127); the largest |acc| is always kept
+    mx = block_max<1024>(mx, s_tmp);
+    if (threadIdx.x == 0) scales[s] = __uint_as_float(mx) / 127.0f;
+  }
 }
 
 // --------------------------------------------------------------------------------- emit
@@ -672,14 +750,25 @@ __global__ __launch_bounds__(1024) void k_scan(DevPlan P) {
 // rank (eq_base + rank among the block's ties) stays below r.  slot_idx(v) gives the
 // segment-local indices of this lane's slot v (loaded only for slots that keep something).
 // A block whose ties are all kept or all dropped skips the tie ranking.
+struct EmitOut {              // where kept entries go
+  float* e;                  // residual: +0 at kept positions (or the quantisation error)
+  float* u;                  // velocity to zero at kept positions, or null
+  float* vals;               // kept values, or null (fused int8 call without values)
+  int32_t* idx;
+  int8_t* codes;             // fused int8: codes, or null
+  const float* scales;       // fused int8: per-segment scales (written by k_scan)
+  float scale;
+  uint32_t seed_lo, seed_hi, step_lo;
+  uint32_t* err;
+  __device__ float scales_of(int s) const { return scales[s]; }
+};
+
 template <typename SlotIdx>
 __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotIdx slot_idx,
                                            uint32_t kth, uint32_t r, uint32_t eq_base,
                                            uint32_t eq_cnt, int64_t out_pos, int64_t out_end,
                                            int64_t s0, int32_t n_s, uint32_t* s_w,
-                                           uint32_t* err, float* __restrict__ e,
-                                           float* __restrict__ u, float* __restrict__ out_vals,
-                                           int32_t* __restrict__ out_idx) {
+                                           const EmitOut& o) {
   const int pb = slot_base();
   uint32_t selb[kSlots], woff[kSlots];
   const bool ties_all = (uint64_t)eq_base + eq_cnt <= r;
@@ -735,27 +824,32 @@ __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotI
       if ((b >> c) & 1u) {
         const int32_t li = li4[c];
         if (q < out_end && li >= 0 && li < n_s) {
-          out_vals[q] = x[v][c];
-          out_idx[q] = li;
+          const float val = x[v][c];
+          if (o.vals) o.vals[q] = val;
+          o.idx[q] = li;
+          float resid = 0.0f;
+          if (o.codes) {
+            float deq;
+            o.codes[q] = (int8_t)quant_code(val, o.scale, s0 + li, o.seed_lo, o.seed_hi,
+                                            o.step_lo, &deq);
+            resid = val - deq;
+          }
           if (GC_NT_ZERO_E) {
-            __builtin_nontemporal_store(0.0f, e + s0 + li);
-            if (u) __builtin_nontemporal_store(0.0f, u + s0 + li);
+            __builtin_nontemporal_store(resid, o.e + s0 + li);
+            if (o.u) __builtin_nontemporal_store(0.0f, o.u + s0 + li);
           } else {
-            e[s0 + li] = 0.0f;
-            if (u) u[s0 + li] = 0.0f;
+            o.e[s0 + li] = resid;
+            if (o.u) o.u[s0 + li] = 0.0f;
           }
         } else {
-          atomicOr(err, 4u);  // a rank outside the segment's output: never expected
+          atomicOr(o.err, 4u);  // a rank outside the segment's output: never expected
         }
         ++q;
       }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_emit_cand(DevPlan P, float* __restrict__ e,
-                                                        float* __restrict__ u_mask,
-                                                        float* __restrict__ out_vals,
-                                                        int32_t* __restrict__ out_idx) {
+__global__ __launch_bounds__(kThreads) void k_emit_cand(DevPlan P, EmitOut o) {
   __shared__ uint32_t s_w[kWaves];
   const int64_t ch = blockIdx.x;
   const int s = P.chunk_seg[ch];
@@ -779,16 +873,13 @@ __global__ __launch_bounds__(kThreads) void k_emit_cand(DevPlan P, float* __rest
     }
     return r;
   };
+  if (o.codes) o.scale = o.scales_of(s);
   emit_block(x, len, slot_idx, P.kth[s], P.ties[s], P.chunk_eq_base[ch], P.chunk_eq[ch],
              P.out_off[s] + P.chunk_sel_base[ch], P.out_off[s + 1], P.seg_off[s],
-             (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, P.err, e, u_mask, out_vals,
-             out_idx);
+             (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, o);
 }
 
-__global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, float* __restrict__ e,
-                                                        float* __restrict__ u_mask,
-                                                        float* __restrict__ out_vals,
-                                                        int32_t* __restrict__ out_idx) {
+__global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, EmitOut o) {
   __shared__ uint32_t s_w[kWaves];
   const uint32_t nf = *P.full_count;
   for (uint32_t li = 0; li < nf; ++li) {
@@ -800,15 +891,16 @@ __global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, float* __rest
       int len;
       tile_range(P, s, t, &start, &len);
       f4 x[kSlots];
-      load_tile(e + start, len, x);
+      load_tile(o.e + start, len, x);
       const int32_t lb = (int32_t)(start - s0) + slot_base();
       auto slot_idx = [&](int v) {
         const int32_t b0 = lb + v * 256;
         return i4{b0, b0 + 1, b0 + 2, b0 + 3};
       };
+      if (o.codes) o.scale = o.scales_of(s);
       emit_block(x, len, slot_idx, kth, r, P.tile_eq_base[t], P.tile_eq[t],
                  P.out_off[s] + P.tile_sel_base[t], P.out_off[s + 1], s0,
-                 (int32_t)(P.seg_off[s + 1] - s0), s_w, P.err, e, u_mask, out_vals, out_idx);
+                 (int32_t)(P.seg_off[s + 1] - s0), s_w, o);
     }
   }
 }
@@ -842,25 +934,6 @@ __global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
 }
 
 // ------------------------------------------------------------------------------ int8 stage
-// Philox4x32-10 (Salmon et al., SC'11), word 0 of the output block.
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
-                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int round = 0; round < 10; ++round) {
-    const uint32_t a = 0xD2511F53u, b = 0xCD9E8D57u;
-    const uint32_t hi0 = __umulhi(a, c0), lo0 = a * c0;
-    const uint32_t hi1 = __umulhi(b, c2), lo1 = b * c2;
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0;
-    c1 = lo1;
-    c2 = n2;
-    c3 = lo0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
-  return c0;
-}
-
 // Per segment: scale = fl(max |v| / 127) over the kept values.
 __global__ __launch_bounds__(1024) void k_absmax(OutPlan O, const float* __restrict__ vals,
                                                  float* __restrict__ scales) {
@@ -895,22 +968,10 @@ __global__ __launch_bounds__(kThreads) void k_quant(OutPlan O, const float* __re
     const float v = vals[j];
     const int32_t li = idx[j];
     const int64_t gi = s0 + li;
-    int q = 0;
-    if (scale != 0.0f) {
-      float a = fabsf(v) / scale;
-      if (a > 127.0f) a = 127.0f;
-      const float f = floorf(a);
-      const float frac = a - f;
-      const uint32_t u24 = philox_word0((uint32_t)gi, (uint32_t)((uint64_t)gi >> 32), step_lo,
-                                        0x51u, seed_lo, seed_hi) >> 8;
-      q = (int)f + (((float)u24 < frac * 16777216.0f) ? 1 : 0);
-    }
-    const int code = signbit(v) ? -q : q;
+    float deq;
+    const int code = quant_code(v, scale, gi, seed_lo, seed_hi, step_lo, &deq);
     codes[j] = (int8_t)code;
-    if (e && li >= 0 && li < n_s) {  // indices come from the compress call
-      const float deq = (float)code * scale;
-      e[gi] = v - deq;
-    }
+    if (e && li >= 0 && li < n_s) e[gi] = v - deq;  // indices come from the compress call
   }
 }
 
@@ -968,8 +1029,8 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 }  // namespace
 
 hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
-                           float* out_vals, int32_t* out_idx, hipStream_t st,
-                           hipEvent_t ev_begin, hipEvent_t ev_end) {
+                           float* out_vals, int32_t* out_idx, const Int8Args& q8,
+                           hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (P.n_seg == 0) return hipSuccess;
   k_prep<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
@@ -994,11 +1055,20 @@ hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u,
   }
   if (P.n_chunks > 0) k_count_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
   k_count_full<<<kFullBlocks, kThreads, 0, st>>>(P, e);
-  k_scan<<<P.n_seg, 1024, 0, st>>>(P);
-  float* u_mask = (u && (P.flags & kFlagMomentumMask)) ? u : nullptr;
-  if (P.n_chunks > 0)
-    k_emit_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P, e, u_mask, out_vals, out_idx);
-  k_emit_full<<<kFullBlocks, kThreads, 0, st>>>(P, e, u_mask, out_vals, out_idx);
+  k_scan<<<P.n_seg, 1024, 0, st>>>(P, q8.enabled ? q8.scales : nullptr);
+  EmitOut o{};
+  o.e = e;
+  o.u = (u && (P.flags & kFlagMomentumMask)) ? u : nullptr;
+  o.vals = out_vals;
+  o.idx = out_idx;
+  o.codes = q8.enabled ? q8.codes : nullptr;
+  o.scales = q8.scales;
+  o.seed_lo = q8.seed_lo;
+  o.seed_hi = q8.seed_hi;
+  o.step_lo = q8.step_lo;
+  o.err = P.err;
+  if (P.n_chunks > 0) k_emit_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P, o);
+  k_emit_full<<<kFullBlocks, kThreads, 0, st>>>(P, o);
   k_finalize<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
   return hipGetLastError();
 }

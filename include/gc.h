@@ -123,6 +123,20 @@ int gc_quant_int8(gc_plan* plan, const float* vals, const int32_t* idx, float* e
                   uint64_t step, int8_t* out_codes, float* out_scales, void* stream);
 
 /*
+ * The compress step and the int8 stage in one call: the same results, bit for bit, as
+ * gc_topk_ef_compress followed by gc_quant_int8 with the residual e (the quantisation error
+ * is fed back into e), with one emission pass instead of two.  The per-segment absmax is
+ * the segment's largest |acc|, which is always kept.
+ *   out_vals  : float[total_k] kept fp32 values, or NULL when only the codes are wanted.
+ *   out_idx   : int32[total_k]; out_codes : int8[total_k]; out_scales : float[n_seg].
+ *   other arguments as for gc_topk_ef_compress and gc_quant_int8.
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_topk_ef_compress_int8(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                             uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
+                             int8_t* out_codes, float* out_scales, void* stream);
+
+/*
  * Scatter kept entries back into a dense float[N] buffer: dense[seg_off[s] + idx] = v, with
  * v = vals[j] when vals is given, else fl(codes[j] * scales[s]).  accumulate = 0 first sets
  * dense to +0 over [seg_off[0], N); accumulate != 0 adds v instead of storing it.

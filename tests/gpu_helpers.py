@@ -41,7 +41,8 @@ def oracle_k(sizes, k=None, ratio=None):
 
 
 def run_parity(sizes, grads, *, k=None, ratio=None, momentum=None, mask=False, flags=0,
-               int8=False, seed=0, plan=None, check_stats=None, label=""):
+               int8=False, fused=False, with_vals=True, seed=0, plan=None, check_stats=None,
+               label=""):
     """grads: iterable of float32 numpy gradients (one per EF iteration), or a pair
     (iters, f) with f(t, residual) -> gradient, the residual being the oracle's current one.
 
@@ -76,7 +77,12 @@ def run_parity(sizes, grads, *, k=None, ratio=None, momentum=None, mask=False, f
         assert g.size == n
         log(f"[parity {label}] iteration {t}: n={n} segs={len(sizes)} total_k={tk}")
         g_d = torch.from_numpy(g).to(dev)
-        plan.compress(g_d, e_d, vals_d, idx_d, u=u_d, momentum=momentum or 0.0)
+        if fused:   # compress and int8 in one call
+            plan.compress_int8(g_d, e_d, idx_d, codes_d, scales_d,
+                               out_vals=vals_d if with_vals else None, u=u_d,
+                               momentum=momentum or 0.0, seed=seed, step=t)
+        else:
+            plan.compress(g_d, e_d, vals_d, idx_d, u=u_d, momentum=momentum or 0.0)
         vals_o, idx_o = oracle.topk_ef(g, e_h, off, ks, u=u_h,
                                        momentum=momentum if momentum is not None else 0.0,
                                        mask_u=mask)
@@ -85,10 +91,18 @@ def run_parity(sizes, grads, *, k=None, ratio=None, momentum=None, mask=False, f
         if check_stats:
             check_stats(t, stats)
         assert_bitwise(idx_d[:tk], idx_o, f"{label} it{t} idx")
-        assert_bitwise(vals_d[:tk], vals_o, f"{label} it{t} vals")
-        assert_bitwise(e_d, e_h, f"{label} it{t} residual")
+        if with_vals:
+            assert_bitwise(vals_d[:tk], vals_o, f"{label} it{t} vals")
         if u_d is not None:
             assert_bitwise(u_d, u_h, f"{label} it{t} velocity")
+        if fused:
+            codes_o, scales_o = oracle.quant_int8(vals_o, idx_o, off, ks, e=e_h, seed=seed,
+                                                  step=t)
+            assert_bitwise(scales_d[:len(sizes)], scales_o, f"{label} it{t} scales")
+            assert_bitwise(codes_d[:tk], codes_o, f"{label} it{t} codes")
+            assert_bitwise(e_d, e_h, f"{label} it{t} residual after fused int8")
+            continue
+        assert_bitwise(e_d, e_h, f"{label} it{t} residual")
         if int8:
             plan.quant_int8(vals_d, idx_d, codes_d, scales_d, e=e_d, seed=seed, step=t)
             codes_o, scales_o = oracle.quant_int8(vals_o, idx_o, off, ks, e=e_h, seed=seed,

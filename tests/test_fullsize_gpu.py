@@ -155,3 +155,33 @@ def test_full_size(name, iters, sample):
                 assert_bitwise(u[a:b], host[s]["u"], f"{name} it{t} seg{s} velocity")
         del e_prev, u_prev, e_cmp
     plan.close()
+
+
+def test_fused_int8_full_size_matches_two_calls():
+    """The hybrid workload at full size: the fused compress+int8 call and the two separate
+    calls give bit-identical values, indices, codes, scales and residuals."""
+    wl = workload("c4_hybrid_int8")
+    off = wl.offsets()
+    dev = torch.device("cuda")
+    p1, p2 = gca.Plan(off, ratio=wl.ratio), gca.Plan(off, ratio=wl.ratio)
+    g = torch.empty(wl.n, dtype=torch.float32, device=dev)
+    e1 = torch.zeros(wl.n, dtype=torch.float32, device=dev)
+    e2 = torch.zeros(wl.n, dtype=torch.float32, device=dev)
+    mk = lambda dt: torch.empty(p1.total_k, dtype=dt, device=dev)   # noqa: E731
+    v1, i1, c1 = mk(torch.float32), mk(torch.int32), mk(torch.int8)
+    v2, i2, c2 = mk(torch.float32), mk(torch.int32), mk(torch.int8)
+    s1 = torch.empty(wl.n_seg, dtype=torch.float32, device=dev)
+    s2 = torch.empty(wl.n_seg, dtype=torch.float32, device=dev)
+    for t in range(3):
+        gen.fill_gradient(g, wl, t)
+        p1.compress(g, e1, v1, i1)
+        p1.quant_int8(v1, i1, c1, s1, e=e1, seed=0, step=t)
+        p2.compress_int8(g, e2, i2, c2, s2, out_vals=v2, seed=0, step=t)
+        torch.cuda.synchronize()
+        log(f"[fused full] it{t}")
+        for a, b, what in ((v1, v2, "vals"), (i1, i2, "idx"), (c1, c2, "codes"), (s1, s2, "scales")):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.int8 else a.view(torch.int32),
+                               b.view(torch.uint8) if b.dtype == torch.int8 else b.view(torch.int32)), what
+        assert torch.equal(e1.view(torch.int32), e2.view(torch.int32)), "residual"
+    p1.close()
+    p2.close()

@@ -178,6 +178,22 @@ def test_hybrid_int8():
                seed=12345678901, label="int8 seed")
 
 
+@pytest.mark.parametrize("flags,momentum,mask,with_vals", [
+    (0, None, False, True),
+    (0, None, False, False),
+    (0x100, None, False, True),          # full-segment path
+    (0x200, None, False, True),          # re-capture path
+    (0, 0.9, True, True),                # momentum with masking
+])
+def test_fused_compress_int8(flags, momentum, mask, with_vals):
+    """The fused call equals compress then int8 with error feedback of the quantisation error
+    (checked against the oracle's two steps); every selection path, with and without values."""
+    sizes = [1 << 18, 70001, 3, 0, 9000]
+    run_parity(sizes, t_grads(sum(sizes), 3, df=2.5, scale=1.0, seed=8), ratio=0.01, fused=True,
+               with_vals=with_vals, flags=flags, momentum=momentum, mask=mask, seed=77,
+               label=f"fused f={flags:#x} m={momentum} mask={mask} vals={with_vals}")
+
+
 def test_decompress_matches_oracle():
     import oracle
     sizes = [100000, 3, 54321]
