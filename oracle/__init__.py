@@ -50,6 +50,10 @@ def load(path: str):
     L.orc_quant_int8.restype = None
     L.orc_decompress.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
     L.orc_decompress.restype = None
+    L.orc_sign_ef_segment.argtypes = [i64, vp, vp, vp, f32, vp, vp]
+    L.orc_sign_ef_segment.restype = None
+    L.orc_sign_decompress_segment.argtypes = [i64, vp, f32, vp, ctypes.c_int]
+    L.orc_sign_decompress_segment.restype = None
     return L
 
 
@@ -167,4 +171,23 @@ def decompress(seg_off, k, idx, vals=None, codes=None, scales=None, dense=None,
         scales = np.ascontiguousarray(scales, np.float32)
     lib().orc_decompress(len(k), _p(seg_off), _p(k), _p(vals), _p(codes), _p(scales), _p(idx),
                          _p(dense), int(bool(accumulate)))
+    return dense
+
+
+def sign_ef_segment(g, e, u=None, momentum=0.9):
+    """1-bit sign compression of one segment with error feedback, in place on e (and u).
+    Returns (bits uint32[ceil(n/32)], scale float32)."""
+    _f32(g, "g"), _f32(e, "e")
+    n = g.size
+    bits = np.empty((n + 31) // 32, np.uint32)
+    scale = np.empty(1, np.float32)
+    lib().orc_sign_ef_segment(n, _p(g), _p(e), _p(u), float(momentum), _p(bits), _p(scale))
+    return bits, scale[0]
+
+
+def sign_decompress_segment(bits, scale, n, dense=None, accumulate=False):
+    bits = np.ascontiguousarray(bits, np.uint32)
+    if dense is None:
+        dense = np.empty(n, np.float32)
+    lib().orc_sign_decompress_segment(n, _p(bits), float(scale), _p(dense), int(bool(accumulate)))
     return dense

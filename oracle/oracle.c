@@ -33,6 +33,10 @@
  * the quantisation error is fed back: e = fl(acc - fl(code*scale)).  u24 is the top 24
  * bits of word 0 of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key (seed lo,
  * seed hi) and counter (global index lo, global index hi, step lo, 0x51).
+ *
+ * 1-bit sign compression with error feedback ("Communication Optimization > Gradient
+ * Compression", 1-bit SGD section): per segment scale = fl32(sum |acc| / n) with the sum
+ * in double, one sign bit per element, residual e = fl(acc - sign * scale).
  */
 #include <math.h>
 #include <stdint.h>
@@ -260,5 +264,53 @@ void orc_decompress(int32_t n_seg, const int64_t* seg_off, const int64_t* k, con
             *d = accumulate ? *d + v : v;
         }
         out += k[s];
+    }
+}
+
+/* ---------------------------------------------------- 1-bit sign with error feedback */
+
+/*
+ * One segment of n elements.  "Communication Optimization > Gradient Compression", 1-bit
+ * SGD section: Q(g) = sign(g) * ||g||_1 / d, the scalar taken per layer; its QSGD paragraph:
+ * 1-bit quantisation needs error feedback like top-K.  With the residual e:
+ *   acc = e + x (x = g, or u = m*u + g with momentum);
+ *   scale = fl32(S / n), S = sum |acc_i| accumulated in double in index order;
+ *   sign_i = -1 where acc_i < 0, +1 otherwise (so -0 and +0 both send +1);
+ *   bit i of the segment's bit array (word i/32, bit i%32) is 1 where sign_i = -1;
+ *   e_i = fl(acc_i - sign_i * scale).
+ * bits: ceil(n/32) words, cleared here.  n == 0 gives scale 0 and no words.
+ */
+void orc_sign_ef_segment(int64_t n, const float* g, float* e, float* u, float m,
+                         uint32_t* bits, float* scale_out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float x = g[i];
+        if (u) {
+            float mu = m * u[i];
+            u[i] = mu + x;
+            x = u[i];
+        }
+        e[i] = e[i] + x;
+    }
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += fabs((double)e[i]);
+    float scale = n > 0 ? (float)(s / (double)n) : 0.0f;
+    *scale_out = scale;
+    for (int64_t w = 0; w < (n + 31) / 32; ++w) bits[w] = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int neg = e[i] < 0.0f;
+        if (neg) bits[i / 32] |= 1u << (i % 32);
+        float q = neg ? -scale : scale;
+        e[i] = e[i] - q;
+    }
+}
+
+/* dense[i] = sign_i * scale (or += with accumulate) for one segment. */
+void orc_sign_decompress_segment(int64_t n, const uint32_t* bits, float scale, float* dense,
+                                 int accumulate)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float v = ((bits[i / 32] >> (i % 32)) & 1u) ? -scale : scale;
+        dense[i] = accumulate ? dense[i] + v : v;
     }
 }
