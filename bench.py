@@ -63,22 +63,29 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--codec", choices=("topk", "sign"), default="topk",
+                    help="topk: EF-Top-k (default); sign: 1-bit sign with error feedback")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-momentum-variant", action="store_true")
     return ap.parse_args()
 
 
-def bytes_per_element(wl):
+def bytes_per_element(wl, codec="topk"):
+    """Algorithmic HBM bytes per element of the timed streaming passes."""
+    if codec == "sign":   # pass 1: g, e (u) in, e (u) out; pass 2: e in, e out, one bit
+        return (20 if wl.momentum is not None else 12) + 8 + 1 / 8
     return 20 if wl.momentum is not None else 12
 
 
-def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup):
+def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
     import torch
     vals, idx, codes, scales = outs
     m = wl.momentum or 0.0
 
     def step(t):
-        if wl.int8:   # compress and int8 (error feedback of the quantisation error) in one call
+        if codec == "sign":
+            plan.sign_compress(gbufs[t % len(gbufs)], e, codes, scales, u=u, momentum=m)
+        elif wl.int8:   # compress and int8 (error feedback of the quantisation error) in one call
             plan.compress_int8(gbufs[t % len(gbufs)], e, idx, codes, scales, out_vals=vals,
                                u=u, momentum=m, seed=0, step=t)
         else:
@@ -102,11 +109,11 @@ def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup):
     return total_ms / steps, k1_ms / max(launches, 1), launches
 
 
-def setup(wl, n_gbufs=4):
+def setup(wl, n_gbufs=4, codec="topk"):
     import torch
     import gradient_compression_amd as gca
     from synth import gen
-    plan = gca.Plan(wl.offsets(), ratio=wl.ratio)
+    plan = gca.Plan(wl.offsets(), ratio=0.0 if codec == "sign" else wl.ratio)
     dev = torch.device("cuda")
     gbufs = []
     for t in range(n_gbufs):
@@ -119,6 +126,9 @@ def setup(wl, n_gbufs=4):
     idx = torch.empty(plan.total_k, dtype=torch.int32, device=dev)
     codes = torch.empty(plan.total_k, dtype=torch.int8, device=dev) if wl.int8 else None
     scales = torch.empty(wl.n_seg, dtype=torch.float32, device=dev) if wl.int8 else None
+    if codec == "sign":   # sign bits in place of codes, one scale per segment
+        codes = torch.empty(plan.total_words, dtype=torch.int32, device=dev)
+        scales = torch.empty(wl.n_seg, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     return plan, gbufs, e, u, (vals, idx, codes, scales)
 
@@ -217,18 +227,20 @@ def main():
     gca.lib()  # fails loudly when the HIP library is not built
     wl = workload(args.workload)
     log(f"[bench] workload {wl.name}: N={wl.n} segments={wl.n_seg} ratio={wl.ratio}")
-    plan, gbufs, e, u, outs = setup(wl)
+    codec = args.codec
+    plan, gbufs, e, u, outs = setup(wl, codec=codec)
     log(f"[bench] inputs resident ({len(gbufs)} gradient buffers); warmup {args.warmup}, "
-        f"timing {args.steps} steps")
-    ms, k1_ms, launches = time_steps(plan, wl, gbufs, e, u, outs, args.steps, args.warmup)
+        f"timing {args.steps} steps, codec {codec}")
+    ms, k1_ms, launches = time_steps(plan, wl, gbufs, e, u, outs, args.steps, args.warmup,
+                                     codec)
     st = plan.last_stats()
-    bpe = bytes_per_element(wl)
+    bpe = bytes_per_element(wl, codec)
     value = 4.0 * wl.n / ms / 1e6                     # GB/s of fp32 gradient
     eff = bpe * wl.n / ms / 1e6
     k1_ach = bpe * wl.n / k1_ms / 1e6
     log(f"[bench] {ms:.3f} ms/step, {value:.1f} GB/s gradient, effective {eff:.1f} GB/s "
         f"({eff / HBM_PEAK_GBPS:.1%} of peak); EF pass {k1_ms:.3f} ms ({k1_ach:.1f} GB/s)")
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name) if codec == "topk" else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -243,7 +255,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": wl.name,
+            "workload": wl.name if codec == "topk" else f"{wl.name}+sign1bit",
+            "codec": codec,
             "n_elements": wl.n,
             "segments": wl.n_seg,
             "k_ratio": wl.ratio,
@@ -259,7 +272,8 @@ def main():
         "full_path_segments_last_step": int((st["mode"] == gca.MODE_FULL).sum()),
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_ef_capture (EF add + key + candidate capture)",
+            "kernel": ("k_ef_capture (EF add + key + candidate capture)" if codec == "topk"
+                       else "k_sign_pass1 + k_sign_scale + k_sign_pass2"),
             "achieved": round(k1_ach, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -270,6 +284,10 @@ def main():
             "launches": launches,
         },
     }
+    if codec != "topk":
+        result["metric"] = "1-bit sign EF compress GB/s of fp32 gradient (1 GPU) and % of HBM peak"
+        print(json.dumps(result), flush=True)
+        return
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline: oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(plan, wl, gbufs[0], e, u)

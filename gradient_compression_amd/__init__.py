@@ -28,7 +28,8 @@ MODE_SKIP, MODE_CANDIDATES, MODE_FULL, MODE_RECAPTURED = 0, 1, 2, 3
 EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layout",
            "gc_topk_ef_compress", "gc_topk_ef_compress_int8", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
            "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32",
-           "gc_status_string")
+           "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
+           "gc_sign_decompress")
 
 _lib = None
 
@@ -65,6 +66,9 @@ def lib() -> ctypes.CDLL:
         "gc_plan_timing": [vp, vp, vp],
         "gc_copy_f32": [vp, vp, i64, vp],
         "gc_status_string": [ctypes.c_int],
+        "gc_sign_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp],
+        "gc_plan_sign_layout": [vp, vp],
+        "gc_sign_decompress": [vp, vp, vp, vp, ctypes.c_int, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -144,6 +148,9 @@ class Plan:
         self.out_off = np.zeros(self.n_seg + 1, np.int64)
         _check(L.gc_plan_layout(self._h, _np_ptr(self.k), _np_ptr(self.out_off)),
                "gc_plan_layout")
+        self.word_off = np.zeros(self.n_seg + 1, np.int64)
+        _check(L.gc_plan_sign_layout(self._h, _np_ptr(self.word_off)), "gc_plan_sign_layout")
+        self.total_words = int(self.word_off[-1])
 
     def close(self):
         if getattr(self, "_h", None) and self._h.value:
@@ -216,6 +223,28 @@ class Plan:
             _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
             _stream(stream))
         _check(rc, "gc_decompress")
+
+    def sign_compress(self, g, e, out_bits, out_scales, u=None, momentum: float = 0.0,
+                      stream=None):
+        """1-bit sign compression with error feedback: bits (uint32 words, torch.int32
+        storage) and one L1 scale per segment; e <- acc - sign * scale."""
+        import torch
+        n = self.n
+        rc = lib().gc_sign_ef_compress(
+            self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
+            _dev_ptr(u, torch.float32, "u", n), float(momentum),
+            _dev_ptr(out_bits, torch.int32, "out_bits", self.total_words),
+            _dev_ptr(out_scales, torch.float32, "out_scales", self.n_seg), _stream(stream))
+        _check(rc, "gc_sign_ef_compress")
+
+    def sign_decompress(self, bits, scales, dense, accumulate=False, stream=None):
+        import torch
+        rc = lib().gc_sign_decompress(
+            self._h, _dev_ptr(bits, torch.int32, "bits", self.total_words),
+            _dev_ptr(scales, torch.float32, "scales", self.n_seg),
+            _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
+            _stream(stream))
+        _check(rc, "gc_sign_decompress")
 
     def reset_estimate(self, stream=None):
         _check(lib().gc_plan_reset_estimate(self._h, _stream(stream)), "gc_plan_reset_estimate")

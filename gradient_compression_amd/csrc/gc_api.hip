@@ -66,7 +66,7 @@ struct gc_plan {
   int device = 0;
   int32_t n_seg = 0;
   uint32_t flags = 0;
-  std::vector<int64_t> seg_off, k, out_off;
+  std::vector<int64_t> seg_off, k, out_off, word_off;
   int64_t total_k = 0;
   gc::DevPlan dp{};
   gc::OutPlan op{};
@@ -134,6 +134,9 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   p->out_off.assign(n_seg + 1, 0);
   for (int32_t s = 0; s < n_seg; ++s) p->out_off[s + 1] = p->out_off[s] + ks[s];
   p->total_k = p->out_off[n_seg];
+  p->word_off.assign(n_seg + 1, 0);
+  for (int32_t s = 0; s < n_seg; ++s)
+    p->word_off[s + 1] = p->word_off[s] + ceil_div(seg_off[s + 1] - seg_off[s], 32);
 
   // tables
   std::vector<int64_t> tile_base(n_seg + 1, 0), chunk_base(n_seg + 1, 0), cand_base(n_seg, 0),
@@ -236,6 +239,9 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   cv.add(&d.chunk_sel_base, n_chunks);
   cv.add(&d.chunk_max, n_chunks);
   cv.add(&d.tile_max, n_tiles);
+  cv.add(&d.tile_l1, n_tiles);
+  int64_t* d_word_off;
+  cv.add(&d_word_off, n_seg + 1);
   cv.add(&d.cand_val, cand_total);
   cv.add(&d.cand_idx, cand_total);
   cv.add(&d.sort_val, cand_total);
@@ -257,6 +263,7 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   d.cand_base = d_cand_base;
   d.cand_cap = d_cap;
   d.thr_init = d_thr_init;
+  d.word_off = d_word_off;
   gc::OutPlan& o = p->op;
   o.n_seg = n_seg;
   o.n_out_chunks = n_out_chunks;
@@ -280,6 +287,7 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   up(upload(d_thr_init, thr_init));
   up(upload(d_out_chunk_seg, out_chunk_seg));
   up(upload(d_out_chunk_base, out_chunk_base));
+  up(upload(d_word_off, p->word_off));
   up(upload(d.thr, thr_init));
   up(upload(d.beta, std::vector<float>(n_seg, kInitialBeta)));
   up(hipMemset(d.cand_cnt, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
@@ -331,6 +339,25 @@ int gc_plan_layout(const gc_plan* plan, int64_t* k, int64_t* out_off) {
 }  // extern "C"
 
 namespace {
+// With timing on, a HIP event pair for the streaming passes of this call.
+int timing_events(gc_plan* plan, hipEvent_t* b, hipEvent_t* en) {
+  if (!plan->timing) return GC_OK;
+  if (plan->spare.empty()) {
+    hipEvent_t x, y;
+    if (hipEventCreate(&x) != hipSuccess) return GC_ERR_HIP;
+    if (hipEventCreate(&y) != hipSuccess) {
+      (void)hipEventDestroy(x);
+      return GC_ERR_HIP;
+    }
+    plan->spare.emplace_back(x, y);
+  }
+  *b = plan->spare.back().first;
+  *en = plan->spare.back().second;
+  plan->pending.push_back(plan->spare.back());
+  plan->spare.pop_back();
+  return GC_OK;
+}
+
 int compress_checked(gc_plan* plan, const float* g, float* e, float* u, float momentum,
                      float* out_vals, int32_t* out_idx, const gc::Int8Args& q8, void* stream) {
   if (!plan) return GC_ERR_INVALID_ARG;
@@ -342,21 +369,7 @@ int compress_checked(gc_plan* plan, const float* g, float* e, float* u, float mo
   if (int rc = check_device(plan)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t b = nullptr, en = nullptr;
-  if (plan->timing) {
-    if (plan->spare.empty()) {
-      hipEvent_t x, y;
-      if (hipEventCreate(&x) != hipSuccess) return GC_ERR_HIP;
-      if (hipEventCreate(&y) != hipSuccess) {
-        (void)hipEventDestroy(x);
-        return GC_ERR_HIP;
-      }
-      plan->spare.emplace_back(x, y);
-    }
-    b = plan->spare.back().first;
-    en = plan->spare.back().second;
-    plan->pending.push_back(plan->spare.back());
-    plan->spare.pop_back();
-  }
+  if (int rc = timing_events(plan, &b, &en)) return rc;
   const hipError_t err =
       gc::launch_compress(plan->dp, g, e, u, momentum, out_vals, out_idx, q8, st, b, en);
   return err == hipSuccess ? GC_OK : GC_ERR_HIP;
@@ -387,6 +400,39 @@ int gc_topk_ef_compress_int8(gc_plan* plan, const float* g, float* e, float* u, 
   q8.step_lo = (uint32_t)step;
   if (plan->n_seg == 0) return GC_OK;
   return compress_checked(plan, g, e, u, momentum, out_vals, out_idx, q8, stream);
+}
+
+int gc_plan_sign_layout(const gc_plan* plan, int64_t* word_off) {
+  if (!plan || !word_off) return GC_ERR_INVALID_ARG;
+  std::memcpy(word_off, plan->word_off.data(), sizeof(int64_t) * (plan->n_seg + 1));
+  return GC_OK;
+}
+
+int gc_sign_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                        uint32_t* out_bits, float* out_scales, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!g || !e || !out_bits || !aligned16(g) || !aligned16(e))) return GC_ERR_INVALID_ARG;
+  if (u && !aligned16(u)) return GC_ERR_INVALID_ARG;
+  if (plan->n_seg > 0 && !out_scales) return GC_ERR_INVALID_ARG;
+  if (any && (g == e || (u && (g == u || e == u)))) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  hipEvent_t b = nullptr, en = nullptr;
+  if (int rc = timing_events(plan, &b, &en)) return rc;
+  const hipError_t err = gc::launch_sign(plan->dp, g, e, u, momentum, out_bits, out_scales,
+                                         static_cast<hipStream_t>(stream), b, en);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_sign_decompress(const gc_plan* plan, const uint32_t* bits, const float* scales,
+                       float* dense, int accumulate, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!bits || !scales || !dense)) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  const hipError_t err = gc::launch_sign_decompress(plan->dp, bits, scales, dense, accumulate,
+                                                    static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
 }
 
 int gc_quant_int8(gc_plan* plan, const float* vals, const int32_t* idx, float* e, uint64_t seed,

@@ -933,6 +933,183 @@ __global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
   P.thr[s] = next;
 }
 
+// ------------------------------------------------------------------------ 1-bit sign
+// 1-bit sign compression with error feedback ("Communication Optimization > Gradient
+// Compression", 1-bit SGD section: Q(g) = sign(g) * ||g||_1 / d, one scale per layer; error
+// feedback as for top-K).  Pass 1 streams acc = e + x into e and takes each tile's sum of
+// |acc| in double; the scale is fl32(S / n) per segment; pass 2 writes the sign bits (bit i
+// of word i/32, 1 = negative) and the residual e = fl(acc - sign * scale).
+
+// Load the tile of g (and u), form acc (momentum first), store acc into e (and u).
+template <bool kMomentum>
+__device__ __forceinline__ void ef_add_tile(const float* __restrict__ g, float* __restrict__ e,
+                                            float* __restrict__ u, float m, int64_t start,
+                                            int len, f4 (&acc)[kSlots]) {
+  const int pb = slot_base();
+  if (len == kTile && (start & 3) == 0) {
+    const f4* g4 = reinterpret_cast<const f4*>(g + start);
+    f4* e4 = reinterpret_cast<f4*>(e + start);
+    f4* u4 = kMomentum ? reinterpret_cast<f4*>(u + start) : nullptr;
+    f4 gv[kSlots], uv[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      gv[v] = GC_NT_LOAD_G ? __builtin_nontemporal_load(g4 + q) : g4[q];
+      acc[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(e4 + q) : e4[q];
+      if (kMomentum) uv[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(u4 + q) : u4[q];
+    }
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      f4 x = gv[v];
+      if (kMomentum) {
+        const f4 mu = m * uv[v];
+        x = mu + x;
+        if (GC_NT_STORE_E) __builtin_nontemporal_store(x, u4 + q); else u4[q] = x;
+      }
+      acc[v] = acc[v] + x;
+      if (GC_NT_STORE_E) __builtin_nontemporal_store(acc[v], e4 + q); else e4[q] = acc[v];
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = pb + v * 256 + c;
+        float a = 0.0f;
+        if (p < len) {
+          const int64_t i = start + p;
+          float x = g[i];
+          if (kMomentum) {
+            const float mu = m * u[i];
+            x = mu + x;
+            u[i] = x;
+          }
+          a = e[i] + x;
+          e[i] = a;
+        }
+        acc[v][c] = a;
+      }
+  }
+}
+
+template <bool kMomentum>
+__global__ __launch_bounds__(kThreads) void k_sign_pass1(DevPlan P, const float* __restrict__ g,
+                                                        float* __restrict__ e,
+                                                        float* __restrict__ u, float m) {
+  __shared__ double s_d[kWaves];
+  const int64_t t = blockIdx.x;
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z;
+  f4 acc[kSlots];
+  ef_add_tile<kMomentum>(g, e, u, m, start, len, acc);
+  double l1 = 0.0;   // lanes past len hold 0
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) l1 += fabs((double)acc[v][c]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) l1 += __shfl_xor(l1, d, 64);
+  if (lane_id() == 0) s_d[wave_id()] = l1;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) sum += s_d[i];
+    P.tile_l1[t] = sum;
+  }
+}
+
+// Per segment: scale = fl32(S / n), S = the tiles' sums (a fixed tree order).
+__global__ __launch_bounds__(1024) void k_sign_scale(DevPlan P, float* __restrict__ scales) {
+  __shared__ double s_d[16];
+  const int s = blockIdx.x;
+  const int64_t t0 = P.tile_base[s], t1 = P.tile_base[s + 1];
+  double sum = 0.0;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += 1024) sum += P.tile_l1[t];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  if (lane_id() == 0) s_d[wave_id()] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < 16; ++i) tot += s_d[i];
+    const int64_t n = P.seg_off[s + 1] - P.seg_off[s];
+    scales[s] = n > 0 ? (float)(tot / (double)n) : 0.0f;
+  }
+}
+
+// Sign bits of one tile-shaped block: lane l of slot v covers 4 elements of the 32-element
+// word (w*kSlots + v)*8 + l/8 (tile-relative); its nibble lands at bit 4*(l%8).
+__global__ __launch_bounds__(kThreads) void k_sign_pass2(DevPlan P, float* __restrict__ e,
+                                                        uint32_t* __restrict__ bits,
+                                                        const float* __restrict__ scales) {
+  const int64_t t = blockIdx.x;
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const float scale = scales[s];
+  const int pb = slot_base(), lane = lane_id();
+  f4 acc[kSlots];
+  load_tile(e + start, len, acc);
+  uint32_t* wb = bits + P.word_off[s] + (t - P.tile_base[s]) * (int64_t)(kTile / 32);
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    uint32_t nib = 0;
+    f4 r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool neg = acc[v][c] < 0.0f;
+      nib |= (neg && pb + v * 256 + c < len) ? (1u << c) : 0u;
+      r[c] = acc[v][c] - (neg ? -scale : scale);
+    }
+    uint32_t word = nib << (4 * (lane & 7));
+    word |= __shfl_xor(word, 1, 64);
+    word |= __shfl_xor(word, 2, 64);
+    word |= __shfl_xor(word, 4, 64);
+    const int wi = (pb + v * 256) / 32;   // tile-relative word of this lane's group
+    if ((lane & 7) == 0 && wi * 32 < len) wb[wi] = word;
+    if (len == kTile && (start & 3) == 0) {
+      f4* e4 = reinterpret_cast<f4*>(e + start);
+      if (GC_NT_STORE_E) __builtin_nontemporal_store(r, e4 + ((pb + v * 256) >> 2));
+      else e4[(pb + v * 256) >> 2] = r;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (pb + v * 256 + c < len) e[start + pb + v * 256 + c] = r[c];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_sign_decompress(DevPlan P,
+                                                             const uint32_t* __restrict__ bits,
+                                                             const float* __restrict__ scales,
+                                                             float* __restrict__ dense,
+                                                             int accumulate) {
+  const int64_t t = blockIdx.x;
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const float scale = scales[s];
+  const int pb = slot_base(), lane = lane_id();
+  const uint32_t* wb = bits + P.word_off[s] + (t - P.tile_base[s]) * (int64_t)(kTile / 32);
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    const int wi = (pb + v * 256) / 32;
+    const uint32_t nib = wi * 32 < len ? (wb[wi] >> (4 * (lane & 7))) & 0xFu : 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int p = pb + v * 256 + c;
+      if (p < len) {
+        const float x = ((nib >> c) & 1u) ? -scale : scale;
+        float* d = dense + start + p;
+        *d = accumulate ? *d + x : x;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------ int8 stage
 // Per segment: scale = fl(max |v| / 127) over the kept values.
 __global__ __launch_bounds__(1024) void k_absmax(OutPlan O, const float* __restrict__ vals,
@@ -1070,6 +1247,31 @@ hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u,
   if (P.n_chunks > 0) k_emit_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P, o);
   k_emit_full<<<kFullBlocks, kThreads, 0, st>>>(P, o);
   k_finalize<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
+  return hipGetLastError();
+}
+
+hipError_t launch_sign(const DevPlan& P, const float* g, float* e, float* u, float m,
+                       uint32_t* bits, float* scales, hipStream_t st, hipEvent_t ev_begin,
+                       hipEvent_t ev_end) {
+  if (P.n_seg == 0) return hipSuccess;
+  if (ev_begin) (void)hipEventRecord(ev_begin, st);
+  if (P.n_tiles > 0) {
+    if (u)
+      k_sign_pass1<true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, u, m);
+    else
+      k_sign_pass1<false><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, nullptr, m);
+  }
+  k_sign_scale<<<P.n_seg, 1024, 0, st>>>(P, scales);
+  if (P.n_tiles > 0) k_sign_pass2<<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, e, bits, scales);
+  if (ev_end) (void)hipEventRecord(ev_end, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_sign_decompress(const DevPlan& P, const uint32_t* bits, const float* scales,
+                                  float* dense, int accumulate, hipStream_t st) {
+  if (P.n_tiles == 0) return hipSuccess;
+  k_sign_decompress<<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, bits, scales, dense,
+                                                             accumulate);
   return hipGetLastError();
 }
 

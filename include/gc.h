@@ -147,6 +147,31 @@ int gc_decompress(const gc_plan* plan, const float* vals, const int8_t* codes,
                   const float* scales, const int32_t* idx, float* dense, int accumulate,
                   void* stream);
 
+/*
+ * 1-bit sign compression with error feedback ("Communication Optimization > Gradient
+ * Compression", 1-bit SGD section: Q(g) = sign(g) * ||g||_1 / d with the scalar computed
+ * per layer; its QSGD paragraph: 1-bit needs error feedback, as top-K does).  Per segment
+ * of n elements, after the same momentum and EF add as gc_topk_ef_compress:
+ *   scale = fl32(S / n), S = sum |acc| accumulated in double (summation order unspecified:
+ *           the scale may differ from the exactly rounded value by 1 ulp);
+ *   sign  = -1 where acc < 0, else +1 (zeros of either sign send +1);
+ *   bit i of the segment (word i/32, bit i%32, least significant first) = 1 for sign -1;
+ *   e = fl(acc - sign * scale).
+ * The plan's k is not used (a plan with k = 0 serves).  out_bits: uint32[word_off[n_seg]]
+ * with the segment offsets of gc_plan_sign_layout; out_scales: float[n_seg].
+ * g, e and u must be 16-byte aligned.  Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_sign_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                        uint32_t* out_bits, float* out_scales, void* stream);
+
+/* First 32-bit word of each segment's sign bits, word_off[s+1] - word_off[s] = ceil(n_s/32)
+ * (host int64[n_seg + 1]). */
+int gc_plan_sign_layout(const gc_plan* plan, int64_t* word_off);
+
+/* dense[seg_off[s] + i] = sign_i * scale_s (or += with accumulate) over every segment. */
+int gc_sign_decompress(const gc_plan* plan, const uint32_t* bits, const float* scales,
+                       float* dense, int accumulate, void* stream);
+
 /* Forget the threshold estimates: the next compress call runs as on a fresh plan. */
 int gc_plan_reset_estimate(gc_plan* plan, void* stream);
 

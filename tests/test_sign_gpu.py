@@ -1,0 +1,154 @@
+"""GPU parity of the 1-bit sign codec with error feedback (C ABI) against the CPU oracle.
+
+Bits are compared bit for bit.  The per-segment scale is fl32(S/n) with S accumulated in
+double in an unspecified order, so it may differ from the oracle's by one ulp (the
+tolerance stated for fp32 scales); when the two scales are equal the residual must be
+bit-exact, otherwise within one ulp of the scale, and the oracle then continues from the
+GPU's residual.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gradient_compression_amd as gca
+import oracle
+from synth import gen, workload
+from tests.gpu_helpers import assert_bitwise, log
+
+pytestmark = pytest.mark.gpu
+
+
+def ulp(x):
+    return float(np.spacing(np.float32(abs(x))))
+
+
+def run_sign(sizes, grads, momentum=None, label=""):
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    plan = gca.Plan(off, k=0)
+    dev = torch.device("cuda")
+    e_d = torch.zeros(n, device=dev)
+    e_h = np.zeros(n, np.float32)
+    u_d = torch.zeros(n, device=dev) if momentum is not None else None
+    u_h = np.zeros(n, np.float32) if momentum is not None else None
+    bits = torch.empty(max(plan.total_words, 1), dtype=torch.int32, device=dev)
+    scales = torch.empty(max(len(sizes), 1), device=dev)
+    resynced = 0
+    for t, g in enumerate(grads):
+        log(f"[sign {label}] iteration {t}")
+        plan.sign_compress(torch.from_numpy(g).to(dev), e_d, bits, scales, u=u_d,
+                           momentum=momentum or 0.0)
+        torch.cuda.synchronize()
+        b_d = bits.cpu().numpy().view(np.uint32)
+        s_d = scales.cpu().numpy()
+        e_dev = e_d.cpu().numpy()
+        for s in range(len(sizes)):
+            a, b = int(off[s]), int(off[s + 1])
+            wa, wb = int(plan.word_off[s]), int(plan.word_off[s + 1])
+            hb, hs = oracle.sign_ef_segment(g[a:b].copy(), e_h[a:b], None if u_h is None else u_h[a:b],
+                                            momentum or 0.0)
+            assert_bitwise(b_d[wa:wb], hb, f"{label} it{t} seg{s} bits")
+            assert abs(float(s_d[s]) - float(hs)) <= ulp(hs), f"{label} it{t} seg{s} scale"
+            if s_d[s] == hs:
+                assert_bitwise(e_dev[a:b], e_h[a:b], f"{label} it{t} seg{s} residual")
+            else:
+                assert np.max(np.abs(e_dev[a:b] - e_h[a:b])) <= 2 * ulp(hs)
+                e_h[a:b] = e_dev[a:b]
+                resynced += 1
+        if u_h is not None:
+            assert_bitwise(u_d, u_h, f"{label} it{t} velocity")
+    plan.close()
+    return resynced
+
+
+def grads(n, T, seed, scale=1e-3):
+    rng = np.random.default_rng(seed)
+    return [(rng.standard_t(3, n) * scale).astype(np.float32) for _ in range(T)]
+
+
+def test_sign_ragged_segments():
+    sizes = [1, 31, 32, 33, 4095, 8192, 8193, 100003, 262144, 0, 7]
+    r = run_sign(sizes, grads(sum(sizes), 4, 1), label="ragged")
+    log(f"scale resyncs: {r}")
+
+
+def test_sign_momentum_and_zeros():
+    sizes = [4096, 50000, 11008 * 3]
+    n = sum(sizes)
+    gs = grads(n, 3, 2, 1e-4)
+    gs[1][:4096] = 0.0
+    gs[1][4096:5000] = -0.0
+    run_sign(sizes, gs, momentum=0.9, label="momentum")
+
+
+def test_sign_decompress():
+    sizes = [1000, 37, 8192 * 3 + 1]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    plan = gca.Plan(off, k=0)
+    g = grads(n, 1, 3)[0]
+    e = torch.zeros(n, device="cuda")
+    bits = torch.empty(plan.total_words, dtype=torch.int32, device="cuda")
+    scales = torch.empty(len(sizes), device="cuda")
+    plan.sign_compress(torch.from_numpy(g).cuda(), e, bits, scales)
+    base = np.random.default_rng(4).standard_normal(n).astype(np.float32)
+    b_h = bits.cpu().numpy().view(np.uint32)
+    s_h = scales.cpu().numpy()
+    for acc in (False, True):
+        dense = torch.from_numpy(base).cuda()
+        plan.sign_decompress(bits, scales, dense, accumulate=acc)
+        want = base.copy()
+        for s in range(len(sizes)):
+            a, b = int(off[s]), int(off[s + 1])
+            want[a:b] = oracle.sign_decompress_segment(
+                b_h[int(plan.word_off[s]):int(plan.word_off[s + 1])], s_h[s], b - a,
+                dense=want[a:b].copy(), accumulate=acc)
+        assert dense.cpu().numpy().tobytes() == want.tobytes()
+    plan.close()
+
+
+def test_sign_full_size_llama2_7b():
+    """Full size: sampled segments against the oracle; every segment's bits, residual and
+    scale (against an fp64 torch sum, within one ulp) checked on the GPU."""
+    wl = workload("c5p_llama2_7b_plain")
+    off = wl.offsets()
+    dev = torch.device("cuda")
+    plan = gca.Plan(off, k=0)
+    g = torch.empty(wl.n, device=dev)
+    e = torch.zeros(wl.n, device=dev)
+    bits = torch.empty(plan.total_words, dtype=torch.int32, device=dev)
+    scales = torch.empty(wl.n_seg, device=dev)
+    sample = [2, 8, 150, 289]
+    host = {s: np.zeros(int(off[s + 1] - off[s]), np.float32) for s in sample}
+    for t in range(2):
+        gen.fill_gradient(g, wl, t)
+        e_prev = e.clone()
+        plan.sign_compress(g, e, bits, scales)
+        torch.cuda.synchronize()
+        log(f"[sign full] it{t}")
+        sc = scales.cpu().numpy()
+        for s in range(wl.n_seg):
+            a, b = int(off[s]), int(off[s + 1])
+            acc = torch.add(e_prev[a:b], g[a:b])
+            want = float((acc.double().abs().sum() / (b - a)).item())
+            assert abs(float(sc[s]) - want) <= ulp(want) * 1.01, f"scale seg {s}"
+            neg = acc < 0
+            q = torch.where(neg, -scales[s], scales[s])
+            assert torch.equal(torch.sub(acc, q).view(torch.int32), e[a:b].view(torch.int32))
+            wa, wb = int(plan.word_off[s]), int(plan.word_off[s + 1])
+            w = bits[wa:wb].view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+            pos = torch.arange(b - a, device=dev)
+            got = ((w[pos // 32] >> (pos % 32)) & 1).bool()
+            assert torch.equal(got, neg), f"bits seg {s}"
+        for s in sample:
+            a, b = int(off[s]), int(off[s + 1])
+            hb, hs = oracle.sign_ef_segment(g[a:b].cpu().numpy(), host[s])
+            assert abs(float(sc[s]) - float(hs)) <= ulp(hs)
+            assert_bitwise(bits[int(plan.word_off[s]):int(plan.word_off[s + 1])], hb.view(np.int32),
+                           f"seg{s} bits")
+            if sc[s] == hs:
+                assert_bitwise(e[a:b], host[s], f"seg{s} residual")
+            else:
+                host[s][:] = e[a:b].cpu().numpy()
+        del e_prev
+    plan.close()
