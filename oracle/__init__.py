@@ -54,6 +54,10 @@ def load(path: str):
     L.orc_sign_ef_segment.restype = None
     L.orc_sign_decompress_segment.argtypes = [i64, vp, f32, vp, ctypes.c_int]
     L.orc_sign_decompress_segment.restype = None
+    L.orc_qsgd_segment.argtypes = [i64, i64, vp, vp, vp, f32, i32, u64, u64, vp, vp]
+    L.orc_qsgd_segment.restype = ctypes.c_int
+    L.orc_qsgd_decompress_segment.argtypes = [i64, vp, f32, i32, vp, ctypes.c_int]
+    L.orc_qsgd_decompress_segment.restype = None
     return L
 
 
@@ -190,4 +194,27 @@ def sign_decompress_segment(bits, scale, n, dense=None, accumulate=False):
     if dense is None:
         dense = np.empty(n, np.float32)
     lib().orc_sign_decompress_segment(n, _p(bits), float(scale), _p(dense), int(bool(accumulate)))
+    return dense
+
+
+def qsgd_segment(g, e=None, u=None, momentum=0.9, levels=127, seed=0, step=0, seg_base=0):
+    """QSGD with `levels` levels of one segment; with e, error feedback in place on e.
+    Returns (codes int8[n], norm float32)."""
+    _f32(g, "g")
+    n = g.size
+    codes = np.empty(n, np.int8)
+    norm = np.empty(1, np.float32)
+    rc = lib().orc_qsgd_segment(n, int(seg_base), _p(g), _p(e), _p(u), float(momentum),
+                                int(levels), int(seed), int(step), _p(codes), _p(norm))
+    if rc:
+        raise ValueError("oracle rejected the QSGD arguments")
+    return codes, norm[0]
+
+
+def qsgd_decompress_segment(codes, norm, levels, dense=None, accumulate=False):
+    codes = np.ascontiguousarray(codes, np.int8)
+    if dense is None:
+        dense = np.empty(codes.size, np.float32)
+    lib().orc_qsgd_decompress_segment(codes.size, _p(codes), float(norm), int(levels), _p(dense),
+                                      int(bool(accumulate)))
     return dense

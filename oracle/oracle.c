@@ -37,6 +37,10 @@
  * 1-bit sign compression with error feedback ("Communication Optimization > Gradient
  * Compression", 1-bit SGD section): per segment scale = fl32(sum |acc| / n) with the sum
  * in double, one sign bit per element, residual e = fl(acc - sign * scale).
+ *
+ * QSGD with s levels (same page, QSGD paragraph, with its missing 1/s restored): one l2
+ * norm per segment, stochastic levels drawn from Philox4x32-10 (counter tag 0x52), error
+ * feedback of the quantisation error optional.
  */
 #include <math.h>
 #include <stdint.h>
@@ -311,6 +315,85 @@ void orc_sign_decompress_segment(int64_t n, const uint32_t* bits, float scale, f
 {
     for (int64_t i = 0; i < n; ++i) {
         float v = ((bits[i / 32] >> (i % 32)) & 1u) ? -scale : scale;
+        dense[i] = accumulate ? dense[i] + v : v;
+    }
+}
+
+/* ------------------------------------------------------------ QSGD s-level codec */
+
+/* Top 24 bits of the QSGD draw of global index gidx (counter tag 0x52). */
+static uint32_t qsgd_draw24(uint64_t seed, uint64_t step, int64_t gidx)
+{
+    uint32_t ctr[4] = {(uint32_t)(uint64_t)gidx, (uint32_t)((uint64_t)gidx >> 32),
+                       (uint32_t)step, 0x52u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t r[4];
+    orc_philox4x32_10(ctr, key, r);
+    return r[0] >> 8;
+}
+
+/*
+ * QSGD with s levels ("Communication Optimization > Gradient Compression", QSGD paragraph:
+ * Q_s(g) = ||g|| sgn(g) xi(g, s), xi rounding |g| / (||g|| / s) up or down at random so that
+ * E[Q_s(g)] = g; at s = 2^b - 1 it is a b-bit code; the printed formula lacks the factor
+ * 1/s that makes the expectation exact, restored here), one norm per segment.  With e (error
+ * feedback, genomic-FL glossary quantization section) acc = e + x, else acc = x; x = g or
+ * the momentum-corrected u.
+ *   norm = fl32(sqrt(S)), S = sum acc_i^2 in double (index order);
+ *   step = fl32(norm / s);  a = min(fl32(|acc| / step), s);  l = floor(a);
+ *   xi = l + [u24 < (a - l) * 2^24]  (u24: top 24 bits of Philox4x32-10 word 0, key (seed lo,
+ *        seed hi), counter (global index lo, hi, step lo, 0x52));
+ *   code = sgn(acc) * xi (int8, |code| <= s <= 127); step == 0 gives code 0;
+ *   with e: e = fl(acc - fl(code * step)).
+ */
+int orc_qsgd_segment(int64_t n, int64_t seg_base, const float* g, float* e, float* u, float m,
+                     int32_t s, uint64_t seed, uint64_t step, int8_t* codes, float* norm_out)
+{
+    if (s < 1 || s > 127 || n < 0) return -1;
+    float* acc = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!acc) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        float x = g[i];
+        if (u) {
+            float mu = m * u[i];
+            u[i] = mu + x;
+            x = u[i];
+        }
+        acc[i] = e ? e[i] + x : x;
+    }
+    double sq = 0.0;
+    for (int64_t i = 0; i < n; ++i) sq += (double)acc[i] * (double)acc[i];
+    float norm = (float)sqrt(sq);
+    float qstep = norm / (float)s;
+    *norm_out = norm;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = acc[i];
+        int q = 0;
+        if (qstep != 0.0f) {
+            float a = fabsf(v) / qstep;
+            if (a > (float)s) a = (float)s;
+            float l = floorf(a);
+            float frac = a - l;
+            q = (int)l + (((float)qsgd_draw24(seed, step, seg_base + i) < frac * 16777216.0f) ? 1 : 0);
+        }
+        int code = signbit(v) ? -q : q;
+        codes[i] = (int8_t)code;
+        if (e) {
+            float deq = (float)code * qstep;
+            e[i] = v - deq;
+        }
+    }
+    free(acc);
+    return 0;
+}
+
+/* dense[i] = fl(code_i * fl(norm / s)) (or += with accumulate). */
+void orc_qsgd_decompress_segment(int64_t n, const int8_t* codes, float norm, int32_t s,
+                                 float* dense, int accumulate)
+{
+    float qstep = norm / (float)s;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = (float)codes[i] * qstep;
         dense[i] = accumulate ? dense[i] + v : v;
     }
 }

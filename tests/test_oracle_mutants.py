@@ -12,6 +12,7 @@ from tests import test_oracle_quant as T_q
 from tests import test_oracle_ratio as T_r
 from tests import test_oracle_select as T_s
 from tests import test_oracle_sign as T_g
+from tests import test_oracle_qsgd as T_q8
 
 MUTANTS = {
     "tie_rule_higher_index_wins": ("return a->pos < b->pos ? -1 : 1;",
@@ -42,6 +43,13 @@ MUTANTS = {
     "sign_residual_added": ("e[i] = e[i] - q;", "e[i] = e[i] + q;"),
     "sign_bits_msb_first": ("if (neg) bits[i / 32] |= 1u << (i % 32);",
                             "if (neg) bits[i / 32] |= 1u << (31 - i % 32);"),
+    "qsgd_step_without_levels": ("float qstep = norm / (float)s;\n    *norm_out",
+                                 "float qstep = norm;\n    *norm_out"),
+    "qsgd_norm_without_sqrt": ("float norm = (float)sqrt(sq);", "float norm = (float)sq;"),
+    "qsgd_round_to_nearest": ("q = (int)l + (((float)qsgd_draw24(seed, step, seg_base + i) < frac * 16777216.0f) ? 1 : 0);",
+                              "q = (int)l + (frac >= 0.5f ? 1 : 0);"),
+    "qsgd_residual_not_fed_back": ("            e[i] = v - deq;\n        }\n    }\n    free(acc);",
+                                   "            e[i] = v;\n        }\n    }\n    free(acc);"),
 }
 
 
@@ -62,6 +70,9 @@ def _pins(orc):
     yield lambda: T_g.test_hand_cases(orc)
     yield lambda: T_g.test_scale_bits_residual(orc, 1000)
     yield lambda: T_g.test_conservation_and_ratio(orc)
+    yield lambda: T_q8.test_hand_integer_levels(orc)
+    yield lambda: T_q8.test_unbiased_and_toy(orc)
+    yield lambda: T_q8.test_norm_codes_and_error_feedback(orc)
 
 
 def _failures():
