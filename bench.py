@@ -63,8 +63,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--codec", choices=("topk", "sign"), default="topk",
-                    help="topk: EF-Top-k (default); sign: 1-bit sign with error feedback")
+    ap.add_argument("--codec", choices=("topk", "sign", "qsgd"), default="topk",
+                    help="topk: EF-Top-k (default); sign: 1-bit sign with error feedback; "
+                         "qsgd: QSGD with 127 levels and error feedback")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-momentum-variant", action="store_true")
     return ap.parse_args()
@@ -74,6 +75,8 @@ def bytes_per_element(wl, codec="topk"):
     """Algorithmic HBM bytes per element of the timed streaming passes."""
     if codec == "sign":   # pass 1: g, e (u) in, e (u) out; pass 2: e in, e out, one bit
         return (20 if wl.momentum is not None else 12) + 8 + 1 / 8
+    if codec == "qsgd":   # pass 1 as for sign; pass 2: e in, e out, one int8 code
+        return (20 if wl.momentum is not None else 12) + 8 + 1
     return 20 if wl.momentum is not None else 12
 
 
@@ -85,6 +88,9 @@ def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
     def step(t):
         if codec == "sign":
             plan.sign_compress(gbufs[t % len(gbufs)], e, codes, scales, u=u, momentum=m)
+        elif codec == "qsgd":
+            plan.qsgd_compress(gbufs[t % len(gbufs)], codes, scales, levels=127, e=e, u=u,
+                               momentum=m, seed=0, step=t)
         elif wl.int8:   # compress and int8 (error feedback of the quantisation error) in one call
             plan.compress_int8(gbufs[t % len(gbufs)], e, idx, codes, scales, out_vals=vals,
                                u=u, momentum=m, seed=0, step=t)
@@ -113,7 +119,7 @@ def setup(wl, n_gbufs=4, codec="topk"):
     import torch
     import gradient_compression_amd as gca
     from synth import gen
-    plan = gca.Plan(wl.offsets(), ratio=0.0 if codec == "sign" else wl.ratio)
+    plan = gca.Plan(wl.offsets(), ratio=wl.ratio if codec == "topk" else 0.0)
     dev = torch.device("cuda")
     gbufs = []
     for t in range(n_gbufs):
@@ -128,6 +134,9 @@ def setup(wl, n_gbufs=4, codec="topk"):
     scales = torch.empty(wl.n_seg, dtype=torch.float32, device=dev) if wl.int8 else None
     if codec == "sign":   # sign bits in place of codes, one scale per segment
         codes = torch.empty(plan.total_words, dtype=torch.int32, device=dev)
+        scales = torch.empty(wl.n_seg, dtype=torch.float32, device=dev)
+    if codec == "qsgd":   # one int8 code per element, one norm per segment
+        codes = torch.empty(wl.n, dtype=torch.int8, device=dev)
         scales = torch.empty(wl.n_seg, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     return plan, gbufs, e, u, (vals, idx, codes, scales)
@@ -255,7 +264,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": wl.name if codec == "topk" else f"{wl.name}+sign1bit",
+            "workload": wl.name if codec == "topk" else f"{wl.name}+{codec}",
             "codec": codec,
             "n_elements": wl.n,
             "segments": wl.n_seg,
@@ -272,8 +281,9 @@ def main():
         "full_path_segments_last_step": int((st["mode"] == gca.MODE_FULL).sum()),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("k_ef_capture (EF add + key + candidate capture)" if codec == "topk"
-                       else "k_sign_pass1 + k_sign_scale + k_sign_pass2"),
+            "kernel": {"topk": "k_ef_capture (EF add + key + candidate capture)",
+                       "sign": "k_sign_pass1 + k_sign_scale + k_sign_pass2",
+                       "qsgd": "k_qsgd_pass1 + k_qsgd_norm + k_qsgd_pass2"}[codec],
             "achieved": round(k1_ach, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -285,7 +295,8 @@ def main():
         },
     }
     if codec != "topk":
-        result["metric"] = "1-bit sign EF compress GB/s of fp32 gradient (1 GPU) and % of HBM peak"
+        name = {"sign": "1-bit sign EF", "qsgd": "QSGD-127 EF"}[codec]
+        result["metric"] = f"{name} compress GB/s of fp32 gradient (1 GPU) and % of HBM peak"
         print(json.dumps(result), flush=True)
         return
     if not args.no_cpu_baseline:

@@ -29,7 +29,7 @@ EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layo
            "gc_topk_ef_compress", "gc_topk_ef_compress_int8", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
            "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32",
            "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
-           "gc_sign_decompress")
+           "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress")
 
 _lib = None
 
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         "gc_sign_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp],
         "gc_plan_sign_layout": [vp, vp],
         "gc_sign_decompress": [vp, vp, vp, vp, ctypes.c_int, vp],
+        "gc_qsgd_compress": [vp, vp, vp, vp, f32, i32, u64, u64, vp, vp, vp],
+        "gc_qsgd_decompress": [vp, vp, vp, i32, vp, ctypes.c_int, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -245,6 +247,29 @@ class Plan:
             _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
             _stream(stream))
         _check(rc, "gc_sign_decompress")
+
+    def qsgd_compress(self, g, out_codes, out_norms, levels: int = 127, e=None, u=None,
+                      momentum: float = 0.0, seed: int = 0, step: int = 0, stream=None):
+        """QSGD with `levels` levels, one l2 norm per segment; with e, error feedback."""
+        import torch
+        n = self.n
+        rc = lib().gc_qsgd_compress(
+            self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
+            _dev_ptr(u, torch.float32, "u", n), float(momentum), int(levels),
+            int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1),
+            _dev_ptr(out_codes, torch.int8, "out_codes", n),
+            _dev_ptr(out_norms, torch.float32, "out_norms", self.n_seg), _stream(stream))
+        _check(rc, "gc_qsgd_compress")
+
+    def qsgd_decompress(self, codes, norms, dense, levels: int = 127, accumulate=False,
+                        stream=None):
+        import torch
+        rc = lib().gc_qsgd_decompress(
+            self._h, _dev_ptr(codes, torch.int8, "codes", self.n),
+            _dev_ptr(norms, torch.float32, "norms", self.n_seg), int(levels),
+            _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
+            _stream(stream))
+        _check(rc, "gc_qsgd_decompress")
 
     def reset_estimate(self, stream=None):
         _check(lib().gc_plan_reset_estimate(self._h, _stream(stream)), "gc_plan_reset_estimate")

@@ -435,6 +435,36 @@ int gc_sign_decompress(const gc_plan* plan, const uint32_t* bits, const float* s
   return err == hipSuccess ? GC_OK : GC_ERR_HIP;
 }
 
+int gc_qsgd_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                     int32_t levels, uint64_t seed, uint64_t step, int8_t* out_codes,
+                     float* out_norms, void* stream) {
+  if (!plan || levels < 1 || levels > 127) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!g || !out_codes || !aligned16(g) || (reinterpret_cast<uintptr_t>(out_codes) & 3)))
+    return GC_ERR_INVALID_ARG;
+  if ((e && !aligned16(e)) || (u && !aligned16(u))) return GC_ERR_INVALID_ARG;
+  if (plan->n_seg > 0 && !out_norms) return GC_ERR_INVALID_ARG;
+  if (any && ((e && (g == e || e == u)) || (u && g == u))) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  hipEvent_t b = nullptr, en = nullptr;
+  if (int rc = timing_events(plan, &b, &en)) return rc;
+  const hipError_t err = gc::launch_qsgd(plan->dp, g, e, u, momentum, levels, seed, step,
+                                         out_codes, out_norms, static_cast<hipStream_t>(stream),
+                                         b, en);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_qsgd_decompress(const gc_plan* plan, const int8_t* codes, const float* norms,
+                       int32_t levels, float* dense, int accumulate, void* stream) {
+  if (!plan || levels < 1 || levels > 127) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!codes || !norms || !dense)) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  const hipError_t err = gc::launch_qsgd_decompress(plan->dp, codes, norms, levels, dense,
+                                                    accumulate, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
 int gc_quant_int8(gc_plan* plan, const float* vals, const int32_t* idx, float* e, uint64_t seed,
                   uint64_t step, int8_t* out_codes, float* out_scales, void* stream) {
   if (!plan) return GC_ERR_INVALID_ARG;

@@ -100,7 +100,7 @@ struct DevPlan {
   float* beta;                 // [n_seg] threshold margin: next threshold = beta * |kth|
   uint32_t* err;               // [1] internal consistency flag (0 = fine)
   uint32_t* tile_max;          // [n_tiles] largest key of a full-path tile (int8 absmax)
-  double* tile_l1;             // [n_tiles] sum |acc| of a tile (1-bit sign scale)
+  double* tile_l1;             // [n_tiles] per-tile sum |acc| (sign) or sum acc^2 (QSGD)
   const int64_t* word_off;     // [n_seg + 1] first 32-bit word of each segment's sign bits
   // per-tile state
   uint32_t* run_off;           // [n_tiles] offset of the tile's run in its segment region
@@ -148,6 +148,11 @@ hipError_t launch_reset(const DevPlan& P, hipStream_t st);
 hipError_t launch_sign(const DevPlan& P, const float* g, float* e, float* u, float m,
                        uint32_t* bits, float* scales, hipStream_t st, hipEvent_t ev_begin,
                        hipEvent_t ev_end);
+hipError_t launch_qsgd(const DevPlan& P, const float* g, float* e, float* u, float m,
+                       int levels, uint64_t seed, uint64_t step, int8_t* codes, float* norms,
+                       hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_qsgd_decompress(const DevPlan& P, const int8_t* codes, const float* norms,
+                                  int levels, float* dense, int accumulate, hipStream_t st);
 hipError_t launch_sign_decompress(const DevPlan& P, const uint32_t* bits, const float* scales,
                                   float* dense, int accumulate, hipStream_t st);
 hipError_t launch_quant(const OutPlan& O, const float* vals, const int32_t* idx, float* e,

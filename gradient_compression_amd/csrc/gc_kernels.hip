@@ -60,23 +60,32 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
   return c0;
 }
 
-// Stochastic int8 code of a kept value v (global index gi) at the segment's scale; returns
-// the code and writes the dequantised value fl(code * scale) to *deq.
-__device__ __forceinline__ int quant_code(float v, float scale, int64_t gi, uint32_t seed_lo,
-                                          uint32_t seed_hi, uint32_t step_lo, float* deq) {
+// Stochastic level of v (global index gi) at quantisation step `scale`: a = min(|v|/scale,
+// limit), level floor(a) or floor(a) + 1 with probability frac(a) (top 24 bits of Philox
+// word 0 at counter (gi lo, gi hi, step lo, tag)); returns sign(v) * level and writes the
+// dequantised value fl(code * scale) to *deq.  scale == 0 gives code 0.
+__device__ __forceinline__ int sr_code(float v, float scale, float limit, int64_t gi,
+                                       uint32_t seed_lo, uint32_t seed_hi, uint32_t step_lo,
+                                       uint32_t tag, float* deq) {
   int q = 0;
   if (scale != 0.0f) {
     float a = fabsf(v) / scale;
-    if (a > 127.0f) a = 127.0f;
+    if (a > limit) a = limit;
     const float f = floorf(a);
     const float frac = a - f;
     const uint32_t u24 = philox_word0((uint32_t)gi, (uint32_t)((uint64_t)gi >> 32), step_lo,
-                                      0x51u, seed_lo, seed_hi) >> 8;
+                                      tag, seed_lo, seed_hi) >> 8;
     q = (int)f + (((float)u24 < frac * 16777216.0f) ? 1 : 0);
   }
   const int code = signbit(v) ? -q : q;
   *deq = (float)code * scale;
   return code;
+}
+
+// The int8 stage of a kept value: 127 levels of fl(absmax / 127), counter tag 0x51.
+__device__ __forceinline__ int quant_code(float v, float scale, int64_t gi, uint32_t seed_lo,
+                                          uint32_t seed_hi, uint32_t step_lo, float* deq) {
+  return sr_code(v, scale, 127.0f, gi, seed_lo, seed_hi, step_lo, 0x51u, deq);
 }
 
 // Exclusive scan of one uint32 per thread over a block of NT threads; *total gets the sum.
@@ -1110,6 +1119,151 @@ __global__ __launch_bounds__(kThreads) void k_sign_decompress(DevPlan P,
   }
 }
 
+// ------------------------------------------------------------------------------ QSGD
+// QSGD with s levels ("Communication Optimization > Gradient Compression", QSGD paragraph,
+// with the 1/s that makes E[Q] = g restored): pass 1 forms acc (e + x with error feedback,
+// else x) and each tile's sum of acc^2 in double; norm = fl32(sqrt(S)) per segment; pass 2
+// draws the levels at step fl32(norm / s) (counter tag 0x52) and, with error feedback,
+// writes e = fl(acc - fl(code * step)).
+
+template <bool kMomentum, bool kEF>
+__global__ __launch_bounds__(kThreads) void k_qsgd_pass1(DevPlan P, const float* __restrict__ g,
+                                                        float* __restrict__ e,
+                                                        float* __restrict__ u, float m) {
+  __shared__ double s_d[kWaves];
+  const int64_t t = blockIdx.x;
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z;
+  f4 acc[kSlots];
+  if (kEF) {
+    ef_add_tile<kMomentum>(g, e, u, m, start, len, acc);
+  } else if (kMomentum) {  // u = m*u + g, stored; acc = u
+    const int pb = slot_base();
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = pb + v * 256 + c;
+        float a = 0.0f;
+        if (p < len) {
+          const float mu = m * u[start + p];
+          a = mu + g[start + p];
+          u[start + p] = a;
+        }
+        acc[v][c] = a;
+      }
+  } else {
+    load_tile(g + start, len, acc);
+  }
+  double sq = 0.0;
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sq += (double)acc[v][c] * (double)acc[v][c];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sq += __shfl_xor(sq, d, 64);
+  if (lane_id() == 0) s_d[wave_id()] = sq;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) sum += s_d[i];
+    P.tile_l1[t] = sum;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_qsgd_norm(DevPlan P, float* __restrict__ norms) {
+  __shared__ double s_d[16];
+  const int s = blockIdx.x;
+  const int64_t t0 = P.tile_base[s], t1 = P.tile_base[s + 1];
+  double sum = 0.0;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += 1024) sum += P.tile_l1[t];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  if (lane_id() == 0) s_d[wave_id()] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < 16; ++i) tot += s_d[i];
+    norms[s] = (float)sqrt(tot);
+  }
+}
+
+// kSrc: 0 = acc in e (error feedback), 1 = acc in u (momentum, no feedback), 2 = acc = g.
+template <int kSrc>
+__global__ __launch_bounds__(kThreads) void k_qsgd_pass2(DevPlan P, const float* __restrict__ g,
+                                                        float* __restrict__ e,
+                                                        const float* __restrict__ u,
+                                                        const float* __restrict__ norms,
+                                                        int levels, int8_t* __restrict__ codes,
+                                                        uint32_t seed_lo, uint32_t seed_hi,
+                                                        uint32_t step_lo) {
+  const int64_t t = blockIdx.x;
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const float qstep = norms[s] / (float)levels;
+  const float limit = (float)levels;
+  const int pb = slot_base();
+  f4 acc[kSlots];
+  load_tile((kSrc == 0 ? e : (kSrc == 1 ? u : g)) + start, len, acc);
+  const bool vec = len == kTile && (start & 3) == 0;
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    f4 r;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float deq;
+      const int code = sr_code(acc[v][c], qstep, limit, start + pb + v * 256 + c, seed_lo,
+                               seed_hi, step_lo, 0x52u, &deq);
+      packed |= ((uint32_t)(uint8_t)(int8_t)code) << (8 * c);
+      r[c] = acc[v][c] - deq;
+    }
+    const int p0 = pb + v * 256;
+    if (vec) {
+      *reinterpret_cast<uint32_t*>(codes + start + p0) = packed;
+      if (kSrc == 0) {
+        f4* e4 = reinterpret_cast<f4*>(e + start);
+        if (GC_NT_STORE_E) __builtin_nontemporal_store(r, e4 + (p0 >> 2)); else e4[p0 >> 2] = r;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (p0 + c < len) {
+          codes[start + p0 + c] = (int8_t)(packed >> (8 * c));
+          if (kSrc == 0) e[start + p0 + c] = r[c];
+        }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_qsgd_decompress(DevPlan P,
+                                                             const int8_t* __restrict__ codes,
+                                                             const float* __restrict__ norms,
+                                                             int levels,
+                                                             float* __restrict__ dense,
+                                                             int accumulate) {
+  const int64_t t = blockIdx.x;
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const float qstep = norms[s] / (float)levels;
+  const int pb = slot_base();
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int p = pb + v * 256 + c;
+      if (p < len) {
+        const float x = (float)codes[start + p] * qstep;
+        float* d = dense + start + p;
+        *d = accumulate ? *d + x : x;
+      }
+    }
+}
+
 // ------------------------------------------------------------------------------ int8 stage
 // Per segment: scale = fl(max |v| / 127) over the kept values.
 __global__ __launch_bounds__(1024) void k_absmax(OutPlan O, const float* __restrict__ vals,
@@ -1271,6 +1425,37 @@ hipError_t launch_sign_decompress(const DevPlan& P, const uint32_t* bits, const 
                                   float* dense, int accumulate, hipStream_t st) {
   if (P.n_tiles == 0) return hipSuccess;
   k_sign_decompress<<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, bits, scales, dense,
+                                                             accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_qsgd(const DevPlan& P, const float* g, float* e, float* u, float m,
+                       int levels, uint64_t seed, uint64_t step, int8_t* codes, float* norms,
+                       hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (P.n_seg == 0) return hipSuccess;
+  const unsigned nt = (unsigned)P.n_tiles;
+  if (ev_begin) (void)hipEventRecord(ev_begin, st);
+  if (nt > 0) {
+    if (e && u) k_qsgd_pass1<true, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
+    else if (e) k_qsgd_pass1<false, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
+    else if (u) k_qsgd_pass1<true, false><<<nt, kThreads, 0, st>>>(P, g, nullptr, u, m);
+    else k_qsgd_pass1<false, false><<<nt, kThreads, 0, st>>>(P, g, nullptr, nullptr, m);
+  }
+  k_qsgd_norm<<<P.n_seg, 1024, 0, st>>>(P, norms);
+  if (nt > 0) {
+    const uint32_t sl = (uint32_t)seed, sh = (uint32_t)(seed >> 32), tl = (uint32_t)step;
+    if (e) k_qsgd_pass2<0><<<nt, kThreads, 0, st>>>(P, g, e, u, norms, levels, codes, sl, sh, tl);
+    else if (u) k_qsgd_pass2<1><<<nt, kThreads, 0, st>>>(P, g, e, u, norms, levels, codes, sl, sh, tl);
+    else k_qsgd_pass2<2><<<nt, kThreads, 0, st>>>(P, g, e, u, norms, levels, codes, sl, sh, tl);
+  }
+  if (ev_end) (void)hipEventRecord(ev_end, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_qsgd_decompress(const DevPlan& P, const int8_t* codes, const float* norms,
+                                  int levels, float* dense, int accumulate, hipStream_t st) {
+  if (P.n_tiles == 0) return hipSuccess;
+  k_qsgd_decompress<<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, codes, norms, levels, dense,
                                                              accumulate);
   return hipGetLastError();
 }

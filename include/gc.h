@@ -172,6 +172,33 @@ int gc_plan_sign_layout(const gc_plan* plan, int64_t* word_off);
 int gc_sign_decompress(const gc_plan* plan, const uint32_t* bits, const float* scales,
                        float* dense, int accumulate, void* stream);
 
+/*
+ * QSGD with `levels` = s levels ("Communication Optimization > Gradient Compression", QSGD
+ * paragraph: Q_s(g) = ||g|| sgn(g) xi(g, s) / s with xi the stochastic rounding of
+ * |g| / (||g|| / s), so that E[Q_s(g)] = g; the printed formula lacks the 1/s, restored
+ * here; s = 2^b - 1 gives b-bit levels), one l2 norm per segment.  Per segment:
+ *   acc = e + x with error feedback (e given; genomic-FL glossary: quantisation combined
+ *         with error feedback), else acc = x; x = g, or u = fl(fl(m*u) + g) with momentum;
+ *   norm = fl32(sqrt(S)), S = sum acc^2 in double (order unspecified: 1 ulp);
+ *   step = fl32(norm / s); a = min(fl32(|acc| / step), s);
+ *   code = sgn(acc) * (floor(a) + [u24 < frac(a) * 2^24]), u24 the top 24 bits of word 0 of
+ *          Philox4x32-10 keyed (seed lo, seed hi) at counter (global index lo, hi, step lo,
+ *          0x52); code = 0 when step is 0;
+ *   with e: e = fl(acc - fl(code * step)).
+ *   levels   : s in [1, 127] (codes fit int8 with the sign).
+ *   e        : float[N] residual (error feedback) or NULL for plain QSGD.
+ *   out_codes: int8[N], element i of the buffer at byte i (4-byte aligned).
+ *   out_norms: float[n_seg].
+ * g, e and u must be 16-byte aligned.  Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_qsgd_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                     int32_t levels, uint64_t seed, uint64_t step, int8_t* out_codes,
+                     float* out_norms, void* stream);
+
+/* dense[i] = fl(code_i * fl(norm_s / levels)) (or += with accumulate) over every segment. */
+int gc_qsgd_decompress(const gc_plan* plan, const int8_t* codes, const float* norms,
+                       int32_t levels, float* dense, int accumulate, void* stream);
+
 /* Forget the threshold estimates: the next compress call runs as on a fresh plan. */
 int gc_plan_reset_estimate(gc_plan* plan, void* stream);
 
