@@ -60,6 +60,45 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
   return c0;
 }
 
+// Philox4x32-10 (Salmon et al., SC'11), all four words of the output block.
+__device__ __forceinline__ void philox4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                        uint32_t k0, uint32_t k1, uint32_t (&out)[4]) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t a = 0xD2511F53u, b = 0xCD9E8D57u;
+    const uint32_t hi0 = __umulhi(a, c0), lo0 = a * c0;
+    const uint32_t hi1 = __umulhi(b, c2), lo1 = b * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// Stochastic level from a given 24-bit draw: a = min(|v|/scale, limit), level floor(a) or
+// floor(a) + 1 when u24 < frac(a) * 2^24; returns sign(v) * level, *deq = fl(code * scale).
+__device__ __forceinline__ int sr_code_u24(float v, float scale, float limit, uint32_t u24,
+                                           float* deq) {
+  int q = 0;
+  if (scale != 0.0f) {
+    float a = fabsf(v) / scale;
+    if (a > limit) a = limit;
+    const float f = floorf(a);
+    const float frac = a - f;
+    q = (int)f + (((float)u24 < frac * 16777216.0f) ? 1 : 0);
+  }
+  const int code = signbit(v) ? -q : q;
+  *deq = (float)code * scale;
+  return code;
+}
+
 // Stochastic level of v (global index gi) at quantisation step `scale`: a = min(|v|/scale,
 // limit), level floor(a) or floor(a) + 1 with probability frac(a) (top 24 bits of Philox
 // word 0 at counter (gi lo, gi hi, step lo, tag)); returns sign(v) * level and writes the
@@ -1213,11 +1252,23 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass2(DevPlan P, const float*
   for (int v = 0; v < kSlots; ++v) {
     f4 r;
     uint32_t packed = 0;
+    // draws: word (gi % 4) of the Philox block at counter gi / 4; a lane's four elements
+    // share one block when they start on a multiple of 4
+    const int64_t g0 = start + pb + v * 256;
+    uint32_t w[4], w2[4];
+    philox4((uint32_t)(uint64_t)(g0 >> 2), (uint32_t)((uint64_t)(g0 >> 2) >> 32), step_lo, 0x52u,
+            seed_lo, seed_hi, w);
+    if (g0 & 3) {
+      const int64_t g1 = (g0 >> 2) + 1;
+      philox4((uint32_t)(uint64_t)g1, (uint32_t)((uint64_t)g1 >> 32), step_lo, 0x52u, seed_lo,
+              seed_hi, w2);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      const int j = (int)(g0 & 3) + c;   // position of element c from the first block
+      const uint32_t word = j < 4 ? w[j] : w2[j - 4];
       float deq;
-      const int code = sr_code(acc[v][c], qstep, limit, start + pb + v * 256 + c, seed_lo,
-                               seed_hi, step_lo, 0x52u, &deq);
+      const int code = sr_code_u24(acc[v][c], qstep, limit, word >> 8, &deq);
       packed |= ((uint32_t)(uint8_t)(int8_t)code) << (8 * c);
       r[c] = acc[v][c] - deq;
     }

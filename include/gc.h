@@ -181,9 +181,9 @@ int gc_sign_decompress(const gc_plan* plan, const uint32_t* bits, const float* s
  *         with error feedback), else acc = x; x = g, or u = fl(fl(m*u) + g) with momentum;
  *   norm = fl32(sqrt(S)), S = sum acc^2 in double (order unspecified: 1 ulp);
  *   step = fl32(norm / s); a = min(fl32(|acc| / step), s);
- *   code = sgn(acc) * (floor(a) + [u24 < frac(a) * 2^24]), u24 the top 24 bits of word 0 of
- *          Philox4x32-10 keyed (seed lo, seed hi) at counter (global index lo, hi, step lo,
- *          0x52); code = 0 when step is 0;
+ *   code = sgn(acc) * (floor(a) + [u24 < frac(a) * 2^24]), u24 the top 24 bits of word
+ *          (global index % 4) of the Philox4x32-10 block keyed (seed lo, seed hi) at counter
+ *          (global index / 4 lo, hi, step lo, 0x52); code = 0 when step is 0;
  *   with e: e = fl(acc - fl(code * step)).
  *   levels   : s in [1, 127] (codes fit int8 with the sign).
  *   e        : float[N] residual (error feedback) or NULL for plain QSGD.

@@ -39,8 +39,8 @@
  * in double, one sign bit per element, residual e = fl(acc - sign * scale).
  *
  * QSGD with s levels (same page, QSGD paragraph, with its missing 1/s restored): one l2
- * norm per segment, stochastic levels drawn from Philox4x32-10 (counter tag 0x52), error
- * feedback of the quantisation error optional.
+ * norm per segment, stochastic levels drawn from Philox4x32-10 (one block per four
+ * consecutive elements, counter tag 0x52), error feedback of the quantisation error optional.
  */
 #include <math.h>
 #include <stdint.h>
@@ -321,15 +321,17 @@ void orc_sign_decompress_segment(int64_t n, const uint32_t* bits, float scale, f
 
 /* ------------------------------------------------------------ QSGD s-level codec */
 
-/* Top 24 bits of the QSGD draw of global index gidx (counter tag 0x52). */
+/* Top 24 bits of the QSGD draw of global index gidx: word gidx % 4 of the Philox4x32-10
+ * block at counter (gidx/4 lo, gidx/4 hi, step lo, 0x52) -- one block serves four
+ * consecutive elements. */
 static uint32_t qsgd_draw24(uint64_t seed, uint64_t step, int64_t gidx)
 {
-    uint32_t ctr[4] = {(uint32_t)(uint64_t)gidx, (uint32_t)((uint64_t)gidx >> 32),
-                       (uint32_t)step, 0x52u};
+    uint64_t blk = (uint64_t)gidx >> 2;
+    uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), (uint32_t)step, 0x52u};
     uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     uint32_t r[4];
     orc_philox4x32_10(ctr, key, r);
-    return r[0] >> 8;
+    return r[(uint64_t)gidx & 3u] >> 8;
 }
 
 /*
@@ -341,8 +343,9 @@ static uint32_t qsgd_draw24(uint64_t seed, uint64_t step, int64_t gidx)
  * the momentum-corrected u.
  *   norm = fl32(sqrt(S)), S = sum acc_i^2 in double (index order);
  *   step = fl32(norm / s);  a = min(fl32(|acc| / step), s);  l = floor(a);
- *   xi = l + [u24 < (a - l) * 2^24]  (u24: top 24 bits of Philox4x32-10 word 0, key (seed lo,
- *        seed hi), counter (global index lo, hi, step lo, 0x52));
+ *   xi = l + [u24 < (a - l) * 2^24]  (u24: top 24 bits of word (global index % 4) of the
+ *        Philox4x32-10 block keyed (seed lo, seed hi) at counter (global index / 4 lo, hi,
+ *        step lo, 0x52));
  *   code = sgn(acc) * xi (int8, |code| <= s <= 127); step == 0 gives code 0;
  *   with e: e = fl(acc - fl(code * step)).
  */
