@@ -54,6 +54,12 @@ def load(path: str):
     L.orc_sign_ef_segment.restype = None
     L.orc_sign_decompress_segment.argtypes = [i64, vp, f32, vp, ctypes.c_int]
     L.orc_sign_decompress_segment.restype = None
+    L.orc_threshold_ef_segment.argtypes = [i64, i64, f32, vp, vp, vp, f32, ctypes.c_int, vp,
+                                           vp, vp]
+    L.orc_threshold_ef_segment.restype = ctypes.c_int
+    L.orc_randk_segment.argtypes = [i64, i64, i64, vp, vp, vp, f32, ctypes.c_int, u64, u64,
+                                    vp, vp]
+    L.orc_randk_segment.restype = ctypes.c_int
     L.orc_qsgd_segment.argtypes = [i64, i64, vp, vp, vp, f32, i32, u64, u64, vp, vp]
     L.orc_qsgd_segment.restype = ctypes.c_int
     L.orc_qsgd_decompress_segment.argtypes = [i64, vp, f32, i32, vp, ctypes.c_int]
@@ -218,3 +224,35 @@ def qsgd_decompress_segment(codes, norm, levels, dense=None, accumulate=False):
     lib().orc_qsgd_decompress_segment(codes.size, _p(codes), float(norm), int(levels), _p(dense),
                                       int(bool(accumulate)))
     return dense
+
+
+def threshold_ef_segment(g, e, k_cap, tau, u=None, momentum=0.9, mask_u=False):
+    """Threshold sparsification of one segment (at most k_cap entries with |acc| >= |tau|),
+    in place on e (and u).  Returns (vals, idx) of the sent entries."""
+    _f32(g, "g"), _f32(e, "e")
+    n = g.size
+    vals = np.empty(max(k_cap, 1), np.float32)
+    idx = np.empty(max(k_cap, 1), np.int32)
+    cnt = np.zeros(1, np.int64)
+    rc = lib().orc_threshold_ef_segment(n, int(k_cap), float(tau), _p(g), _p(e), _p(u),
+                                        float(momentum), int(bool(mask_u)), _p(vals), _p(idx),
+                                        _p(cnt))
+    if rc:
+        raise ValueError("oracle rejected the segment arguments")
+    return vals[:cnt[0]].copy(), idx[:cnt[0]].copy()
+
+
+def randk_segment(g, k, e=None, u=None, momentum=0.9, mask_u=False, seed=0, step=0,
+                  seg_base=0):
+    """Random-k of one segment (global offset seg_base); with e, error feedback in place on
+    e, else values scaled by n/k.  Returns (vals float32[k], idx int32[k])."""
+    _f32(g, "g")
+    n = g.size
+    vals = np.empty(max(k, 1), np.float32)
+    idx = np.empty(max(k, 1), np.int32)
+    rc = lib().orc_randk_segment(n, int(k), int(seg_base), _p(g), _p(e), _p(u),
+                                 float(momentum), int(bool(mask_u)), int(seed), int(step),
+                                 _p(vals), _p(idx))
+    if rc:
+        raise ValueError("oracle rejected the Random-k arguments")
+    return vals[:k].copy(), idx[:k].copy()

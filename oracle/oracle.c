@@ -38,6 +38,15 @@
  * Compression", 1-bit SGD section): per segment scale = fl32(sum |acc| / n) with the sum
  * in double, one sign bit per element, residual e = fl(acc - sign * scale).
  *
+ * Threshold sparsification with error feedback: the entries with |acc| >= tau, at most k of
+ * them (the largest), as above otherwise.
+ *
+ * Random-k (first page, Random-k section; "Gradient Compression" glossary, random
+ * sparsification): exactly k positions per segment, a uniformly random subset drawn anew each
+ * step -- the k largest of a Philox4x32-10 key per element (counter tag 0x53).  With error
+ * feedback the values go unscaled and the residual is kept; without it they are scaled by
+ * n/k so that their expectation is acc.
+ *
  * QSGD with s levels (same page, QSGD paragraph, with its missing 1/s restored): one l2
  * norm per segment, stochastic levels drawn from Philox4x32-10 (one block per four
  * consecutive elements, counter tag 0x52), error feedback of the quantisation error optional.
@@ -142,6 +151,43 @@ int orc_topk_ef_segment(int64_t n, int64_t k, const float* g, float* e, float* u
     }
     free(sel);
     return 0;
+}
+
+/*
+ * Threshold sparsification with error feedback (genomic-FL glossary, sparsification section:
+ * entries below a fixed or adaptive magnitude threshold are dropped; "Gradient
+ * Sparsification" glossary, mechanism section: a dynamic threshold per layer).  One segment:
+ * after the same momentum and EF add, the entries with |acc| >= |tau| are sent, at most
+ * k_cap of them -- the k_cap largest by (|acc| descending, position ascending) when more
+ * reach the threshold.  Writes *count (the number sent, <= k_cap) and that many outputs in
+ * ascending index order; the residual is +0 where sent and acc elsewhere.
+ */
+int orc_threshold_ef_segment(int64_t n, int64_t k_cap, float tau, const float* g, float* e,
+                             float* u, float m, int mask_u, float* vals, int32_t* idx,
+                             int64_t* count)
+{
+    if (n < 0 || n > 0x7FFFFFFF || k_cap < 0 || k_cap > n) return -1;
+    /* acc first (as orc_topk_ef_segment would), then count the entries at the threshold */
+    float* acc_copy = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    float* u_copy = u ? (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float)) : NULL;
+    if (!acc_copy || (u && !u_copy)) { free(acc_copy); free(u_copy); return -1; }
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float x = g[i];
+        if (u) {
+            float mu = m * u[i];
+            u_copy[i] = mu + x;
+            x = u_copy[i];
+        }
+        acc_copy[i] = e[i] + x;
+        if (magnitude_key(acc_copy[i]) >= magnitude_key(tau)) ++c;
+    }
+    free(acc_copy);
+    free(u_copy);
+    int64_t k = c < k_cap ? c : k_cap;
+    *count = k;
+    /* the k largest entries: all of them reach the threshold */
+    return orc_topk_ef_segment(n, k, g, e, u, m, mask_u, vals, idx);
 }
 
 /* Whole segmented buffer: segments [seg_off[s], seg_off[s+1]), k[s] entries each, output
@@ -399,4 +445,72 @@ void orc_qsgd_decompress_segment(int64_t n, const int8_t* codes, float norm, int
         float v = (float)codes[i] * qstep;
         dense[i] = accumulate ? dense[i] + v : v;
     }
+}
+
+/* ------------------------------------------------------------------- Random-k */
+
+/* Random key of global index gidx: word gidx % 4 of the Philox4x32-10 block keyed (seed lo,
+ * seed hi) at counter (gidx/4 lo, gidx/4 hi, step lo, 0x53), shifted right by one (31 bits). */
+static uint32_t randk_key(uint64_t seed, uint64_t step, int64_t gidx)
+{
+    uint64_t blk = (uint64_t)gidx >> 2;
+    uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), (uint32_t)step, 0x53u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t r[4];
+    orc_philox4x32_10(ctr, key, r);
+    return r[(uint64_t)gidx & 3u] >> 1;
+}
+
+/*
+ * Random-k of one segment of n elements (global offset seg_base), k in [0, n]
+ * (first page, Random-k section: a random mask per iteration, unbiased, no sort of the
+ * gradient needed).  The mask is the k positions whose random keys are largest, equal keys
+ * going to the lower position: sorting by independent uniform keys is a uniform random
+ * permutation, so every k-subset is equally likely (up to the rare equal 31-bit keys).
+ *   x = g, or with u the momentum-corrected u = fl(fl(m*u) + g);
+ *   acc = fl(e + x) with e (error feedback), else acc = x;
+ *   vals = acc at the mask in ascending index order, or without e fl(acc * fl32(n / k))
+ *   (n / k formed in double, one rounding to float), whose expectation is acc;
+ *   with e: e = +0 at the mask and acc elsewhere; mask_u zeroes u at the mask.
+ */
+int orc_randk_segment(int64_t n, int64_t k, int64_t seg_base, const float* g, float* e, float* u,
+                      float m, int mask_u, uint64_t seed, uint64_t step, float* vals,
+                      int32_t* idx)
+{
+    if (n < 0 || n > 0x7FFFFFFF || k < 0 || k > n) return -1;
+    if (n == 0) return 0;
+    float* acc = (float*)malloc((size_t)n * sizeof(float));
+    rank_rec* rec = (rank_rec*)malloc((size_t)n * sizeof *rec);
+    uint32_t* sel = (uint32_t*)malloc((size_t)(k > 0 ? k : 1) * sizeof *sel);
+    if (!acc || !rec || !sel) { free(acc); free(rec); free(sel); return -1; }
+    for (int64_t i = 0; i < n; ++i) {
+        float x = g[i];
+        if (u) {
+            float mu = m * u[i];
+            u[i] = mu + x;
+            x = u[i];
+        }
+        acc[i] = e ? e[i] + x : x;
+        rec[i].key = randk_key(seed, step, seg_base + i);
+        rec[i].pos = (uint32_t)i;
+    }
+    qsort(rec, (size_t)n, sizeof *rec, by_rank);
+    for (int64_t j = 0; j < k; ++j) sel[j] = rec[j].pos;
+    free(rec);
+    qsort(sel, (size_t)k, sizeof *sel, by_pos);
+    float scale = k > 0 ? (float)((double)n / (double)k) : 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+        float v = acc[sel[j]];
+        vals[j] = e ? v : v * scale;
+        idx[j] = (int32_t)sel[j];
+    }
+    if (e) {
+        for (int64_t i = 0; i < n; ++i) e[i] = acc[i];
+        for (int64_t j = 0; j < k; ++j) e[sel[j]] = 0.0f;
+    }
+    if (u && mask_u)
+        for (int64_t j = 0; j < k; ++j) u[sel[j]] = 0.0f;
+    free(acc);
+    free(sel);
+    return 0;
 }

@@ -13,6 +13,8 @@ from tests import test_oracle_ratio as T_r
 from tests import test_oracle_select as T_s
 from tests import test_oracle_sign as T_g
 from tests import test_oracle_qsgd as T_q8
+from tests import test_oracle_threshold as T_t
+from tests import test_oracle_randk as T_rk
 
 MUTANTS = {
     "tie_rule_higher_index_wins": ("return a->pos < b->pos ? -1 : 1;",
@@ -50,6 +52,15 @@ MUTANTS = {
                               "q = (int)l + (frac >= 0.5f ? 1 : 0);"),
     "qsgd_residual_not_fed_back": ("            e[i] = v - deq;\n        }\n    }\n    free(acc);",
                                    "            e[i] = v;\n        }\n    }\n    free(acc);"),
+    "threshold_strict": ("if (magnitude_key(acc_copy[i]) >= magnitude_key(tau)) ++c;",
+                         "if (magnitude_key(acc_copy[i]) > magnitude_key(tau)) ++c;"),
+    "threshold_ignored": ("int64_t k = c < k_cap ? c : k_cap;", "int64_t k = k_cap;"),
+    "randk_word0_only": ("return r[(uint64_t)gidx & 3u] >> 1;", "return r[0] >> 1;"),
+    "randk_scale_k_over_n": ("(float)((double)n / (double)k)", "(float)((double)k / (double)n)"),
+    "randk_smallest_keys": ("sel[j] = rec[j].pos;\n    free(rec);\n    qsort(sel, (size_t)k, sizeof *sel, by_pos);\n    float scale",
+                            "sel[j] = rec[n - 1 - j].pos;\n    free(rec);\n    qsort(sel, (size_t)k, sizeof *sel, by_pos);\n    float scale"),
+    "randk_residual_not_kept": ("for (int64_t i = 0; i < n; ++i) e[i] = acc[i];", ""),
+    "randk_same_mask_every_step": ("(uint32_t)step, 0x53u", "0u, 0x53u"),
 }
 
 
@@ -73,6 +84,13 @@ def _pins(orc):
     yield lambda: T_q8.test_hand_integer_levels(orc)
     yield lambda: T_q8.test_unbiased_and_toy(orc)
     yield lambda: T_q8.test_norm_codes_and_error_feedback(orc)
+    yield lambda: [T_t.test_brute_force(orc, s) for s in range(4)]
+    yield lambda: T_t.test_edges(orc)
+    yield lambda: T_rk.test_exact_k_and_conservation(orc, 1000, 37)
+    yield lambda: T_rk.test_marginal_and_pairwise_uniform(orc)
+    yield lambda: T_rk.test_unbiased_without_error_feedback(orc)
+    yield lambda: T_rk.test_mask_depends_on_step_and_segment_not_values(orc)
+    yield lambda: T_rk.test_counter_mapping(orc, 3)
 
 
 def _failures():
