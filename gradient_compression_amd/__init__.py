@@ -29,7 +29,8 @@ EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layo
            "gc_topk_ef_compress", "gc_topk_ef_compress_int8", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
            "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32",
            "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
-           "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress")
+           "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress",
+           "gc_threshold_ef_compress", "gc_randk_compress")
 
 _lib = None
 
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
         "gc_sign_decompress": [vp, vp, vp, vp, ctypes.c_int, vp],
         "gc_qsgd_compress": [vp, vp, vp, vp, f32, i32, u64, u64, vp, vp, vp],
         "gc_qsgd_decompress": [vp, vp, vp, i32, vp, ctypes.c_int, vp],
+        "gc_threshold_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp, vp, vp],
+        "gc_randk_compress": [vp, vp, vp, vp, f32, u64, u64, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -270,6 +273,38 @@ class Plan:
             _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
             _stream(stream))
         _check(rc, "gc_qsgd_decompress")
+
+    def threshold_compress(self, g, e, tau, out_vals, out_idx, out_count=None, u=None,
+                           momentum: float = 0.0, stream=None):
+        """Keep |acc| >= |tau_s|, at most k_s per segment (the largest); e <- the residual.
+
+        ``tau``: device float32 tensor of n_seg thresholds.  Unused output slots get value 0
+        and index -1; ``out_count`` (device int32[n_seg]) receives the kept counts.
+        """
+        import torch
+        n = self.n
+        rc = lib().gc_threshold_ef_compress(
+            self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
+            _dev_ptr(u, torch.float32, "u", n), float(momentum),
+            _dev_ptr(tau, torch.float32, "tau", self.n_seg),
+            _dev_ptr(out_vals, torch.float32, "out_vals", self.total_k),
+            _dev_ptr(out_idx, torch.int32, "out_idx", self.total_k),
+            _dev_ptr(out_count, torch.int32, "out_count", self.n_seg), _stream(stream))
+        _check(rc, "gc_threshold_ef_compress")
+
+    def randk_compress(self, g, out_vals, out_idx, e=None, u=None, momentum: float = 0.0,
+                       seed: int = 0, step: int = 0, stream=None):
+        """Random-k: k_s uniformly random positions per segment (Philox keys of (seed, step,
+        index)); with e, error feedback, else values scaled by n_s / k_s."""
+        import torch
+        n = self.n
+        rc = lib().gc_randk_compress(
+            self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
+            _dev_ptr(u, torch.float32, "u", n), float(momentum), int(seed) & (2 ** 64 - 1),
+            int(step) & (2 ** 64 - 1),
+            _dev_ptr(out_vals, torch.float32, "out_vals", self.total_k),
+            _dev_ptr(out_idx, torch.int32, "out_idx", self.total_k), _stream(stream))
+        _check(rc, "gc_randk_compress")
 
     def reset_estimate(self, stream=None):
         _check(lib().gc_plan_reset_estimate(self._h, _stream(stream)), "gc_plan_reset_estimate")

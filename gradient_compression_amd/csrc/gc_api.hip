@@ -26,6 +26,18 @@ constexpr int64_t kMinCapacity = 65536;
 constexpr float kInitialBeta = 0.9f;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Random-k capture threshold of a segment whose candidates do not cover it whole: the count
+// of 31-bit uniform keys at or above it has mean at least mu = k + 12 sqrt(k) + 64, so by the
+// Chernoff bound fewer than k of them (the exact fallback then runs) has probability below
+// exp(-(mu - k)^2 / (2 mu)) < e^-37 for every k >= 1, and more than the capacity of
+// max(16 k, 65536) is rarer still.
+uint32_t randk_threshold(int64_t n, int64_t k) {
+  const double want = (double)k + 12.0 * std::sqrt((double)k) + 64.0;
+  if (want >= (double)n) return 0;
+  const double span = std::ceil(want * 2147483648.0 / (double)n);
+  return span >= 2147483648.0 ? 0u : (uint32_t)(2147483648.0 - span);
+}
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -141,22 +153,30 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   // tables
   std::vector<int64_t> tile_base(n_seg + 1, 0), chunk_base(n_seg + 1, 0), cand_base(n_seg, 0),
       out_chunk_base(n_seg + 1, 0);
-  std::vector<uint32_t> kk(n_seg), cap(n_seg), thr_init(n_seg);
+  std::vector<uint32_t> kk(n_seg), cap(n_seg), thr_init(n_seg), thr_rand(n_seg);
+  std::vector<float> rk_scale(n_seg, 0.0f);
   int64_t cand_total = 0;
   for (int32_t s = 0; s < n_seg; ++s) {
     const int64_t n = seg_off[s + 1] - seg_off[s];
     tile_base[s + 1] = tile_base[s] + ceil_div(n, gc::kTile);
     int64_t c = 0;
-    uint32_t thr = gc::kNoCapture;
+    uint32_t thr = gc::kNoCapture, thr_r = gc::kNoCapture;
     if (ks[s] > 0) {
       if (n <= kSmallSegment || ks[s] * kCapacityFactor >= n) {
         c = n;
         thr = 0;  // capture everything: the select then runs on the whole segment's copy
+        thr_r = 0;
       } else {
         c = std::min(n, std::max(ks[s] * kCapacityFactor, kMinCapacity));
+        thr_r = randk_threshold(n, ks[s]);
       }
-      if (flags & (GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE)) thr = gc::kNoCapture;
+      if (flags & (GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE)) {
+        thr = gc::kNoCapture;
+        thr_r = gc::kNoCapture;
+      }
+      rk_scale[s] = (float)((double)n / (double)ks[s]);
     }
+    thr_rand[s] = thr_r;
     kk[s] = (uint32_t)ks[s];
     cap[s] = (uint32_t)c;
     thr_init[s] = thr;
@@ -246,6 +266,12 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   cv.add(&d.cand_idx, cand_total);
   cv.add(&d.sort_val, cand_total);
   cv.add(&d.sort_idx, cand_total);
+  uint32_t* d_thr_rand;
+  float* d_rk_scale;
+  cv.add(&d.k_call, n_seg);
+  cv.add(&d.thr_call, n_seg);
+  cv.add(&d_thr_rand, n_seg);
+  cv.add(&d_rk_scale, n_seg);
   if (hipMalloc(&p->mem, cv.total()) != hipSuccess) {
     (void)hipGetLastError();
     delete p;
@@ -264,6 +290,9 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   d.cand_cap = d_cap;
   d.thr_init = d_thr_init;
   d.word_off = d_word_off;
+  d.thr_rand = d_thr_rand;
+  d.rk_scale = d_rk_scale;
+  d.keys = gc::kKeysMagnitude;
   gc::OutPlan& o = p->op;
   o.n_seg = n_seg;
   o.n_out_chunks = n_out_chunks;
@@ -288,6 +317,8 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   up(upload(d_out_chunk_seg, out_chunk_seg));
   up(upload(d_out_chunk_base, out_chunk_base));
   up(upload(d_word_off, p->word_off));
+  up(upload(d_thr_rand, thr_rand));
+  up(upload(d_rk_scale, rk_scale));
   up(upload(d.thr, thr_init));
   up(upload(d.beta, std::vector<float>(n_seg, kInitialBeta)));
   up(hipMemset(d.cand_cnt, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
@@ -400,6 +431,42 @@ int gc_topk_ef_compress_int8(gc_plan* plan, const float* g, float* e, float* u, 
   q8.step_lo = (uint32_t)step;
   if (plan->n_seg == 0) return GC_OK;
   return compress_checked(plan, g, e, u, momentum, out_vals, out_idx, q8, stream);
+}
+
+int gc_threshold_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                             const float* tau, float* out_vals, int32_t* out_idx,
+                             int32_t* out_count, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!g || !e || !aligned16(g) || !aligned16(e))) return GC_ERR_INVALID_ARG;
+  if (u && !aligned16(u)) return GC_ERR_INVALID_ARG;
+  if (plan->n_seg > 0 && !tau) return GC_ERR_INVALID_ARG;
+  if (plan->total_k > 0 && (!out_vals || !out_idx)) return GC_ERR_INVALID_ARG;
+  if (any && (g == e || (u && (g == u || e == u)))) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  hipEvent_t b = nullptr, en = nullptr;
+  if (int rc = timing_events(plan, &b, &en)) return rc;
+  const hipError_t err =
+      gc::launch_threshold(plan->dp, plan->op, g, e, u, momentum, tau, out_vals, out_idx,
+                           out_count, static_cast<hipStream_t>(stream), b, en);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_randk_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                      uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
+                      void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!g || !aligned16(g))) return GC_ERR_INVALID_ARG;
+  if ((e && !aligned16(e)) || (u && !aligned16(u))) return GC_ERR_INVALID_ARG;
+  if (plan->total_k > 0 && (!out_vals || !out_idx)) return GC_ERR_INVALID_ARG;
+  if (any && ((e && (g == e || e == u)) || (u && g == u))) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  hipEvent_t b = nullptr, en = nullptr;
+  if (int rc = timing_events(plan, &b, &en)) return rc;
+  const hipError_t err = gc::launch_randk(plan->dp, g, e, u, momentum, seed, step, out_vals,
+                                          out_idx, static_cast<hipStream_t>(stream), b, en);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
 }
 
 int gc_plan_sign_layout(const gc_plan* plan, int64_t* word_off) {

@@ -64,6 +64,10 @@ enum : uint32_t { kWhyNone = 0, kWhyCold = 1, kWhyMiss = 2, kWhyOverflow = 3 };
 constexpr int32_t kFlagMomentumMask = 0x1;
 constexpr int32_t kFlagForceFull = 0x100;
 constexpr int32_t kFlagNoEstimate = 0x200;
+// What the select ranks: |acc| (Top-k, threshold) or a per-element Philox key (Random-k).
+// Random keys are 31-bit and travel through the candidate buffers as float bit patterns, so
+// the select kernels read both kinds through the same magnitude-key view.
+enum : int32_t { kKeysMagnitude = 0, kKeysRandom = 1 };
 
 // Device view of a plan, passed by value to every kernel.
 struct DevPlan {
@@ -121,6 +125,14 @@ struct DevPlan {
   int32_t* cand_idx;
   float* sort_val;             // the same candidates in ascending index order
   int32_t* sort_idx;
+  // per-call selection (threshold and Random-k calls run on a copy of the plan whose k and
+  // thr point here, so the Top-k threshold estimate is left alone)
+  uint32_t* k_call;            // [n_seg] entries kept this call
+  uint32_t* thr_call;          // [n_seg] capture threshold of this call
+  const uint32_t* thr_rand;    // [n_seg] Random-k capture threshold (fixed per plan)
+  const float* rk_scale;       // [n_seg] fl32(n / k), Random-k value scale without feedback
+  int32_t keys;                // kKeysMagnitude or kKeysRandom
+  uint32_t seed_lo, seed_hi, step_lo;   // Random-k key stream
 };
 
 struct OutPlan {               // tables of the int8 and decompression kernels
@@ -144,6 +156,13 @@ struct Int8Args {
 hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
                            float* out_vals, int32_t* out_idx, const Int8Args& q8,
                            hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, float* e,
+                            float* u, float m, const float* tau, float* out_vals,
+                            int32_t* out_idx, int32_t* out_count, hipStream_t st,
+                            hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, float m,
+                        uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
+                        hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_reset(const DevPlan& P, hipStream_t st);
 hipError_t launch_sign(const DevPlan& P, const float* g, float* e, float* u, float m,
                        uint32_t* bits, float* scales, hipStream_t st, hipEvent_t ev_begin,

@@ -233,6 +233,41 @@ __device__ __forceinline__ void load_tile(const S* __restrict__ base, int len, V
   }
 }
 
+// Random-k keys of the len (<= kTile) elements from global index start, in the tile layout,
+// as float bit patterns: word (gi % 4) of the Philox4x32-10 block keyed (seed lo, seed hi) at
+// counter (gi / 4 lo, gi / 4 hi, step lo, 0x53), shifted right by one (31 bits).  A lane's
+// four elements share one block when start is a multiple of 4.  Lanes past len get key 0.
+__device__ __forceinline__ void rand_key_tile(const DevPlan& P, int64_t start, int len,
+                                              f4 (&x)[kSlots]) {
+  const int pb = slot_base();
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    const int64_t g0 = start + pb + v * 256;
+    const uint64_t b0 = (uint64_t)g0 >> 2;
+    uint32_t w[4], w2[4] = {0u, 0u, 0u, 0u};
+    philox4((uint32_t)b0, (uint32_t)(b0 >> 32), P.step_lo, 0x53u, P.seed_lo, P.seed_hi, w);
+    if (g0 & 3)
+      philox4((uint32_t)(b0 + 1), (uint32_t)((b0 + 1) >> 32), P.step_lo, 0x53u, P.seed_lo,
+              P.seed_hi, w2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = (int)(g0 & 3) + c;   // position of element c from the first block
+      const uint32_t word = j < 4 ? w[j] : w2[j - 4];
+      x[v][c] = pb + v * 256 + c < len ? __uint_as_float(word >> 1) : 0.0f;
+    }
+  }
+}
+
+// What the select ranks for the tile at start: acc read back from e (its magnitude key), or
+// the elements' Random-k keys.
+__device__ __forceinline__ void key_tile(const DevPlan& P, const float* __restrict__ e,
+                                         int64_t start, int len, f4 (&x)[kSlots]) {
+  if (P.keys == kKeysRandom)
+    rand_key_tile(P, start, len, x);
+  else
+    load_tile(e + start, len, x);
+}
+
 // ------------------------------------------------------------------------------ prep
 __global__ __launch_bounds__(kThreads) void k_prep(DevPlan P) {
   const int s = blockIdx.x * kThreads + threadIdx.x;
@@ -247,6 +282,32 @@ __global__ __launch_bounds__(kThreads) void k_prep(DevPlan P) {
 __global__ __launch_bounds__(kThreads) void k_reset(DevPlan P) {
   const int s = blockIdx.x * kThreads + threadIdx.x;
   if (s < P.n_seg) P.thr[s] = P.thr_init[s];
+}
+
+// Threshold and Random-k calls: this call's k (the plan's, reduced after the capture for a
+// threshold call) and capture threshold (key of |tau|, or the plan's Random-k threshold).
+__global__ __launch_bounds__(kThreads) void k_prep_call(DevPlan P, const float* __restrict__ tau) {
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  if (s < P.n_seg) {
+    P.cand_cnt[s] = 0;
+    P.k_call[s] = P.k[s];
+    P.thr_call[s] = tau ? mag_key(tau[s]) : P.thr_rand[s];
+  }
+  if (s == 0) {
+    *P.full_count = 0;
+    *P.recap_count = 0;
+    *P.err = 0;
+  }
+}
+
+// Threshold call: keep min(number of keys at or above the threshold, k) entries per segment.
+// The capture counted every such key, also those past the candidate capacity.
+__global__ __launch_bounds__(kThreads) void k_thresh_k(DevPlan P, int32_t* __restrict__ count) {
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  if (s >= P.n_seg) return;
+  const uint32_t kk = min(P.cand_cnt[s], P.k[s]);
+  P.k_call[s] = kk;
+  if (count) count[s] = (int32_t)kk;
 }
 
 // Tile t of segment s: first element and length.
@@ -381,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_select_init(DevPlan P) {
   uint32_t mode, why = kWhyNone;
   if (k == 0) {
     mode = kModeSkip;
-  } else if (thr != kNoCapture && c >= k && c <= cap) {
+  } else if (thr != kNoCapture && c >= k && c <= cap && !(P.flags & kFlagForceFull)) {
     mode = kModeCand;
   } else {
     mode = kModePending;
@@ -443,7 +504,7 @@ __device__ void hist_listed_tiles(const DevPlan& P, const float* __restrict__ e,
       tile_range(P, s, t, &start, &len);
       for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
       f4 x[kSlots];
-      load_tile(e + start, len, x);
+      key_tile(P, e, start, len, x);
       __syncthreads();
       hist_add(h, x, len, prefix, pass);
       __syncthreads();
@@ -539,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void k_recapture(DevPlan P, const float* 
       int len;
       tile_range(P, s, t, &start, &len);
       f4 x[kSlots];
-      load_tile(e + start, len, x);
+      key_tile(P, e, start, len, x);
       capture_tile(P, s, t, start, len, x, thr, s_w, &s_base);
       __syncthreads();
     }
@@ -728,7 +789,7 @@ __global__ __launch_bounds__(kThreads) void k_count_full(DevPlan P, const float*
       int len;
       tile_range(P, s, t, &start, &len);
       f4 x[kSlots];
-      load_tile(e + start, len, x);
+      key_tile(P, e, start, len, x);
       count_block(x, len, kth, s_tmp, &P.tile_gt[t], &P.tile_eq[t]);
       uint32_t mx = 0;
       const int pb = slot_base();
@@ -808,6 +869,9 @@ struct EmitOut {              // where kept entries go
   float scale;
   uint32_t seed_lo, seed_hi, step_lo;
   uint32_t* err;
+  const float* vsrc;         // Random-k: kept values are read here (the tile holds keys)
+  const float* rk_scale;     // Random-k without feedback: per-segment value scale, or null
+  float vmul;
   __device__ float scales_of(int s) const { return scales[s]; }
 };
 
@@ -872,7 +936,8 @@ __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotI
       if ((b >> c) & 1u) {
         const int32_t li = li4[c];
         if (q < out_end && li >= 0 && li < n_s) {
-          const float val = x[v][c];
+          float val = o.vsrc ? o.vsrc[s0 + li] : x[v][c];
+          if (o.rk_scale) val = val * o.vmul;
           if (o.vals) o.vals[q] = val;
           o.idx[q] = li;
           float resid = 0.0f;
@@ -883,10 +948,10 @@ __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotI
             resid = val - deq;
           }
           if (GC_NT_ZERO_E) {
-            __builtin_nontemporal_store(resid, o.e + s0 + li);
+            if (o.e) __builtin_nontemporal_store(resid, o.e + s0 + li);
             if (o.u) __builtin_nontemporal_store(0.0f, o.u + s0 + li);
           } else {
-            o.e[s0 + li] = resid;
+            if (o.e) o.e[s0 + li] = resid;
             if (o.u) o.u[s0 + li] = 0.0f;
           }
         } else {
@@ -922,6 +987,7 @@ __global__ __launch_bounds__(kThreads) void k_emit_cand(DevPlan P, EmitOut o) {
     return r;
   };
   if (o.codes) o.scale = o.scales_of(s);
+  if (o.rk_scale) o.vmul = o.rk_scale[s];
   emit_block(x, len, slot_idx, P.kth[s], P.ties[s], P.chunk_eq_base[ch], P.chunk_eq[ch],
              P.out_off[s] + P.chunk_sel_base[ch], P.out_off[s + 1], P.seg_off[s],
              (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, o);
@@ -939,13 +1005,14 @@ __global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, EmitOut o) {
       int len;
       tile_range(P, s, t, &start, &len);
       f4 x[kSlots];
-      load_tile(o.e + start, len, x);
+      key_tile(P, o.e, start, len, x);
       const int32_t lb = (int32_t)(start - s0) + slot_base();
       auto slot_idx = [&](int v) {
         const int32_t b0 = lb + v * 256;
         return i4{b0, b0 + 1, b0 + 2, b0 + 3};
       };
       if (o.codes) o.scale = o.scales_of(s);
+      if (o.rk_scale) o.vmul = o.rk_scale[s];
       emit_block(x, len, slot_idx, kth, r, P.tile_eq_base[t], P.tile_eq[t],
                  P.out_off[s] + P.tile_sel_base[t], P.out_off[s + 1], s0,
                  (int32_t)(P.seg_off[s + 1] - s0), s_w, o);
@@ -1315,6 +1382,85 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_decompress(DevPlan P,
     }
 }
 
+// -------------------------------------------------------------------------------- Random-k
+// Random-k (first page, Random-k section): exactly k positions per segment, the k largest
+// random keys (rand_key_tile), a uniformly random subset drawn anew each step.  The streaming
+// pass forms acc as the Top-k pass does and captures by key instead of magnitude; the select
+// and the ordered emit are shared, the kept values then read back from where acc lives.
+
+// u = fl(fl(m*u) + g) over one tile, stored (momentum without error feedback).
+__device__ __forceinline__ void momentum_tile(const float* __restrict__ g, float* __restrict__ u,
+                                              float m, int64_t start, int len) {
+  const int pb = slot_base();
+  if (len == kTile && (start & 3) == 0) {
+    const f4* g4 = reinterpret_cast<const f4*>(g + start);
+    f4* u4 = reinterpret_cast<f4*>(u + start);
+    f4 gv[kSlots], uv[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      gv[v] = GC_NT_LOAD_G ? __builtin_nontemporal_load(g4 + q) : g4[q];
+      uv[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(u4 + q) : u4[q];
+    }
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      const f4 mu = m * uv[v];
+      const f4 x = mu + gv[v];
+      if (GC_NT_STORE_E) __builtin_nontemporal_store(x, u4 + q); else u4[q] = x;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = pb + v * 256 + c;
+        if (p < len) {
+          const float mu = m * u[start + p];
+          u[start + p] = mu + g[start + p];
+        }
+      }
+  }
+}
+
+template <bool kMomentum, bool kEF>
+__global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const float* __restrict__ g,
+                                                           float* __restrict__ e,
+                                                           float* __restrict__ u, float m) {
+  __shared__ uint32_t s_w[kWaves];
+  __shared__ uint32_t s_base;
+  const int64_t t = blockIdx.x;
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  if (kEF) {
+    f4 acc[kSlots];
+    ef_add_tile<kMomentum>(g, e, u, m, start, len, acc);
+  } else if (kMomentum) {
+    momentum_tile(g, u, m, start, len);
+  }  // neither: nothing to stream, g is read at the kept positions only
+  const uint32_t thr = P.thr[s];
+  if (thr == kNoCapture) return;  // uniform: this segment takes the exact fallback
+  f4 key[kSlots];
+  rand_key_tile(P, start, len, key);
+  capture_tile(P, s, t, start, len, key, thr, s_w, &s_base);
+}
+
+// Threshold call: slots past the segment's kept entries get value +0 and index -1.
+__global__ __launch_bounds__(kThreads) void k_pad_out(OutPlan O, const uint32_t* __restrict__ k_call,
+                                                      float* __restrict__ vals,
+                                                      int32_t* __restrict__ idx) {
+  const int64_t ch = blockIdx.x;
+  const int s = O.out_chunk_seg[ch];
+  const int64_t j0 = O.out_off[s] + (ch - O.out_chunk_base[s]) * (int64_t)kOutChunk;
+  const int64_t j1 = min(j0 + kOutChunk, O.out_off[s + 1]);
+  const int64_t keep_end = O.out_off[s] + k_call[s];
+  for (int64_t j = max(j0, keep_end) + threadIdx.x; j < j1; j += kThreads) {
+    vals[j] = 0.0f;
+    idx[j] = -1;
+  }
+}
+
 // ------------------------------------------------------------------------------ int8 stage
 // Per segment: scale = fl(max |v| / 127) over the kept values.
 __global__ __launch_bounds__(1024) void k_absmax(OutPlan O, const float* __restrict__ vals,
@@ -1408,6 +1554,29 @@ __global__ __launch_bounds__(kThreads) void k_copy(const f4* __restrict__ src,
 
 inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
+// Everything after the streaming pass: select (candidates, re-capture or the exact full
+// path), ordered count/scan, emit.  e holds acc (magnitude keys); scales: fused int8 or null.
+void select_emit(const DevPlan& P, const float* e, const EmitOut& o, float* scales,
+                 hipStream_t st) {
+  k_select_init<<<P.n_seg, kThreads, 0, st>>>(P);
+  k_recap_hist<<<kFullBlocks, kThreads, 0, st>>>(P, e);
+  k_recap_decide<<<P.n_seg, kThreads, 0, st>>>(P);
+  k_recapture<<<kFullBlocks, kThreads, 0, st>>>(P, e);
+  k_runs<<<P.n_seg, 1024, 0, st>>>(P);
+  if (P.n_chunks > 0) k_scatter<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
+  k_find<<<P.n_seg, kThreads, 0, st>>>(P, 0);
+  const unsigned mixed = (unsigned)(P.n_chunks + kFullBlocks);
+  for (int pass = 1; pass < 3; ++pass) {
+    k_hist<<<mixed, kThreads, 0, st>>>(P, e, pass);
+    k_find<<<P.n_seg, kThreads, 0, st>>>(P, pass);
+  }
+  if (P.n_chunks > 0) k_count_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
+  k_count_full<<<kFullBlocks, kThreads, 0, st>>>(P, e);
+  k_scan<<<P.n_seg, 1024, 0, st>>>(P, scales);
+  if (P.n_chunks > 0) k_emit_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P, o);
+  k_emit_full<<<kFullBlocks, kThreads, 0, st>>>(P, o);
+}
+
 }  // namespace
 
 hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
@@ -1423,21 +1592,6 @@ hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u,
       k_ef_capture<false><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, nullptr, m);
   }
   if (ev_end) (void)hipEventRecord(ev_end, st);
-  k_select_init<<<P.n_seg, kThreads, 0, st>>>(P);
-  k_recap_hist<<<kFullBlocks, kThreads, 0, st>>>(P, e);
-  k_recap_decide<<<P.n_seg, kThreads, 0, st>>>(P);
-  k_recapture<<<kFullBlocks, kThreads, 0, st>>>(P, e);
-  k_runs<<<P.n_seg, 1024, 0, st>>>(P);
-  if (P.n_chunks > 0) k_scatter<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
-  k_find<<<P.n_seg, kThreads, 0, st>>>(P, 0);
-  const unsigned mixed = (unsigned)(P.n_chunks + kFullBlocks);
-  for (int pass = 1; pass < 3; ++pass) {
-    k_hist<<<mixed, kThreads, 0, st>>>(P, e, pass);
-    k_find<<<P.n_seg, kThreads, 0, st>>>(P, pass);
-  }
-  if (P.n_chunks > 0) k_count_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
-  k_count_full<<<kFullBlocks, kThreads, 0, st>>>(P, e);
-  k_scan<<<P.n_seg, 1024, 0, st>>>(P, q8.enabled ? q8.scales : nullptr);
   EmitOut o{};
   o.e = e;
   o.u = (u && (P.flags & kFlagMomentumMask)) ? u : nullptr;
@@ -1449,11 +1603,75 @@ hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u,
   o.seed_hi = q8.seed_hi;
   o.step_lo = q8.step_lo;
   o.err = P.err;
-  if (P.n_chunks > 0) k_emit_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P, o);
-  k_emit_full<<<kFullBlocks, kThreads, 0, st>>>(P, o);
+  select_emit(P, e, o, q8.enabled ? q8.scales : nullptr, st);
   k_finalize<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
   return hipGetLastError();
 }
+
+hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, float* e,
+                            float* u, float m, const float* tau, float* out_vals,
+                            int32_t* out_idx, int32_t* out_count, hipStream_t st,
+                            hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (P.n_seg == 0) return hipSuccess;
+  DevPlan Q = P;
+  Q.k = P.k_call;
+  Q.thr = P.thr_call;
+  Q.keys = kKeysMagnitude;
+  k_prep_call<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, tau);
+  if (ev_begin) (void)hipEventRecord(ev_begin, st);
+  if (P.n_tiles > 0) {
+    if (u)
+      k_ef_capture<true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(Q, g, e, u, m);
+    else
+      k_ef_capture<false><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+  }
+  if (ev_end) (void)hipEventRecord(ev_end, st);
+  k_thresh_k<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, out_count);
+  EmitOut o{};
+  o.e = e;
+  o.u = (u && (P.flags & kFlagMomentumMask)) ? u : nullptr;
+  o.vals = out_vals;
+  o.idx = out_idx;
+  o.err = P.err;
+  select_emit(Q, e, o, nullptr, st);
+  if (O.n_out_chunks > 0)
+    k_pad_out<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(O, P.k_call, out_vals, out_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, float m,
+                        uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
+                        hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (P.n_seg == 0) return hipSuccess;
+  DevPlan Q = P;
+  Q.k = P.k_call;
+  Q.thr = P.thr_call;
+  Q.keys = kKeysRandom;
+  Q.seed_lo = (uint32_t)seed;
+  Q.seed_hi = (uint32_t)(seed >> 32);
+  Q.step_lo = (uint32_t)step;
+  k_prep_call<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, nullptr);
+  if (ev_begin) (void)hipEventRecord(ev_begin, st);
+  if (P.n_tiles > 0) {
+    const unsigned nt = (unsigned)P.n_tiles;
+    if (e && u) k_randk_capture<true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
+    else if (e) k_randk_capture<false, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+    else if (u) k_randk_capture<true, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, u, m);
+    else k_randk_capture<false, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, nullptr, m);
+  }
+  if (ev_end) (void)hipEventRecord(ev_end, st);
+  EmitOut o{};
+  o.e = e;
+  o.u = (u && (P.flags & kFlagMomentumMask)) ? u : nullptr;
+  o.vals = out_vals;
+  o.idx = out_idx;
+  o.err = P.err;
+  o.vsrc = e ? e : (u ? u : g);
+  o.rk_scale = e ? nullptr : P.rk_scale;
+  select_emit(Q, e, o, nullptr, st);
+  return hipGetLastError();
+}
+
 
 hipError_t launch_sign(const DevPlan& P, const float* g, float* e, float* u, float m,
                        uint32_t* bits, float* scales, hipStream_t st, hipEvent_t ev_begin,

@@ -199,6 +199,49 @@ int gc_qsgd_compress(gc_plan* plan, const float* g, float* e, float* u, float mo
 int gc_qsgd_decompress(const gc_plan* plan, const int8_t* codes, const float* norms,
                        int32_t levels, float* dense, int accumulate, void* stream);
 
+/*
+ * Threshold sparsification with error feedback (genomic-FL glossary, sparsification section:
+ * entries below a fixed or adaptive magnitude threshold are dropped; "Gradient
+ * Sparsification" glossary, mechanism section: the threshold may change per layer and step).
+ * Per segment, after the same momentum and EF add as gc_topk_ef_compress, the entries with
+ * |acc| >= |tau_s| are kept, at most k_s of them (the plan's k is the cap): when more reach
+ * the threshold, the k_s largest by (|acc| descending, index ascending).
+ *   tau       : device float[n_seg], one threshold per segment (|tau| is used; not NaN).
+ *   out_vals, out_idx : the plan's layout; segment s writes its c_s kept entries in
+ *               ascending index order at out_off[s], and the slots [c_s, k_s) get value +0
+ *               and index -1 (gc_decompress skips them).
+ *   out_count : device int32[n_seg] receiving c_s, or NULL.
+ *   e         : +0 at the kept positions, acc elsewhere; u zeroed there with
+ *               GC_MOMENTUM_MASK.
+ * The Top-k threshold estimate of the plan is not touched.  Same alignment and aliasing
+ * rules as gc_topk_ef_compress.  Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_threshold_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                             const float* tau, float* out_vals, int32_t* out_idx,
+                             int32_t* out_count, void* stream);
+
+/*
+ * Random-k sparsification (first page, Random-k section: a random mask per iteration, no
+ * sort of the gradient, unbiased; "Gradient Compression" glossary: random sparsification).
+ * Per segment exactly k_s positions, the k_s largest of a 31-bit key per element -- word
+ * (gi % 4) of the Philox4x32-10 block keyed (seed lo, seed hi) at counter (gi / 4 lo, gi / 4
+ * hi, step lo, 0x53), shifted right by one; gi the global element index; equal keys go to
+ * the lower index.  Ranking by independent uniform keys draws a uniformly random k-subset;
+ * the mask depends on (seed, step, gi) only, so every worker can rebuild it.
+ *   x = g, or with u the momentum-corrected u = fl(fl(m*u) + g) (written back);
+ *   e given (error feedback): acc = fl(e + x), out_vals = acc at the mask, e = +0 there and
+ *         acc elsewhere;
+ *   e NULL: out_vals = fl(x * fl32(n_s / k_s)) at the mask (n_s / k_s formed in double),
+ *         whose expectation is x; nothing else is read for the plain case (g is gathered at
+ *         the mask only).
+ *   out_vals, out_idx : the plan's layout, ascending index per segment.
+ *   u zeroed at the mask with GC_MOMENTUM_MASK.
+ * g, e and u must be 16-byte aligned.  Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_randk_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
+                      uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
+                      void* stream);
+
 /* Forget the threshold estimates: the next compress call runs as on a fresh plan. */
 int gc_plan_reset_estimate(gc_plan* plan, void* stream);
 
