@@ -63,9 +63,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--codec", choices=("topk", "sign", "qsgd"), default="topk",
+    ap.add_argument("--codec", choices=("topk", "sign", "qsgd", "threshold", "randk"),
+                    default="topk",
                     help="topk: EF-Top-k (default); sign: 1-bit sign with error feedback; "
-                         "qsgd: QSGD with 127 levels and error feedback")
+                         "qsgd: QSGD with 127 levels and error feedback; threshold: keep "
+                         "|acc| >= tau_s (at most k_s) with error feedback; randk: Random-k "
+                         "with error feedback")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-momentum-variant", action="store_true")
     return ap.parse_args()
@@ -83,10 +86,16 @@ def bytes_per_element(wl, codec="topk"):
 def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
     import torch
     vals, idx, codes, scales = outs
+    tau = scales if codec == "threshold" else None
     m = wl.momentum or 0.0
 
     def step(t):
-        if codec == "sign":
+        if codec == "threshold":
+            plan.threshold_compress(gbufs[t % len(gbufs)], e, tau, vals, idx, u=u, momentum=m)
+        elif codec == "randk":
+            plan.randk_compress(gbufs[t % len(gbufs)], vals, idx, e=e, u=u, momentum=m, seed=0,
+                                step=t)
+        elif codec == "sign":
             plan.sign_compress(gbufs[t % len(gbufs)], e, codes, scales, u=u, momentum=m)
         elif codec == "qsgd":
             plan.qsgd_compress(gbufs[t % len(gbufs)], codes, scales, levels=127, e=e, u=u,
@@ -119,7 +128,8 @@ def setup(wl, n_gbufs=4, codec="topk"):
     import torch
     import gradient_compression_amd as gca
     from synth import gen
-    plan = gca.Plan(wl.offsets(), ratio=wl.ratio if codec == "topk" else 0.0)
+    plan = gca.Plan(wl.offsets(),
+                    ratio=wl.ratio if codec in ("topk", "threshold", "randk") else 0.0)
     dev = torch.device("cuda")
     gbufs = []
     for t in range(n_gbufs):
@@ -138,6 +148,13 @@ def setup(wl, n_gbufs=4, codec="topk"):
     if codec == "qsgd":   # one int8 code per element, one norm per segment
         codes = torch.empty(wl.n, dtype=torch.int8, device=dev)
         scales = torch.empty(wl.n_seg, dtype=torch.float32, device=dev)
+    if codec == "threshold":
+        # tau_s = |k_s-th largest acc| after 8 EF-Top-k steps (the residual's steady state),
+        # then fixed: about k_s entries reach it per step, the cap k_s binding when more do
+        for t in range(8):
+            plan.compress(gbufs[t % n_gbufs], e, vals, idx, u=u, momentum=wl.momentum or 0.0)
+        kth = torch.from_numpy(plan.last_stats()["kth_key"].astype(np.uint32).view(np.float32))
+        scales = kth.to(dev)   # the thresholds ride in the scales slot
     torch.cuda.synchronize()
     return plan, gbufs, e, u, (vals, idx, codes, scales)
 
@@ -249,7 +266,7 @@ def main():
     k1_ach = bpe * wl.n / k1_ms / 1e6
     log(f"[bench] {ms:.3f} ms/step, {value:.1f} GB/s gradient, effective {eff:.1f} GB/s "
         f"({eff / HBM_PEAK_GBPS:.1%} of peak); EF pass {k1_ms:.3f} ms ({k1_ach:.1f} GB/s)")
-    traffic = measured_traffic(wl.name) if codec == "topk" else None
+    traffic = measured_traffic(wl.name) if codec in ("topk", "threshold") else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -282,6 +299,8 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": {"topk": "k_ef_capture (EF add + key + candidate capture)",
+                       "threshold": "k_ef_capture (EF add + key + capture at tau)",
+                       "randk": "k_randk_capture (EF add + Philox key + capture)",
                        "sign": "k_sign_pass1 + k_sign_scale + k_sign_pass2",
                        "qsgd": "k_qsgd_pass1 + k_qsgd_norm + k_qsgd_pass2"}[codec],
             "achieved": round(k1_ach, 1),
@@ -295,7 +314,8 @@ def main():
         },
     }
     if codec != "topk":
-        name = {"sign": "1-bit sign EF", "qsgd": "QSGD-127 EF"}[codec]
+        name = {"sign": "1-bit sign EF", "qsgd": "QSGD-127 EF", "threshold": "threshold EF",
+                "randk": "Random-k EF"}[codec]
         result["metric"] = f"{name} compress GB/s of fp32 gradient (1 GPU) and % of HBM peak"
         print(json.dumps(result), flush=True)
         return

@@ -269,6 +269,10 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   uint32_t* d_thr_rand;
   float* d_rk_scale;
   cv.add(&d.k_call, n_seg);
+  cv.add(&d.thr_est, n_seg);
+  cv.add(&d.beta_est, n_seg);
+  cv.add(&d.tau_key, n_seg);
+  cv.add(&d.tau_cnt, n_seg);
   cv.add(&d.thr_call, n_seg);
   cv.add(&d_thr_rand, n_seg);
   cv.add(&d_rk_scale, n_seg);
@@ -321,6 +325,8 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   up(upload(d_rk_scale, rk_scale));
   up(upload(d.thr, thr_init));
   up(upload(d.beta, std::vector<float>(n_seg, kInitialBeta)));
+  up(upload(d.thr_est, std::vector<uint32_t>(n_seg, gc::kNoCapture)));
+  up(upload(d.beta_est, std::vector<float>(n_seg, kInitialBeta)));
   up(hipMemset(d.cand_cnt, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
   up(hipMemset(d.mode, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
   up(hipMemset(d.kth, 0, sizeof(uint32_t) * std::max(n_seg, 1)));

@@ -131,6 +131,11 @@ struct DevPlan {
   uint32_t* thr_call;          // [n_seg] capture threshold of this call
   const uint32_t* thr_rand;    // [n_seg] Random-k capture threshold (fixed per plan)
   const float* rk_scale;       // [n_seg] fl32(n / k), Random-k value scale without feedback
+  uint32_t* thr_est;           // [n_seg] threshold calls: capture floor estimate (kNoCapture:
+                               // none); the capture runs at max(key(tau), floor)
+  float* beta_est;             // [n_seg] its margin
+  uint32_t* tau_key;           // [n_seg] threshold calls: key(|tau|) of this call
+  uint32_t* tau_cnt;           // [n_seg] entries with key >= tau_key counted by the capture
   int32_t keys;                // kKeysMagnitude or kKeysRandom
   uint32_t seed_lo, seed_hi, step_lo;   // Random-k key stream
 };

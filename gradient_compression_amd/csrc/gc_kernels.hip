@@ -46,9 +46,10 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t a = 0xD2511F53u, b = 0xCD9E8D57u;
-    const uint32_t hi0 = __umulhi(a, c0), lo0 = a * c0;
-    const uint32_t hi1 = __umulhi(b, c2), lo1 = b * c2;
+    // one 32x32->64 product per multiplier (a single v_mad_u64_u32 gives both halves)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -65,9 +66,10 @@ __device__ __forceinline__ void philox4(uint32_t c0, uint32_t c1, uint32_t c2, u
                                         uint32_t k0, uint32_t k1, uint32_t (&out)[4]) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t a = 0xD2511F53u, b = 0xCD9E8D57u;
-    const uint32_t hi0 = __umulhi(a, c0), lo0 = a * c0;
-    const uint32_t hi1 = __umulhi(b, c2), lo1 = b * c2;
+    // one 32x32->64 product per multiplier (a single v_mad_u64_u32 gives both halves)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -281,17 +283,29 @@ __global__ __launch_bounds__(kThreads) void k_prep(DevPlan P) {
 
 __global__ __launch_bounds__(kThreads) void k_reset(DevPlan P) {
   const int s = blockIdx.x * kThreads + threadIdx.x;
-  if (s < P.n_seg) P.thr[s] = P.thr_init[s];
+  if (s < P.n_seg) {
+    P.thr[s] = P.thr_init[s];
+    P.thr_est[s] = kNoCapture;
+  }
 }
 
 // Threshold and Random-k calls: this call's k (the plan's, reduced after the capture for a
-// threshold call) and capture threshold (key of |tau|, or the plan's Random-k threshold).
+// threshold call) and capture threshold: for a threshold call max(key(|tau|), floor), the floor
+// being the estimate of the k-th largest key kept from the last threshold calls (the capture
+// then stays within capacity when more than k entries reach tau); for Random-k the plan's.
 __global__ __launch_bounds__(kThreads) void k_prep_call(DevPlan P, const float* __restrict__ tau) {
   const int s = blockIdx.x * kThreads + threadIdx.x;
   if (s < P.n_seg) {
     P.cand_cnt[s] = 0;
     P.k_call[s] = P.k[s];
-    P.thr_call[s] = tau ? mag_key(tau[s]) : P.thr_rand[s];
+    if (tau) {
+      const uint32_t tk = mag_key(tau[s]), fl = P.thr_est[s];
+      P.tau_key[s] = tk;
+      P.tau_cnt[s] = 0;
+      P.thr_call[s] = fl == kNoCapture ? tk : max(tk, fl);
+    } else {
+      P.thr_call[s] = P.thr_rand[s];
+    }
   }
   if (s == 0) {
     *P.full_count = 0;
@@ -300,12 +314,14 @@ __global__ __launch_bounds__(kThreads) void k_prep_call(DevPlan P, const float* 
   }
 }
 
-// Threshold call: keep min(number of keys at or above the threshold, k) entries per segment.
-// The capture counted every such key, also those past the candidate capacity.
+// Threshold call: keep min(number of keys at or above key(|tau|), k) entries per segment (the
+// capture counted them all, also above a floor and past the candidate capacity).  The
+// candidates, captured at max(key(|tau|), floor), then hold them iff at least that many were
+// captured; otherwise the segment takes the exact fallback.
 __global__ __launch_bounds__(kThreads) void k_thresh_k(DevPlan P, int32_t* __restrict__ count) {
   const int s = blockIdx.x * kThreads + threadIdx.x;
   if (s >= P.n_seg) return;
-  const uint32_t kk = min(P.cand_cnt[s], P.k[s]);
+  const uint32_t kk = min(P.tau_cnt[s], P.k[s]);
   P.k_call[s] = kk;
   if (count) count[s] = (int32_t)kk;
 }
@@ -370,12 +386,14 @@ __device__ __forceinline__ void capture_tile(const DevPlan& P, int s, int64_t t,
 // -------------------------------------------------------------------------- ef_capture
 // One tile per workgroup.  acc = e + (u = m*u + g | g) is written back into e; elements
 // whose key reaches the segment's threshold are captured (capture_tile).
-template <bool kMomentum>
+// kCountTau (threshold calls): also count the tile's keys >= key(|tau|) into tau_cnt.
+template <bool kMomentum, bool kCountTau = false>
 __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float* __restrict__ g,
                                                         float* __restrict__ e,
                                                         float* __restrict__ u, float m) {
   __shared__ uint32_t s_w[kWaves];
   __shared__ uint32_t s_base;
+  __shared__ uint32_t s_tau[kWaves];
   const int64_t t = blockIdx.x;
   const int4 desc = P.tile_desc[t];  // one load: no dependent lookups before the stream
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
@@ -427,6 +445,25 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
         }
         acc[v][c] = a;
       }
+  }
+  if (kCountTau) {
+    const uint32_t tk = P.tau_key[s];
+    uint32_t c = 0;
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        c += (pb + v * 256 + cc < len && mag_key(acc[v][cc]) >= tk) ? 1u : 0u;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+    if (lane_id() == 0) s_tau[wave_id()] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) tot += s_tau[i];
+      if (tot) atomicAdd(&P.tau_cnt[s], tot);
+    }
   }
   const uint32_t thr = P.thr[s];
   if (thr == kNoCapture) return;  // uniform: this segment re-captures later
@@ -1048,6 +1085,31 @@ __global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
   P.thr[s] = next;
 }
 
+// Threshold calls: the capture floor for the next call, by the rule of k_finalize applied to
+// this call's k (so it tracks the k-th largest kept key while the cap binds and falls below
+// key(|tau|), where it has no effect, while it does not).
+__global__ __launch_bounds__(kThreads) void k_finalize_thr(DevPlan P) {
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  if (s >= P.n_seg) return;
+  const uint32_t mode = P.mode[s];
+  if (P.thr_init[s] != kNoCapture || mode == kModeSkip ||
+      (P.flags & (kFlagForceFull | kFlagNoEstimate)))
+    return;   // small segments capture everything; k = 0 keeps its floor
+  float b = P.beta_est[s];
+  const uint32_t why = P.why[s];
+  if (why == kWhyMiss) {
+    b = fmaxf(b * 0.85f, 0.25f);
+  } else if (why == kWhyOverflow) {
+    b = fminf(b * 1.05f, GC_BETA_MAX);
+  } else if (mode == kModeCand) {
+    const float rho = (float)P.cand_cnt[s] / (float)P.k_call[s];
+    if (rho > GC_RHO_HIGH) b = fminf(b * 1.03f, GC_BETA_MAX);
+    else if (rho < GC_RHO_LOW) b = fmaxf(b * 0.97f, 0.25f);
+  }
+  P.beta_est[s] = b;
+  P.thr_est[s] = mag_key(b * __uint_as_float(P.kth[s]));
+}
+
 // ------------------------------------------------------------------------ 1-bit sign
 // 1-bit sign compression with error feedback ("Communication Optimization > Gradient
 // Compression", 1-bit SGD section: Q(g) = sign(g) * ||g||_1 / d, one scale per layer; error
@@ -1433,16 +1495,45 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
   const int4 desc = P.tile_desc[t];
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
   const int len = desc.z, s = desc.w;
-  if (kEF) {
-    f4 acc[kSlots];
-    ef_add_tile<kMomentum>(g, e, u, m, start, len, acc);
-  } else if (kMomentum) {
-    momentum_tile(g, u, m, start, len);
-  }  // neither: nothing to stream, g is read at the kept positions only
-  const uint32_t thr = P.thr[s];
-  if (thr == kNoCapture) return;  // uniform: this segment takes the exact fallback
+  const uint32_t thr = P.thr[s];  // kNoCapture: this segment takes the exact fallback
   f4 key[kSlots];
-  rand_key_tile(P, start, len, key);
+  if (kEF && len == kTile && (start & 3) == 0) {
+    // whole aligned tile: issue the loads, draw the keys while they are in flight
+    const int pb = slot_base();
+    const f4* g4 = reinterpret_cast<const f4*>(g + start);
+    f4* e4 = reinterpret_cast<f4*>(e + start);
+    f4* u4 = kMomentum ? reinterpret_cast<f4*>(u + start) : nullptr;
+    f4 gv[kSlots], ev[kSlots], uv[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      gv[v] = GC_NT_LOAD_G ? __builtin_nontemporal_load(g4 + q) : g4[q];
+      ev[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(e4 + q) : e4[q];
+      if (kMomentum) uv[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(u4 + q) : u4[q];
+    }
+    if (thr != kNoCapture) rand_key_tile(P, start, len, key);
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      f4 x = gv[v];
+      if (kMomentum) {
+        const f4 mu = m * uv[v];
+        x = mu + x;
+        if (GC_NT_STORE_E) __builtin_nontemporal_store(x, u4 + q); else u4[q] = x;
+      }
+      const f4 a = ev[v] + x;
+      if (GC_NT_STORE_E) __builtin_nontemporal_store(a, e4 + q); else e4[q] = a;
+    }
+  } else {
+    if (kEF) {
+      f4 acc[kSlots];
+      ef_add_tile<kMomentum>(g, e, u, m, start, len, acc);
+    } else if (kMomentum) {
+      momentum_tile(g, u, m, start, len);
+    }  // neither: nothing to stream, g is read at the kept positions only
+    if (thr != kNoCapture) rand_key_tile(P, start, len, key);
+  }
+  if (thr == kNoCapture) return;  // uniform
   capture_tile(P, s, t, start, len, key, thr, s_w, &s_base);
 }
 
@@ -1621,9 +1712,9 @@ hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, 
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (P.n_tiles > 0) {
     if (u)
-      k_ef_capture<true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(Q, g, e, u, m);
+      k_ef_capture<true, true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(Q, g, e, u, m);
     else
-      k_ef_capture<false><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+      k_ef_capture<false, true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(Q, g, e, nullptr, m);
   }
   if (ev_end) (void)hipEventRecord(ev_end, st);
   k_thresh_k<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, out_count);
@@ -1636,6 +1727,7 @@ hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, 
   select_emit(Q, e, o, nullptr, st);
   if (O.n_out_chunks > 0)
     k_pad_out<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(O, P.k_call, out_vals, out_idx);
+  k_finalize_thr<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
   return hipGetLastError();
 }
 

@@ -213,8 +213,11 @@ int gc_qsgd_decompress(const gc_plan* plan, const int8_t* codes, const float* no
  *   out_count : device int32[n_seg] receiving c_s, or NULL.
  *   e         : +0 at the kept positions, acc elsewhere; u zeroed there with
  *               GC_MOMENTUM_MASK.
- * The Top-k threshold estimate of the plan is not touched.  Same alignment and aliasing
- * rules as gc_topk_ef_compress.  Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ * Candidates are captured at max(|tau_s|, a floor estimated from the last threshold calls'
+ * k-th kept magnitude), so that a threshold that many entries reach stays on the fast path;
+ * the result does not depend on the floor.  The Top-k threshold estimate of the plan is not
+ * touched.  Same alignment and aliasing rules as gc_topk_ef_compress.
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
  */
 int gc_threshold_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
                              const float* tau, float* out_vals, int32_t* out_idx,
@@ -242,7 +245,8 @@ int gc_randk_compress(gc_plan* plan, const float* g, float* e, float* u, float m
                       uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
                       void* stream);
 
-/* Forget the threshold estimates: the next compress call runs as on a fresh plan. */
+/* Forget the threshold estimates (of Top-k calls and the capture floor of threshold calls):
+ * the next call runs as on a fresh plan. */
 int gc_plan_reset_estimate(gc_plan* plan, void* stream);
 
 /*

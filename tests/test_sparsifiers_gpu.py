@@ -109,14 +109,42 @@ def test_threshold_fallbacks(flag):
         assert all(m in (gca.MODE_SKIP, gca.MODE_FULL) for m in st["mode"]), st["mode"]
 
 
-def test_threshold_overflow_takes_exact_path():
+def test_threshold_overflow_then_floor():
     """tau = 0 on a segment far larger than its candidate capacity: every element reaches
-    the threshold, the capture overflows, and the k largest still come out exactly."""
-    sizes = [2_000_003]
-    plan = run_threshold(sizes, [1000], _grads(sizes[0], 2, 5), lambda t, g, e: [0.0],
-                         label="overflow")
-    st = plan.last_stats()
-    assert st["mode"][0] in (gca.MODE_FULL, gca.MODE_RECAPTURED)
+    the threshold, the first capture overflows and the k largest still come out exactly (the
+    exact fallback); later calls capture above the floor estimated from the kept entries and
+    stay on the candidate path."""
+    sizes = [2_000_003, 300001]
+    seen = []
+
+    def taus(t, g, e):
+        return [0.0, 3.0]
+    plan = run_threshold(sizes, [1000, 300], _grads(sum(sizes), 1, 5), taus, label="overflow")
+    seen.append(plan.last_stats()["mode"].tolist())
+    assert seen[0][0] in (gca.MODE_FULL, gca.MODE_RECAPTURED)
+    # continue on the same plan: the floor is per plan
+    off = _offsets(sizes)
+    n = int(off[-1])
+    dev = torch.device("cuda")
+    e_d = torch.zeros(n, device=dev)
+    e_h = np.zeros(n, np.float32)
+    vals = torch.empty(plan.total_k, device=dev)
+    idx = torch.empty(plan.total_k, dtype=torch.int32, device=dev)
+    tau = torch.tensor([0.0, 3.0], device=dev)
+    for t, g in enumerate(_grads(n, 6, 55)):
+        plan.threshold_compress(torch.from_numpy(g).to(dev), e_d, tau, vals, idx)
+        torch.cuda.synchronize()
+        seen.append(plan.last_stats()["mode"].tolist())
+        for s in range(2):
+            a, b = int(off[s]), int(off[s + 1])
+            ka = int(plan.out_off[s])
+            hv, hi = oracle.threshold_ef_segment(g[a:b].copy(), e_h[a:b], int(plan.k[s]),
+                                                 float(tau[s]))
+            assert_bitwise(idx[ka:ka + hi.size], hi, f"floor it{t} seg{s} idx")
+            assert_bitwise(vals[ka:ka + hi.size], hv, f"floor it{t} seg{s} vals")
+        assert_bitwise(e_d, e_h, f"floor it{t} residual")
+    log(f"[threshold floor] modes per call: {seen}")
+    assert seen[-1] == [gca.MODE_CANDIDATES, gca.MODE_CANDIDATES], seen
 
 
 def test_side_calls_keep_topk_estimate():
