@@ -1445,10 +1445,11 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_decompress(DevPlan P,
 }
 
 // -------------------------------------------------------------------------------- Random-k
-// Random-k (first page, Random-k section): exactly k positions per segment, the k largest
-// random keys (rand_key_tile), a uniformly random subset drawn anew each step.  The streaming
-// pass forms acc as the Top-k pass does and captures by key instead of magnitude; the select
-// and the ordered emit are shared, the kept values then read back from where acc lives.
+// Random-k ("Gradient Compression", memory-compression glossary, Random-k section): exactly k
+// positions per segment, those with the k largest random keys (rand_key_tile), a uniformly
+// random subset drawn anew each step.  The streaming pass forms acc as the Top-k pass does and
+// captures by key instead of magnitude; the select and the ordered emit are shared, the kept
+// values then read back from where acc lives.
 
 // u = fl(fl(m*u) + g) over one tile, stored (momentum without error feedback).
 __device__ __forceinline__ void momentum_tile(const float* __restrict__ g, float* __restrict__ u,

@@ -224,8 +224,9 @@ int gc_threshold_ef_compress(gc_plan* plan, const float* g, float* e, float* u, 
                              int32_t* out_count, void* stream);
 
 /*
- * Random-k sparsification (first page, Random-k section: a random mask per iteration, no
- * sort of the gradient, unbiased; "Gradient Compression" glossary: random sparsification).
+ * Random-k sparsification ("Gradient Compression", memory-compression glossary, Random-k
+ * section: a random mask per iteration, no sort of the gradient, unbiased; genomic-FL
+ * glossary, sparsification section: random sparsification).
  * Per segment exactly k_s positions, the k_s largest of a 31-bit key per element -- word
  * (gi % 4) of the Philox4x32-10 block keyed (seed lo, seed hi) at counter (gi / 4 lo, gi / 4
  * hi, step lo, 0x53), shifted right by one; gi the global element index; equal keys go to

@@ -41,8 +41,8 @@
  * Threshold sparsification with error feedback: the entries with |acc| >= tau, at most k of
  * them (the largest), as above otherwise.
  *
- * Random-k (first page, Random-k section; "Gradient Compression" glossary, random
- * sparsification): exactly k positions per segment, a uniformly random subset drawn anew each
+ * Random-k ("Gradient Compression", memory-compression glossary, Random-k section; genomic-FL
+ * glossary, sparsification section: random sparsification): exactly k positions per segment, a uniformly random subset drawn anew each
  * step -- the k largest of a Philox4x32-10 key per element (counter tag 0x53).  With error
  * feedback the values go unscaled and the residual is kept; without it they are scaled by
  * n/k so that their expectation is acc.
@@ -463,8 +463,8 @@ static uint32_t randk_key(uint64_t seed, uint64_t step, int64_t gidx)
 
 /*
  * Random-k of one segment of n elements (global offset seg_base), k in [0, n]
- * (first page, Random-k section: a random mask per iteration, unbiased, no sort of the
- * gradient needed).  The mask is the k positions whose random keys are largest, equal keys
+ * (memory-compression glossary, Random-k section: a random mask per iteration, unbiased, no
+ * sort of the gradient needed).  The mask is the k positions whose random keys are largest, equal keys
  * going to the lower position: sorting by independent uniform keys is a uniform random
  * permutation, so every k-subset is equally likely (up to the rare equal 31-bit keys).
  *   x = g, or with u the momentum-corrected u = fl(fl(m*u) + g);
