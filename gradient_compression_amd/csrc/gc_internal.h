@@ -39,6 +39,9 @@ namespace gc {
 #ifndef GC_BETA_MAX         // largest margin: next threshold <= GC_BETA_MAX * |k-th key|
 #define GC_BETA_MAX 0.98f
 #endif
+#ifndef GC_XCD_REMAP        // streaming pass: contiguous tile ranges per XCD
+#define GC_XCD_REMAP 0
+#endif
 constexpr int kThreads = GC_TILE_THREADS;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSlots = GC_TILE_SLOTS;

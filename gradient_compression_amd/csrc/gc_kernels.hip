@@ -394,7 +394,13 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
   __shared__ uint32_t s_w[kWaves];
   __shared__ uint32_t s_base;
   __shared__ uint32_t s_tau[kWaves];
+#if GC_XCD_REMAP
+  // workgroups go round-robin to the 8 XCDs: give XCD x a contiguous range of tiles
+  const int64_t G = gridDim.x, per = G / 8, rem = G % 8, xcd = blockIdx.x % 8;
+  const int64_t t = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / 8;
+#else
   const int64_t t = blockIdx.x;
+#endif
   const int4 desc = P.tile_desc[t];  // one load: no dependent lookups before the stream
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
   const int len = desc.z, s = desc.w;
