@@ -1119,9 +1119,10 @@ __global__ __launch_bounds__(kThreads) void k_finalize_thr(DevPlan P) {
 // ------------------------------------------------------------------------ 1-bit sign
 // 1-bit sign compression with error feedback ("Communication Optimization > Gradient
 // Compression", 1-bit SGD section: Q(g) = sign(g) * ||g||_1 / d, one scale per layer; error
-// feedback as for top-K).  Pass 1 streams acc = e + x into e and takes each tile's sum of
-// |acc| in double; the scale is fl32(S / n) per segment; pass 2 writes the sign bits (bit i
-// of word i/32, 1 = negative) and the residual e = fl(acc - sign * scale).
+// feedback as for top-K).  Pass 1 takes each tile's sum of |acc| in double (with momentum it
+// also stores u and acc = e + u; without, it only reads and pass 2 forms acc = e + g again);
+// the scale is fl32(S / n) per segment; pass 2 writes the sign bits (bit i of word i/32,
+// 1 = negative) and the residual e = fl(acc - sign * scale).
 
 // Load the tile of g (and u), form acc (momentum first), store acc into e (and u).
 template <bool kMomentum>
@@ -1176,6 +1177,49 @@ __device__ __forceinline__ void ef_add_tile(const float* __restrict__ g, float* 
   }
 }
 
+// load_tile for a streaming pass: the full-tile loads are non-temporal.
+__device__ __forceinline__ void load_tile_nt(const float* __restrict__ base, int len,
+                                             f4 (&x)[kSlots]) {
+  const int pb = slot_base();
+  if (len == kTile && ((reinterpret_cast<uintptr_t>(base) & 15) == 0)) {
+    const f4* b4 = reinterpret_cast<const f4*>(base);
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) x[v] = __builtin_nontemporal_load(b4 + ((pb + v * 256) >> 2));
+  } else {
+    load_tile(base, len, x);
+  }
+}
+
+// acc = fl(e + g) over one tile without storing it (lanes past len get 0): the two-pass
+// codecs without momentum form acc in both passes, so their first pass only reads.
+__device__ __forceinline__ void acc_tile(const float* __restrict__ g, const float* __restrict__ e,
+                                         int64_t start, int len, f4 (&acc)[kSlots]) {
+  const int pb = slot_base();
+  if (len == kTile && (start & 3) == 0) {
+    const f4* g4 = reinterpret_cast<const f4*>(g + start);
+    const f4* e4 = reinterpret_cast<const f4*>(e + start);
+    f4 gv[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      const int q = (pb + v * 256) >> 2;
+      gv[v] = GC_NT_LOAD_G ? __builtin_nontemporal_load(g4 + q) : g4[q];
+      acc[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(e4 + q) : e4[q];
+    }
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) acc[v] = acc[v] + gv[v];
+  } else {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = pb + v * 256 + c;
+        acc[v][c] = p < len ? e[start + p] + g[start + p] : 0.0f;
+      }
+  }
+}
+
+// Pass 1: per-tile sum of |acc|.  With momentum acc (and u) is stored for pass 2; without,
+// nothing is written and pass 2 forms acc again from g and e.
 template <bool kMomentum>
 __global__ __launch_bounds__(kThreads) void k_sign_pass1(DevPlan P, const float* __restrict__ g,
                                                         float* __restrict__ e,
@@ -1186,7 +1230,10 @@ __global__ __launch_bounds__(kThreads) void k_sign_pass1(DevPlan P, const float*
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
   const int len = desc.z;
   f4 acc[kSlots];
-  ef_add_tile<kMomentum>(g, e, u, m, start, len, acc);
+  if (kMomentum)
+    ef_add_tile<true>(g, e, u, m, start, len, acc);
+  else
+    acc_tile(g, e, start, len, acc);
   double l1 = 0.0;   // lanes past len hold 0
 #pragma unroll
   for (int v = 0; v < kSlots; ++v)
@@ -1225,7 +1272,10 @@ __global__ __launch_bounds__(1024) void k_sign_scale(DevPlan P, float* __restric
 
 // Sign bits of one tile-shaped block: lane l of slot v covers 4 elements of the 32-element
 // word (w*kSlots + v)*8 + l/8 (tile-relative); its nibble lands at bit 4*(l%8).
-__global__ __launch_bounds__(kThreads) void k_sign_pass2(DevPlan P, float* __restrict__ e,
+// kRecompute: acc = e + g formed here (no momentum); else acc was stored into e by pass 1.
+template <bool kRecompute>
+__global__ __launch_bounds__(kThreads) void k_sign_pass2(DevPlan P, const float* __restrict__ g,
+                                                        float* __restrict__ e,
                                                         uint32_t* __restrict__ bits,
                                                         const float* __restrict__ scales) {
   const int64_t t = blockIdx.x;
@@ -1235,7 +1285,10 @@ __global__ __launch_bounds__(kThreads) void k_sign_pass2(DevPlan P, float* __res
   const float scale = scales[s];
   const int pb = slot_base(), lane = lane_id();
   f4 acc[kSlots];
-  load_tile(e + start, len, acc);
+  if (kRecompute)
+    acc_tile(g, e, start, len, acc);
+  else
+    load_tile_nt(e + start, len, acc);
   uint32_t* wb = bits + P.word_off[s] + (t - P.tile_base[s]) * (int64_t)(kTile / 32);
 #pragma unroll
   for (int v = 0; v < kSlots; ++v) {
@@ -1296,7 +1349,8 @@ __global__ __launch_bounds__(kThreads) void k_sign_decompress(DevPlan P,
 // ------------------------------------------------------------------------------ QSGD
 // QSGD with s levels ("Communication Optimization > Gradient Compression", QSGD paragraph,
 // with the 1/s that makes E[Q] = g restored): pass 1 forms acc (e + x with error feedback,
-// else x) and each tile's sum of acc^2 in double; norm = fl32(sqrt(S)) per segment; pass 2
+// else x; stored only where momentum makes pass 2 unable to form it again from g and e) and
+// each tile's sum of acc^2 in double; norm = fl32(sqrt(S)) per segment; pass 2
 // draws the levels at step fl32(norm / s) (counter tag 0x52) and, with error feedback,
 // writes e = fl(acc - fl(code * step)).
 
@@ -1310,8 +1364,10 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass1(DevPlan P, const float*
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
   const int len = desc.z;
   f4 acc[kSlots];
-  if (kEF) {
-    ef_add_tile<kMomentum>(g, e, u, m, start, len, acc);
+  if (kEF && kMomentum) {
+    ef_add_tile<true>(g, e, u, m, start, len, acc);
+  } else if (kEF) {        // acc = e + g, formed again by pass 2
+    acc_tile(g, e, start, len, acc);
   } else if (kMomentum) {  // u = m*u + g, stored; acc = u
     const int pb = slot_base();
 #pragma unroll
@@ -1364,7 +1420,8 @@ __global__ __launch_bounds__(1024) void k_qsgd_norm(DevPlan P, float* __restrict
   }
 }
 
-// kSrc: 0 = acc in e (error feedback), 1 = acc in u (momentum, no feedback), 2 = acc = g.
+// kSrc: 0 = acc in e (error feedback with momentum), 1 = acc in u (momentum, no feedback),
+// 2 = acc = g, 3 = acc = e + g formed here (error feedback without momentum).
 template <int kSrc>
 __global__ __launch_bounds__(kThreads) void k_qsgd_pass2(DevPlan P, const float* __restrict__ g,
                                                         float* __restrict__ e,
@@ -1381,7 +1438,10 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass2(DevPlan P, const float*
   const float limit = (float)levels;
   const int pb = slot_base();
   f4 acc[kSlots];
-  load_tile((kSrc == 0 ? e : (kSrc == 1 ? u : g)) + start, len, acc);
+  if (kSrc == 3)
+    acc_tile(g, e, start, len, acc);
+  else
+    load_tile_nt((kSrc == 0 ? e : (kSrc == 1 ? u : g)) + start, len, acc);
   const bool vec = len == kTile && (start & 3) == 0;
 #pragma unroll
   for (int v = 0; v < kSlots; ++v) {
@@ -1410,7 +1470,7 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass2(DevPlan P, const float*
     const int p0 = pb + v * 256;
     if (vec) {
       *reinterpret_cast<uint32_t*>(codes + start + p0) = packed;
-      if (kSrc == 0) {
+      if (kSrc == 0 || kSrc == 3) {
         f4* e4 = reinterpret_cast<f4*>(e + start);
         if (GC_NT_STORE_E) __builtin_nontemporal_store(r, e4 + (p0 >> 2)); else e4[p0 >> 2] = r;
       }
@@ -1419,7 +1479,7 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass2(DevPlan P, const float*
       for (int c = 0; c < 4; ++c)
         if (p0 + c < len) {
           codes[start + p0 + c] = (int8_t)(packed >> (8 * c));
-          if (kSrc == 0) e[start + p0 + c] = r[c];
+          if (kSrc == 0 || kSrc == 3) e[start + p0 + c] = r[c];
         }
     }
   }
@@ -1784,7 +1844,12 @@ hipError_t launch_sign(const DevPlan& P, const float* g, float* e, float* u, flo
       k_sign_pass1<false><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, nullptr, m);
   }
   k_sign_scale<<<P.n_seg, 1024, 0, st>>>(P, scales);
-  if (P.n_tiles > 0) k_sign_pass2<<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, e, bits, scales);
+  if (P.n_tiles > 0) {
+    if (u)
+      k_sign_pass2<false><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, bits, scales);
+    else
+      k_sign_pass2<true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, bits, scales);
+  }
   if (ev_end) (void)hipEventRecord(ev_end, st);
   return hipGetLastError();
 }
@@ -1812,7 +1877,8 @@ hipError_t launch_qsgd(const DevPlan& P, const float* g, float* e, float* u, flo
   k_qsgd_norm<<<P.n_seg, 1024, 0, st>>>(P, norms);
   if (nt > 0) {
     const uint32_t sl = (uint32_t)seed, sh = (uint32_t)(seed >> 32), tl = (uint32_t)step;
-    if (e) k_qsgd_pass2<0><<<nt, kThreads, 0, st>>>(P, g, e, u, norms, levels, codes, sl, sh, tl);
+    if (e && u) k_qsgd_pass2<0><<<nt, kThreads, 0, st>>>(P, g, e, u, norms, levels, codes, sl, sh, tl);
+    else if (e) k_qsgd_pass2<3><<<nt, kThreads, 0, st>>>(P, g, e, u, norms, levels, codes, sl, sh, tl);
     else if (u) k_qsgd_pass2<1><<<nt, kThreads, 0, st>>>(P, g, e, u, norms, levels, codes, sl, sh, tl);
     else k_qsgd_pass2<2><<<nt, kThreads, 0, st>>>(P, g, e, u, norms, levels, codes, sl, sh, tl);
   }
