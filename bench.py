@@ -83,28 +83,30 @@ def bytes_per_element(wl, codec="topk"):
     return 20 if wl.momentum is not None else 12
 
 
+def run_step(plan, wl, codec, g, e, u, outs, t):
+    """One step of the codec on gradient g (error feedback state e, velocity u)."""
+    vals, idx, codes, scales = outs
+    m = wl.momentum or 0.0
+    if codec == "threshold":   # the thresholds ride in the scales slot
+        plan.threshold_compress(g, e, scales, vals, idx, u=u, momentum=m)
+    elif codec == "randk":
+        plan.randk_compress(g, vals, idx, e=e, u=u, momentum=m, seed=0, step=t)
+    elif codec == "sign":
+        plan.sign_compress(g, e, codes, scales, u=u, momentum=m)
+    elif codec == "qsgd":
+        plan.qsgd_compress(g, codes, scales, levels=127, e=e, u=u, momentum=m, seed=0, step=t)
+    elif wl.int8:   # compress and int8 (error feedback of the quantisation error) in one call
+        plan.compress_int8(g, e, idx, codes, scales, out_vals=vals, u=u, momentum=m, seed=0,
+                           step=t)
+    else:
+        plan.compress(g, e, vals, idx, u=u, momentum=m)
+
+
 def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
     import torch
-    vals, idx, codes, scales = outs
-    tau = scales if codec == "threshold" else None
-    m = wl.momentum or 0.0
 
     def step(t):
-        if codec == "threshold":
-            plan.threshold_compress(gbufs[t % len(gbufs)], e, tau, vals, idx, u=u, momentum=m)
-        elif codec == "randk":
-            plan.randk_compress(gbufs[t % len(gbufs)], vals, idx, e=e, u=u, momentum=m, seed=0,
-                                step=t)
-        elif codec == "sign":
-            plan.sign_compress(gbufs[t % len(gbufs)], e, codes, scales, u=u, momentum=m)
-        elif codec == "qsgd":
-            plan.qsgd_compress(gbufs[t % len(gbufs)], codes, scales, levels=127, e=e, u=u,
-                               momentum=m, seed=0, step=t)
-        elif wl.int8:   # compress and int8 (error feedback of the quantisation error) in one call
-            plan.compress_int8(gbufs[t % len(gbufs)], e, idx, codes, scales, out_vals=vals,
-                               u=u, momentum=m, seed=0, step=t)
-        else:
-            plan.compress(gbufs[t % len(gbufs)], e, vals, idx, u=u, momentum=m)
+        run_step(plan, wl, codec, gbufs[t % len(gbufs)], e, u, outs, t)
 
     for t in range(warmup):
         step(t)
@@ -180,16 +182,25 @@ def copy_ceiling(n_bytes=8 << 30):
     return 2 * n * 4 / ms / 1e6
 
 
-def cpu_baseline(plan, wl, gbuf, e, u):
-    """Time the CPU oracle on one transformer layer's segments (the first 'layer0' ones, or
-    the first segments up to ~200M elements), in a thread pool over segments; check its
-    output against the GPU's on the same inputs."""
+def _ulp(x):
+    return float(np.spacing(np.float32(abs(x))))
+
+
+def cpu_baseline(plan, wl, gbuf, e, u, outs, codec="topk", t=0):
+    """Time the CPU oracle for the codec on the segments from 1 on, up to a budget of
+    elements (250M for the sorting codecs, about one layer of the 7B shape; 1.2G for sign and
+    QSGD, about six), in a thread pool over segments; check it
+    against the GPU's output of the same step on the same state.  For sign and QSGD the
+    scale / norm is a double sum in an unspecified order (one ulp); their bits, codes and
+    residual are compared where the two agree."""
     import concurrent.futures as cf
     import torch
     import oracle
     off = wl.offsets()
-    segs = [s for s in range(wl.n_seg) if 1 <= s <= 9] if wl.n_seg > 9 else [0]
-    budget = 250_000_000
+    segs = list(range(1, wl.n_seg)) if wl.n_seg > 9 else [0]
+    # the sorting codecs take ~5 s on 250M elements; the streaming ones need ~5x more for
+    # the same order of CPU work
+    budget = 1_200_000_000 if codec in ("sign", "qsgd") else 250_000_000
     total = 0
     pick = []
     for s in segs:
@@ -203,18 +214,36 @@ def cpu_baseline(plan, wl, gbuf, e, u):
         a, b = int(off[s]), int(off[s + 1])
         host[s] = dict(g=gbuf[a:b].cpu().numpy(), e=e[a:b].cpu().numpy(),
                        u=u[a:b].cpu().numpy() if u is not None else None)
-    # the GPU step on the same state, for a parity spot check
-    vals = torch.empty(plan.total_k, dtype=torch.float32, device="cuda")
-    idx = torch.empty(plan.total_k, dtype=torch.int32, device="cuda")
-    plan.compress(gbuf, e, vals, idx, u=u, momentum=wl.momentum or 0.0)
+    vals, idx, codes, scales = outs
+    tau = scales.cpu().numpy() if codec == "threshold" else None
+    if codec == "topk" and wl.int8:   # the bounded sample times the sparsifier alone
+        codec_run = "topk-no-int8"
+        plan.compress(gbuf, e, vals, idx, u=u, momentum=wl.momentum or 0.0)
+    else:
+        codec_run = codec
+        run_step(plan, wl, codec, gbuf, e, u, outs, t)
     torch.cuda.synchronize()
     threads = max(1, min(len(pick), len(os.sched_getaffinity(0)), 16))
     oracle.lib()
+    m = wl.momentum or 0.0
 
     def run(s):
         h = host[s]
-        return s, oracle.topk_ef_segment(h["g"], h["e"], int(plan.k[s]), u=h["u"],
-                                         momentum=wl.momentum or 0.0)
+        a = int(off[s])
+        k = int(plan.k[s])
+        if codec in ("topk",):
+            r = oracle.topk_ef_segment(h["g"], h["e"], k, u=h["u"], momentum=m)
+        elif codec == "threshold":
+            r = oracle.threshold_ef_segment(h["g"], h["e"], k, float(tau[s]), u=h["u"], momentum=m)
+        elif codec == "randk":
+            r = oracle.randk_segment(h["g"], k, e=h["e"], u=h["u"], momentum=m, seed=0, step=t,
+                                     seg_base=a)
+        elif codec == "sign":
+            r = oracle.sign_ef_segment(h["g"], h["e"], u=h["u"], momentum=m)
+        else:
+            r = oracle.qsgd_segment(h["g"], h["e"], u=h["u"], momentum=m, levels=127, seed=0,
+                                    step=t, seg_base=a)
+        return s, r
 
     t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
@@ -222,20 +251,40 @@ def cpu_baseline(plan, wl, gbuf, e, u):
     dt = time.perf_counter() - t0
     ok = True
     for s in pick:
-        ka, kb = int(plan.out_off[s]), int(plan.out_off[s + 1])
         a, b = int(off[s]), int(off[s + 1])
-        hv, hi = res[s]
-        ok &= vals[ka:kb].cpu().numpy().tobytes() == hv.tobytes()
-        ok &= np.array_equal(idx[ka:kb].cpu().numpy(), hi)
-        ok &= e[a:b].cpu().numpy().tobytes() == host[s]["e"].tobytes()
+        e_ok = e[a:b].cpu().numpy().tobytes() == host[s]["e"].tobytes()
+        if codec in ("topk", "threshold", "randk"):
+            hv, hi = res[s]
+            ka = int(plan.out_off[s])
+            ok &= vals[ka:ka + hv.size].cpu().numpy().tobytes() == hv.tobytes()
+            ok &= np.array_equal(idx[ka:ka + hi.size].cpu().numpy(), hi)
+            ok &= e_ok
+        elif codec == "sign":
+            hb, hs = res[s]
+            wa, wb = int(plan.word_off[s]), int(plan.word_off[s + 1])
+            ok &= np.array_equal(codes[wa:wb].cpu().numpy().view(np.uint32), hb)
+            sd = float(scales[s])
+            ok &= abs(sd - float(hs)) <= _ulp(hs)
+            ok &= e_ok or sd != hs
+        else:
+            hc, hn = res[s]
+            nd = float(scales[s])
+            ok &= abs(nd - float(hn)) <= _ulp(hn)
+            if nd == hn:
+                ok &= np.array_equal(codes[a:b].cpu().numpy(), hc) and e_ok
+    what = {"topk": "EF-Top-k step, full sort per segment",
+            "topk-no-int8": "EF-Top-k step (the sparsifier alone), full sort per segment",
+            "threshold": "threshold-EF step, count then full sort per segment",
+            "randk": "Random-k EF step, Philox key per element and full sort per segment",
+            "sign": "1-bit sign EF step",
+            "qsgd": "QSGD-127 EF step, Philox draw per element"}[codec_run]
     return {
         "value": round(4.0 * total / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"one EF-Top-k step of segments {pick[0]}..{pick[-1]} ({len(pick)} tensors, "
-                   f"{total} fp32 elements) of {wl.name}, full sort per segment, "
-                   f"{dt:.2f} s wall on {threads} threads"),
+        "sample": (f"one {what} on segments {pick[0]}..{pick[-1]} ({len(pick)} tensors, "
+                   f"{total} fp32 elements) of {wl.name}, {dt:.2f} s wall on {threads} threads"),
         "parity_with_gpu_on_sample": bool(ok),
     }
 
@@ -313,15 +362,16 @@ def main():
             "launches": launches,
         },
     }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline: oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(plan, wl, gbufs[0], e, u, outs, codec,
+                                              t=args.warmup + args.steps)
     if codec != "topk":
         name = {"sign": "1-bit sign EF", "qsgd": "QSGD-127 EF", "threshold": "threshold EF",
                 "randk": "Random-k EF"}[codec]
         result["metric"] = f"{name} compress GB/s of fp32 gradient (1 GPU) and % of HBM peak"
         print(json.dumps(result), flush=True)
         return
-    if not args.no_cpu_baseline:
-        log("[bench] CPU baseline: oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(plan, wl, gbufs[0], e, u)
     del gbufs, e, u, outs
     plan.close()
     torch.cuda.empty_cache()
