@@ -54,6 +54,8 @@ def load(path: str):
     L.orc_sign_ef_segment.restype = None
     L.orc_sign_decompress_segment.argtypes = [i64, vp, f32, vp, ctypes.c_int]
     L.orc_sign_decompress_segment.restype = None
+    L.orc_decompress_gathered.argtypes = [i32, vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_int]
+    L.orc_decompress_gathered.restype = None
     L.orc_threshold_ef_segment.argtypes = [i64, i64, f32, vp, vp, vp, f32, ctypes.c_int, vp,
                                            vp, vp]
     L.orc_threshold_ef_segment.restype = ctypes.c_int
@@ -181,6 +183,24 @@ def decompress(seg_off, k, idx, vals=None, codes=None, scales=None, dense=None,
         scales = np.ascontiguousarray(scales, np.float32)
     lib().orc_decompress(len(k), _p(seg_off), _p(k), _p(vals), _p(codes), _p(scales), _p(idx),
                          _p(dense), int(bool(accumulate)))
+    return dense
+
+
+def decompress_gathered(seg_off, k, n_workers, idx, vals=None, codes=None, scales=None,
+                        dense=None, accumulate=False):
+    """Add n_workers payloads (back to back in worker order) into dense, worker by worker."""
+    seg_off = np.ascontiguousarray(seg_off, np.int64)
+    k = np.ascontiguousarray(k, np.int64)
+    idx = np.ascontiguousarray(idx, np.int32)
+    assert idx.size == n_workers * int(k.sum())
+    if dense is None:
+        dense = np.empty(int(seg_off[-1]), np.float32)
+    if vals is None:
+        codes = np.ascontiguousarray(codes, np.int8)
+        scales = np.ascontiguousarray(scales, np.float32)
+    lib().orc_decompress_gathered(len(k), _p(seg_off), _p(k), int(n_workers), _p(vals),
+                                  _p(codes), _p(scales), _p(idx), _p(dense),
+                                  int(bool(accumulate)))
     return dense
 
 

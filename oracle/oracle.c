@@ -299,7 +299,9 @@ void orc_quant_int8(int32_t n_seg, const int64_t* seg_off, const int64_t* k, con
 /* ------------------------------------------------------------------ decompress */
 
 /* dense[seg_off[s] + idx] = value (or += with accumulate), value = vals[j] when vals is
- * given, else fl(codes[j] * scales[s]).  Without accumulate, dense is zero-filled first. */
+ * given, else fl(codes[j] * scales[s]).  Without accumulate, dense is zero-filled first.
+ * Entries whose index is outside the segment (the -1 padding of a threshold payload) carry
+ * nothing and are skipped. */
 void orc_decompress(int32_t n_seg, const int64_t* seg_off, const int64_t* k, const float* vals,
                     const int8_t* codes, const float* scales, const int32_t* idx, float* dense,
                     int accumulate)
@@ -309,12 +311,36 @@ void orc_decompress(int32_t n_seg, const int64_t* seg_off, const int64_t* k, con
     int64_t out = 0;
     for (int32_t s = 0; s < n_seg; ++s) {
         for (int64_t j = 0; j < k[s]; ++j) {
+            int32_t i = idx[out + j];
+            if (i < 0 || i >= seg_off[s + 1] - seg_off[s]) continue;
             float v = vals ? vals[out + j] : (float)codes[out + j] * scales[s];
-            float* d = &dense[seg_off[s] + idx[out + j]];
+            float* d = &dense[seg_off[s] + i];
             *d = accumulate ? *d + v : v;
         }
         out += k[s];
     }
+}
+
+/* Receiver side of the data-parallel exchange (memory-compression glossary, systems section:
+ * sparse gradients travel by all-gather of values and indices): the payloads of n_workers
+ * workers, back to back in worker order (worker w's entries from w * K, K = sum of k; codes
+ * likewise; scales from w * n_seg), added into dense one worker after the other: dense = 0
+ * unless accumulate, then dense[pos] = fl(dense[pos] + value) for worker 0, 1, ...  The fp32
+ * additions happen in worker order, so every receiver forms the same sum. */
+void orc_decompress_gathered(int32_t n_seg, const int64_t* seg_off, const int64_t* k,
+                             int32_t n_workers, const float* vals, const int8_t* codes,
+                             const float* scales, const int32_t* idx, float* dense,
+                             int accumulate)
+{
+    int64_t kk = 0;
+    for (int32_t s = 0; s < n_seg; ++s) kk += k[s];
+    if (!accumulate)
+        for (int64_t i = 0; i < seg_off[n_seg]; ++i) dense[i] = 0.0f;
+    for (int32_t w = 0; w < n_workers; ++w)
+        orc_decompress(n_seg, seg_off, k, vals ? vals + (int64_t)w * kk : NULL,
+                       codes ? codes + (int64_t)w * kk : NULL,
+                       scales ? scales + (int64_t)w * n_seg : NULL, idx + (int64_t)w * kk,
+                       dense, 1);
 }
 
 /* ---------------------------------------------------- 1-bit sign with error feedback */
