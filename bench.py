@@ -71,6 +71,8 @@ def parse():
                          "with error feedback")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-momentum-variant", action="store_true")
+    ap.add_argument("--no-receiver", action="store_true",
+                    help="skip the receiver-side sum of 8 workers' payloads (context figure)")
     return ap.parse_args()
 
 
@@ -289,6 +291,37 @@ def cpu_baseline(plan, wl, gbuf, e, u, outs, codec="topk", t=0):
     }
 
 
+def receiver_bench(wl, n_workers=8, reps=5):
+    """Receiver side of an n_workers data-parallel exchange on one GPU: the gathered payloads
+    (synthetic, the plan's layout) added into a resident dense gradient in worker order."""
+    import torch
+    import gradient_compression_amd as gca
+    import synth
+    off = wl.offsets()
+    plan = gca.Plan(off, ratio=wl.ratio)
+    kk = plan.total_k
+    dev = torch.device("cuda")
+    vals = torch.empty(n_workers * kk, device=dev)
+    idx = torch.empty(n_workers * kk, dtype=torch.int32, device=dev)
+    synth.fill_payloads(vals, idx, off, plan.k, n_workers, seed=7)
+    dense = torch.zeros(wl.n, device=dev)
+    plan.decompress_gathered(n_workers, idx, dense, vals=vals, accumulate=True)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        plan.decompress_gathered(n_workers, idx, dense, vals=vals, accumulate=True)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / reps
+    plan.close()
+    entries = n_workers * kk
+    return {"workers": n_workers, "entries": entries, "ms_scatter_add": round(ms, 4),
+            "G_entries_per_s": round(entries / ms / 1e6, 2),
+            "note": "payloads read 8 B/entry sequentially, one scattered 4 B read-modify-write "
+                    "per entry; dense zero fill (4 B/elt) not included"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -394,6 +427,11 @@ def main():
         }
         log(f"[bench] momentum variant: {ms_m:.3f} ms/step")
         plan_m.close()
+        del gb_m, e_m, u_m, outs_m
+        torch.cuda.empty_cache()
+    if not args.no_receiver and wl.name == DEFAULT_WORKLOAD:
+        result["receiver_8_workers"] = receiver_bench(wl)
+        log(f"[bench] receiver: {result['receiver_8_workers']['ms_scatter_add']:.3f} ms")
     print(json.dumps(result), flush=True)
 
 

@@ -30,7 +30,7 @@ EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layo
            "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32",
            "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
            "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress",
-           "gc_threshold_ef_compress", "gc_randk_compress")
+           "gc_threshold_ef_compress", "gc_randk_compress", "gc_decompress_gathered")
 
 _lib = None
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "gc_qsgd_decompress": [vp, vp, vp, i32, vp, ctypes.c_int, vp],
         "gc_threshold_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp, vp, vp],
         "gc_randk_compress": [vp, vp, vp, vp, f32, u64, u64, vp, vp, vp],
+        "gc_decompress_gathered": [vp, i32, vp, vp, vp, vp, vp, ctypes.c_int, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -273,6 +274,19 @@ class Plan:
             _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
             _stream(stream))
         _check(rc, "gc_qsgd_decompress")
+
+    def decompress_gathered(self, n_workers: int, idx, dense, vals=None, codes=None,
+                            scales=None, accumulate=False, stream=None):
+        """Add n_workers payloads (back to back in worker order) into dense, worker by worker."""
+        import torch
+        tk = self.total_k * n_workers
+        rc = lib().gc_decompress_gathered(
+            self._h, int(n_workers), _dev_ptr(vals, torch.float32, "vals", tk),
+            _dev_ptr(codes, torch.int8, "codes", tk),
+            _dev_ptr(scales, torch.float32, "scales", self.n_seg * n_workers),
+            _dev_ptr(idx, torch.int32, "idx", tk), _dev_ptr(dense, torch.float32, "dense", self.n),
+            int(bool(accumulate)), _stream(stream))
+        _check(rc, "gc_decompress_gathered")
 
     def threshold_compress(self, g, e, tau, out_vals, out_idx, out_count=None, u=None,
                            momentum: float = 0.0, stream=None):

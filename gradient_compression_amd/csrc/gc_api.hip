@@ -566,6 +566,28 @@ int gc_decompress(const gc_plan* plan, const float* vals, const int8_t* codes,
   return err == hipSuccess ? GC_OK : GC_ERR_HIP;
 }
 
+int gc_decompress_gathered(const gc_plan* plan, int32_t n_workers, const float* vals,
+                           const int8_t* codes, const float* scales, const int32_t* idx,
+                           float* dense, int accumulate, void* stream) {
+  if (!plan || n_workers < 0) return GC_ERR_INVALID_ARG;
+  if ((vals == nullptr) == (codes == nullptr)) return GC_ERR_INVALID_ARG;
+  if (codes && !scales) return GC_ERR_INVALID_ARG;
+  if (plan->total_k > 0 && n_workers > 0 && !idx) return GC_ERR_INVALID_ARG;
+  if (!dense && plan->seg_off[plan->n_seg] > plan->seg_off[0]) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (!accumulate) err = gc::launch_fill_zero(dense, plan->seg_off[0], plan->seg_off[plan->n_seg], st);
+  const int64_t kk = plan->total_k;
+  // one ordered pass per worker: the additions into each position happen in worker order
+  for (int32_t w = 0; w < n_workers && err == hipSuccess; ++w)
+    err = gc::launch_decompress(plan->op, vals ? vals + (int64_t)w * kk : nullptr,
+                                codes ? codes + (int64_t)w * kk : nullptr,
+                                scales ? scales + (int64_t)w * plan->n_seg : nullptr,
+                                idx + (int64_t)w * kk, dense, 1, st);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
 int gc_plan_reset_estimate(gc_plan* plan, void* stream) {
   if (!plan) return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;

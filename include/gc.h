@@ -246,6 +246,28 @@ int gc_randk_compress(gc_plan* plan, const float* g, float* e, float* u, float m
                       uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
                       void* stream);
 
+/*
+ * Receiver side of the data-parallel exchange ("Gradient Compression", memory-compression
+ * glossary, systems section: sparse gradients are exchanged by all-gather of values and
+ * indices; "Communication Optimization > Gradient Compression", subtlety paragraph: the
+ * workers' supports differ, so the union is denser than one payload).  The payloads of
+ * n_workers workers, gathered back to back in worker order, are added into dense one worker
+ * after the other:
+ *   dense = 0 unless accumulate; then for w = 0, 1, ..., n_workers - 1 and every entry j of
+ *   worker w: dense[seg_off[s] + idx] = fl(dense[...] + value), value = vals[j] or
+ *   fl(codes[j] * scales[w * n_seg + s]); entries with an index outside the segment (the -1
+ *   padding of threshold payloads) are skipped.
+ * The fp32 additions happen in worker order, so every receiver forms the same sum.
+ *   vals / codes, idx : device arrays of n_workers * total_k entries, worker w's payload
+ *                       (the plan's layout) at w * total_k; exactly one of vals and codes.
+ *   scales            : with codes, device float[n_workers * n_seg].
+ *   dense             : device float[N].
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_decompress_gathered(const gc_plan* plan, int32_t n_workers, const float* vals,
+                           const int8_t* codes, const float* scales, const int32_t* idx,
+                           float* dense, int accumulate, void* stream);
+
 /* Forget the threshold estimates (of Top-k calls and the capture floor of threshold calls):
  * the next call runs as on a fresh plan. */
 int gc_plan_reset_estimate(gc_plan* plan, void* stream);

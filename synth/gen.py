@@ -153,3 +153,27 @@ def fill_gradient(buf: torch.Tensor, wl: Workload, it: int, seed: int = 0, segme
             gen = _gen(dev, seed, wl.cfg_id, it, s, c0 // CHUNK)
             buf[o + c0:o + c0 + m].copy_(_draw(wl, m, s, gen, dev).to(torch.float32))
     return buf
+
+
+def fill_payloads(vals: torch.Tensor, idx: torch.Tensor, seg_off, ks, n_workers: int,
+                  seed: int = 0):
+    """Write n_workers synthetic payloads of the plan layout (per segment s, k_s distinct
+    segment-local indices in ascending order and Student-t(3) x 1e-3 values), back to back in
+    worker order, into vals / idx (device tensors of n_workers * sum(k) entries).  They stand
+    in for what the other workers of a data-parallel group would send."""
+    ks = [int(k) for k in ks]
+    kk = sum(ks)
+    assert vals.numel() >= n_workers * kk and idx.numel() >= n_workers * kk
+    dev = vals.device
+    for w in range(n_workers):
+        base = w * kk
+        for s, k_s in enumerate(ks):
+            n_s = int(seg_off[s + 1] - seg_off[s])
+            if k_s:
+                gen = _gen(dev, seed, 0x9A7, w, s)
+                r = torch.rand(n_s, generator=gen, device=dev)
+                sel = torch.topk(r, k_s).indices.sort().values   # k distinct, ascending
+                idx[base:base + k_s] = sel.to(torch.int32)
+                vals[base:base + k_s] = (student_t(k_s, 3.0, gen, dev) * 1e-3).to(torch.float32)
+            base += k_s
+    return vals, idx
