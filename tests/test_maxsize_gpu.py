@@ -1,0 +1,92 @@
+"""The largest segment the boundary accepts: 2^31 - 1 elements (segment-local indices are
+int32).  The oracle's full sort of 2^31 records takes too long for a test, so every element
+is checked with torch on the GPU against the properties that fix each result uniquely."""
+import numpy as np
+import pytest
+import torch
+
+import gradient_compression_amd as gca
+from tests.gpu_helpers import log
+
+pytestmark = pytest.mark.gpu
+
+N = (1 << 31) - 1
+
+
+def _gradient(t):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(977 + t)
+    g = torch.randn(N, generator=gen, device="cuda")
+    g[N - 1] = 40.0 + t      # the last index: the largest magnitude, always kept
+    return g
+
+
+def _check_sparse(acc, e, vals, idx, k, topk):
+    ii = idx.long()
+    assert int(ii.min()) >= 0 and int(ii.max()) < N
+    assert bool((ii[1:] > ii[:-1]).all()), "ascending"
+    assert int(ii[-1]) == N - 1 or not topk
+    assert torch.equal(vals.view(torch.int32), acc[ii].view(torch.int32)), "values"
+    kept = torch.zeros(N, dtype=torch.bool, device="cuda")
+    kept[ii] = True
+    assert torch.equal(e[~kept].view(torch.int32), acc[~kept].view(torch.int32)), "residual"
+    assert bool((e[ii] == 0).all()) and not bool(torch.signbit(e[ii]).any()), "+0 where kept"
+    if topk:
+        lo = float(acc[ii].abs().min())
+        mags = acc.abs()
+        mags[kept] = -1.0
+        hi = float(mags.max())
+        assert lo >= hi, f"top-k: kept {lo} < dropped {hi}"
+        if lo == hi:
+            kept_t = ii[acc[ii].abs() == lo]
+            drop_t = torch.nonzero(mags == lo).flatten()
+            assert int(kept_t.max()) < int(drop_t.min()), "tie rule"
+
+
+def test_max_segment_topk():
+    plan = gca.Plan(np.array([0, N], np.int64), ratio=0.001)
+    k = int(plan.k[0])
+    assert k == 2147484
+    e = torch.zeros(N, device="cuda")
+    vals = torch.empty(k, device="cuda")
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    for t in range(2):
+        g = _gradient(t)
+        acc = torch.add(e, g)
+        plan.compress(g, e, vals, idx)
+        torch.cuda.synchronize()
+        st = plan.last_stats()
+        log(f"[max] top-k call {t}: mode {st['mode'][0]}, candidates {st['candidates'][0]}")
+        del g
+        _check_sparse(acc, e, vals, idx, k, topk=True)
+        del acc
+    plan.close()
+
+
+def test_max_segment_randk_and_threshold():
+    plan = gca.Plan(np.array([0, N], np.int64), ratio=0.001)
+    k = int(plan.k[0])
+    e = torch.zeros(N, device="cuda")
+    vals = torch.empty(k, device="cuda")
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    g = _gradient(5)
+    acc = torch.add(e, g)
+    plan.randk_compress(g, vals, idx, e=e, seed=3, step=0)
+    torch.cuda.synchronize()
+    _check_sparse(acc, e, vals, idx, k, topk=False)
+    log("[max] Random-k checked")
+    # threshold on the same g: e now holds g outside the Random-k mask, so acc is about 2g;
+    # |acc| >= 9 keeps about 7e-6 of the segment (~15k entries), below the cap
+    acc = torch.add(e, g)
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    plan.threshold_compress(g, e, torch.tensor([9.0], device="cuda"), vals, idx, cnt)
+    torch.cuda.synchronize()
+    c = int(cnt[0])
+    want = int((acc.abs() >= 9.0).sum())
+    assert c == min(want, k) and 0 < c < k
+    assert bool((idx[c:] == -1).all())
+    ii = idx[:c].long()
+    assert torch.equal(ii, torch.nonzero(acc.abs() >= 9.0).flatten()), "kept set"
+    assert torch.equal(vals[:c].view(torch.int32), acc[ii].view(torch.int32))
+    log("[max] threshold checked")
+    plan.close()
