@@ -34,11 +34,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments dropped and whitespace collapsed, so that
+    only a change of the code itself invalidates counters taken on it."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "gradient_compression_amd", "csrc")
-    data = b"".join(open(os.path.join(csrc, f), "rb").read()
-                    for f in ("gc_kernels.hip", "gc_internal.h"))
-    return hashlib.sha256(data).hexdigest()[:16]
+    code = []
+    for f in ("gc_kernels.hip", "gc_internal.h"):
+        text = open(os.path.join(csrc, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        code.append(" ".join(text.split()))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def measured_traffic(name):

@@ -1,18 +1,25 @@
-// gc_kernels.hip -- gfx950 kernels of the error-feedback Top-k compressor.
+// gc_kernels.hip -- gfx950 kernels of the error-feedback gradient compressors.
 //
-// Per call (one stream, no host round trip):
+// Top-k call (one stream, no host round trip):
 //   prep        zero the per-call counters
 //   ef_capture  the streaming pass over g, e (and u): momentum, EF add, write acc into e,
 //               and capture every (acc, index) whose magnitude key reaches the segment's
 //               threshold, as one index-ordered run per tile            [HBM-bound]
 //   select_init per segment: keep the candidates if they are complete (count in [k, cap]),
-//               else list the segment for the exact full-segment path
+//               else list the segment for re-capture or the exact full-segment path
+//   recap_*     first-digit histogram of e and capture at the exact bucket floor (only for
+//               segments whose candidates were incomplete)
 //   hist/find   x3  radix select of the k-th largest key, digits of 11, 11 and 9 bits,
 //               LDS histograms; candidates or, on the full path, the whole segment
 //   scatter     candidates into ascending index order (runs placed by tile)
 //   count/scan/emit  order-preserving compaction: keys above the k-th, then the ties in
 //               index order; writes (value, index) and zeroes e (and u) where kept
-//   finalize    next threshold estimate = key(0.75 * kth)
+//   finalize    next threshold estimate = key(beta * kth), beta steered by the last calls
+//
+// Threshold and Random-k calls run the same select and emit on a per-call copy of the plan
+// (their own k and capture threshold); Random-k ranks per-element Philox keys instead of
+// magnitudes.  The 1-bit sign and QSGD codecs are two streaming passes around a per-segment
+// scale; decompression and the receiver-side sum are scatters.
 //
 // The method is the Top-K with error feedback of "Communication Optimization > Gradient
 // Compression" (Top-K section equations); momentum correction per the "Gradient
