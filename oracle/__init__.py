@@ -54,6 +54,8 @@ def load(path: str):
     L.orc_sign_ef_segment.restype = None
     L.orc_sign_decompress_segment.argtypes = [i64, vp, f32, vp, ctypes.c_int]
     L.orc_sign_decompress_segment.restype = None
+    L.orc_clip_by_norm_segment.argtypes = [i64, vp, f32, vp]
+    L.orc_clip_by_norm_segment.restype = None
     L.orc_decompress_gathered.argtypes = [i32, vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_int]
     L.orc_decompress_gathered.restype = None
     L.orc_threshold_ef_segment.argtypes = [i64, i64, f32, vp, vp, vp, f32, ctypes.c_int, vp,
@@ -276,3 +278,11 @@ def randk_segment(g, k, e=None, u=None, momentum=0.9, mask_u=False, seed=0, step
     if rc:
         raise ValueError("oracle rejected the Random-k arguments")
     return vals[:k].copy(), idx[:k].copy()
+
+
+def clip_by_norm_segment(g, c):
+    """l2-norm clipping of one segment in place on g; returns the norm before clipping."""
+    _f32(g, "g")
+    norm = np.empty(1, np.float32)
+    lib().orc_clip_by_norm_segment(g.size, _p(g), float(c), _p(norm))
+    return norm[0]

@@ -47,6 +47,11 @@
  * feedback the values go unscaled and the residual is kept; without it they are scaled by
  * n/k so that their expectation is acc.
  *
+ * Local gradient clipping (genomic-FL glossary, DGC section: the gradient magnitude is
+ * normalised before compression; memory-compression glossary, quantization section: clipping
+ * before quantisation controls the range): per segment, the l2 norm is brought down to a
+ * given bound when it exceeds it.
+ *
  * QSGD with s levels (same page, QSGD paragraph, with its missing 1/s restored): one l2
  * norm per segment, stochastic levels drawn from Philox4x32-10 (one block per four
  * consecutive elements, counter tag 0x52), error feedback of the quantisation error optional.
@@ -539,4 +544,24 @@ int orc_randk_segment(int64_t n, int64_t k, int64_t seg_base, const float* g, fl
     free(acc);
     free(sel);
     return 0;
+}
+
+/* -------------------------------------------------------------- gradient clipping */
+
+/*
+ * Local gradient clipping of one segment (genomic-FL glossary, DGC section; memory-compression
+ * glossary, quantization section), the l2 reading: S = sum g_i^2 in double (index order),
+ * norm = fl32(sqrt(S)); when norm > c, f = fl32(c / norm) and g_i = fl(g_i * f) in place;
+ * otherwise g is left as it is.  *norm_out gets the norm before clipping.  c >= 0.
+ */
+void orc_clip_by_norm_segment(int64_t n, float* g, float c, float* norm_out)
+{
+    double sq = 0.0;
+    for (int64_t i = 0; i < n; ++i) sq += (double)g[i] * (double)g[i];
+    float norm = (float)sqrt(sq);
+    *norm_out = norm;
+    if (norm > c) {
+        float f = c / norm;
+        for (int64_t i = 0; i < n; ++i) g[i] = g[i] * f;
+    }
 }

@@ -16,6 +16,7 @@ from tests import test_oracle_qsgd as T_q8
 from tests import test_oracle_threshold as T_t
 from tests import test_oracle_randk as T_rk
 from tests import test_oracle_gathered as T_ga
+from tests import test_oracle_clip as T_cl
 
 MUTANTS = {
     "tie_rule_higher_index_wins": ("return a->pos < b->pos ? -1 : 1;",
@@ -62,6 +63,9 @@ MUTANTS = {
                             "sel[j] = rec[n - 1 - j].pos;\n    free(rec);\n    qsort(sel, (size_t)k, sizeof *sel, by_pos);\n    float scale"),
     "randk_residual_not_kept": ("for (int64_t i = 0; i < n; ++i) e[i] = acc[i];", ""),
     "randk_same_mask_every_step": ("(uint32_t)step, 0x53u", "0u, 0x53u"),
+    "clip_without_sqrt": ("float norm = (float)sqrt(sq);\n    *norm_out = norm;\n    if (norm > c)",
+                          "float norm = (float)sq;\n    *norm_out = norm;\n    if (norm > c)"),
+    "clip_inverted_factor": ("float f = c / norm;", "float f = norm / c;"),
     "gathered_reverse_worker_order": ("for (int32_t w = 0; w < n_workers; ++w)",
                                       "for (int32_t w = n_workers - 1; w >= 0; --w)"),
     "gathered_overwrite": ("scales ? scales + (int64_t)w * n_seg : NULL, idx + (int64_t)w * kk,\n                       dense, 1);",
@@ -98,6 +102,8 @@ def _pins(orc):
     yield lambda: T_rk.test_counter_mapping(orc, 3)
     yield lambda: T_ga.test_worker_order_is_the_summation_order(orc)
     yield lambda: T_ga.test_numpy_worker_by_worker(orc)
+    yield lambda: T_cl.test_three_four_five(orc)
+    yield lambda: T_cl.test_norm_direction_and_bound(orc, 1)
 
 
 def _failures():
