@@ -298,6 +298,29 @@ def cpu_baseline(plan, wl, gbuf, e, u, outs, codec="topk", t=0):
     }
 
 
+def clip_bench(plan, wl, g, reps=8):
+    """Local gradient clipping of every segment on one resident gradient: call t clips to
+    norm0 * 2^-(t+1), so each call scales every segment (read 4 B in the norm pass, read and
+    write 4 B in the scaling pass: 12 B per element)."""
+    import torch
+    norms = torch.empty(wl.n_seg, device="cuda")
+    plan.clip_by_norm(g, torch.full((wl.n_seg,), float("inf"), device="cuda"), norms)
+    n0 = norms.clone()
+    caps = [n0 * 2.0 ** -(t + 1) for t in range(reps + 1)]
+    plan.clip_by_norm(g, caps[0])
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for t in range(reps):
+        plan.clip_by_norm(g, caps[t + 1])
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / reps
+    return {"ms_per_call": round(ms, 4), "bytes_per_element": 12,
+            "achieved_GBps": round(12 * wl.n / ms / 1e6, 1),
+            "hbm_peak_frac": round(12 * wl.n / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+
+
 def receiver_bench(wl, n_workers=8, reps=5):
     """Receiver side of an n_workers data-parallel exchange on one GPU: the gathered payloads
     (synthetic, the plan's layout) added into a resident dense gradient in worker order."""
@@ -402,6 +425,13 @@ def main():
             "launches": launches,
         },
     }
+    if codec == "qsgd" or (codec == "topk" and wl.name == DEFAULT_WORKLOAD
+                           and not args.no_receiver):
+        # local gradient clipping before compression (a context figure, not in the step)
+        result["clip_all_segments"] = clip_bench(plan, wl, gbufs[-1])
+        log(f"[bench] clipping: {result['clip_all_segments']['ms_per_call']:.3f} ms")
+        gen_mod = __import__("synth").gen
+        gen_mod.fill_gradient(gbufs[-1], wl, len(gbufs) - 1)   # restore the clipped buffer
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline: oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(plan, wl, gbufs[0], e, u, outs, codec,

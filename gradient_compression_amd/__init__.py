@@ -30,7 +30,8 @@ EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layo
            "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32",
            "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
            "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress",
-           "gc_threshold_ef_compress", "gc_randk_compress", "gc_decompress_gathered")
+           "gc_threshold_ef_compress", "gc_randk_compress", "gc_decompress_gathered",
+           "gc_clip_by_norm")
 
 _lib = None
 
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "gc_threshold_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp, vp, vp],
         "gc_randk_compress": [vp, vp, vp, vp, f32, u64, u64, vp, vp, vp],
         "gc_decompress_gathered": [vp, i32, vp, vp, vp, vp, vp, ctypes.c_int, vp],
+        "gc_clip_by_norm": [vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -274,6 +276,16 @@ class Plan:
             _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
             _stream(stream))
         _check(rc, "gc_qsgd_decompress")
+
+    def clip_by_norm(self, g, max_norm, norms_out=None, stream=None):
+        """Per segment: when ||g_s||_2 > max_norm[s], g_s *= max_norm[s] / ||g_s||_2 (in place).
+        ``max_norm``: device float32[n_seg]; ``norms_out`` receives the norms before."""
+        import torch
+        rc = lib().gc_clip_by_norm(
+            self._h, _dev_ptr(g, torch.float32, "g", self.n),
+            _dev_ptr(max_norm, torch.float32, "max_norm", self.n_seg),
+            _dev_ptr(norms_out, torch.float32, "norms_out", self.n_seg), _stream(stream))
+        _check(rc, "gc_clip_by_norm")
 
     def decompress_gathered(self, n_workers: int, idx, dense, vals=None, codes=None,
                             scales=None, accumulate=False, stream=None):

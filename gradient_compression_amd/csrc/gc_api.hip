@@ -269,6 +269,7 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   uint32_t* d_thr_rand;
   float* d_rk_scale;
   cv.add(&d.k_call, n_seg);
+  cv.add(&d.seg_norm, n_seg);
   cv.add(&d.thr_est, n_seg);
   cv.add(&d.beta_est, n_seg);
   cv.add(&d.tau_key, n_seg);
@@ -585,6 +586,19 @@ int gc_decompress_gathered(const gc_plan* plan, int32_t n_workers, const float* 
                                 codes ? codes + (int64_t)w * kk : nullptr,
                                 scales ? scales + (int64_t)w * plan->n_seg : nullptr,
                                 idx + (int64_t)w * kk, dense, 1, st);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_clip_by_norm(gc_plan* plan, float* g, const float* max_norm, float* norms_out,
+                    void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!g || !aligned16(g))) return GC_ERR_INVALID_ARG;
+  if (plan->n_seg > 0 && !max_norm) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  const hipError_t err = gc::launch_clip(plan->dp, g, max_norm,
+                                         norms_out ? norms_out : plan->dp.seg_norm,
+                                         static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GC_OK : GC_ERR_HIP;
 }
 

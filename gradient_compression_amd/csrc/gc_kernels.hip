@@ -1391,7 +1391,7 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass1(DevPlan P, const float*
         acc[v][c] = a;
       }
   } else {
-    load_tile(g + start, len, acc);
+    load_tile_nt(g + start, len, acc);
   }
   double sq = 0.0;
 #pragma unroll
@@ -1623,6 +1623,41 @@ __global__ __launch_bounds__(kThreads) void k_pad_out(OutPlan O, const uint32_t*
   for (int64_t j = max(j0, keep_end) + threadIdx.x; j < j1; j += kThreads) {
     vals[j] = 0.0f;
     idx[j] = -1;
+  }
+}
+
+// ---------------------------------------------------------------------- gradient clipping
+// Local gradient clipping (genomic-FL glossary, DGC section: the gradient magnitude is
+// normalised before compression), per segment: norm = fl32(sqrt(sum g^2)) (k_qsgd_pass1 and
+// k_qsgd_norm on g), then where norm > c: g = fl(g * fl32(c / norm)).  Tiles of segments
+// that are not clipped are left untouched (no write).
+__global__ __launch_bounds__(kThreads) void k_clip_scale(DevPlan P, float* __restrict__ g,
+                                                        const float* __restrict__ max_norm,
+                                                        const float* __restrict__ norms) {
+  const int64_t t = blockIdx.x;
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const float norm = norms[s], c = max_norm[s];
+  if (!(norm > c)) return;   // uniform per tile
+  const float f = c / norm;
+  const int pb = slot_base();
+  if (len == kTile && (start & 3) == 0) {
+    f4* g4 = reinterpret_cast<f4*>(g + start);
+    f4 x[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) x[v] = __builtin_nontemporal_load(g4 + ((pb + v * 256) >> 2));
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+      __builtin_nontemporal_store(x[v] * f, g4 + ((pb + v * 256) >> 2));
+  } else {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int p = pb + v * 256 + c4;
+        if (p < len) g[start + p] = g[start + p] * f;
+      }
   }
 }
 
@@ -1898,6 +1933,16 @@ hipError_t launch_qsgd_decompress(const DevPlan& P, const int8_t* codes, const f
   if (P.n_tiles == 0) return hipSuccess;
   k_qsgd_decompress<<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, codes, norms, levels, dense,
                                                              accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_clip(const DevPlan& P, float* g, const float* max_norm, float* norms,
+                       hipStream_t st) {
+  if (P.n_seg == 0) return hipSuccess;
+  const unsigned nt = (unsigned)P.n_tiles;
+  if (nt > 0) k_qsgd_pass1<false, false><<<nt, kThreads, 0, st>>>(P, g, nullptr, nullptr, 0.0f);
+  k_qsgd_norm<<<P.n_seg, 1024, 0, st>>>(P, norms);
+  if (nt > 0) k_clip_scale<<<nt, kThreads, 0, st>>>(P, g, max_norm, norms);
   return hipGetLastError();
 }
 

@@ -247,6 +247,21 @@ int gc_randk_compress(gc_plan* plan, const float* g, float* e, float* u, float m
                       void* stream);
 
 /*
+ * Local gradient clipping ("Gradient Compression", genomic-FL glossary, DGC section: the
+ * gradient magnitude is normalised before compression; memory-compression glossary,
+ * quantization section: clipping before quantisation controls the range), the l2 reading,
+ * per segment s, in place on g before a compress call:
+ *   norm_s = fl32(sqrt(S)), S = sum g_i^2 in double (order unspecified: within 1 ulp);
+ *   when norm_s > max_norm[s]: g_i = fl(g_i * fl32(max_norm[s] / norm_s)); else g untouched.
+ *   max_norm  : device float[n_seg], >= 0 (0 clears every non-zero segment).
+ *   norms_out : device float[n_seg] receiving norm_s before clipping, or NULL.
+ * g must be 16-byte aligned; inputs with Inf or NaN are outside the contract.
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_clip_by_norm(gc_plan* plan, float* g, const float* max_norm, float* norms_out,
+                    void* stream);
+
+/*
  * Receiver side of the data-parallel exchange ("Gradient Compression", memory-compression
  * glossary, systems section: sparse gradients are exchanged by all-gather of values and
  * indices; "Communication Optimization > Gradient Compression", subtlety paragraph: the
