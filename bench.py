@@ -321,6 +321,42 @@ def clip_bench(plan, wl, g, reps=8):
             "hbm_peak_frac": round(12 * wl.n / ms / 1e6 / HBM_PEAK_GBPS, 4)}
 
 
+def clip_fused_bench(plan, wl, codec, gbufs, e, u, outs, steps, warmup):
+    """The codec's step with local gradient clipping folded into its loads: the norm pass
+    (gc_clip_factors, reads g) then the codec with the per-segment scale set (every segment
+    clipped to half its norm)."""
+    import torch
+    norms = torch.empty(wl.n_seg, device="cuda")
+    caps = []
+    for g in gbufs:
+        plan.clip_factors(g, torch.full((wl.n_seg,), float("inf"), device="cuda"),
+                          torch.empty(wl.n_seg, device="cuda"), norms_out=norms)
+        caps.append(norms * 0.5)
+    factors = torch.empty(wl.n_seg, device="cuda")
+    plan.set_gradient_scale(factors)
+
+    def step(t):
+        i = t % len(gbufs)
+        plan.clip_factors(gbufs[i], caps[i], factors)
+        run_step(plan, wl, codec, gbufs[i], e, u, outs, t)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for t in range(warmup, warmup + steps):
+        step(t)
+    s1.record()
+    torch.cuda.synchronize()
+    plan.set_gradient_scale(None)
+    ms = s0.elapsed_time(s1) / steps
+    bpe = bytes_per_element(wl, codec) + 4
+    return {"ms_per_step": round(ms, 4), "bytes_per_element": bpe,
+            "effective_GBps": round(bpe * wl.n / ms / 1e6, 1),
+            "hbm_peak_frac": round(bpe * wl.n / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+
+
 def receiver_bench(wl, n_workers=8, reps=5):
     """Receiver side of an n_workers data-parallel exchange on one GPU: the gathered payloads
     (synthetic, the plan's layout) added into a resident dense gradient in worker order."""
@@ -429,9 +465,14 @@ def main():
                            and not args.no_receiver):
         # local gradient clipping before compression (a context figure, not in the step)
         result["clip_all_segments"] = clip_bench(plan, wl, gbufs[-1])
-        log(f"[bench] clipping: {result['clip_all_segments']['ms_per_call']:.3f} ms")
         gen_mod = __import__("synth").gen
         gen_mod.fill_gradient(gbufs[-1], wl, len(gbufs) - 1)   # restore the clipped buffer
+        if codec == "qsgd":
+            result["with_clipping_fused"] = clip_fused_bench(
+                plan, wl, codec, gbufs, e, u, outs, max(args.steps // 2, 3), args.warmup)
+            log(f"[bench] QSGD with clipping folded in: "
+                f"{result['with_clipping_fused']['ms_per_step']:.3f} ms/step")
+        log(f"[bench] clipping: {result['clip_all_segments']['ms_per_call']:.3f} ms")
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline: oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(plan, wl, gbufs[0], e, u, outs, codec,

@@ -31,7 +31,7 @@ EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layo
            "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
            "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress",
            "gc_threshold_ef_compress", "gc_randk_compress", "gc_decompress_gathered",
-           "gc_clip_by_norm")
+           "gc_clip_by_norm", "gc_clip_factors", "gc_plan_set_gradient_scale")
 
 _lib = None
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         "gc_randk_compress": [vp, vp, vp, vp, f32, u64, u64, vp, vp, vp],
         "gc_decompress_gathered": [vp, i32, vp, vp, vp, vp, vp, ctypes.c_int, vp],
         "gc_clip_by_norm": [vp, vp, vp, vp, vp],
+        "gc_clip_factors": [vp, vp, vp, vp, vp, vp],
+        "gc_plan_set_gradient_scale": [vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -286,6 +288,25 @@ class Plan:
             _dev_ptr(max_norm, torch.float32, "max_norm", self.n_seg),
             _dev_ptr(norms_out, torch.float32, "norms_out", self.n_seg), _stream(stream))
         _check(rc, "gc_clip_by_norm")
+
+    def clip_factors(self, g, max_norm, factors_out, norms_out=None, stream=None):
+        """Per segment f_s = max_norm[s] / ||g_s||_2 where the norm exceeds it, else 1."""
+        import torch
+        rc = lib().gc_clip_factors(
+            self._h, _dev_ptr(g, torch.float32, "g", self.n),
+            _dev_ptr(max_norm, torch.float32, "max_norm", self.n_seg),
+            _dev_ptr(norms_out, torch.float32, "norms_out", self.n_seg),
+            _dev_ptr(factors_out, torch.float32, "factors_out", self.n_seg), _stream(stream))
+        _check(rc, "gc_clip_factors")
+
+    def set_gradient_scale(self, factors):
+        """Later compress calls read x = g * factors[s] (device float32[n_seg]); None: off.
+        The tensor is kept referenced while it is set."""
+        import torch
+        self._gscale = factors
+        _check(lib().gc_plan_set_gradient_scale(
+            self._h, _dev_ptr(factors, torch.float32, "factors", self.n_seg)),
+            "gc_plan_set_gradient_scale")
 
     def decompress_gathered(self, n_workers: int, idx, dense, vals=None, codes=None,
                             scales=None, accumulate=False, stream=None):

@@ -597,9 +597,28 @@ int gc_clip_by_norm(gc_plan* plan, float* g, const float* max_norm, float* norms
   if (plan->n_seg > 0 && !max_norm) return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   const hipError_t err = gc::launch_clip(plan->dp, g, max_norm,
-                                         norms_out ? norms_out : plan->dp.seg_norm,
+                                         norms_out ? norms_out : plan->dp.seg_norm, nullptr,
                                          static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_clip_factors(gc_plan* plan, const float* g, const float* max_norm, float* norms_out,
+                    float* factors_out, void* stream) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
+  if (any && (!g || !aligned16(g))) return GC_ERR_INVALID_ARG;
+  if (plan->n_seg > 0 && (!max_norm || !factors_out)) return GC_ERR_INVALID_ARG;
+  if (int rc = check_device(plan)) return rc;
+  const hipError_t err = gc::launch_clip(plan->dp, const_cast<float*>(g), max_norm,
+                                         norms_out ? norms_out : plan->dp.seg_norm, factors_out,
+                                         static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
+}
+
+int gc_plan_set_gradient_scale(gc_plan* plan, const float* factors) {
+  if (!plan) return GC_ERR_INVALID_ARG;
+  plan->dp.gscale = factors;
+  return GC_OK;
 }
 
 int gc_plan_reset_estimate(gc_plan* plan, void* stream) {

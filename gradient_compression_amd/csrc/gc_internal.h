@@ -140,6 +140,7 @@ struct DevPlan {
   uint32_t* tau_key;           // [n_seg] threshold calls: key(|tau|) of this call
   uint32_t* tau_cnt;           // [n_seg] entries with key >= tau_key counted by the capture
   float* seg_norm;             // [n_seg] l2 norms of a clipping call (when the caller wants none)
+  const float* gscale;         // [n_seg] caller's gradient scale applied on load, or null
   int32_t keys;                // kKeysMagnitude or kKeysRandom
   uint32_t seed_lo, seed_hi, step_lo;   // Random-k key stream
 };
@@ -172,8 +173,9 @@ hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, 
 hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, float m,
                         uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
                         hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
+// factors null: scale g in place where clipped; else write the per-segment factors only.
 hipError_t launch_clip(const DevPlan& P, float* g, const float* max_norm, float* norms,
-                       hipStream_t st);
+                       float* factors, hipStream_t st);
 hipError_t launch_reset(const DevPlan& P, hipStream_t st);
 hipError_t launch_sign(const DevPlan& P, const float* g, float* e, float* u, float m,
                        uint32_t* bits, float* scales, hipStream_t st, hipEvent_t ev_begin,

@@ -37,6 +37,12 @@ typedef int i4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t mag_key(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
+// Factor on the gradient of segment s: x = fl(g * f) in place of g when the plan carries a
+// per-segment gradient scale (clipping folded into the load), else 1 (fl(g * 1) = g exactly).
+__device__ __forceinline__ float grad_scale(const DevPlan& P, int s) {
+  return P.gscale ? P.gscale[s] : 1.0f;
+}
+
 // Number of set bits of m at lanes below this lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -394,7 +400,9 @@ __device__ __forceinline__ void capture_tile(const DevPlan& P, int s, int64_t t,
 // One tile per workgroup.  acc = e + (u = m*u + g | g) is written back into e; elements
 // whose key reaches the segment's threshold are captured (capture_tile).
 // kCountTau (threshold calls): also count the tile's keys >= key(|tau|) into tau_cnt.
-template <bool kMomentum, bool kCountTau = false>
+// kScale: the plan carries a gradient scale (a separate instantiation, so that the unscaled
+// pass has no dependent load of the factor in front of its stream).
+template <bool kMomentum, bool kCountTau = false, bool kScale = false>
 __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float* __restrict__ g,
                                                         float* __restrict__ e,
                                                         float* __restrict__ u, float m) {
@@ -412,6 +420,7 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
   const int len = desc.z, s = desc.w;
   const int pb = slot_base();
+  const float gf = kScale ? P.gscale[s] : 1.0f;
 
   f4 acc[kSlots];
   if (len == kTile && (start & 3) == 0) {
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
 #pragma unroll
     for (int v = 0; v < kSlots; ++v) {
       const int q = (pb + v * 256) >> 2;
-      f4 x = gv[v];
+      f4 x = gv[v] * gf;
       if (kMomentum) {
         const f4 mu = m * uv[v];
         x = mu + x;
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
         float a = 0.0f;
         if (p < len) {
           const int64_t i = start + p;
-          float x = g[i];
+          float x = g[i] * gf;
           if (kMomentum) {
             const float mu = m * u[i];
             x = mu + x;
@@ -921,7 +930,8 @@ struct EmitOut {              // where kept entries go
   uint32_t* err;
   const float* vsrc;         // Random-k: kept values are read here (the tile holds keys)
   const float* rk_scale;     // Random-k without feedback: per-segment value scale, or null
-  float vmul;
+  const float* vsrc_scale;   // Random-k reading g itself: the gradient scale, or null
+  float vmul, gmul;
   __device__ float scales_of(int s) const { return scales[s]; }
 };
 
@@ -987,6 +997,7 @@ __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotI
         const int32_t li = li4[c];
         if (q < out_end && li >= 0 && li < n_s) {
           float val = o.vsrc ? o.vsrc[s0 + li] : x[v][c];
+          if (o.vsrc_scale) val = val * o.gmul;
           if (o.rk_scale) val = val * o.vmul;
           if (o.vals) o.vals[q] = val;
           o.idx[q] = li;
@@ -1038,6 +1049,7 @@ __global__ __launch_bounds__(kThreads) void k_emit_cand(DevPlan P, EmitOut o) {
   };
   if (o.codes) o.scale = o.scales_of(s);
   if (o.rk_scale) o.vmul = o.rk_scale[s];
+  if (o.vsrc_scale) o.gmul = o.vsrc_scale[s];
   emit_block(x, len, slot_idx, P.kth[s], P.ties[s], P.chunk_eq_base[ch], P.chunk_eq[ch],
              P.out_off[s] + P.chunk_sel_base[ch], P.out_off[s + 1], P.seg_off[s],
              (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, o);
@@ -1063,6 +1075,7 @@ __global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, EmitOut o) {
       };
       if (o.codes) o.scale = o.scales_of(s);
       if (o.rk_scale) o.vmul = o.rk_scale[s];
+      if (o.vsrc_scale) o.gmul = o.vsrc_scale[s];
       emit_block(x, len, slot_idx, kth, r, P.tile_eq_base[t], P.tile_eq[t],
                  P.out_off[s] + P.tile_sel_base[t], P.out_off[s + 1], s0,
                  (int32_t)(P.seg_off[s + 1] - s0), s_w, o);
@@ -1131,11 +1144,13 @@ __global__ __launch_bounds__(kThreads) void k_finalize_thr(DevPlan P) {
 // the scale is fl32(S / n) per segment; pass 2 writes the sign bits (bit i of word i/32,
 // 1 = negative) and the residual e = fl(acc - sign * scale).
 
-// Load the tile of g (and u), form acc (momentum first), store acc into e (and u).
+// Load the tile of g (and u), form acc (momentum first, x = fl(g * gf)), store acc into e
+// (and u).
 template <bool kMomentum>
-__device__ __forceinline__ void ef_add_tile(const float* __restrict__ g, float* __restrict__ e,
-                                            float* __restrict__ u, float m, int64_t start,
-                                            int len, f4 (&acc)[kSlots]) {
+__device__ __forceinline__ void ef_add_tile(const float* __restrict__ g, float gf,
+                                            float* __restrict__ e, float* __restrict__ u,
+                                            float m, int64_t start, int len,
+                                            f4 (&acc)[kSlots]) {
   const int pb = slot_base();
   if (len == kTile && (start & 3) == 0) {
     const f4* g4 = reinterpret_cast<const f4*>(g + start);
@@ -1152,7 +1167,7 @@ __device__ __forceinline__ void ef_add_tile(const float* __restrict__ g, float* 
 #pragma unroll
     for (int v = 0; v < kSlots; ++v) {
       const int q = (pb + v * 256) >> 2;
-      f4 x = gv[v];
+      f4 x = gv[v] * gf;
       if (kMomentum) {
         const f4 mu = m * uv[v];
         x = mu + x;
@@ -1170,7 +1185,7 @@ __device__ __forceinline__ void ef_add_tile(const float* __restrict__ g, float* 
         float a = 0.0f;
         if (p < len) {
           const int64_t i = start + p;
-          float x = g[i];
+          float x = g[i] * gf;
           if (kMomentum) {
             const float mu = m * u[i];
             x = mu + x;
@@ -1197,10 +1212,11 @@ __device__ __forceinline__ void load_tile_nt(const float* __restrict__ base, int
   }
 }
 
-// acc = fl(e + g) over one tile without storing it (lanes past len get 0): the two-pass
+// acc = fl(e + fl(g * gf)) over one tile without storing it (lanes past len get 0): the two-pass
 // codecs without momentum form acc in both passes, so their first pass only reads.
-__device__ __forceinline__ void acc_tile(const float* __restrict__ g, const float* __restrict__ e,
-                                         int64_t start, int len, f4 (&acc)[kSlots]) {
+__device__ __forceinline__ void acc_tile(const float* __restrict__ g, float gf,
+                                         const float* __restrict__ e, int64_t start, int len,
+                                         f4 (&acc)[kSlots]) {
   const int pb = slot_base();
   if (len == kTile && (start & 3) == 0) {
     const f4* g4 = reinterpret_cast<const f4*>(g + start);
@@ -1213,14 +1229,14 @@ __device__ __forceinline__ void acc_tile(const float* __restrict__ g, const floa
       acc[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(e4 + q) : e4[q];
     }
 #pragma unroll
-    for (int v = 0; v < kSlots; ++v) acc[v] = acc[v] + gv[v];
+    for (int v = 0; v < kSlots; ++v) acc[v] = acc[v] + gv[v] * gf;
   } else {
 #pragma unroll
     for (int v = 0; v < kSlots; ++v)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int p = pb + v * 256 + c;
-        acc[v][c] = p < len ? e[start + p] + g[start + p] : 0.0f;
+        acc[v][c] = p < len ? e[start + p] + g[start + p] * gf : 0.0f;
       }
   }
 }
@@ -1236,11 +1252,12 @@ __global__ __launch_bounds__(kThreads) void k_sign_pass1(DevPlan P, const float*
   const int4 desc = P.tile_desc[t];
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
   const int len = desc.z;
+  const float gf = grad_scale(P, desc.w);
   f4 acc[kSlots];
   if (kMomentum)
-    ef_add_tile<true>(g, e, u, m, start, len, acc);
+    ef_add_tile<true>(g, gf, e, u, m, start, len, acc);
   else
-    acc_tile(g, e, start, len, acc);
+    acc_tile(g, gf, e, start, len, acc);
   double l1 = 0.0;   // lanes past len hold 0
 #pragma unroll
   for (int v = 0; v < kSlots; ++v)
@@ -1293,7 +1310,7 @@ __global__ __launch_bounds__(kThreads) void k_sign_pass2(DevPlan P, const float*
   const int pb = slot_base(), lane = lane_id();
   f4 acc[kSlots];
   if (kRecompute)
-    acc_tile(g, e, start, len, acc);
+    acc_tile(g, grad_scale(P, s), e, start, len, acc);
   else
     load_tile_nt(e + start, len, acc);
   uint32_t* wb = bits + P.word_off[s] + (t - P.tile_base[s]) * (int64_t)(kTile / 32);
@@ -1370,11 +1387,12 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass1(DevPlan P, const float*
   const int4 desc = P.tile_desc[t];
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
   const int len = desc.z;
+  const float gf = grad_scale(P, desc.w);
   f4 acc[kSlots];
   if (kEF && kMomentum) {
-    ef_add_tile<true>(g, e, u, m, start, len, acc);
+    ef_add_tile<true>(g, gf, e, u, m, start, len, acc);
   } else if (kEF) {        // acc = e + g, formed again by pass 2
-    acc_tile(g, e, start, len, acc);
+    acc_tile(g, gf, e, start, len, acc);
   } else if (kMomentum) {  // u = m*u + g, stored; acc = u
     const int pb = slot_base();
 #pragma unroll
@@ -1385,13 +1403,15 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass1(DevPlan P, const float*
         float a = 0.0f;
         if (p < len) {
           const float mu = m * u[start + p];
-          a = mu + g[start + p];
+          a = mu + g[start + p] * gf;
           u[start + p] = a;
         }
         acc[v][c] = a;
       }
   } else {
     load_tile_nt(g + start, len, acc);
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) acc[v] = acc[v] * gf;
   }
   double sq = 0.0;
 #pragma unroll
@@ -1445,10 +1465,16 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_pass2(DevPlan P, const float*
   const float limit = (float)levels;
   const int pb = slot_base();
   f4 acc[kSlots];
-  if (kSrc == 3)
-    acc_tile(g, e, start, len, acc);
-  else
+  if (kSrc == 3) {
+    acc_tile(g, grad_scale(P, s), e, start, len, acc);
+  } else {
     load_tile_nt((kSrc == 0 ? e : (kSrc == 1 ? u : g)) + start, len, acc);
+    if (kSrc == 2) {
+      const float gf = grad_scale(P, s);
+#pragma unroll
+      for (int v = 0; v < kSlots; ++v) acc[v] = acc[v] * gf;
+    }
+  }
   const bool vec = len == kTile && (start & 3) == 0;
 #pragma unroll
   for (int v = 0; v < kSlots; ++v) {
@@ -1524,9 +1550,10 @@ __global__ __launch_bounds__(kThreads) void k_qsgd_decompress(DevPlan P,
 // captures by key instead of magnitude; the select and the ordered emit are shared, the kept
 // values then read back from where acc lives.
 
-// u = fl(fl(m*u) + g) over one tile, stored (momentum without error feedback).
-__device__ __forceinline__ void momentum_tile(const float* __restrict__ g, float* __restrict__ u,
-                                              float m, int64_t start, int len) {
+// u = fl(fl(m*u) + fl(g * gf)) over one tile, stored (momentum without error feedback).
+__device__ __forceinline__ void momentum_tile(const float* __restrict__ g, float gf,
+                                              float* __restrict__ u, float m, int64_t start,
+                                              int len) {
   const int pb = slot_base();
   if (len == kTile && (start & 3) == 0) {
     const f4* g4 = reinterpret_cast<const f4*>(g + start);
@@ -1542,7 +1569,7 @@ __device__ __forceinline__ void momentum_tile(const float* __restrict__ g, float
     for (int v = 0; v < kSlots; ++v) {
       const int q = (pb + v * 256) >> 2;
       const f4 mu = m * uv[v];
-      const f4 x = mu + gv[v];
+      const f4 x = mu + gv[v] * gf;
       if (GC_NT_STORE_E) __builtin_nontemporal_store(x, u4 + q); else u4[q] = x;
     }
   } else {
@@ -1553,13 +1580,13 @@ __device__ __forceinline__ void momentum_tile(const float* __restrict__ g, float
         const int p = pb + v * 256 + c;
         if (p < len) {
           const float mu = m * u[start + p];
-          u[start + p] = mu + g[start + p];
+          u[start + p] = mu + g[start + p] * gf;
         }
       }
   }
 }
 
-template <bool kMomentum, bool kEF>
+template <bool kMomentum, bool kEF, bool kScale = false>
 __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const float* __restrict__ g,
                                                            float* __restrict__ e,
                                                            float* __restrict__ u, float m) {
@@ -1570,6 +1597,7 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
   const int len = desc.z, s = desc.w;
   const uint32_t thr = P.thr[s];  // kNoCapture: this segment takes the exact fallback
+  const float gf = kScale ? P.gscale[s] : 1.0f;
   f4 key[kSlots];
   if (kEF && len == kTile && (start & 3) == 0) {
     // whole aligned tile: issue the loads, draw the keys while they are in flight
@@ -1589,7 +1617,7 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
 #pragma unroll
     for (int v = 0; v < kSlots; ++v) {
       const int q = (pb + v * 256) >> 2;
-      f4 x = gv[v];
+      f4 x = gv[v] * gf;
       if (kMomentum) {
         const f4 mu = m * uv[v];
         x = mu + x;
@@ -1601,9 +1629,9 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
   } else {
     if (kEF) {
       f4 acc[kSlots];
-      ef_add_tile<kMomentum>(g, e, u, m, start, len, acc);
+      ef_add_tile<kMomentum>(g, gf, e, u, m, start, len, acc);
     } else if (kMomentum) {
-      momentum_tile(g, u, m, start, len);
+      momentum_tile(g, gf, u, m, start, len);
     }  // neither: nothing to stream, g is read at the kept positions only
     if (thr != kNoCapture) rand_key_tile(P, start, len, key);
   }
@@ -1659,6 +1687,18 @@ __global__ __launch_bounds__(kThreads) void k_clip_scale(DevPlan P, float* __res
         if (p < len) g[start + p] = g[start + p] * f;
       }
   }
+}
+
+// Per segment: the clipping factor fl32(c / norm) where norm > c, else 1 (the scale that a
+// later compress call applies to g on load, when the plan carries it).
+__global__ __launch_bounds__(kThreads) void k_clip_factor(int32_t n_seg,
+                                                         const float* __restrict__ max_norm,
+                                                         const float* __restrict__ norms,
+                                                         float* __restrict__ factors) {
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  if (s >= n_seg) return;
+  const float norm = norms[s], c = max_norm[s];
+  factors[s] = norm > c ? c / norm : 1.0f;
 }
 
 // ------------------------------------------------------------------------------ int8 stage
@@ -1786,10 +1826,14 @@ hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u,
   k_prep<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (P.n_tiles > 0) {
-    if (u)
-      k_ef_capture<true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, u, m);
-    else
-      k_ef_capture<false><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(P, g, e, nullptr, m);
+    const unsigned nt = (unsigned)P.n_tiles;
+    if (P.gscale) {
+      if (u) k_ef_capture<true, false, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
+      else k_ef_capture<false, false, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
+    } else {
+      if (u) k_ef_capture<true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
+      else k_ef_capture<false><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
+    }
   }
   if (ev_end) (void)hipEventRecord(ev_end, st);
   EmitOut o{};
@@ -1820,10 +1864,14 @@ hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, 
   k_prep_call<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, tau);
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (P.n_tiles > 0) {
-    if (u)
-      k_ef_capture<true, true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(Q, g, e, u, m);
-    else
-      k_ef_capture<false, true><<<(unsigned)P.n_tiles, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+    const unsigned nt = (unsigned)P.n_tiles;
+    if (P.gscale) {
+      if (u) k_ef_capture<true, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
+      else k_ef_capture<false, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+    } else {
+      if (u) k_ef_capture<true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
+      else k_ef_capture<false, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+    }
   }
   if (ev_end) (void)hipEventRecord(ev_end, st);
   k_thresh_k<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, out_count);
@@ -1855,10 +1903,18 @@ hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, fl
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (P.n_tiles > 0) {
     const unsigned nt = (unsigned)P.n_tiles;
-    if (e && u) k_randk_capture<true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
-    else if (e) k_randk_capture<false, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
-    else if (u) k_randk_capture<true, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, u, m);
-    else k_randk_capture<false, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, nullptr, m);
+    if (P.gscale) {
+      if (e && u) k_randk_capture<true, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
+      else if (e) k_randk_capture<false, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+      else if (u) k_randk_capture<true, false, true><<<nt, kThreads, 0, st>>>(Q, g, nullptr, u, m);
+      // neither: the capture reads no g (the emit applies the scale to the gathered values)
+      else k_randk_capture<false, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, nullptr, m);
+    } else {
+      if (e && u) k_randk_capture<true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
+      else if (e) k_randk_capture<false, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+      else if (u) k_randk_capture<true, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, u, m);
+      else k_randk_capture<false, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, nullptr, m);
+    }
   }
   if (ev_end) (void)hipEventRecord(ev_end, st);
   EmitOut o{};
@@ -1868,6 +1924,7 @@ hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, fl
   o.idx = out_idx;
   o.err = P.err;
   o.vsrc = e ? e : (u ? u : g);
+  o.vsrc_scale = (!e && !u) ? P.gscale : nullptr;
   o.rk_scale = e ? nullptr : P.rk_scale;
   select_emit(Q, e, o, nullptr, st);
   return hipGetLastError();
@@ -1937,12 +1994,18 @@ hipError_t launch_qsgd_decompress(const DevPlan& P, const int8_t* codes, const f
 }
 
 hipError_t launch_clip(const DevPlan& P, float* g, const float* max_norm, float* norms,
-                       hipStream_t st) {
+                       float* factors, hipStream_t st) {
   if (P.n_seg == 0) return hipSuccess;
-  const unsigned nt = (unsigned)P.n_tiles;
-  if (nt > 0) k_qsgd_pass1<false, false><<<nt, kThreads, 0, st>>>(P, g, nullptr, nullptr, 0.0f);
-  k_qsgd_norm<<<P.n_seg, 1024, 0, st>>>(P, norms);
-  if (nt > 0) k_clip_scale<<<nt, kThreads, 0, st>>>(P, g, max_norm, norms);
+  DevPlan Q = P;
+  Q.gscale = nullptr;   // the norm is the raw gradient's
+  const unsigned nt = (unsigned)Q.n_tiles;
+  if (nt > 0) k_qsgd_pass1<false, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, nullptr, 0.0f);
+  k_qsgd_norm<<<Q.n_seg, 1024, 0, st>>>(Q, norms);
+  if (factors)
+    k_clip_factor<<<blocks_for(Q.n_seg, kThreads), kThreads, 0, st>>>(Q.n_seg, max_norm, norms,
+                                                                      factors);
+  else if (nt > 0)
+    k_clip_scale<<<nt, kThreads, 0, st>>>(Q, g, max_norm, norms);
   return hipGetLastError();
 }
 

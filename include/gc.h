@@ -271,6 +271,20 @@ int gc_clip_by_norm(gc_plan* plan, float* g, const float* max_norm, float* norms
                     void* stream);
 
 /*
+ * Clipping folded into the compress calls.  gc_clip_factors runs only the norm pass of
+ * gc_clip_by_norm and writes, per segment, f_s = fl32(max_norm[s] / norm_s) where
+ * norm_s > max_norm[s], else 1 (factors_out: device float[n_seg]; g is not modified).
+ * gc_plan_set_gradient_scale(plan, factors) makes every later compress call of the plan
+ * (Top-k, int8, threshold, Random-k, sign, QSGD) use x = fl(g_i * f_s) wherever it reads g,
+ * which is bit-identical to gc_clip_by_norm followed by that call, without its 8 B/element
+ * scaling pass; NULL switches it off.  The factors array must stay valid while it is set.
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ */
+int gc_clip_factors(gc_plan* plan, const float* g, const float* max_norm, float* norms_out,
+                    float* factors_out, void* stream);
+int gc_plan_set_gradient_scale(gc_plan* plan, const float* factors);
+
+/*
  * Receiver side of the data-parallel exchange ("Gradient Compression", memory-compression
  * glossary, systems section: sparse gradients are exchanged by all-gather of values and
  * indices; "Communication Optimization > Gradient Compression", subtlety paragraph: the
