@@ -357,6 +357,33 @@ def clip_fused_bench(plan, wl, codec, gbufs, e, u, outs, steps, warmup):
             "hbm_peak_frac": round(bpe * wl.n / ms / 1e6 / HBM_PEAK_GBPS, 4)}
 
 
+def randk_plain_bench(plan, wl, gbufs, outs, steps):
+    """Random-k without error feedback or momentum: the pass draws a Philox key per element
+    and reads nothing; the k kept values are gathered from g and scaled by n/k."""
+    import torch
+    vals, idx, _, _ = outs
+    for t in range(2):
+        plan.randk_compress(gbufs[t % len(gbufs)], vals, idx, seed=0, step=t)
+    torch.cuda.synchronize()
+    plan.timing()
+    plan.set_timing(True)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for t in range(steps):
+        plan.randk_compress(gbufs[t % len(gbufs)], vals, idx, seed=0, step=t + 2)
+    s1.record()
+    torch.cuda.synchronize()
+    plan.set_timing(False)
+    ms = s0.elapsed_time(s1) / steps
+    k1_ms, n = plan.timing()
+    k1 = k1_ms / max(n, 1)
+    # Philox4x32-10 per 4 elements: 10 rounds of two 32x32->64 products (v_mad_u64_u32)
+    blocks = wl.n / 4
+    return {"ms_per_step": round(ms, 4), "key_pass_ms": round(k1, 4),
+            "G_keys_per_s": round(wl.n / k1 / 1e6, 1),
+            "philox_blocks_per_s_G": round(blocks / k1 / 1e6, 1)}
+
+
 def receiver_bench(wl, n_workers=8, reps=5):
     """Receiver side of an n_workers data-parallel exchange on one GPU: the gathered payloads
     (synthetic, the plan's layout) added into a resident dense gradient in worker order."""
@@ -473,6 +500,11 @@ def main():
             log(f"[bench] QSGD with clipping folded in: "
                 f"{result['with_clipping_fused']['ms_per_step']:.3f} ms/step")
         log(f"[bench] clipping: {result['clip_all_segments']['ms_per_call']:.3f} ms")
+    if codec == "randk":
+        result["without_error_feedback"] = randk_plain_bench(plan, wl, gbufs, outs,
+                                                             max(args.steps // 2, 3))
+        log(f"[bench] Random-k without feedback: "
+            f"{result['without_error_feedback']['ms_per_step']:.3f} ms/step")
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline: oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(plan, wl, gbufs[0], e, u, outs, codec,
