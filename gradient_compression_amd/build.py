@@ -15,7 +15,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgc.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("gc_kernels.hip", "gc_api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("gc_topk.hip", "gc_codecs.hip", "gc_scatter.hip",
+                                                       "gc_api.hip")]
 ARCH = "gfx950"
 
 

@@ -162,7 +162,8 @@ struct Int8Args {
   uint32_t seed_lo, seed_hi, step_lo;
 };
 
-// Launchers (gc_kernels.hip).  Each returns the hipError_t of its launches.
+// Launchers (gc_topk.hip, gc_codecs.hip, gc_scatter.hip).  Each returns the hipError_t of
+// its launches.
 hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
                            float* out_vals, int32_t* out_idx, const Int8Args& q8,
                            hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
