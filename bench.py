@@ -118,9 +118,16 @@ def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
     def step(t):
         run_step(plan, wl, codec, gbufs[t % len(gbufs)], e, u, outs, t)
 
-    for t in range(warmup):
-        step(t)
+    cold = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    for t in range(warmup):
+        if t == 0:
+            cold[0].record()
+        step(t)
+        if t == 0:
+            cold[1].record()
+    torch.cuda.synchronize()
+    cold_ms = cold[0].elapsed_time(cold[1]) if warmup > 0 else None
     plan.timing()                       # drop the warm-up events
     plan.set_timing(True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -133,7 +140,7 @@ def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
     plan.set_timing(False)
     total_ms = start.elapsed_time(stop)
     k1_ms, launches = plan.timing()
-    return total_ms / steps, k1_ms / max(launches, 1), launches
+    return total_ms / steps, k1_ms / max(launches, 1), launches, cold_ms
 
 
 def setup(wl, n_gbufs=4, codec="topk"):
@@ -433,8 +440,8 @@ def main():
     plan, gbufs, e, u, outs = setup(wl, codec=codec)
     log(f"[bench] inputs resident ({len(gbufs)} gradient buffers); warmup {args.warmup}, "
         f"timing {args.steps} steps, codec {codec}")
-    ms, k1_ms, launches = time_steps(plan, wl, gbufs, e, u, outs, args.steps, args.warmup,
-                                     codec)
+    ms, k1_ms, launches, cold_ms = time_steps(plan, wl, gbufs, e, u, outs, args.steps,
+                                              args.warmup, codec)
     st = plan.last_stats()
     bpe = bytes_per_element(wl, codec)
     value = 4.0 * wl.n / ms / 1e6                     # GB/s of fp32 gradient
@@ -468,6 +475,8 @@ def main():
             "gradient_dist": f"{wl.scale} * Student-t({wl.df})" if wl.dist == "t" else wl.dist,
         },
         "elements_per_s": round(wl.n / ms * 1e3, 1),
+        # the plan's first call (no threshold estimate yet; warm-up, not in the timed steps)
+        "first_call_ms": round(cold_ms, 4) if cold_ms is not None else None,
         "effective_GBps": round(eff, 1),
         "hbm_peak_frac_effective": round(eff / HBM_PEAK_GBPS, 4),
         "candidates_per_k": round(float(st["candidates"].sum()) / max(plan.total_k, 1), 3),
@@ -527,8 +536,8 @@ def main():
         # the same shape with momentum correction (u = 0.9 u + g), as the 7B workload states
         wm = workload("c5_llama2_7b")
         plan_m, gb_m, e_m, u_m, outs_m = setup(wm)
-        ms_m, k1m, _ = time_steps(plan_m, wm, gb_m, e_m, u_m, outs_m, max(args.steps // 2, 3),
-                                  args.warmup)
+        ms_m, k1m, _, _ = time_steps(plan_m, wm, gb_m, e_m, u_m, outs_m,
+                                     max(args.steps // 2, 3), args.warmup)
         result["momentum_variant"] = {
             "workload": wm.name, "ms_per_step": round(ms_m, 4),
             "GBps_gradient": round(4.0 * wm.n / ms_m / 1e6, 2),

@@ -24,6 +24,8 @@ constexpr int64_t kCapacityFactor = 16;
 constexpr int64_t kMinCapacity = 65536;
 // First margin of the threshold estimate (next threshold = beta * |k-th largest|).
 constexpr float kInitialBeta = 0.9f;
+// Tiles per segment that the cold-start sample reads (about 0.5M elements).
+constexpr int64_t kSampleTiles = 64;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -84,6 +86,7 @@ struct gc_plan {
   gc::OutPlan op{};
   void* mem = nullptr;
   bool timing = false;
+  bool cold = true;   // no threshold estimate yet (fresh plan, or after a reset)
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending, spare;
 };
 
@@ -186,6 +189,22 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
     out_chunk_base[s + 1] = out_chunk_base[s] + ceil_div(ks[s], gc::kOutChunk);
   }
   const int64_t n_tiles = tile_base[n_seg], n_chunks = chunk_base[n_seg];
+  // cold-start sample: about kSampleTiles evenly spaced tiles of each segment that starts
+  // without an estimate (large segments with k > 0; none when the debug flags forbid one)
+  std::vector<int32_t> sample_tile;
+  std::vector<int64_t> sample_elems(n_seg, 0);
+  if (!(flags & (GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE))) {
+    for (int32_t s = 0; s < n_seg; ++s) {
+      if (ks[s] == 0 || thr_init[s] != gc::kNoCapture) continue;   // nothing to estimate
+      const int64_t nt = tile_base[s + 1] - tile_base[s];
+      const int64_t stride = std::max<int64_t>(1, ceil_div(nt, kSampleTiles));
+      for (int64_t j = 0; j < nt; j += stride) {
+        sample_tile.push_back((int32_t)(tile_base[s] + j));
+        sample_elems[s] += std::min<int64_t>(gc::kTile, seg_off[s + 1] - seg_off[s] - j * gc::kTile);
+      }
+    }
+  }
+  const int64_t n_sample = (int64_t)sample_tile.size();
   const int64_t n_out_chunks = out_chunk_base[n_seg];
   if (n_tiles > INT32_MAX || n_chunks + gc::kFullBlocks > INT32_MAX || n_out_chunks > INT32_MAX ||
       cand_total > UINT32_MAX * 4ll) {
@@ -270,6 +289,10 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   float* d_rk_scale;
   cv.add(&d.k_call, n_seg);
   cv.add(&d.seg_norm, n_seg);
+  int32_t* d_sample_tile;
+  int64_t* d_sample_elems;
+  cv.add(&d_sample_tile, n_sample);
+  cv.add(&d_sample_elems, n_seg);
   cv.add(&d.thr_est, n_seg);
   cv.add(&d.beta_est, n_seg);
   cv.add(&d.tau_key, n_seg);
@@ -298,6 +321,9 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   d.thr_rand = d_thr_rand;
   d.rk_scale = d_rk_scale;
   d.keys = gc::kKeysMagnitude;
+  d.n_sample = n_sample;
+  d.sample_tile = d_sample_tile;
+  d.sample_elems = d_sample_elems;
   gc::OutPlan& o = p->op;
   o.n_seg = n_seg;
   o.n_out_chunks = n_out_chunks;
@@ -324,6 +350,8 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   up(upload(d_word_off, p->word_off));
   up(upload(d_thr_rand, thr_rand));
   up(upload(d_rk_scale, rk_scale));
+  up(upload(d_sample_tile, sample_tile));
+  up(upload(d_sample_elems, sample_elems));
   up(upload(d.thr, thr_init));
   up(upload(d.beta, std::vector<float>(n_seg, kInitialBeta)));
   up(upload(d.thr_est, std::vector<uint32_t>(n_seg, gc::kNoCapture)));
@@ -408,8 +436,9 @@ int compress_checked(gc_plan* plan, const float* g, float* e, float* u, float mo
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t b = nullptr, en = nullptr;
   if (int rc = timing_events(plan, &b, &en)) return rc;
-  const hipError_t err =
-      gc::launch_compress(plan->dp, g, e, u, momentum, out_vals, out_idx, q8, st, b, en);
+  const hipError_t err = gc::launch_compress(plan->dp, g, e, u, momentum, out_vals, out_idx,
+                                             q8, plan->cold, st, b, en);
+  plan->cold = false;
   return err == hipSuccess ? GC_OK : GC_ERR_HIP;
 }
 
@@ -624,6 +653,7 @@ int gc_plan_set_gradient_scale(gc_plan* plan, const float* factors) {
 int gc_plan_reset_estimate(gc_plan* plan, void* stream) {
   if (!plan) return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
+  plan->cold = true;
   return gc::launch_reset(plan->dp, static_cast<hipStream_t>(stream)) == hipSuccess ? GC_OK
                                                                                      : GC_ERR_HIP;
 }

@@ -36,6 +36,9 @@ namespace gc {
 #ifndef GC_NT_ZERO_E        // the scattered residual zeroing of kept entries non-temporal
 #define GC_NT_ZERO_E 1
 #endif
+#ifndef GC_SAMPLE_MARGIN    // cold start: capture this many first-key digits below the sample's
+#define GC_SAMPLE_MARGIN 2  // estimate of the k-th key (a digit is a factor of 2^(1/8))
+#endif
 #ifndef GC_BETA_MAX         // largest margin: next threshold <= GC_BETA_MAX * |k-th key|
 #define GC_BETA_MAX 0.98f
 #endif
@@ -141,6 +144,10 @@ struct DevPlan {
   uint32_t* tau_cnt;           // [n_seg] entries with key >= tau_key counted by the capture
   float* seg_norm;             // [n_seg] l2 norms of a clipping call (when the caller wants none)
   const float* gscale;         // [n_seg] caller's gradient scale applied on load, or null
+  // cold-start sample: about 64 evenly spaced tiles of each large segment
+  int64_t n_sample;
+  const int32_t* sample_tile;  // [n_sample] tiles whose acc is histogrammed on a cold call
+  const int64_t* sample_elems; // [n_seg] elements in the segment's sample (0: not sampled)
   int32_t keys;                // kKeysMagnitude or kKeysRandom
   uint32_t seed_lo, seed_hi, step_lo;   // Random-k key stream
 };
@@ -164,8 +171,9 @@ struct Int8Args {
 
 // Launchers (gc_topk.hip, gc_codecs.hip, gc_scatter.hip).  Each returns the hipError_t of
 // its launches.
+// cold: the plan has no threshold estimate yet; a sample of tiles sets a first one.
 hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
-                           float* out_vals, int32_t* out_idx, const Int8Args& q8,
+                           float* out_vals, int32_t* out_idx, const Int8Args& q8, bool cold,
                            hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, float* e,
                             float* u, float m, const float* tau, float* out_vals,

@@ -833,6 +833,72 @@ __global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, EmitOut o) {
   }
 }
 
+// ---------------------------------------------------------------------------- cold start
+// A plan's first call has no k-th key to start from.  Rather than capture nothing and
+// re-capture every large segment from two extra passes over it, the call first forms acc on
+// about 64 evenly spaced tiles of each such segment (exactly as the streaming pass will, but
+// without storing it), histograms the first key digit, and sets the capture threshold
+// GC_SAMPLE_MARGIN digits below the sample's estimate of the k-th key.  A wrong estimate only costs the usual
+// re-capture: the candidates are checked for completeness as on every call.
+__global__ __launch_bounds__(kThreads) void k_sample_zero(DevPlan P) {
+  const int s = blockIdx.x;
+  if (P.sample_elems[s] == 0) return;
+  uint32_t* h = P.hist + (size_t)s * 3 * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+}
+
+template <bool kMomentum>
+__global__ __launch_bounds__(kThreads) void k_sample_hist(DevPlan P, const float* __restrict__ g,
+                                                         const float* __restrict__ e,
+                                                         const float* __restrict__ u, float m) {
+  __shared__ uint32_t h[kHistBins];
+  const int64_t t = P.sample_tile[blockIdx.x];
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const float gf = grad_scale(P, s);
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+  f4 gv[kSlots], acc[kSlots], uv[kSlots];
+  load_tile(g + start, len, gv);
+  load_tile(e + start, len, acc);
+  if (kMomentum) load_tile(u + start, len, uv);
+  __syncthreads();
+  const int pb = slot_base();
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v) {
+    f4 x = gv[v] * gf;
+    if (kMomentum) {
+      const f4 mu = m * uv[v];
+      x = mu + x;
+    }
+    acc[v] = acc[v] + x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (pb + v * 256 + c < len) atomicAdd(&h[mag_key(acc[v][c]) >> 20], 1u);
+  }
+  __syncthreads();
+  hist_flush(h, P.hist + (size_t)s * 3 * kHistBins);
+}
+
+// Per sampled segment still without an estimate: the first-digit bucket d that holds the
+// sample's ceil(k * sample / n)-th largest key; the threshold is the floor of bucket
+// d - GC_SAMPLE_MARGIN.
+__global__ __launch_bounds__(kThreads) void k_sample_decide(DevPlan P) {
+  __shared__ uint32_t s_tmp[kWaves];
+  __shared__ uint32_t s_out[3];
+  const int s = blockIdx.x;
+  const int64_t ns = P.sample_elems[s];
+  if (ns == 0 || P.thr[s] != kNoCapture) return;
+  const int64_t n = P.seg_off[s + 1] - P.seg_off[s];
+  const int64_t k = P.k[s];
+  const uint32_t kk = (uint32_t)max((int64_t)1, (k * ns + n - 1) / n);
+  uint32_t d, above, bin;
+  const bool ok = find_digit(P.hist + (size_t)s * 3 * kHistBins, kk, s_tmp, s_out, &d, &above,
+                             &bin);
+  if (threadIdx.x == 0 && ok)
+    P.thr[s] = d > (uint32_t)GC_SAMPLE_MARGIN ? (d - (uint32_t)GC_SAMPLE_MARGIN) << 20 : 0u;
+}
+
 // ----------------------------------------------------------------------------- finalize
 // Threshold for the next call: beta * |kth|, where the margin beta follows the last calls:
 // lowered after too few candidates, raised after an overflow or far more than needed.  beta
@@ -987,10 +1053,18 @@ void select_emit(const DevPlan& P, const float* e, const EmitOut& o, float* scal
 }  // namespace
 
 hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
-                           float* out_vals, int32_t* out_idx, const Int8Args& q8,
+                           float* out_vals, int32_t* out_idx, const Int8Args& q8, bool cold,
                            hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (P.n_seg == 0) return hipSuccess;
   k_prep<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
+  if (cold && P.n_sample > 0) {
+    k_sample_zero<<<P.n_seg, kThreads, 0, st>>>(P);
+    if (u)
+      k_sample_hist<true><<<(unsigned)P.n_sample, kThreads, 0, st>>>(P, g, e, u, m);
+    else
+      k_sample_hist<false><<<(unsigned)P.n_sample, kThreads, 0, st>>>(P, g, e, nullptr, m);
+    k_sample_decide<<<P.n_seg, kThreads, 0, st>>>(P);
+  }
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (P.n_tiles > 0) {
     const unsigned nt = (unsigned)P.n_tiles;
