@@ -31,7 +31,7 @@ EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layo
            "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
            "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress",
            "gc_threshold_ef_compress", "gc_randk_compress", "gc_decompress_gathered",
-           "gc_clip_by_norm", "gc_clip_factors", "gc_plan_set_gradient_scale")
+           "gc_clip_by_norm", "gc_clip_factors", "gc_plan_set_gradient_scale", "gc_layout")
 
 _lib = None
 
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
         "gc_clip_by_norm": [vp, vp, vp, vp, vp],
         "gc_clip_factors": [vp, vp, vp, vp, vp, vp],
         "gc_plan_set_gradient_scale": [vp, vp],
+        "gc_layout": [vp, i32, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -95,6 +96,24 @@ def status_string(status: int) -> str:
 def _check(rc: int, what: str):
     if rc != GC_OK:
         raise GCError(rc, what)
+
+
+def layout(seg_off, k=None, ratio=None):
+    """Host-only: (k per segment, output offsets) of a plan with these arguments."""
+    off = np.ascontiguousarray(seg_off, dtype=np.int64)
+    n_seg = int(off.size - 1)
+    kp = rp = None
+    if k is not None:
+        k_in = np.ascontiguousarray(np.broadcast_to(np.asarray(k, np.int64), (n_seg,)))
+        kp = _np_ptr(k_in)
+    if ratio is not None:
+        r_in = np.ascontiguousarray(np.broadcast_to(np.asarray(ratio, np.float64), (n_seg,)))
+        rp = _np_ptr(r_in)
+    k_out = np.zeros(max(n_seg, 0), np.int64)
+    out_off = np.zeros(max(n_seg, 0) + 1, np.int64)
+    _check(lib().gc_layout(_np_ptr(off), n_seg, kp, rp, _np_ptr(k_out), _np_ptr(out_off)),
+           "gc_layout")
+    return k_out, out_off
 
 
 def _np_ptr(a):
@@ -386,6 +405,6 @@ def copy_f32(src, dst, stream=None):
            "gc_copy_f32")
 
 
-__all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "EXPORTS",
+__all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "layout", "EXPORTS",
            "GC_MOMENTUM_MASK", "GC_DEBUG_FORCE_FALLBACK", "GC_DEBUG_NO_ESTIMATE", "MODE_SKIP",
            "MODE_CANDIDATES", "MODE_FULL", "MODE_RECAPTURED"]

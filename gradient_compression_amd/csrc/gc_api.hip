@@ -119,22 +119,34 @@ const char* gc_status_string(int status) {
   }
 }
 
+int gc_layout(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
+              int64_t* k_out, int64_t* out_off) {
+  if (n_seg < 0 || !seg_off) return GC_ERR_INVALID_ARG;
+  if (n_seg > 0 && (k == nullptr) == (ratio == nullptr)) return GC_ERR_INVALID_ARG;
+  if (seg_off[0] < 0) return GC_ERR_INVALID_ARG;
+  int64_t total = 0;
+  for (int32_t s = 0; s < n_seg; ++s) {
+    const int64_t n = seg_off[s + 1] - seg_off[s];
+    if (n < 0 || n > INT32_MAX) return GC_ERR_INVALID_ARG;
+    const int64_t ks = k ? k[s] : k_from_ratio(n, ratio[s]);
+    if (ks < 0 || ks > n) return GC_ERR_INVALID_ARG;
+    if (k_out) k_out[s] = ks;
+    if (out_off) out_off[s] = total;
+    total += ks;
+  }
+  if (out_off) out_off[n_seg] = total;
+  return GC_OK;
+}
+
 int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
                    uint32_t flags, gc_plan** out) {
   if (!out) return GC_ERR_INVALID_ARG;
   *out = nullptr;
   if (n_seg < 0 || !seg_off) return GC_ERR_INVALID_ARG;
-  if (n_seg > 0 && (k == nullptr) == (ratio == nullptr)) return GC_ERR_INVALID_ARG;
   if (flags & ~(uint32_t)(GC_MOMENTUM_MASK | GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE))
     return GC_ERR_INVALID_ARG;
-  if (seg_off[0] < 0) return GC_ERR_INVALID_ARG;
   std::vector<int64_t> ks(n_seg);
-  for (int32_t s = 0; s < n_seg; ++s) {
-    const int64_t n = seg_off[s + 1] - seg_off[s];
-    if (n < 0 || n > INT32_MAX) return GC_ERR_INVALID_ARG;
-    ks[s] = k ? k[s] : k_from_ratio(n, ratio[s]);
-    if (ks[s] < 0 || ks[s] > n) return GC_ERR_INVALID_ARG;
-  }
+  if (int rc = gc_layout(seg_off, n_seg, k, ratio, ks.data(), nullptr)) return rc;
 
   gc_plan* p = new (std::nothrow) gc_plan();
   if (!p) return GC_ERR_OOM;

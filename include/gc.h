@@ -66,6 +66,16 @@ typedef enum {
 typedef struct gc_plan gc_plan;
 
 /*
+ * Host-only (no GPU needed): the k per segment and the output layout a plan with these
+ * arguments has, with the checks of gc_plan_create on seg_off, k and ratio.
+ *   k_out   : host int64[n_seg] receiving k[s], or NULL.
+ *   out_off : host int64[n_seg + 1] receiving the exclusive prefix sum of k, or NULL.
+ * Errors: GC_ERR_INVALID_ARG.
+ */
+int gc_layout(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
+              int64_t* k_out, int64_t* out_off);
+
+/*
  * Build a plan for a segmented buffer and allocate its device workspace on the current
  * device.
  *   seg_off : host int64[n_seg + 1], non-decreasing, seg_off[0] >= 0; segment s covers
