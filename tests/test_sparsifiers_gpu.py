@@ -404,3 +404,38 @@ def test_threshold_full_size_llama2_7b():
             assert_bitwise(vals[ka:ka + hi.size], hv, f"threshold full it{t} seg{s} vals")
             assert_bitwise(e[a:b], host[s], f"threshold full it{t} seg{s} residual")
     plan.close()
+
+
+def test_int8_stage_on_threshold_payloads():
+    """gc_quant_int8 on a threshold payload: the (+0, -1) padding neither moves the scale nor
+    touches the residual; the kept entries' codes and the fed-back error match the oracle's
+    int8 stage on the kept entries alone."""
+    off = np.concatenate([[0], np.cumsum(SIZES)]).astype(np.int64)
+    n = int(off[-1])
+    ks = np.array([50, 300, 40, 500, 4097, 3], np.int64)
+    plan = gca.Plan(off, k=ks)
+    g = _grads(n, 1, 71)[0]
+    tau = np.array(_taus_mixed(0, g, None), np.float32)
+    dev = torch.device("cuda")
+    e_d = torch.zeros(n, device=dev)
+    vals = torch.empty(plan.total_k, device=dev)
+    idx = torch.empty(plan.total_k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(len(SIZES), dtype=torch.int32, device=dev)
+    codes = torch.empty(plan.total_k, dtype=torch.int8, device=dev)
+    scales = torch.empty(len(SIZES), device=dev)
+    plan.threshold_compress(torch.from_numpy(g).to(dev), e_d, torch.from_numpy(tau).to(dev),
+                            vals, idx, cnt)
+    plan.quant_int8(vals, idx, codes, scales, e=e_d, seed=5, step=1)
+    torch.cuda.synchronize()
+    e_h = np.zeros(n, np.float32)
+    c = cnt.cpu().numpy()
+    for s in range(len(SIZES)):
+        a, b = int(off[s]), int(off[s + 1])
+        ka = int(plan.out_off[s])
+        hv, hi = oracle.threshold_ef_segment(g[a:b].copy(), e_h[a:b], int(ks[s]), float(tau[s]))
+        assert hi.size == c[s]
+        hc, hs = oracle.quant_int8_segment(hv, hi, a, e_h[a:b], seed=5, step=1)
+        assert_bitwise(codes[ka:ka + hi.size], hc, f"seg {s} codes")
+        assert_bitwise(scales[s:s + 1], np.array([hs], np.float32), f"seg {s} scale")
+        assert bool((codes[ka + hi.size:int(plan.out_off[s + 1])] == 0).all())
+    assert_bitwise(e_d, e_h, "residual with the quantisation error fed back")
