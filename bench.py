@@ -9,8 +9,14 @@ gradient.  Prints one JSON line.
 value = GB/s of fp32 input gradient (4 N bytes per step / step time), whole job.
 roofline = the streaming EF pass (the dominant kernel): algorithmic bytes per launch
 (12 N: read g, read e, write e; 20 N with momentum) / its average HIP-event duration,
-against the 8 TB/s HBM3E peak.
-cpu_baseline = the CPU oracle on one transformer layer's segments of the same workload.
+against the 8 TB/s HBM3E peak; traffic = the HBM bytes the committed rocprofv3 counters
+measured for it (null once its code has changed since).
+cpu_baseline = the CPU oracle on a bounded sample of the same workload's segments.
+
+--codec selects the threshold, Random-k, sign or QSGD codec instead of Top-k (the same
+fields, their own pass bytes).  The default run also reports, as context: the same shape
+with momentum, the plan's first (cold) call, local gradient clipping, the receiver-side sum
+of eight workers' payloads and the copy kernel's bandwidth.
 """
 from __future__ import annotations
 
