@@ -573,9 +573,7 @@ __device__ __forceinline__ void count_block(const f4 (&x)[kSlots], int len, uint
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_count_cand(DevPlan P) {
-  __shared__ uint32_t s_tmp[kWaves];
-  const int64_t ch = blockIdx.x;
+__device__ __forceinline__ void count_cand_chunk(const DevPlan& P, int64_t ch, uint32_t* s_tmp) {
   const int s = P.chunk_seg[ch];
   if (!has_candidates(P.mode[s])) return;
   const int64_t c = P.cand_cnt[s];
@@ -587,13 +585,13 @@ __global__ __launch_bounds__(kThreads) void k_count_cand(DevPlan P) {
   count_block(x, len, P.kth[s], s_tmp, &P.chunk_gt[ch], &P.chunk_eq[ch]);
 }
 
-__global__ __launch_bounds__(kThreads) void k_count_full(DevPlan P, const float* __restrict__ e) {
-  __shared__ uint32_t s_tmp[kWaves];
+__device__ __forceinline__ void count_full_tiles(const DevPlan& P, const float* __restrict__ e,
+                                                 int fb, uint32_t* s_tmp) {
   const uint32_t nf = *P.full_count;
   for (uint32_t li = 0; li < nf; ++li) {
     const int s = (int)P.full_list[li];
     const uint32_t kth = P.kth[s];
-    for (int64_t t = P.tile_base[s] + blockIdx.x; t < P.tile_base[s + 1]; t += kFullBlocks) {
+    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
       int64_t start;
       int len;
       tile_range(P, s, t, &start, &len);
@@ -611,6 +609,16 @@ __global__ __launch_bounds__(kThreads) void k_count_full(DevPlan P, const float*
       if (threadIdx.x == 0) P.tile_max[t] = mx;
     }
   }
+}
+
+// Workgroups [0, n_chunks) count candidate chunks; the last kFullBlocks the tiles of the
+// segments on the full path (one launch for both).
+__global__ __launch_bounds__(kThreads) void k_count(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t s_tmp[kWaves];
+  if (blockIdx.x < P.n_chunks)
+    count_cand_chunk(P, blockIdx.x, s_tmp);
+  else
+    count_full_tiles(P, e, (int)(blockIdx.x - P.n_chunks), s_tmp);
 }
 
 // --------------------------------------------------------------------------------- scan
@@ -773,9 +781,8 @@ __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotI
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_emit_cand(DevPlan P, EmitOut o) {
-  __shared__ uint32_t s_w[kWaves];
-  const int64_t ch = blockIdx.x;
+__device__ __forceinline__ void emit_cand_chunk(const DevPlan& P, EmitOut o, int64_t ch,
+                                                uint32_t* s_w) {
   const int s = P.chunk_seg[ch];
   if (!has_candidates(P.mode[s])) return;
   const int64_t c = P.cand_cnt[s];
@@ -805,14 +812,14 @@ __global__ __launch_bounds__(kThreads) void k_emit_cand(DevPlan P, EmitOut o) {
              (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, o);
 }
 
-__global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, EmitOut o) {
-  __shared__ uint32_t s_w[kWaves];
+__device__ __forceinline__ void emit_full_tiles(const DevPlan& P, EmitOut o, int fb,
+                                                uint32_t* s_w) {
   const uint32_t nf = *P.full_count;
   for (uint32_t li = 0; li < nf; ++li) {
     const int s = (int)P.full_list[li];
     const uint32_t kth = P.kth[s], r = P.ties[s];
     const int64_t s0 = P.seg_off[s];
-    for (int64_t t = P.tile_base[s] + blockIdx.x; t < P.tile_base[s + 1]; t += kFullBlocks) {
+    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
       int64_t start;
       int len;
       tile_range(P, s, t, &start, &len);
@@ -831,6 +838,16 @@ __global__ __launch_bounds__(kThreads) void k_emit_full(DevPlan P, EmitOut o) {
                  (int32_t)(P.seg_off[s + 1] - s0), s_w, o);
     }
   }
+}
+
+// Workgroups [0, n_chunks) emit candidate chunks; the last kFullBlocks the tiles of the
+// segments on the full path (one launch for both).
+__global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, EmitOut o) {
+  __shared__ uint32_t s_w[kWaves];
+  if (blockIdx.x < P.n_chunks)
+    emit_cand_chunk(P, o, blockIdx.x, s_w);
+  else
+    emit_full_tiles(P, o, (int)(blockIdx.x - P.n_chunks), s_w);
 }
 
 // ---------------------------------------------------------------------------- cold start
@@ -1043,11 +1060,9 @@ void select_emit(const DevPlan& P, const float* e, const EmitOut& o, float* scal
     k_hist<<<mixed, kThreads, 0, st>>>(P, e, pass);
     k_find<<<P.n_seg, kThreads, 0, st>>>(P, pass);
   }
-  if (P.n_chunks > 0) k_count_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
-  k_count_full<<<kFullBlocks, kThreads, 0, st>>>(P, e);
+  k_count<<<mixed, kThreads, 0, st>>>(P, e);
   k_scan<<<P.n_seg, 1024, 0, st>>>(P, scales);
-  if (P.n_chunks > 0) k_emit_cand<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P, o);
-  k_emit_full<<<kFullBlocks, kThreads, 0, st>>>(P, o);
+  k_emit<<<mixed, kThreads, 0, st>>>(P, o);
 }
 
 }  // namespace
