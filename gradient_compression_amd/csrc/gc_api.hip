@@ -9,6 +9,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
+#include <memory>
 #include <new>
 #include <utility>
 #include <vector>
@@ -104,6 +106,32 @@ hipError_t upload(T* dst, const std::vector<T>& src) {
   return hipMemcpy(dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
 }
 
+// The bytes a call touches through one pointer.  Dense buffers are indexed by the absolute
+// offsets of the segment table, so they span [seg_off[0], seg_off[n_seg]) elements.
+struct Span {
+  const void* p;
+  uint64_t bytes;
+};
+Span dense_span(const gc_plan* plan, const void* p, uint64_t elt) {
+  if (!p) return {nullptr, 0};
+  const int64_t lo = plan->seg_off[0], hi = plan->seg_off[plan->n_seg];
+  return {static_cast<const char*>(p) + lo * (int64_t)elt, (uint64_t)(hi - lo) * elt};
+}
+Span flat(const void* p, int64_t count, uint64_t elt) {
+  return {p, p ? (uint64_t)count * elt : 0};
+}
+// True when two of the spans share a byte (NULL and empty spans share none).
+bool any_overlap(std::initializer_list<Span> spans) {
+  for (const Span* a = spans.begin(); a != spans.end(); ++a)
+    for (const Span* b = a + 1; b != spans.end(); ++b) {
+      if (!a->bytes || !b->bytes) continue;
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(a->p);
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(b->p);
+      if (a0 < b0 + b->bytes && b0 < a0 + a->bytes) return true;
+    }
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,22 +166,20 @@ int gc_layout(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const dou
   return GC_OK;
 }
 
-int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
-                   uint32_t flags, gc_plan** out) {
-  if (!out) return GC_ERR_INVALID_ARG;
-  *out = nullptr;
-  if (n_seg < 0 || !seg_off) return GC_ERR_INVALID_ARG;
-  if (flags & ~(uint32_t)(GC_MOMENTUM_MASK | GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE))
-    return GC_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// gc_plan_create's work; host allocations may throw std::bad_alloc, which the entry point
+// turns into GC_ERR_OOM.  The device workspace is allocated after the last host allocation,
+// so a throw never leaves it behind.
+int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
+                uint32_t flags, gc_plan** out) {
   std::vector<int64_t> ks(n_seg);
   if (int rc = gc_layout(seg_off, n_seg, k, ratio, ks.data(), nullptr)) return rc;
 
-  gc_plan* p = new (std::nothrow) gc_plan();
-  if (!p) return GC_ERR_OOM;
-  if (hipGetDevice(&p->device) != hipSuccess) {
-    delete p;
-    return GC_ERR_HIP;
-  }
+  std::unique_ptr<gc_plan> p(new gc_plan());
+  if (hipGetDevice(&p->device) != hipSuccess) return GC_ERR_HIP;
   p->n_seg = n_seg;
   p->flags = flags;
   p->seg_off.assign(seg_off, seg_off + n_seg + 1);
@@ -219,10 +245,8 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   const int64_t n_sample = (int64_t)sample_tile.size();
   const int64_t n_out_chunks = out_chunk_base[n_seg];
   if (n_tiles > INT32_MAX || n_chunks + gc::kFullBlocks > INT32_MAX || n_out_chunks > INT32_MAX ||
-      cand_total > UINT32_MAX * 4ll) {
-    delete p;
+      cand_total > UINT32_MAX * 4ll)
     return GC_ERR_UNSUPPORTED;
-  }
   std::vector<int32_t> tile_seg(n_tiles), chunk_seg(n_chunks), out_chunk_seg(n_out_chunks);
   std::vector<int4> tile_desc(n_tiles);
   for (int32_t s = 0; s < n_seg; ++s) {
@@ -312,9 +336,10 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   cv.add(&d.thr_call, n_seg);
   cv.add(&d_thr_rand, n_seg);
   cv.add(&d_rk_scale, n_seg);
+  const std::vector<float> beta_init(n_seg, kInitialBeta);
+  const std::vector<uint32_t> no_estimate(n_seg, gc::kNoCapture);
   if (hipMalloc(&p->mem, cv.total()) != hipSuccess) {
     (void)hipGetLastError();
-    delete p;
     return GC_ERR_OOM;
   }
   cv.place(static_cast<char*>(p->mem));
@@ -365,9 +390,9 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   up(upload(d_sample_tile, sample_tile));
   up(upload(d_sample_elems, sample_elems));
   up(upload(d.thr, thr_init));
-  up(upload(d.beta, std::vector<float>(n_seg, kInitialBeta)));
-  up(upload(d.thr_est, std::vector<uint32_t>(n_seg, gc::kNoCapture)));
-  up(upload(d.beta_est, std::vector<float>(n_seg, kInitialBeta)));
+  up(upload(d.beta, beta_init));
+  up(upload(d.thr_est, no_estimate));
+  up(upload(d.beta_est, beta_init));
   up(hipMemset(d.cand_cnt, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
   up(hipMemset(d.mode, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
   up(hipMemset(d.kth, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
@@ -377,16 +402,36 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   if (err != hipSuccess) {
     (void)hipGetLastError();
     (void)hipFree(p->mem);
-    delete p;
     return GC_ERR_HIP;
   }
-  *out = p;
+  *out = p.release();
   return GC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
+                   uint32_t flags, gc_plan** out) {
+  if (!out) return GC_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (n_seg < 0 || !seg_off) return GC_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)(GC_MOMENTUM_MASK | GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE))
+    return GC_ERR_INVALID_ARG;
+  try {
+    return plan_create(seg_off, n_seg, k, ratio, flags, out);
+  } catch (const std::bad_alloc&) {
+    return GC_ERR_OOM;
+  }
 }
 
 int gc_plan_destroy(gc_plan* plan) {
   if (!plan) return GC_OK;
   int rc = GC_OK;
+  int cur = -1;
+  const bool switched = hipGetDevice(&cur) == hipSuccess && cur != plan->device &&
+                        hipSetDevice(plan->device) == hipSuccess;
   if (hipDeviceSynchronize() != hipSuccess) rc = GC_ERR_HIP;
   for (auto& pr : plan->pending) {
     (void)hipEventDestroy(pr.first);
@@ -397,6 +442,7 @@ int gc_plan_destroy(gc_plan* plan) {
     (void)hipEventDestroy(pr.second);
   }
   if (plan->mem && hipFree(plan->mem) != hipSuccess) rc = GC_ERR_HIP;
+  if (switched) (void)hipSetDevice(cur);
   delete plan;
   return rc;
 }
@@ -420,6 +466,12 @@ namespace {
 // With timing on, a HIP event pair for the streaming passes of this call.
 int timing_events(gc_plan* plan, hipEvent_t* b, hipEvent_t* en) {
   if (!plan->timing) return GC_OK;
+  try {  // room for the pair in both lists, so nothing below can throw
+    plan->pending.reserve(plan->pending.size() + 1);
+    plan->spare.reserve(plan->spare.size() + plan->pending.size() + 1);
+  } catch (const std::bad_alloc&) {
+    return GC_ERR_OOM;
+  }
   if (plan->spare.empty()) {
     hipEvent_t x, y;
     if (hipEventCreate(&x) != hipSuccess) return GC_ERR_HIP;
@@ -443,7 +495,10 @@ int compress_checked(gc_plan* plan, const float* g, float* e, float* u, float mo
   if (any && (!g || !e || !aligned16(g) || !aligned16(e))) return GC_ERR_INVALID_ARG;
   if (u && !aligned16(u)) return GC_ERR_INVALID_ARG;
   if (plan->total_k > 0 && !out_idx) return GC_ERR_INVALID_ARG;
-  if (any && (g == e || (u && (g == u || e == u)))) return GC_ERR_INVALID_ARG;
+  const int64_t kt = plan->total_k;
+  if (any_overlap({dense_span(plan, g, 4), dense_span(plan, e, 4), dense_span(plan, u, 4), flat(out_vals, kt, 4),
+                   flat(out_idx, kt, 4), flat(q8.codes, kt, 1), flat(q8.scales, plan->n_seg, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t b = nullptr, en = nullptr;
@@ -490,7 +545,10 @@ int gc_threshold_ef_compress(gc_plan* plan, const float* g, float* e, float* u, 
   if (u && !aligned16(u)) return GC_ERR_INVALID_ARG;
   if (plan->n_seg > 0 && !tau) return GC_ERR_INVALID_ARG;
   if (plan->total_k > 0 && (!out_vals || !out_idx)) return GC_ERR_INVALID_ARG;
-  if (any && (g == e || (u && (g == u || e == u)))) return GC_ERR_INVALID_ARG;
+  const int64_t kt = plan->total_k, ns = plan->n_seg;
+  if (any_overlap({dense_span(plan, g, 4), dense_span(plan, e, 4), dense_span(plan, u, 4), flat(tau, ns, 4),
+                   flat(out_vals, kt, 4), flat(out_idx, kt, 4), flat(out_count, ns, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   hipEvent_t b = nullptr, en = nullptr;
   if (int rc = timing_events(plan, &b, &en)) return rc;
@@ -508,7 +566,10 @@ int gc_randk_compress(gc_plan* plan, const float* g, float* e, float* u, float m
   if (any && (!g || !aligned16(g))) return GC_ERR_INVALID_ARG;
   if ((e && !aligned16(e)) || (u && !aligned16(u))) return GC_ERR_INVALID_ARG;
   if (plan->total_k > 0 && (!out_vals || !out_idx)) return GC_ERR_INVALID_ARG;
-  if (any && ((e && (g == e || e == u)) || (u && g == u))) return GC_ERR_INVALID_ARG;
+  const int64_t kt = plan->total_k;
+  if (any_overlap({dense_span(plan, g, 4), dense_span(plan, e, 4), dense_span(plan, u, 4), flat(out_vals, kt, 4),
+                   flat(out_idx, kt, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   hipEvent_t b = nullptr, en = nullptr;
   if (int rc = timing_events(plan, &b, &en)) return rc;
@@ -530,7 +591,10 @@ int gc_sign_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float
   if (any && (!g || !e || !out_bits || !aligned16(g) || !aligned16(e))) return GC_ERR_INVALID_ARG;
   if (u && !aligned16(u)) return GC_ERR_INVALID_ARG;
   if (plan->n_seg > 0 && !out_scales) return GC_ERR_INVALID_ARG;
-  if (any && (g == e || (u && (g == u || e == u)))) return GC_ERR_INVALID_ARG;
+  if (any_overlap({dense_span(plan, g, 4), dense_span(plan, e, 4), dense_span(plan, u, 4),
+                   flat(out_bits, plan->word_off[plan->n_seg], 4),
+                   flat(out_scales, plan->n_seg, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   hipEvent_t b = nullptr, en = nullptr;
   if (int rc = timing_events(plan, &b, &en)) return rc;
@@ -544,6 +608,9 @@ int gc_sign_decompress(const gc_plan* plan, const uint32_t* bits, const float* s
   if (!plan) return GC_ERR_INVALID_ARG;
   const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
   if (any && (!bits || !scales || !dense)) return GC_ERR_INVALID_ARG;
+  if (any_overlap({dense_span(plan, dense, 4), flat(bits, plan->word_off[plan->n_seg], 4),
+                   flat(scales, plan->n_seg, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   const hipError_t err = gc::launch_sign_decompress(plan->dp, bits, scales, dense, accumulate,
                                                     static_cast<hipStream_t>(stream));
@@ -559,7 +626,9 @@ int gc_qsgd_compress(gc_plan* plan, const float* g, float* e, float* u, float mo
     return GC_ERR_INVALID_ARG;
   if ((e && !aligned16(e)) || (u && !aligned16(u))) return GC_ERR_INVALID_ARG;
   if (plan->n_seg > 0 && !out_norms) return GC_ERR_INVALID_ARG;
-  if (any && ((e && (g == e || e == u)) || (u && g == u))) return GC_ERR_INVALID_ARG;
+  if (any_overlap({dense_span(plan, g, 4), dense_span(plan, e, 4), dense_span(plan, u, 4),
+                   dense_span(plan, out_codes, 1), flat(out_norms, plan->n_seg, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   hipEvent_t b = nullptr, en = nullptr;
   if (int rc = timing_events(plan, &b, &en)) return rc;
@@ -574,6 +643,8 @@ int gc_qsgd_decompress(const gc_plan* plan, const int8_t* codes, const float* no
   if (!plan || levels < 1 || levels > 127) return GC_ERR_INVALID_ARG;
   const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
   if (any && (!codes || !norms || !dense)) return GC_ERR_INVALID_ARG;
+  if (any_overlap({dense_span(plan, dense, 4), dense_span(plan, codes, 1), flat(norms, plan->n_seg, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   const hipError_t err = gc::launch_qsgd_decompress(plan->dp, codes, norms, levels, dense,
                                                     accumulate, static_cast<hipStream_t>(stream));
@@ -585,6 +656,10 @@ int gc_quant_int8(gc_plan* plan, const float* vals, const int32_t* idx, float* e
   if (!plan) return GC_ERR_INVALID_ARG;
   if (plan->total_k > 0 && (!vals || !idx || !out_codes)) return GC_ERR_INVALID_ARG;
   if (plan->n_seg > 0 && !out_scales) return GC_ERR_INVALID_ARG;
+  const int64_t kt = plan->total_k;
+  if (any_overlap({flat(vals, kt, 4), flat(idx, kt, 4), dense_span(plan, e, 4), flat(out_codes, kt, 1),
+                   flat(out_scales, plan->n_seg, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   const hipError_t err = gc::launch_quant(plan->op, vals, idx, e, seed, step, out_codes,
                                           out_scales, static_cast<hipStream_t>(stream));
@@ -599,6 +674,13 @@ int gc_decompress(const gc_plan* plan, const float* vals, const int8_t* codes,
   if (codes && !scales) return GC_ERR_INVALID_ARG;
   if (plan->total_k > 0 && !idx) return GC_ERR_INVALID_ARG;
   if (!dense && plan->seg_off[plan->n_seg] > plan->seg_off[0]) return GC_ERR_INVALID_ARG;
+  {
+    const int64_t kt = plan->total_k;
+    const Span out = dense_span(plan, dense, 4);
+    if (any_overlap({out, flat(vals, kt, 4)}) || any_overlap({out, flat(codes, kt, 1)}) ||
+        any_overlap({out, flat(scales, plan->n_seg, 4)}) || any_overlap({out, flat(idx, kt, 4)}))
+      return GC_ERR_INVALID_ARG;
+  }
   if (int rc = check_device(plan)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
@@ -616,6 +698,14 @@ int gc_decompress_gathered(const gc_plan* plan, int32_t n_workers, const float* 
   if (codes && !scales) return GC_ERR_INVALID_ARG;
   if (plan->total_k > 0 && n_workers > 0 && !idx) return GC_ERR_INVALID_ARG;
   if (!dense && plan->seg_off[plan->n_seg] > plan->seg_off[0]) return GC_ERR_INVALID_ARG;
+  {
+    const int64_t wk = (int64_t)n_workers * plan->total_k;
+    const Span out = dense_span(plan, dense, 4);
+    if (any_overlap({out, flat(vals, wk, 4)}) || any_overlap({out, flat(codes, wk, 1)}) ||
+        any_overlap({out, flat(scales, (int64_t)n_workers * plan->n_seg, 4)}) ||
+        any_overlap({out, flat(idx, wk, 4)}))
+      return GC_ERR_INVALID_ARG;
+  }
   if (int rc = check_device(plan)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
@@ -636,6 +726,9 @@ int gc_clip_by_norm(gc_plan* plan, float* g, const float* max_norm, float* norms
   const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
   if (any && (!g || !aligned16(g))) return GC_ERR_INVALID_ARG;
   if (plan->n_seg > 0 && !max_norm) return GC_ERR_INVALID_ARG;
+  if (any_overlap({dense_span(plan, g, 4), flat(max_norm, plan->n_seg, 4),
+                   flat(norms_out, plan->n_seg, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   const hipError_t err = gc::launch_clip(plan->dp, g, max_norm,
                                          norms_out ? norms_out : plan->dp.seg_norm, nullptr,
@@ -649,6 +742,9 @@ int gc_clip_factors(gc_plan* plan, const float* g, const float* max_norm, float*
   const bool any = plan->seg_off[plan->n_seg] > plan->seg_off[0];
   if (any && (!g || !aligned16(g))) return GC_ERR_INVALID_ARG;
   if (plan->n_seg > 0 && (!max_norm || !factors_out)) return GC_ERR_INVALID_ARG;
+  if (any_overlap({dense_span(plan, g, 4), flat(max_norm, plan->n_seg, 4),
+                   flat(norms_out, plan->n_seg, 4), flat(factors_out, plan->n_seg, 4)}))
+    return GC_ERR_INVALID_ARG;
   if (int rc = check_device(plan)) return rc;
   const hipError_t err = gc::launch_clip(plan->dp, const_cast<float*>(g), max_norm,
                                          norms_out ? norms_out : plan->dp.seg_norm, factors_out,

@@ -33,8 +33,10 @@
  * `stream` (a hipStream_t; NULL = the default stream): arguments are checked on the host
  * before anything is launched, and errors of the launched work surface at the caller's
  * next synchronisation.  No call allocates device memory except gc_plan_create.  A plan
- * serves one stream at a time; calls on one plan must not overlap.  No exception crosses
- * this interface; every function returns a gc_status (0 = success).
+ * serves one stream at a time; calls on one plan must not overlap.  The buffers of one call
+ * must not share any byte (a dense buffer spans elements [seg_off[0], seg_off[n_seg]), the
+ * others their stated length); the host check rejects a violation with GC_ERR_INVALID_ARG.
+ * No exception crosses this interface; every function returns a gc_status (0 = success).
  */
 #ifndef GC_H
 #define GC_H
@@ -111,7 +113,7 @@ int gc_plan_layout(const gc_plan* plan, int64_t* k /* host or NULL */,
 
 /*
  * The error-feedback Top-k step over every segment.
- *   g        : float[N] fresh gradient, read only; must not alias e, u or the outputs.
+ *   g        : float[N] fresh gradient, read only; must not overlap e, u or the outputs.
  *   e        : float[N] residual, read and rewritten in place.
  *   u        : float[N] velocity, updated in place (u = fl(fl(momentum*u) + g)), or NULL for
  *              plain error feedback (momentum is then ignored).
@@ -119,7 +121,8 @@ int gc_plan_layout(const gc_plan* plan, int64_t* k /* host or NULL */,
  *              writes [out_off[s], out_off[s+1]) in ascending index order.
  * N = seg_off[n_seg]; elements outside the segments are not touched.  g, e and u must be
  * 16-byte aligned.
- * Errors: GC_ERR_INVALID_ARG (NULL or misaligned pointer), GC_ERR_HIP (launch failure).
+ * Errors: GC_ERR_INVALID_ARG (NULL, misaligned or overlapping buffers), GC_ERR_HIP (launch
+ * failure).
  */
 int gc_topk_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float momentum,
                         float* out_vals, int32_t* out_idx, void* stream);

@@ -243,7 +243,19 @@ def test_argument_errors_on_gpu():
         plan.compress(torch.zeros(1001, device="cuda")[1:], e, v, i)
     with pytest.raises(gca.GCError):          # g aliases e
         plan.compress(e, e, v, i)
+    buf = torch.zeros(2000, device="cuda")
+    with pytest.raises(gca.GCError):          # g and e overlap in part
+        plan.compress(buf[:1000], buf[4:1004], v, i)
+    with pytest.raises(gca.GCError):          # the output values lie inside e
+        plan.compress(g, buf[:1000], buf[500:510], i)
+    with pytest.raises(gca.GCError):          # the output indices lie inside g
+        plan.compress(buf[:1000], e, v, buf[100:110].view(torch.int32))
+    dense = torch.zeros(1000, device="cuda")
+    with pytest.raises(gca.GCError):          # decompression into its own input
+        plan.decompress(i, dense, vals=dense[:10])
+    plan.compress(buf[:1000], buf[1000:], v, i)   # disjoint views of one buffer are fine
     plan.compress(g, e, v, i)
+    plan.decompress(i, dense, vals=v)
     torch.cuda.synchronize()
     plan.close()
 
