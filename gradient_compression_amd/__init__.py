@@ -129,6 +129,10 @@ def _dev_ptr(t, dtype, name, numel=None):
         raise TypeError(f"{name} must be a torch tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU")
+    cur = torch.cuda.current_device()
+    if t.device.index is not None and t.device.index != cur:
+        # the library runs on the current device (which must be the plan's)
+        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{cur}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
