@@ -72,11 +72,17 @@ def load(path: str):
 
 
 def lib():
+    """The oracle library: liboracle.so, or the build of oracle.c that GC_ORACLE_LIB names
+    (the sanitizer test runs the oracle's tests against an ASan/UBSan build that way)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
-        _lib = load(_LIB)
+        other = os.environ.get("GC_ORACLE_LIB")
+        if other:
+            _lib = load(other)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            _lib = load(_LIB)
     return _lib
 
 
