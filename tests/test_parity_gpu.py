@@ -109,6 +109,30 @@ def test_forced_fallback_matches():
                pytest.fail("forced full path not taken"))
 
 
+def _many_sizes(n_seg, seed):
+    """Mostly tiny segments, some below and some above a tile, a few large ones."""
+    rng = np.random.default_rng(seed)
+    kind = rng.choice(4, n_seg, p=[0.6, 0.3, 0.09, 0.01])
+    lo = np.array([0, 64, 9000, 70000])[kind]
+    hi = np.array([64, 9000, 70000, 300000])[kind]
+    return [int(x) for x in rng.integers(lo, hi)]
+
+
+def test_thousands_of_segments():
+    """3000 segments (including empty ones) in one plan, k = 1%, three EF steps."""
+    sizes = _many_sizes(3000, 41)
+    log(f"many segments: n_seg={len(sizes)} n={sum(sizes)} empty={sizes.count(0)}")
+    run_parity(sizes, t_grads(sum(sizes), 3, seed=42), ratio=0.01, label="3000 segments")
+
+
+def test_thousands_of_segments_full_path():
+    """Every one of 800 segments on the exact full path at once (its workgroups walk the
+    whole list of full-path segments)."""
+    sizes = _many_sizes(800, 43)
+    run_parity(sizes, t_grads(sum(sizes), 2, seed=44), ratio=0.01,
+               flags=gca.GC_DEBUG_FORCE_FALLBACK, label="800 segments, full path")
+
+
 def test_no_estimate_recaptures_every_call():
     sizes = [300000, 20000, 8192 * 9 + 5]
     seen = []
