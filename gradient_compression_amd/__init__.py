@@ -33,7 +33,7 @@ EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layo
            "gc_threshold_ef_compress", "gc_randk_compress", "gc_decompress_gathered",
            "gc_clip_by_norm", "gc_clip_factors", "gc_plan_set_gradient_scale", "gc_layout")
 
-_lib = None
+_libs: dict = {}
 
 
 class GCError(RuntimeError):
@@ -42,15 +42,23 @@ class GCError(RuntimeError):
         super().__init__(f"{what}: {status_string(status)} ({status})")
 
 
-def lib() -> ctypes.CDLL:
-    """Load libgc.so (built by ``__graft_entry__.build()``); raise if it is not built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+def lib(variant: str | None = None) -> ctypes.CDLL:
+    """Load libgc.so (built by ``__graft_entry__.build()``); raise if it is not built.
+
+    ``variant``: one of the other tile geometries that the build also compiles
+    (``build.VARIANTS``, e.g. "t256s2"); the default geometry when None."""
+    key = variant or ""
+    if key in _libs:
+        return _libs[key]
+    if variant is None:
+        path = LIB_PATH
+    else:
+        from . import build as _build
+        path = _build.variant_path(variant)
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run __graft_entry__.build() "
                           "(there is no fallback implementation)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i32, i64, u32, u64, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                    ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float)
     sig = {
@@ -85,7 +93,7 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_char_p if name == "gc_status_string" else ctypes.c_int
-    _lib = L
+    _libs[key] = L
     return L
 
 
@@ -152,10 +160,12 @@ class Plan:
     """A compression plan over a segmented buffer (one segment per parameter tensor).
 
     ``seg_off``: int64[n_seg + 1] segment offsets; give per-segment ``k`` or ``ratio``.
+    ``variant``: run on a library built at another tile geometry (see ``lib``).
     """
 
-    def __init__(self, seg_off, k=None, ratio=None, flags: int = 0):
-        L = lib()
+    def __init__(self, seg_off, k=None, ratio=None, flags: int = 0, variant: str | None = None):
+        self._L = L = lib(variant)
+        self.variant = variant
         self._h = ctypes.c_void_p()
         off = np.ascontiguousarray(seg_off, dtype=np.int64)
         self.n_seg = int(off.size - 1)
@@ -187,7 +197,7 @@ class Plan:
 
     def close(self):
         if getattr(self, "_h", None) and self._h.value:
-            lib().gc_plan_destroy(self._h)
+            self._L.gc_plan_destroy(self._h)
             self._h = ctypes.c_void_p()
 
     def __del__(self):
@@ -210,7 +220,7 @@ class Plan:
         """
         import torch
         n = self.n
-        rc = lib().gc_topk_ef_compress(
+        rc = self._L.gc_topk_ef_compress(
             self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
             _dev_ptr(u, torch.float32, "u", n), float(momentum),
             _dev_ptr(out_vals, torch.float32, "out_vals", self.total_k),
@@ -222,7 +232,7 @@ class Plan:
         """compress then int8 in one call (the quantisation error goes back into e)."""
         import torch
         n = self.n
-        rc = lib().gc_topk_ef_compress_int8(
+        rc = self._L.gc_topk_ef_compress_int8(
             self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
             _dev_ptr(u, torch.float32, "u", n), float(momentum), int(seed) & (2 ** 64 - 1),
             int(step) & (2 ** 64 - 1),
@@ -237,7 +247,7 @@ class Plan:
         """int8 codes and per-segment scales of the kept values (stochastic rounding);
         with ``e`` the quantisation error is fed back into the residual."""
         import torch
-        rc = lib().gc_quant_int8(
+        rc = self._L.gc_quant_int8(
             self._h, _dev_ptr(vals, torch.float32, "vals", self.total_k),
             _dev_ptr(idx, torch.int32, "idx", self.total_k), _dev_ptr(e, torch.float32, "e", self.n),
             int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1),
@@ -248,7 +258,7 @@ class Plan:
     def decompress(self, idx, dense, vals=None, codes=None, scales=None, accumulate=False,
                    stream=None):
         import torch
-        rc = lib().gc_decompress(
+        rc = self._L.gc_decompress(
             self._h, _dev_ptr(vals, torch.float32, "vals", self.total_k),
             _dev_ptr(codes, torch.int8, "codes", self.total_k),
             _dev_ptr(scales, torch.float32, "scales", self.n_seg),
@@ -263,7 +273,7 @@ class Plan:
         storage) and one L1 scale per segment; e <- acc - sign * scale."""
         import torch
         n = self.n
-        rc = lib().gc_sign_ef_compress(
+        rc = self._L.gc_sign_ef_compress(
             self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
             _dev_ptr(u, torch.float32, "u", n), float(momentum),
             _dev_ptr(out_bits, torch.int32, "out_bits", self.total_words),
@@ -272,7 +282,7 @@ class Plan:
 
     def sign_decompress(self, bits, scales, dense, accumulate=False, stream=None):
         import torch
-        rc = lib().gc_sign_decompress(
+        rc = self._L.gc_sign_decompress(
             self._h, _dev_ptr(bits, torch.int32, "bits", self.total_words),
             _dev_ptr(scales, torch.float32, "scales", self.n_seg),
             _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
@@ -284,7 +294,7 @@ class Plan:
         """QSGD with `levels` levels, one l2 norm per segment; with e, error feedback."""
         import torch
         n = self.n
-        rc = lib().gc_qsgd_compress(
+        rc = self._L.gc_qsgd_compress(
             self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
             _dev_ptr(u, torch.float32, "u", n), float(momentum), int(levels),
             int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1),
@@ -295,7 +305,7 @@ class Plan:
     def qsgd_decompress(self, codes, norms, dense, levels: int = 127, accumulate=False,
                         stream=None):
         import torch
-        rc = lib().gc_qsgd_decompress(
+        rc = self._L.gc_qsgd_decompress(
             self._h, _dev_ptr(codes, torch.int8, "codes", self.n),
             _dev_ptr(norms, torch.float32, "norms", self.n_seg), int(levels),
             _dev_ptr(dense, torch.float32, "dense", self.n), int(bool(accumulate)),
@@ -306,7 +316,7 @@ class Plan:
         """Per segment: when ||g_s||_2 > max_norm[s], g_s *= max_norm[s] / ||g_s||_2 (in place).
         ``max_norm``: device float32[n_seg]; ``norms_out`` receives the norms before."""
         import torch
-        rc = lib().gc_clip_by_norm(
+        rc = self._L.gc_clip_by_norm(
             self._h, _dev_ptr(g, torch.float32, "g", self.n),
             _dev_ptr(max_norm, torch.float32, "max_norm", self.n_seg),
             _dev_ptr(norms_out, torch.float32, "norms_out", self.n_seg), _stream(stream))
@@ -315,7 +325,7 @@ class Plan:
     def clip_factors(self, g, max_norm, factors_out, norms_out=None, stream=None):
         """Per segment f_s = max_norm[s] / ||g_s||_2 where the norm exceeds it, else 1."""
         import torch
-        rc = lib().gc_clip_factors(
+        rc = self._L.gc_clip_factors(
             self._h, _dev_ptr(g, torch.float32, "g", self.n),
             _dev_ptr(max_norm, torch.float32, "max_norm", self.n_seg),
             _dev_ptr(norms_out, torch.float32, "norms_out", self.n_seg),
@@ -327,7 +337,7 @@ class Plan:
         The tensor is kept referenced while it is set."""
         import torch
         self._gscale = factors
-        _check(lib().gc_plan_set_gradient_scale(
+        _check(self._L.gc_plan_set_gradient_scale(
             self._h, _dev_ptr(factors, torch.float32, "factors", self.n_seg)),
             "gc_plan_set_gradient_scale")
 
@@ -336,7 +346,7 @@ class Plan:
         """Add n_workers payloads (back to back in worker order) into dense, worker by worker."""
         import torch
         tk = self.total_k * n_workers
-        rc = lib().gc_decompress_gathered(
+        rc = self._L.gc_decompress_gathered(
             self._h, int(n_workers), _dev_ptr(vals, torch.float32, "vals", tk),
             _dev_ptr(codes, torch.int8, "codes", tk),
             _dev_ptr(scales, torch.float32, "scales", self.n_seg * n_workers),
@@ -353,7 +363,7 @@ class Plan:
         """
         import torch
         n = self.n
-        rc = lib().gc_threshold_ef_compress(
+        rc = self._L.gc_threshold_ef_compress(
             self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
             _dev_ptr(u, torch.float32, "u", n), float(momentum),
             _dev_ptr(tau, torch.float32, "tau", self.n_seg),
@@ -368,7 +378,7 @@ class Plan:
         index)); with e, error feedback, else values scaled by n_s / k_s."""
         import torch
         n = self.n
-        rc = lib().gc_randk_compress(
+        rc = self._L.gc_randk_compress(
             self._h, _dev_ptr(g, torch.float32, "g", n), _dev_ptr(e, torch.float32, "e", n),
             _dev_ptr(u, torch.float32, "u", n), float(momentum), int(seed) & (2 ** 64 - 1),
             int(step) & (2 ** 64 - 1),
@@ -377,26 +387,26 @@ class Plan:
         _check(rc, "gc_randk_compress")
 
     def reset_estimate(self, stream=None):
-        _check(lib().gc_plan_reset_estimate(self._h, _stream(stream)), "gc_plan_reset_estimate")
+        _check(self._L.gc_plan_reset_estimate(self._h, _stream(stream)), "gc_plan_reset_estimate")
 
     def last_stats(self, stream=None) -> dict:
         """Per-segment mode, candidate count, k-th key and ties of the last call (syncs)."""
         out = {name: np.zeros(self.n_seg, np.uint32)
                for name in ("mode", "candidates", "kth_key", "ties")}
-        rc = lib().gc_plan_last_stats(self._h, _np_ptr(out["mode"]), _np_ptr(out["candidates"]),
+        rc = self._L.gc_plan_last_stats(self._h, _np_ptr(out["mode"]), _np_ptr(out["candidates"]),
                                       _np_ptr(out["kth_key"]), _np_ptr(out["ties"]),
                                       _stream(stream))
         _check(rc, "gc_plan_last_stats")
         return out
 
     def set_timing(self, enable: bool = True):
-        _check(lib().gc_plan_set_timing(self._h, int(bool(enable))), "gc_plan_set_timing")
+        _check(self._L.gc_plan_set_timing(self._h, int(bool(enable))), "gc_plan_set_timing")
 
     def timing(self):
         """(milliseconds, launches) of the streaming pass since the last query."""
         ms = ctypes.c_double()
         n = ctypes.c_int64()
-        _check(lib().gc_plan_timing(self._h, ctypes.byref(ms), ctypes.byref(n)), "gc_plan_timing")
+        _check(self._L.gc_plan_timing(self._h, ctypes.byref(ms), ctypes.byref(n)), "gc_plan_timing")
         return ms.value, n.value
 
 

@@ -1,4 +1,6 @@
-"""Build the HIP library libgc.so (gfx950 only) next to this file.
+"""Build the HIP library libgc.so (gfx950 only) next to this file, and the same library at
+other tile geometries (libgc_<name>.so, see VARIANTS) for the tests that check that no result
+depends on the geometry.
 
 Flags that the results depend on:
   -ffp-contract=off                  no fused multiply-add: u = fl(fl(m*u) + g)
@@ -18,6 +20,21 @@ LIB = os.path.join(HERE, "libgc.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("gc_topk.hip", "gc_codecs.hip", "gc_scatter.hip",
                                                        "gc_api.hip")]
 ARCH = "gfx950"
+
+# Tile geometries besides the default (1024 threads x 2 slots, 8192-element tiles).  A tile is
+# threads * 4 * slots elements; a different geometry moves every tile, chunk and run boundary,
+# the cold-start sample and the order of the per-tile partial sums.
+VARIANTS = {
+    "t512s4": ("GC_TILE_THREADS=512", "GC_TILE_SLOTS=4"),    # 8192 elements, 8 waves
+    "t1024s1": ("GC_TILE_THREADS=1024", "GC_TILE_SLOTS=1"),  # 4096 elements, 16 waves
+    "t256s2": ("GC_TILE_THREADS=256", "GC_TILE_SLOTS=2"),    # 2048 elements, 4 waves
+}
+
+
+def variant_path(name: str) -> str:
+    if name not in VARIANTS:
+        raise KeyError(f"unknown tile geometry {name!r}; built ones: {sorted(VARIANTS)}")
+    return os.path.join(HERE, f"libgc_{name}.so")
 
 
 def hipcc() -> str:
@@ -52,5 +69,14 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> list[str]:
+    """libgc.so and every VARIANTS geometry (the hipcc runs in parallel)."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [(LIB, ())] + [(variant_path(n), d) for n, d in VARIANTS.items()]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        futs = [ex.submit(build, verbose, out, d) for out, d in jobs]
+        return [f.result() for f in futs]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print("\n".join(build_all(verbose=True)))

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import gradient_compression_amd as gca
+from gradient_compression_amd import build as gc_build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -26,6 +27,15 @@ def test_exports_every_declared_symbol():
     for name in names:
         assert hasattr(L, name), name
     assert sorted(gca.EXPORTS) == names
+
+
+@pytest.mark.parametrize("variant", sorted(gc_build.VARIANTS))
+def test_tile_geometry_variants_export_every_symbol(variant):
+    """The same library at the other tile geometries (the GPU tests check that their results
+    equal the default geometry's)."""
+    L = gca.lib(variant)
+    for name in declared_functions():
+        assert hasattr(L, name), f"{variant}: {name}"
 
 
 def test_status_strings():
