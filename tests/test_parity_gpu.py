@@ -284,6 +284,29 @@ def test_argument_errors_on_gpu():
     plan.close()
 
 
+def test_workspace_out_of_memory_and_unsupported_size_are_reported():
+    """A plan whose workspace does not fit in what the device has left fails with
+    GC_ERR_OOM; one whose candidate buffers would pass the library's 32-bit chunk addressing
+    (64 segments of 2^31 - 1 elements with k = n) fails with GC_ERR_UNSUPPORTED before any
+    allocation.  The library and the device stay usable afterwards."""
+    n_s = 2 ** 31 - 1
+    with pytest.raises(gca.GCError) as err:
+        gca.Plan(np.arange(65, dtype=np.int64) * n_s, ratio=1.0)
+    assert err.value.status == gca.GC_ERR_UNSUPPORTED, err.value
+    free, _ = torch.cuda.mem_get_info()
+    hold = torch.empty(max(free - (8 << 30), 0), dtype=torch.uint8, device="cuda")
+    try:
+        # one segment with k = n: candidate buffers of 16 B per element, about 34 GB
+        with pytest.raises(gca.GCError) as err:
+            gca.Plan(np.array([0, n_s], np.int64), ratio=1.0)
+        assert err.value.status == gca.GC_ERR_OOM, err.value
+    finally:
+        del hold
+        torch.cuda.empty_cache()
+    sizes = [30000, 4097]
+    run_parity(sizes, t_grads(sum(sizes), 2, seed=13), ratio=0.01, label="after OOM")
+
+
 def test_checkpoint_resume_matches_straight_run():
     """The error-feedback state is e (and u): five steps straight equal three steps, a
     save and restore of e and u into fresh buffers (and a fresh plan), then two steps."""
