@@ -95,7 +95,10 @@ int gc_layout(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const dou
  * tile, and 16 B per candidate slot (max(16 k_s, 65536) slots per segment, n_s for segments
  * of at most 65536 elements): about 1.8 GB for a 6.7e9-element, 291-segment gradient at
  * k = 0.1%.
- * Errors: GC_ERR_INVALID_ARG (any check above), GC_ERR_OOM, GC_ERR_HIP.
+ * Errors: GC_ERR_INVALID_ARG (any check above), GC_ERR_OOM (the workspace does not fit),
+ * GC_ERR_UNSUPPORTED (2^31 or more tiles, candidate chunks or int8 output chunks, or more
+ * than 4 * (2^32 - 1) candidate slots in all: the kernels' 32-bit grid and slot counts;
+ * nothing is allocated), GC_ERR_HIP.
  */
 int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const double* ratio,
                    uint32_t flags, gc_plan** out);
