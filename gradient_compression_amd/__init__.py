@@ -12,7 +12,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgc.so")
+# GC_LIB_PATH: load another build of the same library (the host-sanitizer test uses it)
+LIB_PATH = os.environ.get("GC_LIB_PATH") or os.path.join(_HERE, "libgc.so")
 
 GC_OK = 0
 GC_ERR_INVALID_ARG = -1
