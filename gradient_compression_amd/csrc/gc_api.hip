@@ -267,6 +267,7 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   d.flags = (int32_t)flags;
   d.n_tiles = n_tiles;
   d.n_chunks = n_chunks;
+  d.n_chunk_blocks = (int32_t)std::min<int64_t>(n_chunks, gc::kChunkBlocks);
   int64_t *d_seg_off, *d_tile_base, *d_chunk_base, *d_out_off, *d_cand_base, *d_out_chunk_base;
   int32_t *d_tile_seg, *d_chunk_seg, *d_out_chunk_seg;
   int4* d_tile_desc;
@@ -313,6 +314,8 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   cv.add(&d.chunk_eq_base, n_chunks);
   cv.add(&d.chunk_sel_base, n_chunks);
   cv.add(&d.chunk_max, n_chunks);
+  cv.add(&d.act_chunk, n_chunks);
+  cv.add(&d.act_count, 1);
   cv.add(&d.tile_max, n_tiles);
   cv.add(&d.tile_l1, n_tiles);
   int64_t* d_word_off;

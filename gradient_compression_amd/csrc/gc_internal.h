@@ -54,6 +54,9 @@ constexpr int kTile = kWaves * kWaveSpan;
 constexpr int kChunk = kTile;
 // Workgroups that serve the exact full-segment path, striding over listed segments.
 constexpr int kFullBlocks = 1024;
+// Most workgroups that walk the candidate chunks of a call (the chunks that hold candidates
+// are listed per call; a plan has chunks for its full capacity, mostly unused).
+constexpr int kChunkBlocks = 1024;
 // Output chunks for the int8 and decompression kernels.
 constexpr int kOutChunk = 4096;
 constexpr int kHistBins = 2048;
@@ -81,6 +84,7 @@ struct DevPlan {
   int32_t flags;
   int64_t n_tiles;
   int64_t n_chunks;
+  int32_t n_chunk_blocks;      // min(n_chunks, kChunkBlocks): the chunk walkers of a launch
   // host-built tables
   const int64_t* seg_off;      // [n_seg + 1]
   const int64_t* tile_base;    // [n_seg + 1] first tile of each segment
@@ -126,6 +130,8 @@ struct DevPlan {
   uint32_t* chunk_eq_base;
   uint32_t* chunk_sel_base;
   uint32_t* chunk_max;         // [n_chunks] largest candidate key of the chunk (int8 absmax)
+  uint32_t* act_chunk;         // [n_chunks] the chunks that hold candidates this call, any order
+  uint32_t* act_count;         // [1] their number
   // candidate buffers, segment s at [cand_base[s], cand_base[s] + cand_cap[s])
   float* cand_val;
   int32_t* cand_idx;

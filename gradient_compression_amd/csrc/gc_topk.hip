@@ -40,6 +40,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(DevPlan P) {
   if (s == 0) {
     *P.full_count = 0;
     *P.recap_count = 0;
+    *P.act_count = 0;
     *P.err = 0;
   }
 }
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_call(DevPlan P, const float* 
   if (s == 0) {
     *P.full_count = 0;
     *P.recap_count = 0;
+    *P.act_count = 0;
     *P.err = 0;
   }
 }
@@ -422,8 +424,11 @@ __device__ __forceinline__ bool has_candidates(uint32_t mode) {
 
 // Per segment with candidates: index-ordered destination of every tile's run (exclusive
 // scan of the run sizes over the segment's tiles).
+// Also appends the segment's chunks that hold candidates to the call's list of active chunks
+// (the later chunk kernels walk that list instead of every chunk of the capacity).
 __global__ __launch_bounds__(1024) void k_runs(DevPlan P) {
   __shared__ uint32_t s_tmp[16];
+  __shared__ uint32_t s_act;
   const int s = blockIdx.x;
   if (!has_candidates(P.mode[s])) return;
   const int64_t t0 = P.tile_base[s], t1 = P.tile_base[s + 1];
@@ -436,14 +441,18 @@ __global__ __launch_bounds__(1024) void k_runs(DevPlan P) {
     if (t < t1) P.run_dst[t] = carry + ex;
     carry += tot;
   }
+  const int64_t c0 = P.chunk_base[s];
+  const uint32_t na = (uint32_t)min(((int64_t)P.cand_cnt[s] + kChunk - 1) / kChunk,
+                                    P.chunk_base[s + 1] - c0);
+  if (threadIdx.x == 0) s_act = na ? atomicAdd(P.act_count, na) : 0u;
+  __syncthreads();
+  for (uint32_t j = threadIdx.x; j < na; j += 1024) P.act_chunk[s_act + j] = (uint32_t)(c0 + j);
 }
 
 // ------------------------------------------------------------------------------ scatter
 // Candidates into ascending index order (tile t's run goes to run_dst[t]); on the estimate
-// path, also the first-digit histogram of the candidates.
-__global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
-  __shared__ uint32_t h[kHistBins];
-  const int64_t ch = blockIdx.x;
+// path, also the first-digit histogram of the candidates.  One chunk; contains barriers.
+__device__ void scatter_chunk(const DevPlan& P, int64_t ch, uint32_t* h, uint32_t* s_m) {
   const int s = P.chunk_seg[ch];
   const uint32_t mode = P.mode[s];
   if (!has_candidates(mode)) return;
@@ -484,7 +493,6 @@ __global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
 #pragma unroll
   for (int r = 0; r < kPer; ++r)
     if (r * kThreads + (int)threadIdx.x < len) mx = max(mx, mag_key(vx[r]));
-  __shared__ uint32_t s_m[kWaves];
   mx = block_max<kThreads>(mx, s_m);
   if (threadIdx.x == 0) P.chunk_max[ch] = mx;
   if (do_hist) {
@@ -493,32 +501,50 @@ __global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
   }
 }
 
+// The workgroups walk the call's list of chunks that hold candidates.
+__global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t s_m[kWaves];
+  const uint32_t na = *P.act_count;
+  for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks) {
+    scatter_chunk(P, P.act_chunk[i], h, s_m);
+    __syncthreads();   // the next chunk reuses h
+  }
+}
+
 // --------------------------------------------------------------------------------- hist
-// Passes 1 and 2.  Workgroups [0, n_chunks) histogram sorted candidate chunks; the last
-// kFullBlocks histogram the tiles of the segments on the full path.
+// Passes 1 and 2.  Workgroups [0, n_chunk_blocks) histogram the sorted candidate chunks of the
+// call's active list; the last kFullBlocks the tiles of the segments on the full path.
+__device__ void hist_chunk(const DevPlan& P, int64_t ch, int pass, uint32_t* h) {
+  const int s = P.chunk_seg[ch];
+  if (!has_candidates(P.mode[s])) return;
+  const int64_t c = P.cand_cnt[s];
+  const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+  if (j0 >= c) return;
+  const int len = (int)min((int64_t)kChunk, c - j0);
+  const uint32_t prefix = P.prefix[s];
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+  f4 x[kSlots];
+  load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
+  __syncthreads();
+  hist_add(h, x, len, prefix, pass);
+  __syncthreads();
+  hist_flush(h, P.hist + ((size_t)s * 3 + pass) * kHistBins);
+}
+
 __global__ __launch_bounds__(kThreads) void k_hist(DevPlan P, const float* __restrict__ e,
                                                    int pass) {
   __shared__ uint32_t h[kHistBins];
-  if (blockIdx.x < P.n_chunks) {
-    const int64_t ch = blockIdx.x;
-    const int s = P.chunk_seg[ch];
-    if (!has_candidates(P.mode[s])) return;
-    const int64_t c = P.cand_cnt[s];
-    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
-    if (j0 >= c) return;
-    const int len = (int)min((int64_t)kChunk, c - j0);
-    const uint32_t prefix = P.prefix[s];
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
-    f4 x[kSlots];
-    load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
-    __syncthreads();
-    hist_add(h, x, len, prefix, pass);
-    __syncthreads();
-    hist_flush(h, P.hist + ((size_t)s * 3 + pass) * kHistBins);
+  if (blockIdx.x < (uint32_t)P.n_chunk_blocks) {
+    const uint32_t na = *P.act_count;
+    for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks) {
+      hist_chunk(P, P.act_chunk[i], pass, h);
+      __syncthreads();   // the next chunk reuses h
+    }
     return;
   }
   hist_listed_tiles(P, e, P.full_list, *P.full_count, kModeFull, pass,
-                    blockIdx.x - (int)P.n_chunks, h);
+                    blockIdx.x - P.n_chunk_blocks, h);
 }
 
 // --------------------------------------------------------------------------------- find
@@ -611,14 +637,17 @@ __device__ __forceinline__ void count_full_tiles(const DevPlan& P, const float* 
   }
 }
 
-// Workgroups [0, n_chunks) count candidate chunks; the last kFullBlocks the tiles of the
-// segments on the full path (one launch for both).
+// Workgroups [0, n_chunk_blocks) count the active candidate chunks; the last kFullBlocks the
+// tiles of the segments on the full path (one launch for both).
 __global__ __launch_bounds__(kThreads) void k_count(DevPlan P, const float* __restrict__ e) {
   __shared__ uint32_t s_tmp[kWaves];
-  if (blockIdx.x < P.n_chunks)
-    count_cand_chunk(P, blockIdx.x, s_tmp);
-  else
-    count_full_tiles(P, e, (int)(blockIdx.x - P.n_chunks), s_tmp);
+  if (blockIdx.x < (uint32_t)P.n_chunk_blocks) {
+    const uint32_t na = *P.act_count;
+    for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks)
+      count_cand_chunk(P, P.act_chunk[i], s_tmp);
+  } else {
+    count_full_tiles(P, e, (int)(blockIdx.x - P.n_chunk_blocks), s_tmp);
+  }
 }
 
 // --------------------------------------------------------------------------------- scan
@@ -840,14 +869,17 @@ __device__ __forceinline__ void emit_full_tiles(const DevPlan& P, EmitOut o, int
   }
 }
 
-// Workgroups [0, n_chunks) emit candidate chunks; the last kFullBlocks the tiles of the
-// segments on the full path (one launch for both).
+// Workgroups [0, n_chunk_blocks) emit the active candidate chunks; the last kFullBlocks the
+// tiles of the segments on the full path (one launch for both).
 __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, EmitOut o) {
   __shared__ uint32_t s_w[kWaves];
-  if (blockIdx.x < P.n_chunks)
-    emit_cand_chunk(P, o, blockIdx.x, s_w);
-  else
-    emit_full_tiles(P, o, (int)(blockIdx.x - P.n_chunks), s_w);
+  if (blockIdx.x < (uint32_t)P.n_chunk_blocks) {
+    const uint32_t na = *P.act_count;
+    for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks)
+      emit_cand_chunk(P, o, P.act_chunk[i], s_w);
+  } else {
+    emit_full_tiles(P, o, (int)(blockIdx.x - P.n_chunk_blocks), s_w);
+  }
 }
 
 // ---------------------------------------------------------------------------- cold start
@@ -1053,9 +1085,9 @@ void select_emit(const DevPlan& P, const float* e, const EmitOut& o, float* scal
   k_recap_decide<<<P.n_seg, kThreads, 0, st>>>(P);
   k_recapture<<<kFullBlocks, kThreads, 0, st>>>(P, e);
   k_runs<<<P.n_seg, 1024, 0, st>>>(P);
-  if (P.n_chunks > 0) k_scatter<<<(unsigned)P.n_chunks, kThreads, 0, st>>>(P);
+  if (P.n_chunk_blocks > 0) k_scatter<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
   k_find<<<P.n_seg, kThreads, 0, st>>>(P, 0);
-  const unsigned mixed = (unsigned)(P.n_chunks + kFullBlocks);
+  const unsigned mixed = (unsigned)(P.n_chunk_blocks + kFullBlocks);
   for (int pass = 1; pass < 3; ++pass) {
     k_hist<<<mixed, kThreads, 0, st>>>(P, e, pass);
     k_find<<<P.n_seg, kThreads, 0, st>>>(P, pass);
