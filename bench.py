@@ -16,7 +16,9 @@ cpu_baseline = the CPU oracle on a bounded sample of the same workload's segment
 --codec selects the threshold, Random-k, sign or QSGD codec instead of Top-k (the same
 fields, their own pass bytes).  The default run also reports, as context: the same shape
 with momentum, the plan's first (cold) call, local gradient clipping, the receiver-side sum
-of eight workers' payloads and the copy kernel's bandwidth.
+of eight workers' payloads, the copy kernel's bandwidth, and the bandwidth of a bare kernel
+with the pass's memory instructions (y += x: two reads, one write, the same tile layout and
+cache policy) and none of its selection work.
 """
 from __future__ import annotations
 
@@ -203,6 +205,28 @@ def copy_ceiling(n_bytes=8 << 30):
     ms = s.elapsed_time(t) / 10
     del a, b
     return 2 * n * 4 / ms / 1e6
+
+
+def bare_ef_add(n_bytes=8 << 30):
+    """Reference for the streaming pass: the library's y += x kernel (the pass's tile layout
+    and non-temporal loads and stores, nothing else), GB/s of its two reads and one write."""
+    import torch
+    import gradient_compression_amd as gca
+    n = n_bytes // 4
+    x = torch.zeros(n, dtype=torch.float32, device="cuda")
+    y = torch.zeros(n, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        gca.add_f32(x, y)
+    torch.cuda.synchronize()
+    s, t = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(10):
+        gca.add_f32(x, y)
+    t.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(t) / 10
+    del x, y
+    return 3 * n * 4 / ms / 1e6
 
 
 def _ulp(x):
@@ -536,8 +560,13 @@ def main():
     torch.cuda.empty_cache()
     try:
         result["copy_ceiling_GBps"] = round(copy_ceiling(), 1)
-    except Exception as ex:  # noqa: BLE001 - context figure only
-        log(f"[bench] copy ceiling skipped: {ex}")
+        add = bare_ef_add()
+        result["bare_ef_add_GBps"] = round(add, 1)
+        if "roofline" in result:
+            # the pass against the same 2-read/1-write stream without its selection work
+            result["pass_vs_bare_ef_add"] = round(result["roofline"]["achieved"] / add, 4)
+    except Exception as ex:  # noqa: BLE001 - context figures only
+        log(f"[bench] stream ceilings skipped: {ex}")
     if not args.no_momentum_variant and wl.name == DEFAULT_WORKLOAD:
         # the same shape with momentum correction (u = 0.9 u + g), as the 7B workload states
         wm = workload("c5_llama2_7b")

@@ -17,6 +17,11 @@
 
 #include "gc_internal.h"
 
+namespace gc {
+// The calibration stream of gc_add_f32 (gc_scatter.hip).
+hipError_t launch_add(const float* x, float* y, int64_t n, hipStream_t st);
+}  // namespace gc
+
 namespace {
 
 // Segments at most this long capture every element (their select runs on the candidates).
@@ -821,6 +826,13 @@ int gc_copy_f32(const float* src, float* dst, int64_t n, void* stream) {
     return GC_ERR_INVALID_ARG;
   return gc::launch_copy(src, dst, n, static_cast<hipStream_t>(stream)) == hipSuccess ? GC_OK
                                                                                       : GC_ERR_HIP;
+}
+
+int gc_add_f32(const float* x, float* y, int64_t n, void* stream) {
+  if (n < 0 || (n && (!x || !y || !aligned16(x) || !aligned16(y)))) return GC_ERR_INVALID_ARG;
+  if (any_overlap({flat(x, n, 4), flat(y, n, 4)})) return GC_ERR_INVALID_ARG;
+  return gc::launch_add(x, y, n, static_cast<hipStream_t>(stream)) == hipSuccess ? GC_OK
+                                                                                 : GC_ERR_HIP;
 }
 
 }  // extern "C"

@@ -122,6 +122,44 @@ hipError_t launch_decompress(const OutPlan& O, const float* vals, const int8_t* 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------ add
+// y = fl(y + x) with the streaming pass's memory pattern and none of its other work: the same
+// tile layout, non-temporal dwordx4 loads of both inputs and a non-temporal store of y.  Its
+// bandwidth is the practical ceiling of a 2-read/1-write stream on this GPU.
+__global__ __launch_bounds__(kThreads) void k_add(const float* __restrict__ x,
+                                                  float* __restrict__ y, int64_t n) {
+  const int64_t start = (int64_t)blockIdx.x * kTile;
+  const int64_t rem = n - start;
+  const int len = rem < kTile ? (int)rem : kTile;
+  const int pb = slot_base();
+  if (len == kTile) {
+    const f4* x4 = reinterpret_cast<const f4*>(x + start);
+    f4* y4 = reinterpret_cast<f4*>(y + start);
+    f4 a[kSlots], b[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      a[v] = __builtin_nontemporal_load(x4 + ((pb + v * 256) >> 2));
+      b[v] = __builtin_nontemporal_load(y4 + ((pb + v * 256) >> 2));
+    }
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) __builtin_nontemporal_store(b[v] + a[v], y4 + ((pb + v * 256) >> 2));
+    return;
+  }
+#pragma unroll
+  for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int p = pb + v * 256 + c;
+      if (p < len) y[start + p] = y[start + p] + x[start + p];
+    }
+}
+
+hipError_t launch_add(const float* x, float* y, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  k_add<<<blocks_for(n, kTile), kThreads, 0, st>>>(x, y, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(float* dense, int64_t a, int64_t b, hipStream_t st) {
   if (b <= a) return hipSuccess;
   const int64_t want = (b - a + kThreads - 1) / kThreads;

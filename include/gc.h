@@ -350,6 +350,12 @@ int gc_plan_timing(gc_plan* plan, double* ms /* host */, int64_t* launches /* ho
  * 16-byte loads and stores (n a multiple of 4, both pointers 16-byte aligned). */
 int gc_copy_f32(const float* src, float* dst, int64_t n, void* stream);
 
+/* Reference streaming kernel for the error-feedback pass's memory pattern: y[i] = fl(y[i] +
+ * x[i]) for n floats (two reads, one write per element) with the pass's tile layout and
+ * non-temporal 16-byte loads and stores, and none of its selection work.  Both pointers
+ * 16-byte aligned; x and y must not overlap.  Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP. */
+int gc_add_f32(const float* x, float* y, int64_t n, void* stream);
+
 /* Static text for a status code. */
 const char* gc_status_string(int status);
 

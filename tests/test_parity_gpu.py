@@ -409,3 +409,21 @@ def test_cold_plan_starts_from_a_sampled_threshold():
             assert_bitwise(vals[ka:kb], hv, f"cold call {t} seg {s} vals")
             assert_bitwise(e[a:b], host[s], f"cold call {t} seg {s} residual")
     plan.close()
+
+
+def test_calibration_kernels_match_torch():
+    """The bandwidth references the bench reports: the copy and the y += x stream give the
+    bytes torch's own copy and fp32 add give (whole tiles and a ragged tail)."""
+    n = 8192 * 37 + 12
+    rng = np.random.default_rng(31)
+    x = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
+    y0 = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
+    y = y0.clone()
+    gca.add_f32(x, y)
+    dst = torch.empty_like(x)
+    gca.copy_f32(x, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), torch.add(y0, x).view(torch.int32))
+    assert torch.equal(dst.view(torch.int32), x.view(torch.int32))
+    with pytest.raises(gca.GCError):          # x and y overlap
+        gca.add_f32(y[:100], y[52:152])
