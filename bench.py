@@ -138,17 +138,28 @@ def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
     cold_ms = cold[0].elapsed_time(cold[1]) if warmup > 0 else None
     plan.timing()                       # drop the warm-up events
     plan.set_timing(True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event after every step: the total is first to last, the median comes from the gaps
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    start.record()
-    for t in range(warmup, warmup + steps):
+    marks[0].record()
+    for j, t in enumerate(range(warmup, warmup + steps)):
         step(t)
-    stop.record()
+        marks[j + 1].record()
     torch.cuda.synchronize()
     plan.set_timing(False)
-    total_ms = start.elapsed_time(stop)
+    total_ms = marks[0].elapsed_time(marks[-1])
+    per_step = [marks[j].elapsed_time(marks[j + 1]) for j in range(steps)]
+    time_steps.median_ms = float(np.median(per_step)) if per_step else None
     k1_ms, launches = plan.timing()
     return total_ms / steps, k1_ms / max(launches, 1), launches, cold_ms
+
+
+def gradient_fingerprint(g, n_max=1 << 24):
+    """SHA-256 (first 16 hex digits) of the first min(N, 2^24) fp32 gradient elements of the
+    first timed buffer: a record of the synthetic bytes (they depend on the generator's
+    library, so they are recorded rather than predicted)."""
+    import hashlib
+    return hashlib.sha256(g[:n_max].cpu().numpy().tobytes()).hexdigest()[:16]
 
 
 def setup(wl, n_gbufs=4, codec="topk"):
@@ -507,6 +518,8 @@ def main():
         "elements_per_s": round(wl.n / ms * 1e3, 1),
         # the plan's first call (no threshold estimate yet; warm-up, not in the timed steps)
         "first_call_ms": round(cold_ms, 4) if cold_ms is not None else None,
+        "median_ms_per_step": round(time_steps.median_ms, 4) if time_steps.median_ms else None,
+        "gradient_sha256_16": gradient_fingerprint(gbufs[0]),
         "effective_GBps": round(eff, 1),
         "hbm_peak_frac_effective": round(eff / HBM_PEAK_GBPS, 4),
         "candidates_per_k": round(float(st["candidates"].sum()) / max(plan.total_k, 1), 3),

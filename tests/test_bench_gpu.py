@@ -39,3 +39,6 @@ def test_bench_json_line(codec):
         assert key in cb, key
     assert cb["kind"] == "oracle" and cb["cores"] >= 1
     assert cb["parity_with_gpu_on_sample"] is True
+    # the median of the timed steps and the record of the synthetic gradient's bytes
+    assert d["median_ms_per_step"] > 0
+    assert len(d["gradient_sha256_16"]) == 16
