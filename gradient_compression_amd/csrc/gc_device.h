@@ -227,28 +227,43 @@ __device__ __forceinline__ void load_tile(const S* __restrict__ base, int len, V
   }
 }
 
+// The Random-k keys of the four elements from global index g0: word (gi % 4) of the
+// Philox4x32-10 block keyed (seed lo, seed hi) at counter (gi / 4 lo, gi / 4 hi, step lo, 0x53),
+// shifted right by one (31 bits).  The four share one block when g0 is a multiple of 4.
+__device__ __forceinline__ void rand_key4(const DevPlan& P, int64_t g0, uint32_t (&k)[4]) {
+  const uint64_t b0 = (uint64_t)g0 >> 2;
+  uint32_t w[4], w2[4];
+  philox4((uint32_t)b0, (uint32_t)(b0 >> 32), P.step_lo, 0x53u, P.seed_lo, P.seed_hi, w);
+  if ((g0 & 3) == 0) {   // the four elements are the block's four words
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k[c] = w[c] >> 1;
+    return;
+  }
+  philox4((uint32_t)(b0 + 1), (uint32_t)((b0 + 1) >> 32), P.step_lo, 0x53u, P.seed_lo,
+          P.seed_hi, w2);
+  // element c is word (g0 % 4) + c of the two blocks, selected with constant indices only so
+  // that w and w2 stay in registers
+  const int a = (int)(g0 & 3);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int j = a + c;
+    const uint32_t word = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : j == 3 ? w[3]
+                        : j == 4 ? w2[0] : j == 5 ? w2[1] : w2[2];
+    k[c] = word >> 1;
+  }
+}
+
 // Random-k keys of the len (<= kTile) elements from global index start, in the tile layout,
-// as float bit patterns: word (gi % 4) of the Philox4x32-10 block keyed (seed lo, seed hi) at
-// counter (gi / 4 lo, gi / 4 hi, step lo, 0x53), shifted right by one (31 bits).  A lane's
-// four elements share one block when start is a multiple of 4.  Lanes past len get key 0.
+// as float bit patterns (rand_key4 per slot).  Lanes past len get key 0.
 __device__ __forceinline__ void rand_key_tile(const DevPlan& P, int64_t start, int len,
                                               f4 (&x)[kSlots]) {
   const int pb = slot_base();
 #pragma unroll
   for (int v = 0; v < kSlots; ++v) {
-    const int64_t g0 = start + pb + v * 256;
-    const uint64_t b0 = (uint64_t)g0 >> 2;
-    uint32_t w[4], w2[4] = {0u, 0u, 0u, 0u};
-    philox4((uint32_t)b0, (uint32_t)(b0 >> 32), P.step_lo, 0x53u, P.seed_lo, P.seed_hi, w);
-    if (g0 & 3)
-      philox4((uint32_t)(b0 + 1), (uint32_t)((b0 + 1) >> 32), P.step_lo, 0x53u, P.seed_lo,
-              P.seed_hi, w2);
+    uint32_t k[4];
+    rand_key4(P, start + pb + v * 256, k);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = (int)(g0 & 3) + c;   // position of element c from the first block
-      const uint32_t word = j < 4 ? w[j] : w2[j - 4];
-      x[v][c] = pb + v * 256 + c < len ? __uint_as_float(word >> 1) : 0.0f;
-    }
+    for (int c = 0; c < 4; ++c) x[v][c] = pb + v * 256 + c < len ? __uint_as_float(k[c]) : 0.0f;
   }
 }
 

@@ -1054,11 +1054,94 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
       ef_add_tile<kMomentum>(g, gf, e, u, m, start, len, acc);
     } else if (kMomentum) {
       momentum_tile(g, gf, u, m, start, len);
-    }  // neither: nothing to stream, g is read at the kept positions only
+    }  // neither is served by k_randk_keys (nothing to stream; g is read at the kept positions)
     if (thr != kNoCapture) rand_key_tile(P, start, len, key);
   }
   if (thr == kNoCapture) return;  // uniform
   capture_tile(P, s, t, start, len, key, thr, s_w, &s_base);
+}
+
+// Random-k without error feedback or momentum reads nothing in its pass: it only draws keys
+// and captures the ones at or above the threshold, as k_randk_capture does, with the same
+// runs and order.  With no memory stream to hide behind, the workgroup-wide ranks and barriers
+// of the tile layout dominate, so here one wave owns a whole tile: slot v (0 .. kTile/256 - 1) of lane l
+// holds the 4 elements from v * 256 + l * 4 (index order is slot, lane, element), the wave
+// counts its keys, reserves the tile's run with one atomic and writes the candidates, with
+// ballots and no LDS or barriers.  kRkWaves waves per workgroup, one tile each.
+constexpr int kRkWaves = 4;
+constexpr int kRkSlots = kTile / 256;
+static_assert(kRkSlots % 8 == 0, "a tile must hold whole words of eight 256-element slots");
+
+__global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kRkWaves + (threadIdx.x >> 6);
+  if (t >= P.n_tiles) return;   // wave-uniform
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const uint32_t thr = P.thr[s];
+  if (thr == kNoCapture) return;   // this segment takes the exact fallback
+  // count: one nibble of flags per slot, eight slots per word (the word loop is unrolled so
+  // that pk stays in registers)
+  uint32_t pk[kRkSlots / 8];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int wi = 0; wi < kRkSlots / 8; ++wi) {
+    uint32_t word = 0;
+    for (int j = 0; j < 8; ++j) {
+      const int p0 = (wi * 8 + j) * 256 + lane * 4;
+      uint32_t k[4];
+      rand_key4(P, start + p0, k);
+      uint32_t nib = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) nib |= (p0 + c < len && k[c] >= thr) ? (1u << c) : 0u;
+      word |= nib << (4 * j);
+    }
+    pk[wi] = word;
+    cnt += __popc(word);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d, 64);
+  uint32_t base = 0;
+  if (lane == 0) {
+    base = cnt ? atomicAdd(&P.cand_cnt[s], cnt) : 0u;
+    P.run_off[t] = base;
+    P.run_cnt[t] = cnt;
+  }
+  if (cnt == 0) return;   // wave-uniform
+  base = __shfl(base, 0, 64);
+  const uint32_t cap = P.cand_cap[s];
+  float* cv = P.cand_val + P.cand_base[s];
+  int32_t* ci = P.cand_idx + P.cand_base[s];
+  const int32_t lstart = (int32_t)(start - P.seg_off[s]);
+  uint32_t run = 0;   // candidates of the wave's earlier slots
+#pragma unroll
+  for (int wi = 0; wi < kRkSlots / 8; ++wi) {
+    const uint32_t word = pk[wi];
+    if (!__ballot(word != 0)) continue;   // uniform
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t nib = (word >> (4 * j)) & 0xFu;
+      if (!__ballot(nib != 0)) continue;   // uniform
+      const uint64_t m0 = __ballot(nib & 1u), m1 = __ballot(nib & 2u);
+      const uint64_t m2 = __ballot(nib & 4u), m3 = __ballot(nib & 8u);
+      uint32_t q = base + run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) +
+                   lanes_below(m3);
+      run += __popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3);
+      if (!nib) continue;
+      const int p0 = (wi * 8 + j) * 256 + lane * 4;
+      uint32_t k[4];
+      rand_key4(P, start + p0, k);   // drawn again: only the slots that keep something
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((nib >> c) & 1u) {
+          if (q < cap) {
+            cv[q] = __uint_as_float(k[c]);
+            ci[q] = lstart + p0 + c;
+          }
+          ++q;
+        }
+    }
+  }
 }
 
 // Threshold call: slots past the segment's kept entries get value +0 and index -1.
@@ -1196,12 +1279,12 @@ hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, fl
       else if (e) k_randk_capture<false, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
       else if (u) k_randk_capture<true, false, true><<<nt, kThreads, 0, st>>>(Q, g, nullptr, u, m);
       // neither: the capture reads no g (the emit applies the scale to the gathered values)
-      else k_randk_capture<false, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, nullptr, m);
+      else k_randk_keys<<<blocks_for(P.n_tiles, kRkWaves), kRkWaves * 64, 0, st>>>(Q);
     } else {
       if (e && u) k_randk_capture<true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
       else if (e) k_randk_capture<false, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
       else if (u) k_randk_capture<true, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, u, m);
-      else k_randk_capture<false, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, nullptr, m);
+      else k_randk_keys<<<blocks_for(P.n_tiles, kRkWaves), kRkWaves * 64, 0, st>>>(Q);
     }
   }
   if (ev_end) (void)hipEventRecord(ev_end, st);
