@@ -75,6 +75,15 @@ def test_max_segment_randk_and_threshold():
     torch.cuda.synchronize()
     _check_sparse(acc, e, vals, idx, k, topk=False)
     log("[max] Random-k checked")
+    # without feedback (the keys-only kernel): the same mask, the values scaled by fl32(n / k)
+    vals2 = torch.empty(k, device="cuda")
+    idx2 = torch.empty(k, dtype=torch.int32, device="cuda")
+    plan.randk_compress(g, vals2, idx2, seed=3, step=0)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx), "mask without feedback"
+    scale = float(np.float32(N / k))
+    assert torch.equal(vals2.view(torch.int32), torch.mul(g[idx2.long()], scale).view(torch.int32))
+    log("[max] Random-k without feedback checked")
     # threshold on the same g: e now holds g outside the Random-k mask, so acc is about 2g;
     # |acc| >= 9 keeps about 7e-6 of the segment (~15k entries), below the cap
     acc = torch.add(e, g)
