@@ -1,6 +1,7 @@
 // gc_scatter.hip -- gfx950 kernels over the compressed payloads: the int8 stage of kept
 // values (per-segment absmax, Philox stochastic rounding, quantisation error fed back),
-// decompression into a dense buffer, and the reference copy used to calibrate bandwidth.
+// decompression into a dense buffer, and the reference copy and y += x streams used to
+// calibrate bandwidth.
 #include "gc_device.h"
 
 #pragma clang fp contract(off)
@@ -99,29 +100,6 @@ __global__ __launch_bounds__(kThreads) void k_copy(const f4* __restrict__ src,
   }
 }
 
-}  // namespace
-
-hipError_t launch_quant(const OutPlan& O, const float* vals, const int32_t* idx, float* e,
-                        uint64_t seed, uint64_t step, int8_t* codes, float* scales,
-                        hipStream_t st) {
-  if (O.n_seg == 0) return hipSuccess;
-  k_absmax<<<O.n_seg, 1024, 0, st>>>(O, vals, scales);
-  if (O.n_out_chunks > 0)
-    k_quant<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(
-        O, vals, idx, e, (uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)step, codes, scales);
-  return hipGetLastError();
-}
-
-hipError_t launch_decompress(const OutPlan& O, const float* vals, const int8_t* codes,
-                             const float* scales, const int32_t* idx, float* dense,
-                             int accumulate, hipStream_t st) {
-  if (O.n_seg == 0) return hipSuccess;
-  if (O.n_out_chunks > 0)
-    k_scatter_out<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(O, vals, codes, scales, idx,
-                                                                 dense, accumulate);
-  return hipGetLastError();
-}
-
 // ------------------------------------------------------------------------------ add
 // y = fl(y + x) with the streaming pass's memory pattern and none of its other work: the same
 // tile layout, non-temporal dwordx4 loads of both inputs and a non-temporal store of y.  Its
@@ -152,6 +130,29 @@ __global__ __launch_bounds__(kThreads) void k_add(const float* __restrict__ x,
       const int p = pb + v * 256 + c;
       if (p < len) y[start + p] = y[start + p] + x[start + p];
     }
+}
+
+}  // namespace
+
+hipError_t launch_quant(const OutPlan& O, const float* vals, const int32_t* idx, float* e,
+                        uint64_t seed, uint64_t step, int8_t* codes, float* scales,
+                        hipStream_t st) {
+  if (O.n_seg == 0) return hipSuccess;
+  k_absmax<<<O.n_seg, 1024, 0, st>>>(O, vals, scales);
+  if (O.n_out_chunks > 0)
+    k_quant<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(
+        O, vals, idx, e, (uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)step, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_decompress(const OutPlan& O, const float* vals, const int8_t* codes,
+                             const float* scales, const int32_t* idx, float* dense,
+                             int accumulate, hipStream_t st) {
+  if (O.n_seg == 0) return hipSuccess;
+  if (O.n_out_chunks > 0)
+    k_scatter_out<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(O, vals, codes, scales, idx,
+                                                                 dense, accumulate);
+  return hipGetLastError();
 }
 
 hipError_t launch_add(const float* x, float* y, int64_t n, hipStream_t st) {
