@@ -467,7 +467,7 @@ def receiver_bench(wl, n_workers=8, reps=5):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). Compression is worker-local; run one process per GPU.",
               file=sys.stderr)
         sys.exit(2)

@@ -52,7 +52,7 @@ typedef enum {
     GC_ERR_INVALID_ARG = -1,   /* a bad argument; nothing was launched */
     GC_ERR_OOM = -2,           /* device memory for the plan could not be allocated */
     GC_ERR_HIP = -3,           /* the HIP runtime reported an error (no device, launch failure) */
-    GC_ERR_UNSUPPORTED = -4    /* a valid request this build does not handle */
+    GC_ERR_UNSUPPORTED = -4    /* a valid request the library does not handle */
 } gc_status;
 
 /* Plan flags. */
