@@ -229,12 +229,14 @@ __device__ __forceinline__ void load_tile(const S* __restrict__ base, int len, V
 
 // The Random-k keys of the four elements from global index g0: word (gi % 4) of the
 // Philox4x32-10 block keyed (seed lo, seed hi) at counter (gi / 4 lo, gi / 4 hi, step lo, 0x53),
-// shifted right by one (31 bits).  The four share one block when g0 is a multiple of 4.
+// shifted right by one (31 bits).  The four share one block when g0 is a multiple of 4
+// (kAligned: the caller knows that it is).
+template <bool kAligned = false>
 __device__ __forceinline__ void rand_key4(const DevPlan& P, int64_t g0, uint32_t (&k)[4]) {
   const uint64_t b0 = (uint64_t)g0 >> 2;
   uint32_t w[4], w2[4];
   philox4((uint32_t)b0, (uint32_t)(b0 >> 32), P.step_lo, 0x53u, P.seed_lo, P.seed_hi, w);
-  if ((g0 & 3) == 0) {   // the four elements are the block's four words
+  if (kAligned || (g0 & 3) == 0) {   // the four elements are the block's four words
 #pragma unroll
     for (int c = 0; c < 4; ++c) k[c] = w[c] >> 1;
     return;

@@ -1064,57 +1064,73 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
 // Random-k without error feedback or momentum reads nothing in its pass: it only draws keys
 // and captures the ones at or above the threshold, as k_randk_capture does, with the same
 // runs and order.  With no memory stream to hide behind, the workgroup-wide ranks and barriers
-// of the tile layout dominate, so here one wave owns a whole tile: slot v (0 .. kTile/256 - 1) of lane l
-// holds the 4 elements from v * 256 + l * 4 (index order is slot, lane, element), the wave
-// counts its keys, reserves the tile's run with one atomic and writes the candidates, with
-// ballots and no LDS or barriers.  kRkWaves waves per workgroup, one tile each.
+// of the tile layout dominate, so here one wave owns a whole tile: slot v (0 .. kTile/256 - 1)
+// of lane l holds the 4 elements from v * 256 + l * 4 (index order is slot, lane, element).
+// The wave draws its keys slot by slot, ranks the flagged ones with ballots as it goes and
+// stages the first kRkStage of them (key, tile offset) in its own LDS rows; then it reserves
+// the tile's run with one atomic and copies the staged entries out.  Entries past the staging
+// rows (dense segments) are drawn again from the per-slot flags.  No barrier anywhere.
 constexpr int kRkWaves = 4;
 constexpr int kRkSlots = kTile / 256;
+constexpr int kRkStage = 256;
 static_assert(kRkSlots % 8 == 0, "a tile must hold whole words of eight 256-element slots");
 
-__global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kRkWaves + (threadIdx.x >> 6);
-  if (t >= P.n_tiles) return;   // wave-uniform
-  const int4 desc = P.tile_desc[t];
-  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
-  const int len = desc.z, s = desc.w;
-  const uint32_t thr = P.thr[s];
-  if (thr == kNoCapture) return;   // this segment takes the exact fallback
-  // count: one nibble of flags per slot, eight slots per word (the word loop is unrolled so
-  // that pk stays in registers)
-  uint32_t pk[kRkSlots / 8];
-  uint32_t cnt = 0;
+template <bool kAligned>
+__device__ __forceinline__ void rk_tile(const DevPlan& P, int64_t t, int64_t start, int len,
+                                        int s, uint32_t thr, int lane, uint32_t* sk,
+                                        int32_t* si) {
+  uint32_t pk[kRkSlots / 8];   // flags, one nibble per slot (the word loop is unrolled)
+  uint32_t cnt = 0;            // wave-uniform: flagged entries so far
 #pragma unroll
   for (int wi = 0; wi < kRkSlots / 8; ++wi) {
     uint32_t word = 0;
     for (int j = 0; j < 8; ++j) {
       const int p0 = (wi * 8 + j) * 256 + lane * 4;
       uint32_t k[4];
-      rand_key4(P, start + p0, k);
+      rand_key4<kAligned>(P, start + p0, k);
       uint32_t nib = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) nib |= (p0 + c < len && k[c] >= thr) ? (1u << c) : 0u;
       word |= nib << (4 * j);
+      if (!__ballot(nib != 0)) continue;   // uniform
+      const uint64_t m0 = __ballot(nib & 1u), m1 = __ballot(nib & 2u);
+      const uint64_t m2 = __ballot(nib & 4u), m3 = __ballot(nib & 8u);
+      uint32_t r = cnt + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+      cnt += __popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((nib >> c) & 1u) {
+          if (r < (uint32_t)kRkStage) {
+            sk[r] = k[c];
+            si[r] = p0 + c;
+          }
+          ++r;
+        }
     }
     pk[wi] = word;
-    cnt += __popc(word);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d, 64);
   uint32_t base = 0;
   if (lane == 0) {
     base = cnt ? atomicAdd(&P.cand_cnt[s], cnt) : 0u;
     P.run_off[t] = base;
     P.run_cnt[t] = cnt;
   }
-  if (cnt == 0) return;   // wave-uniform
+  if (cnt == 0) return;   // uniform
   base = __shfl(base, 0, 64);
   const uint32_t cap = P.cand_cap[s];
   float* cv = P.cand_val + P.cand_base[s];
   int32_t* ci = P.cand_idx + P.cand_base[s];
   const int32_t lstart = (int32_t)(start - P.seg_off[s]);
-  uint32_t run = 0;   // candidates of the wave's earlier slots
+  const uint32_t staged = min(cnt, (uint32_t)kRkStage);
+  for (uint32_t i = lane; i < staged; i += 64) {   // the wave's own LDS rows, written above
+    const uint32_t q = base + i;
+    if (q < cap) {
+      cv[q] = __uint_as_float(sk[i]);
+      ci[q] = lstart + si[i];
+    }
+  }
+  if (cnt <= (uint32_t)kRkStage) return;   // uniform
+  uint32_t run = 0;   // ranks past the staging rows: draw those keys again
 #pragma unroll
   for (int wi = 0; wi < kRkSlots / 8; ++wi) {
     const uint32_t word = pk[wi];
@@ -1124,24 +1140,41 @@ __global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
       if (!__ballot(nib != 0)) continue;   // uniform
       const uint64_t m0 = __ballot(nib & 1u), m1 = __ballot(nib & 2u);
       const uint64_t m2 = __ballot(nib & 4u), m3 = __ballot(nib & 8u);
-      uint32_t q = base + run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) +
-                   lanes_below(m3);
+      uint32_t r = run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
       run += __popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3);
-      if (!nib) continue;
+      if (!nib || r + (uint32_t)__popc(nib) <= (uint32_t)kRkStage) continue;
       const int p0 = (wi * 8 + j) * 256 + lane * 4;
       uint32_t k[4];
-      rand_key4(P, start + p0, k);   // drawn again: only the slots that keep something
+      rand_key4<kAligned>(P, start + p0, k);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         if ((nib >> c) & 1u) {
-          if (q < cap) {
+          const uint32_t q = base + r;
+          if (r >= (uint32_t)kRkStage && q < cap) {
             cv[q] = __uint_as_float(k[c]);
             ci[q] = lstart + p0 + c;
           }
-          ++q;
+          ++r;
         }
     }
   }
+}
+
+__global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
+  __shared__ uint32_t s_key[kRkWaves][kRkStage];
+  __shared__ int32_t s_idx[kRkWaves][kRkStage];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * kRkWaves + w;
+  if (t >= P.n_tiles) return;   // wave-uniform
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const uint32_t thr = P.thr[s];
+  if (thr == kNoCapture) return;   // this segment takes the exact fallback
+  if ((start & 3) == 0)   // wave-uniform: every lane's four elements share one Philox block
+    rk_tile<true>(P, t, start, len, s, thr, lane, s_key[w], s_idx[w]);
+  else
+    rk_tile<false>(P, t, start, len, s, thr, lane, s_key[w], s_idx[w]);
 }
 
 // Threshold call: slots past the segment's kept entries get value +0 and index -1.
