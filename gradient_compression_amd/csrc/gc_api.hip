@@ -29,8 +29,6 @@ constexpr int64_t kSmallSegment = 65536;
 // Candidate capacity of a larger segment, in multiples of its k (at least kMinCapacity).
 constexpr int64_t kCapacityFactor = 16;
 constexpr int64_t kMinCapacity = 65536;
-// First margin of the threshold estimate (next threshold = beta * |k-th largest|).
-constexpr float kInitialBeta = 0.9f;
 // Tiles per segment that the cold-start sample reads (about 0.5M elements).
 constexpr int64_t kSampleTiles = 64;
 
@@ -344,7 +342,7 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   cv.add(&d.thr_call, n_seg);
   cv.add(&d_thr_rand, n_seg);
   cv.add(&d_rk_scale, n_seg);
-  const std::vector<float> beta_init(n_seg, kInitialBeta);
+  const std::vector<float> beta_init(n_seg, gc::kInitialBeta);
   const std::vector<uint32_t> no_estimate(n_seg, gc::kNoCapture);
   if (hipMalloc(&p->mem, cv.total()) != hipSuccess) {
     (void)hipGetLastError();

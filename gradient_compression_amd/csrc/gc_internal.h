@@ -42,6 +42,9 @@ namespace gc {
 #ifndef GC_BETA_MAX         // largest margin: next threshold <= GC_BETA_MAX * |k-th key|
 #define GC_BETA_MAX 0.98f
 #endif
+// First margin of the threshold estimate (next threshold = beta * |k-th largest|), on a fresh
+// plan and after an estimate reset.
+constexpr float kInitialBeta = 0.9f;
 #ifndef GC_XCD_REMAP        // streaming pass: contiguous tile ranges per XCD
 #define GC_XCD_REMAP 0
 #endif

@@ -47,9 +47,11 @@ __global__ __launch_bounds__(kThreads) void k_prep(DevPlan P) {
 
 __global__ __launch_bounds__(kThreads) void k_reset(DevPlan P) {
   const int s = blockIdx.x * kThreads + threadIdx.x;
-  if (s < P.n_seg) {
+  if (s < P.n_seg) {   // as on a fresh plan: no estimate, first margins
     P.thr[s] = P.thr_init[s];
     P.thr_est[s] = kNoCapture;
+    P.beta[s] = kInitialBeta;
+    P.beta_est[s] = kInitialBeta;
   }
 }
 
@@ -950,8 +952,9 @@ __global__ __launch_bounds__(kThreads) void k_sample_decide(DevPlan P) {
 
 // ----------------------------------------------------------------------------- finalize
 // Threshold for the next call: beta * |kth|, where the margin beta follows the last calls:
-// lowered after too few candidates, raised after an overflow or far more than needed.  beta
-// may exceed 1: while the residual still grows, the next k-th key lies above the last one.
+// lowered after too few candidates, raised after an overflow or far more than needed, and
+// kept in [0.25, GC_BETA_MAX]; a cap near 1 suits a residual that still grows, whose next
+// k-th key lies above the last one.
 // Segments that capture everything (small) or nothing (k = 0) keep their setting.
 __global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
   const int s = blockIdx.x * kThreads + threadIdx.x;

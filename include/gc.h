@@ -30,7 +30,9 @@
  *   - NaN inputs are outside the contract.
  *
  * All pointers are device pointers unless marked "host".  Calls are asynchronous on
- * `stream` (a hipStream_t; NULL = the default stream): arguments are checked on the host
+ * `stream`, a hipStream_t passed as void* (NULL = the default stream).  The signatures take
+ * void* so that this header needs no HIP include and callers that only hold an opaque
+ * handle (ctypes, torch's stream pointer) pass it unchanged: arguments are checked on the host
  * before anything is launched, and errors of the launched work surface at the caller's
  * next synchronisation.  No call allocates device memory except gc_plan_create.  A plan
  * serves one stream at a time; calls on one plan must not overlap.  The buffers of one call
@@ -162,11 +164,21 @@ int gc_topk_ef_compress_int8(gc_plan* plan, const float* g, float* e, float* u, 
                              int8_t* out_codes, float* out_scales, void* stream);
 
 /*
+ * The receiver's step: rebuild the sparse update from a payload of (value, index) pairs
+ * ("Communication Optimization > Gradient Compression", Top-K section, wire-format
+ * paragraph: each kept entry travels as its value and its position; "Gradient Compression"
+ * memory-compression glossary, systems section: the values and indices that workers exchange
+ * are what the receiver adds up; an int8 payload is dequantised with the per-segment scale
+ * that travels alongside it, layer-wise scaling paragraph).
  * Scatter kept entries back into a dense float[N] buffer: dense[seg_off[s] + idx] = v, with
  * v = vals[j] when vals is given, else fl(codes[j] * scales[s]).  accumulate = 0 first sets
- * dense to +0 over [seg_off[0], N); accumulate != 0 adds v instead of storing it.
+ * dense to +0 over [seg_off[0], N); accumulate != 0 adds v instead of storing it.  Entries
+ * with index -1 (the padding of a threshold call) are skipped.
+ *   vals  : float[total_k] in the plan's layout (out_off), or NULL when codes are given.
+ *   codes : int8[total_k], or NULL; scales : float[n_seg] (with codes).
+ *   idx   : int32[total_k] segment-local indices; dense : float[N], owned by the caller.
  * Exactly one of vals and codes must be non-NULL (scales with codes).
- * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP.
+ * Errors: GC_ERR_INVALID_ARG (nothing launched), GC_ERR_HIP.
  */
 int gc_decompress(const gc_plan* plan, const float* vals, const int8_t* codes,
                   const float* scales, const int32_t* idx, float* dense, int accumulate,
@@ -226,8 +238,9 @@ int gc_qsgd_decompress(const gc_plan* plan, const int8_t* codes, const float* no
 
 /*
  * Threshold sparsification with error feedback (genomic-FL glossary, sparsification section:
- * entries below a fixed or adaptive magnitude threshold are dropped; "Gradient
- * Sparsification" glossary, mechanism section: the threshold may change per layer and step).
+ * an entry is sent only if its magnitude reaches a threshold, which may be fixed or may
+ * adapt; "Gradient Sparsification" glossary, mechanism section: the threshold may change
+ * per layer and step).
  * Per segment, after the same momentum and EF add as gc_topk_ef_compress, the entries with
  * |acc| >= |tau_s| are kept, at most k_s of them (the plan's k is the cap): when more reach
  * the threshold, the k_s largest by (|acc| descending, index ascending).

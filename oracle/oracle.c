@@ -160,8 +160,9 @@ int orc_topk_ef_segment(int64_t n, int64_t k, const float* g, float* e, float* u
 
 /*
  * Threshold sparsification with error feedback (genomic-FL glossary, sparsification section:
- * entries below a fixed or adaptive magnitude threshold are dropped; "Gradient
- * Sparsification" glossary, mechanism section: a dynamic threshold per layer).  One segment:
+ * an entry is sent only if its magnitude reaches a threshold, which may be fixed or may
+ * adapt; "Gradient Sparsification" glossary, mechanism section: a dynamic threshold per
+ * layer).  One segment:
  * after the same momentum and EF add, the entries with |acc| >= |tau| are sent, at most
  * k_cap of them -- the k_cap largest by (|acc| descending, position ascending) when more
  * reach the threshold.  Writes *count (the number sent, <= k_cap) and that many outputs in

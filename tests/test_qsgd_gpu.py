@@ -1,8 +1,8 @@
 """GPU parity of the QSGD codec (C ABI) against the CPU oracle.
 
 Codes are compared bit for bit whenever the segment's norm matches the oracle's; the norm
-(a double sum of squares in an unspecified order, rounded once) must be within one ulp, and
-when it differs by that ulp the oracle continues from the GPU's state.
+(a double sum of squares in an unspecified order, rounded once) must be within one ulp by definition,
+and the tests require it to be equal (a one-ulp difference would be a one-in-a-million event).
 """
 import numpy as np
 import pytest
@@ -55,6 +55,10 @@ def run_qsgd(sizes, grads, levels, ef=True, momentum=None, seed=3, label=""):
         if u_h is not None:
             assert_bitwise(u_d, u_h, f"{label} it{t} velocity")
     plan.close()
+    # One ulp is allowed by the definition, but the two double sums differ by about 1e-13
+    # relative, so a norm on the other side of an fp32 rounding boundary has odds near 1e-6
+    # per segment: any difference is treated as a failure, so that a drift cannot hide.
+    assert mism == 0, f"{label}: {mism} norms differed from the oracle's by one ulp"
     return mism
 
 
@@ -143,10 +147,8 @@ def test_qsgd_full_size_bert_large():
             a, b = int(off[s]), int(off[s + 1])
             hc, hn = oracle.qsgd_segment(g[a:b].cpu().numpy(), host[s], levels=127, seed=9, step=t,
                                          seg_base=a)
-            if nn[s] == hn:
-                assert_bitwise(codes[a:b], hc, f"seg{s} codes")
-                assert_bitwise(e[a:b], host[s], f"seg{s} residual")
-            else:
-                host[s][:] = e[a:b].cpu().numpy()
+            assert nn[s] == hn, f"seg{s} norm differs from the oracle's by one ulp"
+            assert_bitwise(codes[a:b], hc, f"seg{s} codes")
+            assert_bitwise(e[a:b], host[s], f"seg{s} residual")
         del e_prev
     plan.close()

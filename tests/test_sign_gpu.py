@@ -58,6 +58,11 @@ def run_sign(sizes, grads, momentum=None, label=""):
         if u_h is not None:
             assert_bitwise(u_d, u_h, f"{label} it{t} velocity")
     plan.close()
+    # The definition allows one ulp on the scale (a double sum in an unspecified order,
+    # rounded once), but the two sums differ by about 1e-13 relative, so a scale that lands
+    # on the other side of an fp32 rounding boundary has odds near 1e-6 per segment: any
+    # resynchronisation here is treated as a failure, so that a drift cannot hide.
+    assert resynced == 0, f"{label}: {resynced} scales differed from the oracle's by one ulp"
     return resynced
 
 
@@ -146,9 +151,7 @@ def test_sign_full_size_llama2_7b():
             assert abs(float(sc[s]) - float(hs)) <= ulp(hs)
             assert_bitwise(bits[int(plan.word_off[s]):int(plan.word_off[s + 1])], hb.view(np.int32),
                            f"seg{s} bits")
-            if sc[s] == hs:
-                assert_bitwise(e[a:b], host[s], f"seg{s} residual")
-            else:
-                host[s][:] = e[a:b].cpu().numpy()
+            assert sc[s] == hs, f"seg{s} scale differs from the oracle's by one ulp"
+            assert_bitwise(e[a:b], host[s], f"seg{s} residual")
         del e_prev
     plan.close()
