@@ -14,11 +14,14 @@ measured for it (null once its code has changed since).
 cpu_baseline = the CPU oracle on a bounded sample of the same workload's segments.
 
 --codec selects the threshold, Random-k, sign or QSGD codec instead of Top-k (the same
-fields, their own pass bytes).  The default run also reports, as context: the same shape
-with momentum, the plan's first (cold) call, local gradient clipping, the receiver-side sum
-of eight workers' payloads, the copy kernel's bandwidth, and the bandwidth of a bare kernel
-with the pass's memory instructions (y += x: two reads, one write, the same tile layout and
-cache policy) and none of its selection work.
+fields, their own pass bytes).  The default run also reports, as context: every workload
+(`all_configs`: single 1M segment, ResNet-50, BERT-large, hybrid int8, the 7B shape with
+momentum, and the headline 7B plain step) with its step time, effective fraction of peak
+and streaming-pass time; the plan's first (cold) call; local gradient clipping; the
+receiver-side sum of eight workers' payloads; and three reference streams in the pass's tile
+layout (`reference_streams`: a pure read, a copy, and a bare y += x with the pass's memory
+instructions and none of its selection work).  They are measured references, not ceilings:
+the pass streams faster than the bare y += x.
 """
 from __future__ import annotations
 
@@ -86,7 +89,9 @@ def parse():
                          "|acc| >= tau_s (at most k_s) with error feedback; randk: Random-k "
                          "with error feedback")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-momentum-variant", action="store_true")
+    ap.add_argument("--no-all-configs", "--no-momentum-variant", dest="no_all_configs",
+                    action="store_true",
+                    help="skip the other workloads (timed in the default run as context)")
     ap.add_argument("--no-receiver", action="store_true",
                     help="skip the receiver-side sum of 8 workers' payloads (context figure)")
     return ap.parse_args()
@@ -197,7 +202,7 @@ def setup(wl, n_gbufs=4, codec="topk"):
     return plan, gbufs, e, u, (vals, idx, codes, scales)
 
 
-def copy_ceiling(n_bytes=8 << 30):
+def copy_stream(n_bytes=8 << 30):
     """Reference: the library's dwordx4 copy kernel, GB/s of read + write."""
     import torch
     import gradient_compression_amd as gca
@@ -218,7 +223,29 @@ def copy_ceiling(n_bytes=8 << 30):
     return 2 * n * 4 / ms / 1e6
 
 
-def bare_ef_add(n_bytes=8 << 30):
+def read_stream(n_bytes=16 << 30):
+    """Reference: a pure read stream in the pass's tile layout (non-temporal dwordx4 loads),
+    GB/s read."""
+    import torch
+    import gradient_compression_amd as gca
+    n = n_bytes // 4
+    x = torch.zeros(n, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        gca.read_f32(x, sink)
+    torch.cuda.synchronize()
+    s, t = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(10):
+        gca.read_f32(x, sink)
+    t.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(t) / 10
+    del x, sink
+    return n * 4 / ms / 1e6
+
+
+def add_stream(n_bytes=8 << 30):
     """Reference for the streaming pass: the library's y += x kernel (the pass's tile layout
     and non-temporal loads and stores, nothing else), GB/s of its two reads and one write."""
     import torch
@@ -244,29 +271,34 @@ def _ulp(x):
     return float(np.spacing(np.float32(abs(x))))
 
 
+def host_threads():
+    """The oracle's threads: the host cores this process may use, at most 16 (the CPU share
+    of one GPU on the machines this runs on)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
 def cpu_baseline(plan, wl, gbuf, e, u, outs, codec="topk", t=0):
-    """Time the CPU oracle for the codec on the segments from 1 on, up to a budget of
-    elements (250M for the sorting codecs, about one layer of the 7B shape; 1.2G for sign and
-    QSGD, about six), in a thread pool over segments; check it
-    against the GPU's output of the same step on the same state.  For sign and QSGD the
-    scale / norm is a double sum in an unspecified order (one ulp); their bits, codes and
-    residual are compared where the two agree."""
+    """Time the CPU oracle for the codec on a bounded sample of the workload's segments (from
+    segment 1 on, at least one per host thread and at least a budget of elements: 800M for
+    the sorting codecs, about four layers of the 7B shape, some 10 s on 16 threads; 3.2G for
+    sign and QSGD, which do not sort), in a thread pool over segments; check it against the
+    GPU's output of the same step on the same state.  For sign and QSGD the scale / norm is a
+    double sum in an unspecified order (one ulp); their bits, codes and residual are compared
+    where the two agree."""
     import concurrent.futures as cf
     import torch
     import oracle
     off = wl.offsets()
-    segs = list(range(1, wl.n_seg)) if wl.n_seg > 9 else [0]
-    # the sorting codecs take ~5 s on 250M elements; the streaming ones need ~5x more for
-    # the same order of CPU work
-    budget = 1_200_000_000 if codec in ("sign", "qsgd") else 250_000_000
+    segs = list(range(1, wl.n_seg)) if wl.n_seg > 9 else list(range(wl.n_seg))
+    threads = host_threads()
+    budget = 3_200_000_000 if codec in ("sign", "qsgd") else 800_000_000
     total = 0
     pick = []
     for s in segs:
-        n = int(off[s + 1] - off[s])
-        if total + n > budget and pick:
+        if len(pick) >= threads and total >= budget:
             break
         pick.append(s)
-        total += n
+        total += int(off[s + 1] - off[s])
     host = {}
     for s in pick:
         a, b = int(off[s]), int(off[s + 1])
@@ -281,7 +313,6 @@ def cpu_baseline(plan, wl, gbuf, e, u, outs, codec="topk", t=0):
         codec_run = codec
         run_step(plan, wl, codec, gbuf, e, u, outs, t)
     torch.cuda.synchronize()
-    threads = max(1, min(len(pick), len(os.sched_getaffinity(0)), 16))
     oracle.lib()
     m = wl.momentum or 0.0
 
@@ -340,9 +371,11 @@ def cpu_baseline(plan, wl, gbuf, e, u, outs, codec="topk", t=0):
         "value": round(4.0 * total / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
+        "host_affinity_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"one {what} on segments {pick[0]}..{pick[-1]} ({len(pick)} tensors, "
-                   f"{total} fp32 elements) of {wl.name}, {dt:.2f} s wall on {threads} threads"),
+                   f"{total} fp32 elements) of {wl.name}, {dt:.2f} s wall on {threads} threads "
+                   f"(the host cores this process may use, at most 16)"),
         "parity_with_gpu_on_sample": bool(ok),
     }
 
@@ -431,6 +464,52 @@ def randk_plain_bench(plan, wl, gbufs, outs, steps):
     return {"ms_per_step": round(ms, 4), "key_pass_ms": round(k1, 4),
             "G_keys_per_s": round(wl.n / k1 / 1e6, 1),
             "philox_blocks_per_s_G": round(blocks / k1 / 1e6, 1)}
+
+
+# Every other workload, timed in the same run as the headline step (steps per workload: at
+# least these, so that the short steps are timed over a few milliseconds).
+ALL_CONFIGS = {"c1_single_1m": 200, "c2_resnet50": 100, "c3_bert_large": 30,
+               "c4_hybrid_int8": 12, "c5_llama2_7b": 8}
+
+
+def config_record(wl, ms, pass_ms, median_ms, st, total_k, steps):
+    """Step and streaming-pass figures of one workload: effective bytes per element are 12
+    (read g, read e, write e), 20 with momentum (u read and written too)."""
+    bpe = bytes_per_element(wl)
+    rec = {"n_elements": wl.n, "segments": wl.n_seg, "k_ratio": wl.ratio,
+           "total_k": int(total_k), "momentum": wl.momentum, "int8": wl.int8,
+           "steps": steps, "ms_per_step": round(ms, 4),
+           "median_ms_per_step": round(median_ms, 4) if median_ms else None,
+           "GBps_gradient": round(4.0 * wl.n / ms / 1e6, 2),
+           "bytes_per_element": bpe,
+           "hbm_peak_frac_effective": round(bpe * wl.n / ms / 1e6 / HBM_PEAK_GBPS, 4),
+           "pass_ms": round(pass_ms, 4),
+           "pass_achieved_GBps": round(bpe * wl.n / pass_ms / 1e6, 1),
+           "pass_hbm_peak_frac": round(bpe * wl.n / pass_ms / 1e6 / HBM_PEAK_GBPS, 4),
+           "after_pass_ms": round(ms - pass_ms, 4),
+           "candidates_per_k": round(float(st["candidates"].sum()) / max(total_k, 1), 3)}
+    if wl.momentum is not None:   # also on the 12 B/elt basis of the metric
+        rec["hbm_peak_frac_effective_12B"] = round(12.0 * wl.n / ms / 1e6 / HBM_PEAK_GBPS, 4)
+    if wl.n * 12 < 512e6:
+        rec["note"] = "fits the 256 MB on-package cache: not an HBM measurement"
+    return rec
+
+
+def bench_config(name, steps, warmup):
+    """One workload's Top-k step (int8 fused for the hybrid one), on its own plan and
+    buffers, freed afterwards."""
+    import torch
+    from synth import workload
+    w = workload(name)
+    steps = max(steps, ALL_CONFIGS[name])
+    plan, gbufs, e, u, outs = setup(w)
+    ms, pass_ms, _, _ = time_steps(plan, w, gbufs, e, u, outs, steps, warmup)
+    rec = config_record(w, ms, pass_ms, time_steps.median_ms, plan.last_stats(), plan.total_k,
+                        steps)
+    plan.close()
+    del gbufs, e, u, outs
+    torch.cuda.empty_cache()
+    return rec
 
 
 def receiver_bench(wl, n_workers=8, reps=5):
@@ -572,31 +651,27 @@ def main():
     plan.close()
     torch.cuda.empty_cache()
     try:
-        result["copy_ceiling_GBps"] = round(copy_ceiling(), 1)
-        add = bare_ef_add()
-        result["bare_ef_add_GBps"] = round(add, 1)
-        if "roofline" in result:
+        add = add_stream()
+        result["reference_streams"] = {
+            "note": "measured streams in the pass's tile layout with non-temporal dwordx4 "
+                    "accesses; references, not ceilings (the pass streams faster than the "
+                    "bare 2-read/1-write kernel)",
+            "read_GBps": round(read_stream(), 1),
+            "copy_1r1w_GBps": round(copy_stream(), 1),
+            "add_2r1w_GBps": round(add, 1),
             # the pass against the same 2-read/1-write stream without its selection work
-            result["pass_vs_bare_ef_add"] = round(result["roofline"]["achieved"] / add, 4)
-    except Exception as ex:  # noqa: BLE001 - context figures only
-        log(f"[bench] stream ceilings skipped: {ex}")
-    if not args.no_momentum_variant and wl.name == DEFAULT_WORKLOAD:
-        # the same shape with momentum correction (u = 0.9 u + g), as the 7B workload states
-        wm = workload("c5_llama2_7b")
-        plan_m, gb_m, e_m, u_m, outs_m = setup(wm)
-        ms_m, k1m, _, _ = time_steps(plan_m, wm, gb_m, e_m, u_m, outs_m,
-                                     max(args.steps // 2, 3), args.warmup)
-        result["momentum_variant"] = {
-            "workload": wm.name, "ms_per_step": round(ms_m, 4),
-            "GBps_gradient": round(4.0 * wm.n / ms_m / 1e6, 2),
-            "hbm_peak_frac_12B": round(12.0 * wm.n / ms_m / 1e6 / HBM_PEAK_GBPS, 4),
-            "hbm_peak_frac_20B": round(20.0 * wm.n / ms_m / 1e6 / HBM_PEAK_GBPS, 4),
-            "ef_pass_ms": round(k1m, 4),
+            "pass_vs_add_2r1w": round(result["roofline"]["achieved"] / add, 4),
         }
-        log(f"[bench] momentum variant: {ms_m:.3f} ms/step")
-        plan_m.close()
-        del gb_m, e_m, u_m, outs_m
-        torch.cuda.empty_cache()
+    except Exception as ex:  # noqa: BLE001 - context figures only
+        log(f"[bench] reference streams skipped: {ex}")
+    if not args.no_all_configs and wl.name == DEFAULT_WORKLOAD:
+        result["all_configs"] = {DEFAULT_WORKLOAD: config_record(
+            wl, ms, k1_ms, time_steps.median_ms, st, plan.total_k, args.steps)}
+        for name in ALL_CONFIGS:
+            rec = bench_config(name, args.steps, args.warmup)
+            result["all_configs"][name] = rec
+            log(f"[bench] {name}: {rec['ms_per_step']:.4f} ms/step, "
+                f"{rec['hbm_peak_frac_effective']:.1%} effective, pass {rec['pass_ms']:.4f} ms")
     if not args.no_receiver and wl.name == DEFAULT_WORKLOAD:
         result["receiver_8_workers"] = receiver_bench(wl)
         log(f"[bench] receiver: {result['receiver_8_workers']['ms_scatter_add']:.3f} ms")

@@ -29,6 +29,7 @@ MODE_SKIP, MODE_CANDIDATES, MODE_FULL, MODE_RECAPTURED = 0, 1, 2, 3
 EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layout",
            "gc_topk_ef_compress", "gc_topk_ef_compress_int8", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
            "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32", "gc_add_f32",
+           "gc_read_f32",
            "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
            "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress",
            "gc_threshold_ef_compress", "gc_randk_compress", "gc_decompress_gathered",
@@ -77,6 +78,7 @@ def lib(variant: str | None = None) -> ctypes.CDLL:
         "gc_plan_timing": [vp, vp, vp],
         "gc_copy_f32": [vp, vp, i64, vp],
         "gc_add_f32": [vp, vp, i64, vp],
+        "gc_read_f32": [vp, i64, vp, vp],
         "gc_status_string": [ctypes.c_int],
         "gc_sign_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp],
         "gc_plan_sign_layout": [vp, vp],
@@ -422,14 +424,23 @@ def copy_f32(src, dst, stream=None):
 
 
 def add_f32(x, y, stream=None):
-    """y += x (fp32, in place) with the error-feedback pass's memory pattern: the practical
-    bandwidth ceiling of its two-read/one-write stream."""
+    """y += x (fp32, in place) with the error-feedback pass's memory pattern: a reference
+    two-read/one-write stream (not a ceiling: the pass streams faster than it)."""
     import torch
     n = x.numel()
     _check(lib().gc_add_f32(_dev_ptr(x, torch.float32, "x"), _dev_ptr(y, torch.float32, "y", n),
                             n, _stream(stream)), "gc_add_f32")
 
 
-__all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "add_f32", "layout", "EXPORTS",
+def read_f32(x, sink, stream=None):
+    """A pure read stream over x (the pass's tile layout and non-temporal loads); sink is a
+    device int32[64] that nothing is written to for real data."""
+    import torch
+    _check(lib().gc_read_f32(_dev_ptr(x, torch.float32, "x"), x.numel(),
+                             _dev_ptr(sink, torch.int32, "sink", 64), _stream(stream)),
+           "gc_read_f32")
+
+
+__all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "add_f32", "read_f32", "layout", "EXPORTS",
            "GC_MOMENTUM_MASK", "GC_DEBUG_FORCE_FALLBACK", "GC_DEBUG_NO_ESTIMATE", "MODE_SKIP",
            "MODE_CANDIDATES", "MODE_FULL", "MODE_RECAPTURED"]

@@ -18,8 +18,9 @@
 #include "gc_internal.h"
 
 namespace gc {
-// The calibration stream of gc_add_f32 (gc_scatter.hip).
+// The reference streams of gc_add_f32 and gc_read_f32 (gc_scatter.hip).
 hipError_t launch_add(const float* x, float* y, int64_t n, hipStream_t st);
+hipError_t launch_read(const float* x, int64_t n, uint32_t* sink, hipStream_t st);
 }  // namespace gc
 
 namespace {
@@ -831,6 +832,14 @@ int gc_add_f32(const float* x, float* y, int64_t n, void* stream) {
   if (any_overlap({flat(x, n, 4), flat(y, n, 4)})) return GC_ERR_INVALID_ARG;
   return gc::launch_add(x, y, n, static_cast<hipStream_t>(stream)) == hipSuccess ? GC_OK
                                                                                  : GC_ERR_HIP;
+}
+
+int gc_read_f32(const float* x, int64_t n, uint32_t* sink, void* stream) {
+  if (n < 0 || (n && (!x || !sink || !aligned16(x)))) return GC_ERR_INVALID_ARG;
+  if (any_overlap({flat(x, n, 4), flat(sink, 64, 4)})) return GC_ERR_INVALID_ARG;
+  return gc::launch_read(x, n, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? GC_OK
+             : GC_ERR_HIP;
 }
 
 }  // extern "C"

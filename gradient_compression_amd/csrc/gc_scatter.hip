@@ -102,8 +102,9 @@ __global__ __launch_bounds__(kThreads) void k_copy(const f4* __restrict__ src,
 
 // ------------------------------------------------------------------------------ add
 // y = fl(y + x) with the streaming pass's memory pattern and none of its other work: the same
-// tile layout, non-temporal dwordx4 loads of both inputs and a non-temporal store of y.  Its
-// bandwidth is the practical ceiling of a 2-read/1-write stream on this GPU.
+// tile layout, non-temporal dwordx4 loads of both inputs and a non-temporal store of y.  A
+// reference 2-read/1-write stream (the pass itself streams faster than this bare kernel, so it
+// is not a ceiling).
 __global__ __launch_bounds__(kThreads) void k_add(const float* __restrict__ x,
                                                   float* __restrict__ y, int64_t n) {
   const int64_t start = (int64_t)blockIdx.x * kTile;
@@ -132,7 +133,45 @@ __global__ __launch_bounds__(kThreads) void k_add(const float* __restrict__ x,
     }
 }
 
+// ----------------------------------------------------------------------------- read
+// A pure read stream in the pass's tile layout: non-temporal dwordx4 loads of x, folded into
+// an xor of the bit patterns, which is stored only if it equals a value no real stream of
+// floats produces here (so the loads cannot be dropped and nothing is written).
+__global__ __launch_bounds__(kThreads) void k_read(const float* __restrict__ x, int64_t n,
+                                                   uint32_t* __restrict__ sink) {
+  const int64_t start = (int64_t)blockIdx.x * kTile;
+  const int64_t rem = n - start;
+  const int len = rem < kTile ? (int)rem : kTile;
+  const int pb = slot_base();
+  uint32_t h = 0;
+  if (len == kTile) {
+    const f4* x4 = reinterpret_cast<const f4*>(x + start);
+    f4 a[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) a[v] = __builtin_nontemporal_load(x4 + ((pb + v * 256) >> 2));
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) h ^= __float_as_uint(a[v][c]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = pb + v * 256 + c;
+        if (p < len) h ^= __float_as_uint(x[start + p]);
+      }
+  }
+  if (h == 0x7FC0A5A5u) sink[threadIdx.x & 63] = h;
+}
+
 }  // namespace
+
+hipError_t launch_read(const float* x, int64_t n, uint32_t* sink, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  k_read<<<blocks_for(n, kTile), kThreads, 0, st>>>(x, n, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant(const OutPlan& O, const float* vals, const int32_t* idx, float* e,
                         uint64_t seed, uint64_t step, int8_t* codes, float* scales,

@@ -365,9 +365,16 @@ int gc_copy_f32(const float* src, float* dst, int64_t n, void* stream);
 
 /* Reference streaming kernel for the error-feedback pass's memory pattern: y[i] = fl(y[i] +
  * x[i]) for n floats (two reads, one write per element) with the pass's tile layout and
- * non-temporal 16-byte loads and stores, and none of its selection work.  Both pointers
+ * non-temporal 16-byte loads and stores, and none of its selection work (a reference stream,
+ * not a ceiling: the pass streams faster than this bare kernel).  Both pointers
  * 16-byte aligned; x and y must not overlap.  Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP. */
 int gc_add_f32(const float* x, float* y, int64_t n, void* stream);
+
+/* Reference pure read stream: reads n floats at x (16-byte aligned) with the pass's tile
+ * layout and non-temporal 16-byte loads, and writes nothing (sink, 64 uint32 of device
+ * memory, is written only in a case that does not arise for real data).
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_HIP. */
+int gc_read_f32(const float* x, int64_t n, uint32_t* sink, void* stream);
 
 /* Static text for a status code. */
 const char* gc_status_string(int status);

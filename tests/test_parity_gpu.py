@@ -37,12 +37,6 @@ def test_single_segment_c1_full():
     assert all(m == gca.MODE_CANDIDATES for m in modes), modes
 
 
-def test_resnet50_c2_full_size():
-    """ResNet-50's 161 tensors (25.6M), k = 1%, per-layer scaled normals; 4 iterations."""
-    wl = workload("c2_resnet50")
-    run_parity(wl.sizes, synth_grads(wl, 4, "cuda"), ratio=wl.ratio, label="c2")
-
-
 RAGGED = [1, 3, 64, 4095, 8192, 8193, 70001, 123457, 300001, 2, 65536, 65537]
 
 
