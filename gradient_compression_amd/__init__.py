@@ -29,7 +29,7 @@ MODE_SKIP, MODE_CANDIDATES, MODE_FULL, MODE_RECAPTURED = 0, 1, 2, 3
 EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layout",
            "gc_topk_ef_compress", "gc_topk_ef_compress_int8", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
            "gc_plan_last_stats", "gc_plan_set_timing", "gc_plan_timing", "gc_copy_f32", "gc_add_f32",
-           "gc_read_f32",
+           "gc_read_f32", "gc_topk_ef_compress_noalloc",
            "gc_status_string", "gc_sign_ef_compress", "gc_plan_sign_layout",
            "gc_sign_decompress", "gc_qsgd_compress", "gc_qsgd_decompress",
            "gc_threshold_ef_compress", "gc_randk_compress", "gc_decompress_gathered",
@@ -79,6 +79,7 @@ def lib(variant: str | None = None) -> ctypes.CDLL:
         "gc_copy_f32": [vp, vp, i64, vp],
         "gc_add_f32": [vp, vp, i64, vp],
         "gc_read_f32": [vp, i64, vp, vp],
+        "gc_topk_ef_compress_noalloc": [vp, i32, vp, vp, u32, vp, vp, vp, f32, vp, vp, vp],
         "gc_status_string": [ctypes.c_int],
         "gc_sign_ef_compress": [vp, vp, vp, vp, f32, vp, vp, vp],
         "gc_plan_sign_layout": [vp, vp],
@@ -126,6 +127,33 @@ def layout(seg_off, k=None, ratio=None):
     _check(lib().gc_layout(_np_ptr(off), n_seg, kp, rp, _np_ptr(k_out), _np_ptr(out_off)),
            "gc_layout")
     return k_out, out_off
+
+
+def topk_ef_compress_noalloc(seg_off, g, e, out_vals, out_idx, k=None, ratio=None,
+                             flags: int = 0, u=None, momentum: float = 0.0, stream=None,
+                             variant: str | None = None):
+    """The Top-k step without a plan, for callers that cannot allocate device memory: the
+    library keeps the call's state in a static device array (limits: GC_NOALLOC_MAX_*).
+    Results equal Plan(seg_off, k, ratio, flags).compress(...) bit for bit."""
+    import torch
+    off = np.ascontiguousarray(seg_off, dtype=np.int64)
+    n_seg = int(off.size - 1)
+    kp = rp = None
+    if k is not None:
+        k_in = np.ascontiguousarray(np.broadcast_to(np.asarray(k, np.int64), (n_seg,)))
+        kp = _np_ptr(k_in)
+    if ratio is not None:
+        r_in = np.ascontiguousarray(np.broadcast_to(np.asarray(ratio, np.float64), (n_seg,)))
+        rp = _np_ptr(r_in)
+    k_out, out_off = layout(off, k=k, ratio=ratio)
+    n = int(off[-1]) if n_seg >= 0 else 0
+    tk = int(out_off[-1])
+    rc = lib(variant).gc_topk_ef_compress_noalloc(
+        _np_ptr(off), n_seg, kp, rp, int(flags), _dev_ptr(g, torch.float32, "g", n),
+        _dev_ptr(e, torch.float32, "e", n), _dev_ptr(u, torch.float32, "u", n), float(momentum),
+        _dev_ptr(out_vals, torch.float32, "out_vals", tk),
+        _dev_ptr(out_idx, torch.int32, "out_idx", tk), _stream(stream))
+    _check(rc, "gc_topk_ef_compress_noalloc")
 
 
 def _np_ptr(a):
@@ -441,6 +469,7 @@ def read_f32(x, sink, stream=None):
            "gc_read_f32")
 
 
-__all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "add_f32", "read_f32", "layout", "EXPORTS",
+__all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "add_f32", "read_f32", "layout",
+           "topk_ef_compress_noalloc", "EXPORTS",
            "GC_MOMENTUM_MASK", "GC_DEBUG_FORCE_FALLBACK", "GC_DEBUG_NO_ESTIMATE", "MODE_SKIP",
            "MODE_CANDIDATES", "MODE_FULL", "MODE_RECAPTURED"]

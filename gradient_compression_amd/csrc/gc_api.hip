@@ -11,6 +11,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <memory>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -832,6 +833,270 @@ int gc_add_f32(const float* x, float* y, int64_t n, void* stream) {
   if (any_overlap({flat(x, n, 4), flat(y, n, 4)})) return GC_ERR_INVALID_ARG;
   return gc::launch_add(x, y, n, static_cast<hipStream_t>(stream)) == hipSuccess ? GC_OK
                                                                                  : GC_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------
+// The entry point that allocates nothing (gc_topk_ef_compress_noalloc).  Its plan lives in
+// `scratch`, a file-scope device array: the segment table, the tile and chunk tables, the
+// per-segment and per-tile state, the histograms and the candidate buffers of one call, for
+// at most GC_NOALLOC_MAX_SEGMENTS segments and GC_NOALLOC_MAX_ELEMENTS elements.  A setup
+// kernel writes the tables and clears the state at the start of every call (no host table is
+// built, no memory is allocated, no memset is recorded), then the call runs the same kernels
+// as gc_topk_ef_compress, without a threshold estimate (every segment takes the exact
+// re-capture or full path).  Every call on a device shares that device's array: calls that
+// overlap on one device race.
+namespace {
+
+constexpr int kNaSeg = GC_NOALLOC_MAX_SEGMENTS;
+constexpr int64_t kNaElems = GC_NOALLOC_MAX_ELEMENTS;
+constexpr int64_t kNaCand = GC_NOALLOC_MAX_CANDIDATES;
+constexpr int64_t kNaTiles = kNaElems / gc::kTile + kNaSeg;         // ragged tail per segment
+constexpr int64_t kNaCandSlots = kNaCand + 4 * kNaSeg;              // each region rounded up to 4
+constexpr int64_t kNaChunks = kNaCandSlots / gc::kChunk + kNaSeg;
+constexpr size_t kScratchBytes = (size_t)24 << 20;
+constexpr int kNaMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_na_mu;
+void* g_na_ptr[kNaMaxDevices];   // the device address of `scratch` on each device
+
+// Segment table of one call, passed to the setup kernel by value.
+struct NaArgs {
+  int32_t n_seg;
+  int32_t flags;
+  int64_t seg_off[kNaSeg + 1];
+  int64_t k[kNaSeg];
+  int64_t cap[kNaSeg];
+};
+
+// Candidate capacity of a segment in the static array (the results never depend on it: a
+// bucket larger than the capacity takes the exact full-segment path).
+inline int64_t na_capacity(int64_t n, int64_t k) {
+  if (k == 0) return 0;
+  return std::min(n, std::max(k * 4, (int64_t)65536));
+}
+
+// Sequential 256-byte-aligned pieces of the static array.
+struct NaCarve {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(int64_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = reinterpret_cast<T*>(base + off);
+    off += (size_t)std::max<int64_t>(count, 1) * sizeof(T);
+    return p;
+  }
+};
+
+// The plan of a call inside the static array (host arithmetic on the device address only).
+size_t na_layout(char* base, gc::DevPlan& d) {
+  NaCarve c{base};
+  d.seg_off = c.take<int64_t>(kNaSeg + 1);
+  d.tile_base = c.take<int64_t>(kNaSeg + 1);
+  d.chunk_base = c.take<int64_t>(kNaSeg + 1);
+  d.out_off = c.take<int64_t>(kNaSeg + 1);
+  d.cand_base = c.take<int64_t>(kNaSeg);
+  d.word_off = c.take<int64_t>(kNaSeg + 1);
+  d.sample_elems = c.take<int64_t>(kNaSeg);
+  d.k = c.take<uint32_t>(kNaSeg);
+  d.cand_cap = c.take<uint32_t>(kNaSeg);
+  d.thr_init = c.take<uint32_t>(kNaSeg);
+  d.thr_rand = c.take<uint32_t>(kNaSeg);
+  d.rk_scale = c.take<float>(kNaSeg);
+  d.thr = c.take<uint32_t>(kNaSeg);
+  d.cand_cnt = c.take<uint32_t>(kNaSeg);
+  d.mode = c.take<uint32_t>(kNaSeg);
+  d.prefix = c.take<uint32_t>(kNaSeg);
+  d.kk = c.take<uint32_t>(kNaSeg);
+  d.kth = c.take<uint32_t>(kNaSeg);
+  d.ties = c.take<uint32_t>(kNaSeg);
+  d.why = c.take<uint32_t>(kNaSeg);
+  d.beta = c.take<float>(kNaSeg);
+  d.full_list = c.take<uint32_t>(kNaSeg);
+  d.recap_list = c.take<uint32_t>(kNaSeg);
+  d.k_call = c.take<uint32_t>(kNaSeg);
+  d.thr_call = c.take<uint32_t>(kNaSeg);
+  d.thr_est = c.take<uint32_t>(kNaSeg);
+  d.beta_est = c.take<float>(kNaSeg);
+  d.tau_key = c.take<uint32_t>(kNaSeg);
+  d.tau_cnt = c.take<uint32_t>(kNaSeg);
+  d.seg_norm = c.take<float>(kNaSeg);
+  d.full_count = c.take<uint32_t>(1);
+  d.recap_count = c.take<uint32_t>(1);
+  d.act_count = c.take<uint32_t>(1);
+  d.err = c.take<uint32_t>(1);
+  d.hist = c.take<uint32_t>((int64_t)kNaSeg * 3 * gc::kHistBins);
+  d.tile_seg = c.take<int32_t>(kNaTiles);
+  d.tile_desc = c.take<int4>(kNaTiles);
+  d.run_off = c.take<uint32_t>(kNaTiles);
+  d.run_cnt = c.take<uint32_t>(kNaTiles);
+  d.run_dst = c.take<uint32_t>(kNaTiles);
+  d.tile_gt = c.take<uint32_t>(kNaTiles);
+  d.tile_eq = c.take<uint32_t>(kNaTiles);
+  d.tile_eq_base = c.take<uint32_t>(kNaTiles);
+  d.tile_sel_base = c.take<uint32_t>(kNaTiles);
+  d.tile_max = c.take<uint32_t>(kNaTiles);
+  d.tile_l1 = c.take<double>(kNaTiles);
+  d.chunk_seg = c.take<int32_t>(kNaChunks);
+  d.chunk_gt = c.take<uint32_t>(kNaChunks);
+  d.chunk_eq = c.take<uint32_t>(kNaChunks);
+  d.chunk_eq_base = c.take<uint32_t>(kNaChunks);
+  d.chunk_sel_base = c.take<uint32_t>(kNaChunks);
+  d.chunk_max = c.take<uint32_t>(kNaChunks);
+  d.act_chunk = c.take<uint32_t>(kNaChunks);
+  d.cand_val = c.take<float>(kNaCandSlots);
+  d.cand_idx = c.take<int32_t>(kNaCandSlots);
+  d.sort_val = c.take<float>(kNaCandSlots);
+  d.sort_idx = c.take<int32_t>(kNaCandSlots);
+  return c.off;
+}
+
+// One workgroup: the per-segment tables (thread 0, at most kNaSeg segments), then the tile and
+// chunk tables, and the per-call state cleared (thresholds: none, so every segment takes the
+// exact path; counters, flags and the per-segment state zero).
+__global__ __launch_bounds__(1024) void k_noalloc_setup(gc::DevPlan P, NaArgs a) {
+  __shared__ int64_t s_tile_base[kNaSeg + 1], s_chunk_base[kNaSeg + 1];
+  if (threadIdx.x == 0) {
+    int64_t tb = 0, cb = 0, ob = 0, kb = 0;
+    for (int s = 0; s < a.n_seg; ++s) {
+      const int64_t n = a.seg_off[s + 1] - a.seg_off[s];
+      const_cast<int64_t*>(P.seg_off)[s] = a.seg_off[s];
+      const_cast<int64_t*>(P.tile_base)[s] = tb;
+      const_cast<int64_t*>(P.chunk_base)[s] = cb;
+      const_cast<int64_t*>(P.out_off)[s] = ob;
+      const_cast<int64_t*>(P.cand_base)[s] = kb;
+      const_cast<int64_t*>(P.sample_elems)[s] = 0;
+      const_cast<uint32_t*>(P.k)[s] = (uint32_t)a.k[s];
+      const_cast<uint32_t*>(P.cand_cap)[s] = (uint32_t)a.cap[s];
+      const_cast<uint32_t*>(P.thr_init)[s] = gc::kNoCapture;
+      P.thr[s] = gc::kNoCapture;
+      P.beta[s] = gc::kInitialBeta;
+      P.cand_cnt[s] = 0;
+      P.mode[s] = 0;
+      P.kth[s] = 0;
+      P.ties[s] = 0;
+      s_tile_base[s] = tb;
+      s_chunk_base[s] = cb;
+      tb += (n + gc::kTile - 1) / gc::kTile;
+      cb += (a.cap[s] + gc::kChunk - 1) / gc::kChunk;
+      ob += a.k[s];
+      kb += (a.cap[s] + 3) / 4 * 4;
+    }
+    const_cast<int64_t*>(P.seg_off)[a.n_seg] = a.seg_off[a.n_seg];
+    const_cast<int64_t*>(P.tile_base)[a.n_seg] = tb;
+    const_cast<int64_t*>(P.chunk_base)[a.n_seg] = cb;
+    const_cast<int64_t*>(P.out_off)[a.n_seg] = ob;
+    s_tile_base[a.n_seg] = tb;
+    s_chunk_base[a.n_seg] = cb;
+    *P.full_count = 0;
+    *P.recap_count = 0;
+    *P.act_count = 0;
+    *P.err = 0;
+  }
+  __syncthreads();
+  for (int64_t t = threadIdx.x; t < s_tile_base[a.n_seg]; t += blockDim.x) {
+    int s = 0;
+    while (s_tile_base[s + 1] <= t) ++s;
+    const int64_t start = a.seg_off[s] + (t - s_tile_base[s]) * gc::kTile;
+    const int64_t len = std::min<int64_t>(gc::kTile, a.seg_off[s + 1] - start);
+    const_cast<int32_t*>(P.tile_seg)[t] = s;
+    const_cast<int4*>(P.tile_desc)[t] =
+        make_int4((int)(uint32_t)start, (int)(uint32_t)((uint64_t)start >> 32), (int)len, s);
+  }
+  for (int64_t c = threadIdx.x; c < s_chunk_base[a.n_seg]; c += blockDim.x) {
+    int s = 0;
+    while (s_chunk_base[s + 1] <= c) ++s;
+    const_cast<int32_t*>(P.chunk_seg)[c] = s;
+  }
+}
+
+// The device address of `scratch` on the current device, looked up once per device.
+int na_scratch(int dev, char** out) {
+  if (dev < 0 || dev >= kNaMaxDevices) return GC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_na_mu);
+  if (!g_na_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return GC_ERR_HIP;
+    }
+    g_na_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_na_ptr[dev]);
+  return GC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gc_topk_ef_compress_noalloc(const int64_t* seg_off, int32_t n_seg, const int64_t* k,
+                                const double* ratio, uint32_t flags, const float* g, float* e,
+                                float* u, float momentum, float* out_vals, int32_t* out_idx,
+                                void* stream) {
+  if (n_seg < 0 || !seg_off) return GC_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)GC_MOMENTUM_MASK) return GC_ERR_INVALID_ARG;
+  if (n_seg > kNaSeg) return GC_ERR_UNSUPPORTED;
+  NaArgs a{};
+  a.n_seg = n_seg;
+  a.flags = (int32_t)flags;
+  int64_t ks[kNaSeg > 0 ? kNaSeg : 1];
+  if (int rc = gc_layout(seg_off, n_seg, k, ratio, ks, nullptr)) return rc;
+  int64_t total_k = 0, cand = 0, tiles = 0, chunks = 0;
+  for (int32_t s = 0; s < n_seg; ++s) {
+    const int64_t n = seg_off[s + 1] - seg_off[s];
+    a.seg_off[s] = seg_off[s];
+    a.k[s] = ks[s];
+    a.cap[s] = na_capacity(n, ks[s]);
+    total_k += ks[s];
+    cand += (a.cap[s] + 3) / 4 * 4;
+    tiles += (n + gc::kTile - 1) / gc::kTile;
+    chunks += (a.cap[s] + gc::kChunk - 1) / gc::kChunk;
+  }
+  a.seg_off[n_seg] = seg_off[n_seg];
+  const int64_t n_all = seg_off[n_seg] - seg_off[0];
+  if (n_all > kNaElems || cand > kNaCandSlots || tiles > kNaTiles || chunks > kNaChunks)
+    return GC_ERR_UNSUPPORTED;
+  if (n_all > 0 && (!g || !e || !aligned16(g) || !aligned16(e))) return GC_ERR_INVALID_ARG;
+  if (u && !aligned16(u)) return GC_ERR_INVALID_ARG;
+  if (total_k > 0 && (!out_vals || !out_idx)) return GC_ERR_INVALID_ARG;
+  {
+    const int64_t lo = seg_off[0];
+    auto dspan = [&](const void* p) -> Span {
+      if (!p) return {nullptr, 0};
+      return {static_cast<const char*>(p) + lo * 4, (uint64_t)n_all * 4};
+    };
+    if (any_overlap({dspan(g), dspan(e), dspan(u), flat(out_vals, total_k, 4),
+                     flat(out_idx, total_k, 4)}))
+      return GC_ERR_INVALID_ARG;
+  }
+  if (n_seg == 0) return GC_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GC_ERR_HIP;
+  char* base = nullptr;
+  if (int rc = na_scratch(dev, &base)) return rc;
+  gc::DevPlan d{};
+  if (na_layout(base, d) > kScratchBytes) return GC_ERR_UNSUPPORTED;
+  d.n_seg = n_seg;
+  d.flags = (int32_t)(flags | gc::kFlagNoEstimate);
+  d.n_tiles = tiles;
+  d.n_chunks = chunks;
+  d.n_chunk_blocks = (int32_t)std::min<int64_t>(chunks, gc::kChunkBlocks);
+  d.keys = gc::kKeysMagnitude;
+  d.n_sample = 0;
+  d.sample_tile = nullptr;
+  d.gscale = nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  k_noalloc_setup<<<1, 1024, 0, st>>>(d, a);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess)
+    err = gc::launch_compress(d, g, e, u, momentum, out_vals, out_idx, gc::Int8Args{}, false,
+                              st, nullptr, nullptr);
+  return err == hipSuccess ? GC_OK : GC_ERR_HIP;
 }
 
 int gc_read_f32(const float* x, int64_t n, uint32_t* sink, void* stream) {

@@ -133,6 +133,36 @@ int gc_topk_ef_compress(gc_plan* plan, const float* g, float* e, float* u, float
                         float* out_vals, int32_t* out_idx, void* stream);
 
 /*
+ * gc_topk_ef_compress for callers that cannot allocate device memory at any point: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It takes
+ * the segment table instead of a plan and allocates nothing (no hipMalloc, no hipFree, no
+ * host heap): its per-call state lives in a static device array of 24 MiB that the library
+ * holds on each device it runs on until the process ends, set up afresh by a small kernel at
+ * the start of every call.  The results are bit-identical to gc_topk_ef_compress on a plan
+ * made from the same arguments; there is no threshold estimate between calls, so every
+ * segment takes the exact re-capture (or full-segment) path, which is slower than a warm plan.
+ *   seg_off, n_seg, k, ratio : as for gc_plan_create (host arrays, read during the call).
+ *   flags    : GC_MOMENTUM_MASK or 0.
+ *   g, e, u, momentum, out_vals, out_idx, stream : as for gc_topk_ef_compress (out_off is
+ *              the exclusive prefix sum of k).
+ * Limits: n_seg <= GC_NOALLOC_MAX_SEGMENTS, seg_off[n_seg] - seg_off[0] <=
+ * GC_NOALLOC_MAX_ELEMENTS, and the candidate capacity, sum over segments of
+ * min(n_s, max(4 k_s, 65536)), at most GC_NOALLOC_MAX_CANDIDATES; beyond them the call
+ * returns GC_ERR_UNSUPPORTED and launches nothing.  Every call on a device uses that device's
+ * one array, which keeps the last call's contents: calls that overlap on one device (other
+ * streams, other threads) race and must be serialised by the caller.
+ * Errors: GC_ERR_INVALID_ARG, GC_ERR_UNSUPPORTED, GC_ERR_HIP.
+ */
+#define GC_NOALLOC_MAX_SEGMENTS 64
+#define GC_NOALLOC_MAX_ELEMENTS (1ll << 22)
+#define GC_NOALLOC_MAX_CANDIDATES (1ll << 20)
+int gc_topk_ef_compress_noalloc(const int64_t* seg_off /* host */, int32_t n_seg,
+                                const int64_t* k /* host or NULL */,
+                                const double* ratio /* host or NULL */, uint32_t flags,
+                                const float* g, float* e, float* u, float momentum,
+                                float* out_vals, int32_t* out_idx, void* stream);
+
+/*
  * Quantise the kept values to int8, one scale per segment, with stochastic rounding:
  *   scale_s = fl(absmax_s / 127) over the segment's kept values (0 when all are 0);
  *   a = min(fl(|v| / scale_s), 127); q = floor(a) + [u24 < (a - floor(a)) * 2^24];
