@@ -24,7 +24,9 @@ GC_MOMENTUM_MASK = 0x1
 GC_DEBUG_FORCE_FALLBACK = 0x100
 GC_DEBUG_NO_ESTIMATE = 0x200
 
-MODE_SKIP, MODE_CANDIDATES, MODE_FULL, MODE_RECAPTURED = 0, 1, 2, 3
+MODE_SKIP, MODE_CANDIDATES, MODE_FULL, MODE_RECAPTURED, MODE_SMALL = 0, 1, 2, 3, 5
+# Segments of at most this many elements are selected whole by one workgroup (MODE_SMALL).
+SMALL_SEGMENT = 16384
 
 EXPORTS = ("gc_plan_create", "gc_plan_destroy", "gc_plan_total_k", "gc_plan_layout",
            "gc_topk_ef_compress", "gc_topk_ef_compress_int8", "gc_quant_int8", "gc_decompress", "gc_plan_reset_estimate",
@@ -472,4 +474,4 @@ def read_f32(x, sink, stream=None):
 __all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "add_f32", "read_f32", "layout",
            "topk_ef_compress_noalloc", "EXPORTS",
            "GC_MOMENTUM_MASK", "GC_DEBUG_FORCE_FALLBACK", "GC_DEBUG_NO_ESTIMATE", "MODE_SKIP",
-           "MODE_CANDIDATES", "MODE_FULL", "MODE_RECAPTURED"]
+           "MODE_CANDIDATES", "MODE_FULL", "MODE_RECAPTURED", "MODE_SMALL", "SMALL_SEGMENT"]

@@ -26,8 +26,6 @@ hipError_t launch_read(const float* x, int64_t n, uint32_t* sink, hipStream_t st
 
 namespace {
 
-// Segments at most this long capture every element (their select runs on the candidates).
-constexpr int64_t kSmallSegment = 65536;
 // Candidate capacity of a larger segment, in multiples of its k (at least kMinCapacity).
 constexpr int64_t kCapacityFactor = 16;
 constexpr int64_t kMinCapacity = 65536;
@@ -199,16 +197,21 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   // tables
   std::vector<int64_t> tile_base(n_seg + 1, 0), chunk_base(n_seg + 1, 0), cand_base(n_seg, 0),
       out_chunk_base(n_seg + 1, 0);
-  std::vector<uint32_t> kk(n_seg), cap(n_seg), thr_init(n_seg), thr_rand(n_seg);
+  std::vector<uint32_t> kk(n_seg), cap(n_seg), thr_init(n_seg), thr_rand(n_seg),
+      seg_flags(n_seg, 0);
   std::vector<float> rk_scale(n_seg, 0.0f);
   int64_t cand_total = 0;
+  const bool no_estimate = (flags & (GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE)) != 0;
   for (int32_t s = 0; s < n_seg; ++s) {
     const int64_t n = seg_off[s + 1] - seg_off[s];
     tile_base[s + 1] = tile_base[s] + ceil_div(n, gc::kTile);
     int64_t c = 0;
     uint32_t thr = gc::kNoCapture, thr_r = gc::kNoCapture;
-    if (ks[s] > 0) {
-      if (n <= kSmallSegment || ks[s] * kCapacityFactor >= n) {
+    if (n <= gc::kSmallSegment) {
+      // selected whole by one workgroup of the select kernel: no capture, no candidates
+      seg_flags[s] = gc::kSegSmall;
+    } else if (ks[s] > 0) {
+      if (ks[s] * kCapacityFactor >= n) {
         c = n;
         thr = 0;  // capture everything: the select then runs on the whole segment's copy
         thr_r = 0;
@@ -216,12 +219,12 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
         c = std::min(n, std::max(ks[s] * kCapacityFactor, kMinCapacity));
         thr_r = randk_threshold(n, ks[s]);
       }
-      if (flags & (GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE)) {
+      if (no_estimate) {
         thr = gc::kNoCapture;
         thr_r = gc::kNoCapture;
       }
-      rk_scale[s] = (float)((double)n / (double)ks[s]);
     }
+    if (ks[s] > 0) rk_scale[s] = (float)((double)n / (double)ks[s]);
     thr_rand[s] = thr_r;
     kk[s] = (uint32_t)ks[s];
     cap[s] = (uint32_t)c;
@@ -236,9 +239,9 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   // without an estimate (large segments with k > 0; none when the debug flags forbid one)
   std::vector<int32_t> sample_tile;
   std::vector<int64_t> sample_elems(n_seg, 0);
-  if (!(flags & (GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE))) {
+  if (!no_estimate) {
     for (int32_t s = 0; s < n_seg; ++s) {
-      if (ks[s] == 0 || thr_init[s] != gc::kNoCapture) continue;   // nothing to estimate
+      if (ks[s] == 0 || thr_init[s] != gc::kNoCapture || seg_flags[s]) continue;   // no estimate
       const int64_t nt = tile_base[s + 1] - tile_base[s];
       const int64_t stride = std::max<int64_t>(1, ceil_div(nt, kSampleTiles));
       for (int64_t j = 0; j < nt; j += stride) {
@@ -291,19 +294,26 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   cv.add(&d_thr_init, n_seg);
   cv.add(&d_out_chunk_seg, n_out_chunks);
   cv.add(&d_out_chunk_base, n_seg + 1);
+  uint32_t* d_seg_flags;
+  cv.add(&d_seg_flags, n_seg);
   cv.add(&d.thr, n_seg);
   cv.add(&d.cand_cnt, n_seg);
+  cv.add(&d.recap_cnt, n_seg);
   cv.add(&d.mode, n_seg);
-  cv.add(&d.prefix, n_seg);
-  cv.add(&d.kk, n_seg);
+  cv.add(&d.thr_lo, n_seg);
+  cv.add(&d.pfx1, n_seg);
+  cv.add(&d.kk1, n_seg);
+  cv.add(&d.pfx2, n_seg);
+  cv.add(&d.kk2, n_seg);
   cv.add(&d.kth, n_seg);
   cv.add(&d.ties, n_seg);
+  cv.add(&d.sel_cnt, n_seg);
   cv.add(&d.hist, (int64_t)n_seg * 3 * gc::kHistBins);
   cv.add(&d.full_list, n_seg);
   cv.add(&d.full_count, 1);
-  cv.add(&d.recap_list, n_seg);
-  cv.add(&d.recap_count, 1);
-  cv.add(&d.why, n_seg);
+  cv.add(&d.pend_list, n_seg);
+  cv.add(&d.pend_count, 1);
+  cv.add(&d.near_cnt, n_seg);
   cv.add(&d.beta, n_seg);
   cv.add(&d.err, 1);
 
@@ -315,10 +325,10 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   cv.add(&d.tile_eq_base, n_tiles);
   cv.add(&d.tile_sel_base, n_tiles);
   cv.add(&d.chunk_gt, n_chunks);
+  cv.add(&d.chunk_max, n_chunks);
   cv.add(&d.chunk_eq, n_chunks);
   cv.add(&d.chunk_eq_base, n_chunks);
   cv.add(&d.chunk_sel_base, n_chunks);
-  cv.add(&d.chunk_max, n_chunks);
   cv.add(&d.act_chunk, n_chunks);
   cv.add(&d.act_count, 1);
   cv.add(&d.tile_max, n_tiles);
@@ -331,7 +341,6 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   cv.add(&d.sort_idx, cand_total);
   uint32_t* d_thr_rand;
   float* d_rk_scale;
-  cv.add(&d.k_call, n_seg);
   cv.add(&d.seg_norm, n_seg);
   int32_t* d_sample_tile;
   int64_t* d_sample_elems;
@@ -339,13 +348,11 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   cv.add(&d_sample_elems, n_seg);
   cv.add(&d.thr_est, n_seg);
   cv.add(&d.beta_est, n_seg);
-  cv.add(&d.tau_key, n_seg);
   cv.add(&d.tau_cnt, n_seg);
-  cv.add(&d.thr_call, n_seg);
   cv.add(&d_thr_rand, n_seg);
   cv.add(&d_rk_scale, n_seg);
   const std::vector<float> beta_init(n_seg, gc::kInitialBeta);
-  const std::vector<uint32_t> no_estimate(n_seg, gc::kNoCapture);
+  const std::vector<uint32_t> no_floor(n_seg, gc::kNoCapture);
   if (hipMalloc(&p->mem, cv.total()) != hipSuccess) {
     (void)hipGetLastError();
     return GC_ERR_OOM;
@@ -362,6 +369,8 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   d.cand_base = d_cand_base;
   d.cand_cap = d_cap;
   d.thr_init = d_thr_init;
+  d.seg_flags = d_seg_flags;
+  d.codec = gc::kCodecTopk;
   d.word_off = d_word_off;
   d.thr_rand = d_thr_rand;
   d.rk_scale = d_rk_scale;
@@ -390,6 +399,7 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   up(upload(d_cand_base, cand_base));
   up(upload(d_cap, cap));
   up(upload(d_thr_init, thr_init));
+  up(upload(d_seg_flags, seg_flags));
   up(upload(d_out_chunk_seg, out_chunk_seg));
   up(upload(d_out_chunk_base, out_chunk_base));
   up(upload(d_word_off, p->word_off));
@@ -399,13 +409,18 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   up(upload(d_sample_elems, sample_elems));
   up(upload(d.thr, thr_init));
   up(upload(d.beta, beta_init));
-  up(upload(d.thr_est, no_estimate));
+  up(upload(d.thr_est, no_floor));
   up(upload(d.beta_est, beta_init));
-  up(hipMemset(d.cand_cnt, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
-  up(hipMemset(d.mode, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
-  up(hipMemset(d.kth, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
-  up(hipMemset(d.ties, 0, sizeof(uint32_t) * std::max(n_seg, 1)));
+  // the per-call counters and histograms start at zero (each call clears what it used)
+  const size_t seg_bytes = sizeof(uint32_t) * std::max(n_seg, 1);
+  for (uint32_t* a : {d.cand_cnt, d.recap_cnt, d.tau_cnt, d.near_cnt, d.mode, d.kth, d.ties,
+                      d.sel_cnt})
+    up(hipMemset(a, 0, seg_bytes));
+  up(hipMemset(d.pend_count, 0, sizeof(uint32_t)));
+  up(hipMemset(d.hist, 0, sizeof(uint32_t) * std::max<int64_t>((int64_t)n_seg * 3 * gc::kHistBins, 1)));
   up(hipMemset(d.err, 0, sizeof(uint32_t)));
+  up(hipMemset(d.act_count, 0, sizeof(uint32_t)));
+  up(hipMemset(d.full_count, 0, sizeof(uint32_t)));
   up(hipDeviceSynchronize());
   if (err != hipSuccess) {
     (void)hipGetLastError();
@@ -561,7 +576,7 @@ int gc_threshold_ef_compress(gc_plan* plan, const float* g, float* e, float* u, 
   hipEvent_t b = nullptr, en = nullptr;
   if (int rc = timing_events(plan, &b, &en)) return rc;
   const hipError_t err =
-      gc::launch_threshold(plan->dp, plan->op, g, e, u, momentum, tau, out_vals, out_idx,
+      gc::launch_threshold(plan->dp, g, e, u, momentum, tau, out_vals, out_idx,
                            out_count, static_cast<hipStream_t>(stream), b, en);
   return err == hipSuccess ? GC_OK : GC_ERR_HIP;
 }
@@ -785,7 +800,7 @@ int gc_plan_last_stats(gc_plan* plan, uint32_t* mode, uint32_t* candidates, uint
     if (dst && bytes && err == hipSuccess) err = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, st);
   };
   cp(mode, plan->dp.mode);
-  cp(candidates, plan->dp.cand_cnt);
+  cp(candidates, plan->dp.sel_cnt);
   cp(kth_key, plan->dp.kth);
   cp(ties_taken, plan->dp.ties);
   uint32_t flag = 0;
@@ -875,7 +890,7 @@ struct NaArgs {
 // Candidate capacity of a segment in the static array (the results never depend on it: a
 // bucket larger than the capacity takes the exact full-segment path).
 inline int64_t na_capacity(int64_t n, int64_t k) {
-  if (k == 0) return 0;
+  if (k == 0 || n <= gc::kSmallSegment) return 0;   // small segments are selected whole
   return std::min(n, std::max(k * 4, (int64_t)65536));
 }
 
@@ -905,28 +920,31 @@ size_t na_layout(char* base, gc::DevPlan& d) {
   d.k = c.take<uint32_t>(kNaSeg);
   d.cand_cap = c.take<uint32_t>(kNaSeg);
   d.thr_init = c.take<uint32_t>(kNaSeg);
+  d.seg_flags = c.take<uint32_t>(kNaSeg);
   d.thr_rand = c.take<uint32_t>(kNaSeg);
   d.rk_scale = c.take<float>(kNaSeg);
   d.thr = c.take<uint32_t>(kNaSeg);
   d.cand_cnt = c.take<uint32_t>(kNaSeg);
+  d.recap_cnt = c.take<uint32_t>(kNaSeg);
   d.mode = c.take<uint32_t>(kNaSeg);
-  d.prefix = c.take<uint32_t>(kNaSeg);
-  d.kk = c.take<uint32_t>(kNaSeg);
+  d.thr_lo = c.take<uint32_t>(kNaSeg);
+  d.pfx1 = c.take<uint32_t>(kNaSeg);
+  d.kk1 = c.take<uint32_t>(kNaSeg);
+  d.pfx2 = c.take<uint32_t>(kNaSeg);
+  d.kk2 = c.take<uint32_t>(kNaSeg);
   d.kth = c.take<uint32_t>(kNaSeg);
   d.ties = c.take<uint32_t>(kNaSeg);
-  d.why = c.take<uint32_t>(kNaSeg);
+  d.sel_cnt = c.take<uint32_t>(kNaSeg);
   d.beta = c.take<float>(kNaSeg);
   d.full_list = c.take<uint32_t>(kNaSeg);
-  d.recap_list = c.take<uint32_t>(kNaSeg);
-  d.k_call = c.take<uint32_t>(kNaSeg);
-  d.thr_call = c.take<uint32_t>(kNaSeg);
+  d.pend_list = c.take<uint32_t>(kNaSeg);
+  d.near_cnt = c.take<uint32_t>(kNaSeg);
   d.thr_est = c.take<uint32_t>(kNaSeg);
   d.beta_est = c.take<float>(kNaSeg);
-  d.tau_key = c.take<uint32_t>(kNaSeg);
   d.tau_cnt = c.take<uint32_t>(kNaSeg);
   d.seg_norm = c.take<float>(kNaSeg);
   d.full_count = c.take<uint32_t>(1);
-  d.recap_count = c.take<uint32_t>(1);
+  d.pend_count = c.take<uint32_t>(1);
   d.act_count = c.take<uint32_t>(1);
   d.err = c.take<uint32_t>(1);
   d.hist = c.take<uint32_t>((int64_t)kNaSeg * 3 * gc::kHistBins);
@@ -943,10 +961,10 @@ size_t na_layout(char* base, gc::DevPlan& d) {
   d.tile_l1 = c.take<double>(kNaTiles);
   d.chunk_seg = c.take<int32_t>(kNaChunks);
   d.chunk_gt = c.take<uint32_t>(kNaChunks);
+  d.chunk_max = c.take<uint32_t>(kNaChunks);
   d.chunk_eq = c.take<uint32_t>(kNaChunks);
   d.chunk_eq_base = c.take<uint32_t>(kNaChunks);
   d.chunk_sel_base = c.take<uint32_t>(kNaChunks);
-  d.chunk_max = c.take<uint32_t>(kNaChunks);
   d.act_chunk = c.take<uint32_t>(kNaChunks);
   d.cand_val = c.take<float>(kNaCandSlots);
   d.cand_idx = c.take<int32_t>(kNaCandSlots);
@@ -956,8 +974,9 @@ size_t na_layout(char* base, gc::DevPlan& d) {
 }
 
 // One workgroup: the per-segment tables (thread 0, at most kNaSeg segments), then the tile and
-// chunk tables, and the per-call state cleared (thresholds: none, so every segment takes the
-// exact path; counters, flags and the per-segment state zero).
+// chunk tables, and the per-call state cleared: no threshold (every segment takes the exact
+// path), counters, flags and histograms zero.  It runs before every call, so nothing of the
+// previous call (which may have had another segment table) is seen.
 __global__ __launch_bounds__(1024) void k_noalloc_setup(gc::DevPlan P, NaArgs a) {
   __shared__ int64_t s_tile_base[kNaSeg + 1], s_chunk_base[kNaSeg + 1];
   if (threadIdx.x == 0) {
@@ -973,12 +992,17 @@ __global__ __launch_bounds__(1024) void k_noalloc_setup(gc::DevPlan P, NaArgs a)
       const_cast<uint32_t*>(P.k)[s] = (uint32_t)a.k[s];
       const_cast<uint32_t*>(P.cand_cap)[s] = (uint32_t)a.cap[s];
       const_cast<uint32_t*>(P.thr_init)[s] = gc::kNoCapture;
+      const_cast<uint32_t*>(P.seg_flags)[s] = n <= gc::kSmallSegment ? gc::kSegSmall : 0u;
       P.thr[s] = gc::kNoCapture;
       P.beta[s] = gc::kInitialBeta;
       P.cand_cnt[s] = 0;
+      P.recap_cnt[s] = 0;
+      P.tau_cnt[s] = 0;
+      P.near_cnt[s] = 0;
       P.mode[s] = 0;
       P.kth[s] = 0;
       P.ties[s] = 0;
+      P.sel_cnt[s] = 0;
       s_tile_base[s] = tb;
       s_chunk_base[s] = cb;
       tb += (n + gc::kTile - 1) / gc::kTile;
@@ -993,10 +1017,12 @@ __global__ __launch_bounds__(1024) void k_noalloc_setup(gc::DevPlan P, NaArgs a)
     s_tile_base[a.n_seg] = tb;
     s_chunk_base[a.n_seg] = cb;
     *P.full_count = 0;
-    *P.recap_count = 0;
+    *P.pend_count = 0;
     *P.act_count = 0;
     *P.err = 0;
   }
+  for (int64_t i = threadIdx.x; i < (int64_t)a.n_seg * 3 * gc::kHistBins; i += blockDim.x)
+    P.hist[i] = 0;
   __syncthreads();
   for (int64_t t = threadIdx.x; t < s_tile_base[a.n_seg]; t += blockDim.x) {
     int s = 0;

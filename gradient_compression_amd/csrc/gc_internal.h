@@ -60,18 +60,35 @@ constexpr int kFullBlocks = 1024;
 // Most workgroups that walk the candidate chunks of a call (the chunks that hold candidates
 // are listed per call; a plan has chunks for its full capacity, mostly unused).
 constexpr int kChunkBlocks = 1024;
+// Workgroups of the fallback kernels (histograms, re-capture and counts over the tiles of the
+// segments whose captured candidates were not complete).
+constexpr int kFallbackBlocks = 1024;
 // Output chunks for the int8 and decompression kernels.
 constexpr int kOutChunk = 4096;
 constexpr int kHistBins = 2048;
+// Segments of at most this many elements are selected whole by one workgroup of the finish
+// kernel, their keys held in registers (read from the residual, which holds acc after the
+// streaming pass); they capture nothing.
+constexpr int64_t kSmallSegment = 16384;
+constexpr int kSmallTiles = (int)(kSmallSegment / kTile);
+static_assert(kSmallSegment % kTile == 0, "a small segment is a whole number of tiles at most");
+// Keys the finish workgroup ranks in its LDS once the range holding the k-th key is this
+// small.
+constexpr int kListCap = 4096;
+// Output chunks whose counts the finish workgroup keeps in LDS at a time.
+constexpr int kFinishChunks = 1024;
 
 constexpr uint32_t kNoCapture = 0xFFFFFFFFu;        // threshold above every key
 // Per-segment path of a call.  kModeCand: the candidates captured at the estimated threshold
 // hold the k largest.  kModeRecap: they did not, the segment's first-digit histogram was
 // taken and the candidates re-captured at the exact bucket floor.  kModeFull: the bucket is
-// larger than the capacity (or forced): radix select over the whole segment.
-enum : uint32_t { kModeSkip = 0, kModeCand = 1, kModeFull = 2, kModeRecap = 3, kModePending = 4 };
-// Why a segment left the estimate path (for the estimate's feedback).
-enum : uint32_t { kWhyNone = 0, kWhyCold = 1, kWhyMiss = 2, kWhyOverflow = 3 };
+// larger than the capacity (or forced): radix select over the whole segment.  kModeSmall: a
+// small segment, selected whole from its residual by one workgroup.
+enum : uint32_t {
+  kModeSkip = 0, kModeCand = 1, kModeFull = 2, kModeRecap = 3, kModePending = 4, kModeSmall = 5
+};
+// Per-segment plan flags.
+constexpr uint32_t kSegSmall = 0x1;
 // Plan flags seen by the kernels (same values as the public ones).
 constexpr int32_t kFlagMomentumMask = 0x1;
 constexpr int32_t kFlagForceFull = 0x100;
@@ -80,14 +97,22 @@ constexpr int32_t kFlagNoEstimate = 0x200;
 // Random keys are 31-bit and travel through the candidate buffers as float bit patterns, so
 // the select kernels read both kinds through the same magnitude-key view.
 enum : int32_t { kKeysMagnitude = 0, kKeysRandom = 1 };
+// Which codec a call of the shared select runs for.
+enum : int32_t { kCodecTopk = 0, kCodecThreshold = 1, kCodecRandk = 2 };
 
 // Device view of a plan, passed by value to every kernel.
+//
+// Per-call counters (cand_cnt, recap_cnt, tau_cnt, near_cnt) and the digit histograms are
+// zero at the start of every call: the plan starts them at zero and the finish kernel clears
+// what a call used once it no longer needs it.  The call's lists (pending, active chunks,
+// full path) and the error flag are cleared by the streaming pass's first workgroup.
 struct DevPlan {
   int32_t n_seg;
   int32_t flags;
   int64_t n_tiles;
   int64_t n_chunks;
   int32_t n_chunk_blocks;      // min(n_chunks, kChunkBlocks): the chunk walkers of a launch
+  int32_t codec;               // kCodec* of this call
   // host-built tables
   const int64_t* seg_off;      // [n_seg + 1]
   const int64_t* tile_base;    // [n_seg + 1] first tile of each segment
@@ -100,20 +125,26 @@ struct DevPlan {
   const int64_t* cand_base;    // [n_seg] start of the segment's candidate region
   const uint32_t* cand_cap;    // [n_seg] its capacity
   const uint32_t* thr_init;    // [n_seg] threshold of a fresh plan
+  const uint32_t* seg_flags;   // [n_seg] kSeg* flags
   // per-segment state
-  uint32_t* thr;               // capture threshold of the next call
-  uint32_t* cand_cnt;          // candidates captured this call
+  uint32_t* thr;               // capture threshold of the next call (Random-k: the plan's)
+  uint32_t* cand_cnt;          // candidates captured by this call's streaming pass
+  uint32_t* recap_cnt;         // candidates re-captured by the fallback
   uint32_t* mode;
-  uint32_t* prefix;            // radix-select prefix so far
-  uint32_t* kk;                // rank still to find inside the prefix
+  uint32_t* thr_lo;            // re-capture floor of the call
+  uint32_t* pfx1;              // full path: prefix after the first digit, and the rank left
+  uint32_t* kk1;
+  uint32_t* pfx2;              // full path: prefix after the second digit, and the rank left
+  uint32_t* kk2;
   uint32_t* kth;               // k-th largest key
   uint32_t* ties;              // entries taken at exactly kth
+  uint32_t* sel_cnt;           // candidates the select ran over (emission and statistics)
   uint32_t* hist;              // [n_seg][3][kHistBins]
   uint32_t* full_list;         // [n_seg] segments on the exact full-segment path
   uint32_t* full_count;        // [1]
-  uint32_t* recap_list;        // [n_seg] segments whose candidates were not complete
-  uint32_t* recap_count;       // [1]
-  uint32_t* why;               // [n_seg] kWhy* of this call
+  uint32_t* pend_list;         // [n_seg] segments whose captured candidates were not complete
+  uint32_t* pend_count;        // [1]
+  uint32_t* near_cnt;          // [n_seg] candidates in the range that holds the k-th key
   float* beta;                 // [n_seg] threshold margin: next threshold = beta * |kth|
   uint32_t* err;               // [1] internal consistency flag (0 = fine)
   uint32_t* tile_max;          // [n_tiles] largest key of a full-path tile (int8 absmax)
@@ -128,11 +159,11 @@ struct DevPlan {
   uint32_t* tile_eq_base;      // [n_tiles] ties before the tile
   uint32_t* tile_sel_base;     // [n_tiles] kept entries before the tile
   // per-chunk state (candidate path)
-  uint32_t* chunk_gt;          // [n_chunks]
-  uint32_t* chunk_eq;
-  uint32_t* chunk_eq_base;
-  uint32_t* chunk_sel_base;
-  uint32_t* chunk_max;         // [n_chunks] largest candidate key of the chunk (int8 absmax)
+  uint32_t* chunk_gt;          // [n_chunks] keys above kth in the chunk
+  uint32_t* chunk_max;         // [n_chunks] largest key of the chunk (int8 absmax)
+  uint32_t* chunk_eq;          // [n_chunks] keys equal to kth in the chunk
+  uint32_t* chunk_eq_base;     // ties before the chunk
+  uint32_t* chunk_sel_base;    // kept entries before the chunk
   uint32_t* act_chunk;         // [n_chunks] the chunks that hold candidates this call, any order
   uint32_t* act_count;         // [1] their number
   // candidate buffers, segment s at [cand_base[s], cand_base[s] + cand_cap[s])
@@ -140,19 +171,19 @@ struct DevPlan {
   int32_t* cand_idx;
   float* sort_val;             // the same candidates in ascending index order
   int32_t* sort_idx;
-  // per-call selection (threshold and Random-k calls run on a copy of the plan whose k and
-  // thr point here, so the Top-k threshold estimate is left alone)
-  uint32_t* k_call;            // [n_seg] entries kept this call
-  uint32_t* thr_call;          // [n_seg] capture threshold of this call
+  // threshold and Random-k state
   const uint32_t* thr_rand;    // [n_seg] Random-k capture threshold (fixed per plan)
   const float* rk_scale;       // [n_seg] fl32(n / k), Random-k value scale without feedback
   uint32_t* thr_est;           // [n_seg] threshold calls: capture floor estimate (kNoCapture:
                                // none); the capture runs at max(key(tau), floor)
   float* beta_est;             // [n_seg] its margin
-  uint32_t* tau_key;           // [n_seg] threshold calls: key(|tau|) of this call
-  uint32_t* tau_cnt;           // [n_seg] entries with key >= tau_key counted by the capture
+  uint32_t* tau_cnt;           // [n_seg] entries with key >= key(|tau|) counted by the capture
   float* seg_norm;             // [n_seg] l2 norms of a clipping call (when the caller wants none)
   const float* gscale;         // [n_seg] caller's gradient scale applied on load, or null
+  // per call
+  const float* tau;            // threshold call: per-segment thresholds
+  int32_t* out_count;          // threshold call: entries kept per segment, or null
+  float* scales;               // fused int8: per-segment scales written by the select
   // cold-start sample: about 64 evenly spaced tiles of each large segment
   int64_t n_sample;
   const int32_t* sample_tile;  // [n_sample] tiles whose acc is histogrammed on a cold call
@@ -184,10 +215,10 @@ struct Int8Args {
 hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
                            float* out_vals, int32_t* out_idx, const Int8Args& q8, bool cold,
                            hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
-hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, float* e,
-                            float* u, float m, const float* tau, float* out_vals,
-                            int32_t* out_idx, int32_t* out_count, hipStream_t st,
-                            hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_threshold(const DevPlan& P, const float* g, float* e, float* u, float m,
+                            const float* tau, float* out_vals, int32_t* out_idx,
+                            int32_t* out_count, hipStream_t st, hipEvent_t ev_begin,
+                            hipEvent_t ev_end);
 hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, float m,
                         uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
                         hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);

@@ -1,21 +1,25 @@
 // gc_topk.hip -- gfx950 kernels of the error-feedback Top-k path, and the threshold and
 // Random-k sparsifiers that share its select and ordered emission.
 //
-// Top-k call (one stream, no host round trip):
-//   prep        zero the per-call counters
+// Top-k call (one stream, no host round trip; ten launches on a warm plan):
 //   ef_capture  the streaming pass over g, e (and u): momentum, EF add, write acc into e,
 //               and capture every (acc, index) whose magnitude key reaches the segment's
 //               threshold, as one index-ordered run per tile            [HBM-bound]
-//   select_init per segment: keep the candidates if they are complete (count in [k, cap]),
-//               else list the segment for re-capture or the exact full-segment path
-//   recap_*     first-digit histogram of e and capture at the exact bucket floor (only for
-//               segments whose candidates were incomplete)
-//   hist/find   x3  radix select of the k-th largest key, digits of 11, 11 and 9 bits,
-//               LDS histograms; candidates or, on the full path, the whole segment
-//   scatter     candidates into ascending index order (runs placed by tile)
-//   count/scan/emit  order-preserving compaction: keys above the k-th, then the ties in
-//               index order; writes (value, index) and zeroes e (and u) where kept
-//   finalize    next threshold estimate = key(beta * kth), beta steered by the last calls
+//   list        per segment: its path (candidates complete, small, or pending), the places
+//               of its runs in index order, its candidate chunks listed
+//   fb_hist     \   only for pending segments (too few or too many candidates, or no
+//   fb_capture   |  threshold yet); they end at once when none is pending: first-digit
+//   fb_hist2     |  histogram of e, then a re-capture at the exact bucket floor, or (a bucket
+//   fb_count    /   larger than the capacity) the radix select over the whole segment
+//   scatter     candidates into ascending index order; a histogram of their keys in bins
+//               that start at the capture threshold (two binades wide)
+//   collect     per chunk: keys above the bin that holds the k-th key, and the keys inside
+//               it appended to the segment's near list
+//   finish      one workgroup per segment: the exact k-th key from the near list (in LDS),
+//               the per-chunk offsets of the ordered emission; small segments are selected
+//               and emitted here whole, from the residual; the next threshold estimate
+//   emit        order-preserving compaction: keys above the k-th, then the ties in index
+//               order; writes (value, index) and zeroes e (and u) where kept
 //
 // Threshold and Random-k calls run the same select and emit on a per-call copy of the plan
 // (their own k and capture threshold); Random-k ranks per-element Philox keys instead of
@@ -33,18 +37,6 @@
 namespace gc {
 namespace {
 
-// ------------------------------------------------------------------------------ prep
-__global__ __launch_bounds__(kThreads) void k_prep(DevPlan P) {
-  const int s = blockIdx.x * kThreads + threadIdx.x;
-  if (s < P.n_seg) P.cand_cnt[s] = 0;
-  if (s == 0) {
-    *P.full_count = 0;
-    *P.recap_count = 0;
-    *P.act_count = 0;
-    *P.err = 0;
-  }
-}
-
 __global__ __launch_bounds__(kThreads) void k_reset(DevPlan P) {
   const int s = blockIdx.x * kThreads + threadIdx.x;
   if (s < P.n_seg) {   // as on a fresh plan: no estimate, first margins
@@ -55,42 +47,35 @@ __global__ __launch_bounds__(kThreads) void k_reset(DevPlan P) {
   }
 }
 
-// Threshold and Random-k calls: this call's k (the plan's, reduced after the capture for a
-// threshold call) and capture threshold: for a threshold call max(key(|tau|), floor), the floor
-// being the estimate of the k-th largest key kept from the last threshold calls (the capture
-// then stays within capacity when more than k entries reach tau); for Random-k the plan's.
-__global__ __launch_bounds__(kThreads) void k_prep_call(DevPlan P, const float* __restrict__ tau) {
-  const int s = blockIdx.x * kThreads + threadIdx.x;
-  if (s < P.n_seg) {
-    P.cand_cnt[s] = 0;
-    P.k_call[s] = P.k[s];
-    if (tau) {
-      const uint32_t tk = mag_key(tau[s]), fl = P.thr_est[s];
-      P.tau_key[s] = tk;
-      P.tau_cnt[s] = 0;
-      P.thr_call[s] = fl == kNoCapture ? tk : max(tk, fl);
-    } else {
-      P.thr_call[s] = P.thr_rand[s];
-    }
-  }
-  if (s == 0) {
-    *P.full_count = 0;
-    *P.recap_count = 0;
-    *P.act_count = 0;
-    *P.err = 0;
-  }
+// ------------------------------------------------------------------- per-call segment state
+// Entries segment s keeps in this call: the plan's k, or for a threshold call the number of
+// keys at or above key(|tau_s|) when that is smaller (the plan's k is then a cap).
+__device__ __forceinline__ uint32_t call_k(const DevPlan& P, int s) {
+  const uint32_t k = P.k[s];
+  return P.codec == kCodecThreshold ? min(P.tau_cnt[s], k) : k;
 }
 
-// Threshold call: keep min(number of keys at or above key(|tau|), k) entries per segment (the
-// capture counted them all, also above a floor and past the candidate capacity).  The
-// candidates, captured at max(key(|tau|), floor), then hold them iff at least that many were
-// captured; otherwise the segment takes the exact fallback.
-__global__ __launch_bounds__(kThreads) void k_thresh_k(DevPlan P, int32_t* __restrict__ count) {
-  const int s = blockIdx.x * kThreads + threadIdx.x;
-  if (s >= P.n_seg) return;
-  const uint32_t kk = min(P.tau_cnt[s], P.k[s]);
-  P.k_call[s] = kk;
-  if (count) count[s] = (int32_t)kk;
+// Capture threshold of segment s in this call: the Top-k estimate, the Random-k plan
+// threshold, or for a threshold call max(key(|tau|), floor), the floor being the estimate of
+// the k-th largest key kept from the last threshold calls (so the capture stays within its
+// capacity when more than k entries reach tau).  Small segments capture nothing.
+__device__ __forceinline__ uint32_t capture_thr(const DevPlan& P, int s) {
+  if (P.codec != kCodecThreshold) return P.thr[s];
+  if (P.seg_flags[s] & kSegSmall) return kNoCapture;
+  const uint32_t tk = mag_key(P.tau[s]), fl = P.thr_est[s];
+  return fl == kNoCapture ? tk : max(tk, fl);
+}
+
+// True when the streaming pass's capture does not hold segment s's k largest keys (fewer
+// than k candidates, more than the capacity, or no threshold yet), so the fallback kernels
+// re-capture it or select it over the whole segment.  Small segments and k = 0 never are.
+__device__ __forceinline__ bool seg_pending(const DevPlan& P, int s) {
+  if (P.seg_flags[s] & kSegSmall) return false;
+  const uint32_t k = call_k(P, s);
+  if (k == 0) return false;
+  if (P.flags & kFlagForceFull) return true;
+  const uint32_t c = P.cand_cnt[s];
+  return capture_thr(P, s) == kNoCapture || c < k || c > P.cand_cap[s];
 }
 
 // Tile t of segment s: first element and length.
@@ -103,11 +88,11 @@ __device__ __forceinline__ void tile_range(const DevPlan& P, int s, int64_t t, i
 }
 
 // Capture, in index order, the elements of tile t (values acc in the tile layout) whose key
-// reaches thr: one atomic on the segment's counter reserves the tile's run; entries past the
-// capacity are counted but not stored (the segment then leaves the candidate path).
+// reaches thr: one atomic on the segment's counter (*count) reserves the tile's run; entries
+// past the capacity are counted but not stored (the segment then leaves the candidate path).
 __device__ __forceinline__ void capture_tile(const DevPlan& P, int s, int64_t t, int64_t start,
                                              int len, const f4 (&acc)[kSlots], uint32_t thr,
-                                             uint32_t* s_w, uint32_t* s_base) {
+                                             uint32_t* count, uint32_t* s_w, uint32_t* s_base) {
   const int pb = slot_base();
   uint32_t bits[kSlots];
 #pragma unroll
@@ -121,7 +106,7 @@ __device__ __forceinline__ void capture_tile(const DevPlan& P, int s, int64_t t,
   uint32_t woff[kSlots];
   const uint32_t total = tile_rank(bits, woff, s_w);
   if (threadIdx.x == 0) {
-    const uint32_t base = total ? atomicAdd(&P.cand_cnt[s], total) : 0u;
+    const uint32_t base = total ? atomicAdd(count, total) : 0u;
     P.run_off[t] = base;
     P.run_cnt[t] = total;
     *s_base = base;
@@ -150,6 +135,17 @@ __device__ __forceinline__ void capture_tile(const DevPlan& P, int s, int64_t t,
   }
 }
 
+// The call's lists and the error flag start empty: cleared by the first workgroup of the
+// streaming pass (the kernels that fill them run after it; the last call's readers have ended).
+__device__ __forceinline__ void reset_call_lists(const DevPlan& P) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *P.pend_count = 0;
+    *P.act_count = 0;
+    *P.full_count = 0;
+    *P.err = 0;
+  }
+}
+
 // -------------------------------------------------------------------------- ef_capture
 // One tile per workgroup.  acc = e + (u = m*u + g | g) is written back into e; elements
 // whose key reaches the segment's threshold are captured (capture_tile).
@@ -175,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
   const int len = desc.z, s = desc.w;
   const int pb = slot_base();
   const float gf = kScale ? P.gscale[s] : 1.0f;
+  reset_call_lists(P);
 
   f4 acc[kSlots];
   if (len == kTile && (start & 3) == 0) {
@@ -223,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
       }
   }
   if (kCountTau) {
-    const uint32_t tk = P.tau_key[s];
+    const uint32_t tk = mag_key(P.tau[s]);
     uint32_t c = 0;
 #pragma unroll
     for (int v = 0; v < kSlots; ++v)
@@ -241,44 +238,19 @@ __global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float*
       if (tot) atomicAdd(&P.tau_cnt[s], tot);
     }
   }
-  const uint32_t thr = P.thr[s];
-  if (thr == kNoCapture) return;  // uniform: this segment re-captures later
-  capture_tile(P, s, t, start, len, acc, thr, s_w, &s_base);
+  const uint32_t thr = kCountTau ? capture_thr(P, s) : P.thr[s];
+  if (thr == kNoCapture) return;  // uniform: nothing to capture (small, or not estimated yet)
+  capture_tile(P, s, t, start, len, acc, thr, &P.cand_cnt[s], s_w, &s_base);
 }
 
-// ------------------------------------------------------------------------- select_init
-// Per segment: are the captured candidates complete?  Complete means at least k of them
-// and none lost to the capacity; then every key >= the k-th largest was captured.
-__global__ __launch_bounds__(kThreads) void k_select_init(DevPlan P) {
-  const int s = blockIdx.x;
-  const uint32_t k = P.k[s], thr = P.thr[s], c = P.cand_cnt[s], cap = P.cand_cap[s];
-  uint32_t mode, why = kWhyNone;
-  if (k == 0) {
-    mode = kModeSkip;
-  } else if (thr != kNoCapture && c >= k && c <= cap && !(P.flags & kFlagForceFull)) {
-    mode = kModeCand;
-  } else {
-    mode = kModePending;
-    why = thr == kNoCapture ? kWhyCold : (c < k ? kWhyMiss : kWhyOverflow);
-  }
-  if (threadIdx.x == 0) {
-    P.mode[s] = mode;
-    P.why[s] = why;
-    P.prefix[s] = 0;
-    P.kk[s] = k;
-    P.kth[s] = 0;
-    P.ties[s] = 0;
-    if (mode == kModePending) P.recap_list[atomicAdd(P.recap_count, 1u)] = (uint32_t)s;
-  }
-  if (mode == kModeSkip) return;
-  uint32_t* h = P.hist + (size_t)s * 3 * kHistBins;
-  for (int i = threadIdx.x; i < 3 * kHistBins; i += kThreads) h[i] = 0;
-}
-
+// ------------------------------------------------------------------------ digit histograms
 __device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 9 : 0); }
 __device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 0x1FFu : 0x7FFu; }
 __device__ __forceinline__ uint32_t prefix_mask(int pass) {
   return pass == 0 ? 0u : (pass == 1 ? 0x7FF00000u : 0x7FFFFE00u);
+}
+__device__ __forceinline__ uint32_t* seg_hist(const DevPlan& P, int s, int pass) {
+  return P.hist + ((size_t)s * 3 + pass) * kHistBins;
 }
 
 // Add the keys of one tile-shaped block of values into the LDS histogram.
@@ -302,40 +274,25 @@ __device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* gh) {
   }
 }
 
-// Histogram of one digit over every tile of the listed segments (values read from e).
-__device__ void hist_listed_tiles(const DevPlan& P, const float* __restrict__ e,
-                                  const uint32_t* list, uint32_t count, uint32_t want_mode,
-                                  int pass, int fb, uint32_t* h) {
-  for (uint32_t li = 0; li < count; ++li) {
-    const int s = (int)list[li];
-    if (P.mode[s] != want_mode) continue;
-    const uint32_t prefix = P.prefix[s];
-    uint32_t* gh = P.hist + ((size_t)s * 3 + pass) * kHistBins;
-    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
-      int64_t start;
-      int len;
-      tile_range(P, s, t, &start, &len);
-      for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
-      f4 x[kSlots];
-      key_tile(P, e, start, len, x);
-      __syncthreads();
-      hist_add(h, x, len, prefix, pass);
-      __syncthreads();
-      hist_flush(h, gh);
-      __syncthreads();
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------- recapture
-// First-digit histogram of the segments whose candidates were not complete.
-__global__ __launch_bounds__(kThreads) void k_recap_hist(DevPlan P, const float* __restrict__ e) {
-  __shared__ uint32_t h[kHistBins];
-  hist_listed_tiles(P, e, P.recap_list, *P.recap_count, kModePending, 0, blockIdx.x, h);
+// One digit's histogram of tile t of segment s (keys read from e, or Random-k keys), added
+// into the segment's global histogram.  Contains barriers.
+__device__ void hist_tile(const DevPlan& P, const float* __restrict__ e, int s, int64_t t,
+                          uint32_t prefix, int pass, uint32_t* h) {
+  int64_t start;
+  int len;
+  tile_range(P, s, t, &start, &len);
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+  f4 x[kSlots];
+  key_tile(P, e, start, len, x);
+  __syncthreads();
+  hist_add(h, x, len, prefix, pass);
+  __syncthreads();
+  hist_flush(h, seg_hist(P, s, pass));
+  __syncthreads();
 }
 
 // Digit of the k-th largest key in a histogram (descending scan): d and the count above it.
-// s_tmp: __shared__ uint32_t[kWaves]; s_out: __shared__ uint32_t[2].  Contains barriers.
+// s_tmp: __shared__ uint32_t[kWaves]; s_out: __shared__ uint32_t[3].  Contains barriers.
 __device__ bool find_digit(const uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
                            uint32_t* d_out, uint32_t* above_out, uint32_t* bin_out) {
   constexpr int kPer = kHistBins / kThreads;
@@ -366,219 +323,169 @@ __device__ bool find_digit(const uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uin
   *d_out = s_out[0];
   *above_out = s_out[1];
   *bin_out = s_out[2];
-  return s_out[0] != 0xFFFFFFFFu;
+  __syncthreads();   // s_out may be written again by the next call
+  return *d_out != 0xFFFFFFFFu;
 }
 
-// Per pending segment: the first digit of the k-th largest key.  If the keys at or above
-// that bucket's floor fit the capacity, they are re-captured (kModeRecap); otherwise the
-// segment runs the radix select over all its elements (kModeFull).  Pass 0 is done here.
-__global__ __launch_bounds__(kThreads) void k_recap_decide(DevPlan P) {
-  __shared__ uint32_t s_tmp[kWaves];
-  __shared__ uint32_t s_out[3];
-  const int s = blockIdx.x;
-  if (P.mode[s] != kModePending) return;
-  const uint32_t k = P.k[s];
-  uint32_t d, above, bin;
-  const bool ok = find_digit(P.hist + (size_t)s * 3 * kHistBins, k, s_tmp, s_out, &d, &above,
-                             &bin);
-  if (threadIdx.x != 0) return;
-  if (!ok) {
-    atomicOr(P.err, 1u);
-    P.mode[s] = kModeSkip;
-    return;
-  }
-  P.prefix[s] = d << 20;
-  P.kk[s] = k - above;
-  if (!(P.flags & kFlagForceFull) && above + bin <= P.cand_cap[s]) {
-    P.mode[s] = kModeRecap;
-    P.thr[s] = d << 20;
-    P.cand_cnt[s] = 0;
-  } else {
-    P.mode[s] = kModeFull;
-    P.full_list[atomicAdd(P.full_count, 1u)] = (uint32_t)s;
-  }
-}
-
-// Re-capture from e (which holds acc) at the exact bucket floor.
-__global__ __launch_bounds__(kThreads) void k_recapture(DevPlan P, const float* __restrict__ e) {
-  __shared__ uint32_t s_w[kWaves];
-  __shared__ uint32_t s_base;
-  const uint32_t count = *P.recap_count;
-  for (uint32_t li = 0; li < count; ++li) {
-    const int s = (int)P.recap_list[li];
-    if (P.mode[s] != kModeRecap) continue;
-    const uint32_t thr = P.thr[s];
-    for (int64_t t = P.tile_base[s] + blockIdx.x; t < P.tile_base[s + 1]; t += kFullBlocks) {
-      int64_t start;
-      int len;
-      tile_range(P, s, t, &start, &len);
-      f4 x[kSlots];
-      key_tile(P, e, start, len, x);
-      capture_tile(P, s, t, start, len, x, thr, s_w, &s_base);
-      __syncthreads();
-    }
-  }
-}
-
-__device__ __forceinline__ bool has_candidates(uint32_t mode) {
-  return mode == kModeCand || mode == kModeRecap;
-}
-
-// Per segment with candidates: index-ordered destination of every tile's run (exclusive
-// scan of the run sizes over the segment's tiles).
-// Also appends the segment's chunks that hold candidates to the call's list of active chunks
-// (the later chunk kernels walk that list instead of every chunk of the capacity).
-__global__ __launch_bounds__(1024) void k_runs(DevPlan P) {
-  __shared__ uint32_t s_tmp[16];
-  __shared__ uint32_t s_act;
-  const int s = blockIdx.x;
-  if (!has_candidates(P.mode[s])) return;
+// ---------------------------------------------------------------------- list and runs
+// Index-ordered place of every tile's run of segment s (an exclusive scan of the run sizes
+// over its tiles, four per thread), and the segment's candidate chunks appended to the call's
+// list of active chunks.  Contains barriers.
+__device__ void seg_runs(const DevPlan& P, int s, uint32_t c, uint32_t* s_tmp, uint32_t* s_act) {
   const int64_t t0 = P.tile_base[s], t1 = P.tile_base[s + 1];
   uint32_t carry = 0;
-  for (int64_t tb = t0; tb < t1; tb += 1024) {
-    const int64_t t = tb + threadIdx.x;
-    const uint32_t n = t < t1 ? P.run_cnt[t] : 0u;
+  for (int64_t tb = t0; tb < t1; tb += kThreads * 4) {
+    const int64_t tq = tb + (int64_t)threadIdx.x * 4;
+    uint32_t n[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) n[q] = tq + q < t1 ? P.run_cnt[tq + q] : 0u;
     uint32_t tot;
-    const uint32_t ex = block_excl_scan<1024>(n, s_tmp, &tot);
-    if (t < t1) P.run_dst[t] = carry + ex;
+    uint32_t run = carry + block_excl_scan<kThreads>(n[0] + n[1] + n[2] + n[3], s_tmp, &tot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (tq + q < t1) P.run_dst[tq + q] = run;
+      run += n[q];
+    }
     carry += tot;
   }
-  const int64_t c0 = P.chunk_base[s];
-  const uint32_t na = (uint32_t)min(((int64_t)P.cand_cnt[s] + kChunk - 1) / kChunk,
-                                    P.chunk_base[s + 1] - c0);
-  if (threadIdx.x == 0) s_act = na ? atomicAdd(P.act_count, na) : 0u;
+  const uint32_t nch = (c + kChunk - 1) / kChunk;
+  if (threadIdx.x == 0) {
+    if (carry != c) atomicOr(P.err, 8u);
+    *s_act = atomicAdd(P.act_count, nch);
+  }
   __syncthreads();
-  for (uint32_t j = threadIdx.x; j < na; j += 1024) P.act_chunk[s_act + j] = (uint32_t)(c0 + j);
+  for (uint32_t i = threadIdx.x; i < nch; i += kThreads)
+    P.act_chunk[*s_act + i] = (uint32_t)(P.chunk_base[s] + i);
 }
 
-// ------------------------------------------------------------------------------ scatter
-// Candidates into ascending index order (tile t's run goes to run_dst[t]); on the estimate
-// path, also the first-digit histogram of the candidates.  One chunk; contains barriers.
-__device__ void scatter_chunk(const DevPlan& P, int64_t ch, uint32_t* h, uint32_t* s_m) {
-  const int s = P.chunk_seg[ch];
-  const uint32_t mode = P.mode[s];
-  if (!has_candidates(mode)) return;
-  const int64_t c = P.cand_cnt[s];
-  const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
-  if (j0 >= c) return;
-  const bool do_hist = mode == kModeCand;
-  if (do_hist)
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
-  const int len = (int)min((int64_t)kChunk, c - j0);
-  const int64_t cb = P.cand_base[s], tb = P.tile_base[s];
-  constexpr int kPer = kChunk / kThreads;
-  int32_t ix[kPer];
-  float vx[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int p = r * kThreads + threadIdx.x;
-    ix[r] = p < len ? P.cand_idx[cb + j0 + p] : 0;
-    vx[r] = p < len ? P.cand_val[cb + j0 + p] : 0.0f;
-  }
-  if (do_hist) __syncthreads();
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int p = r * kThreads + threadIdx.x;
-    if (p < len) {
-      const int64_t t = tb + ix[r] / kTile;
-      const uint32_t dst = P.run_dst[t] + ((uint32_t)(j0 + p) - P.run_off[t]);
-      if (ix[r] >= 0 && t < P.tile_base[s + 1] && dst < (uint32_t)c) {
-        P.sort_val[cb + dst] = vx[r];
-        P.sort_idx[cb + dst] = ix[r];
-      } else {
-        atomicOr(P.err, 8u);
-      }
-      if (do_hist) atomicAdd(&h[mag_key(vx[r]) >> 20], 1u);
-    }
-  }
-  uint32_t mx = 0;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r)
-    if (r * kThreads + (int)threadIdx.x < len) mx = max(mx, mag_key(vx[r]));
-  mx = block_max<kThreads>(mx, s_m);
-  if (threadIdx.x == 0) P.chunk_max[ch] = mx;
-  if (do_hist) {
-    __syncthreads();
-    hist_flush(h, P.hist + (size_t)s * 3 * kHistBins);
-  }
-}
-
-// The workgroups walk the call's list of chunks that hold candidates.
-__global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t s_m[kWaves];
-  const uint32_t na = *P.act_count;
-  for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks) {
-    scatter_chunk(P, P.act_chunk[i], h, s_m);
-    __syncthreads();   // the next chunk reuses h
-  }
-}
-
-// --------------------------------------------------------------------------------- hist
-// Passes 1 and 2.  Workgroups [0, n_chunk_blocks) histogram the sorted candidate chunks of the
-// call's active list; the last kFullBlocks the tiles of the segments on the full path.
-__device__ void hist_chunk(const DevPlan& P, int64_t ch, int pass, uint32_t* h) {
-  const int s = P.chunk_seg[ch];
-  if (!has_candidates(P.mode[s])) return;
-  const int64_t c = P.cand_cnt[s];
-  const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
-  if (j0 >= c) return;
-  const int len = (int)min((int64_t)kChunk, c - j0);
-  const uint32_t prefix = P.prefix[s];
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
-  f4 x[kSlots];
-  load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
-  __syncthreads();
-  hist_add(h, x, len, prefix, pass);
-  __syncthreads();
-  hist_flush(h, P.hist + ((size_t)s * 3 + pass) * kHistBins);
-}
-
-__global__ __launch_bounds__(kThreads) void k_hist(DevPlan P, const float* __restrict__ e,
-                                                   int pass) {
-  __shared__ uint32_t h[kHistBins];
-  if (blockIdx.x < (uint32_t)P.n_chunk_blocks) {
-    const uint32_t na = *P.act_count;
-    for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks) {
-      hist_chunk(P, P.act_chunk[i], pass, h);
-      __syncthreads();   // the next chunk reuses h
-    }
-    return;
-  }
-  hist_listed_tiles(P, e, P.full_list, *P.full_count, kModeFull, pass,
-                    blockIdx.x - P.n_chunk_blocks, h);
-}
-
-// --------------------------------------------------------------------------------- find
-// Per segment: the digit of this pass that holds the kk-th largest key of the prefix.
-// Pass 0 only for the estimate path (the others took it in k_recap_decide).
-__global__ __launch_bounds__(kThreads) void k_find(DevPlan P, int pass) {
+// ------------------------------------------------------------------------------- fallback
+// The tiles of the listed pending segments for which pick(s) holds, in list order, dealt to
+// the workgroups of the launch in turn (picked tile j goes to workgroup j mod G).  For each
+// picked segment that has tiles here, seg_fn(s, owner) runs first (owner: this workgroup has
+// the segment's first tile, so exactly one workgroup is the owner), then tile_fn(s, t) for
+// each of its tiles here.  With no pending segment the kernel ends at once.  The picks, the
+// segment loop and the tile loop are uniform over the workgroup, so both functions may
+// contain barriers.
+template <typename Pick, typename SegFn, typename TileFn>
+__device__ void for_pending_tiles(const DevPlan& P, Pick pick, SegFn seg_fn, TileFn tile_fn) {
+  __shared__ uint32_t s_seg[kThreads];
+  __shared__ uint32_t s_first[kThreads];
   __shared__ uint32_t s_tmp[kWaves];
-  __shared__ uint32_t s_out[3];
-  const int s = blockIdx.x;
-  const uint32_t mode = P.mode[s];
-  if (mode == kModeSkip || (pass == 0 && mode != kModeCand)) return;
-  const uint32_t kk = P.kk[s];
-  uint32_t d, above, bin;
-  const bool ok = find_digit(P.hist + ((size_t)s * 3 + pass) * kHistBins, kk, s_tmp, s_out, &d,
-                             &above, &bin);
-  if (threadIdx.x != 0) return;
-  if (!ok) {  // cannot happen when the histogram holds >= kk keys
-    atomicOr(P.err, 1u);
-    return;
-  }
-  const uint32_t prefix = P.prefix[s] | (d << digit_shift(pass));
-  const uint32_t nk = kk - above;
-  P.prefix[s] = prefix;
-  P.kk[s] = nk;
-  if (pass == 2) {
-    P.kth[s] = prefix;
-    P.ties[s] = nk;
+  const uint32_t np = *P.pend_count;
+  if (np == 0) return;   // uniform
+  const uint32_t G = gridDim.x, w = blockIdx.x;
+  uint64_t rot = 0;   // picked tiles of the segments before this chunk of the list
+  for (uint32_t c0 = 0; c0 < np; c0 += kThreads) {
+    const uint32_t i = c0 + threadIdx.x;
+    const int s = i < np ? (int)P.pend_list[i] : -1;
+    const bool p = s >= 0 && pick(s);
+    const uint32_t nt = p ? (uint32_t)(P.tile_base[s + 1] - P.tile_base[s]) : 0u;
+    uint32_t m, tt;
+    const uint32_t at = block_excl_scan<kThreads>(p ? 1u : 0u, s_tmp, &m);
+    const uint32_t toff = block_excl_scan<kThreads>(nt, s_tmp, &tt);
+    if (p) {
+      s_seg[at] = (uint32_t)s;
+      s_first[at] = (uint32_t)((w + G - (uint32_t)((rot + toff) % G)) % G);
+    }
+    __syncthreads();
+    for (uint32_t q = 0; q < m; ++q) {
+      const int si = (int)s_seg[q];
+      const int64_t j0 = s_first[q];
+      const int64_t t0 = P.tile_base[si], nts = P.tile_base[si + 1] - t0;
+      if (j0 >= nts) continue;   // uniform: none of this segment's tiles is here
+      seg_fn(si, j0 == 0);
+      for (int64_t j = j0; j < nts; j += G) tile_fn(si, t0 + j);
+    }
+    rot += tt;
+    __syncthreads();   // s_seg and s_first are rewritten for the next chunk
   }
 }
 
-// -------------------------------------------------------------------------------- count
-// Keys above and equal to the k-th, per candidate chunk (sorted) or per full-path tile.
+// First-digit histogram of e over the pending segments.
+__global__ __launch_bounds__(kThreads) void k_fb_hist(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t h[kHistBins];
+  for_pending_tiles(
+      P, [&](int) { return true; }, [&](int, bool) {},
+      [&](int s, int64_t t) { hist_tile(P, e, s, t, 0u, 0, h); });
+}
+
+// Per pending segment: the first digit of the k-th largest key.  If the keys at or above that
+// bucket's floor fit the capacity, they are re-captured (kModeRecap, runs rewritten for every
+// tile); otherwise the segment takes the radix select over all its elements (kModeFull) and
+// its second digit is histogrammed here.  The owner workgroup records the decision.
+__global__ __launch_bounds__(kThreads) void k_fb_capture(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t s_tmp[kWaves], s_out[3], s_w[kWaves], s_base;
+  uint32_t d0 = 0, kk = 0;
+  bool ok = false, fits = false;
+  for_pending_tiles(
+      P, [&](int) { return true; },
+      [&](int s, bool owner) {
+        const uint32_t k = call_k(P, s);
+        uint32_t above, bin;
+        ok = find_digit(seg_hist(P, s, 0), k, s_tmp, s_out, &d0, &above, &bin);
+        fits = ok && !(P.flags & kFlagForceFull) && above + bin <= P.cand_cap[s];
+        kk = ok ? k - above : 0u;
+        if (owner && threadIdx.x == 0) {
+          if (!ok) atomicOr(P.err, 1u);
+          P.mode[s] = fits ? kModeRecap : kModeFull;
+          P.thr_lo[s] = d0 << 20;
+          P.pfx1[s] = d0 << 20;
+          P.kk1[s] = kk;
+        }
+      },
+      [&](int s, int64_t t) {
+        if (!ok) return;   // uniform
+        if (fits) {
+          int64_t start;
+          int len;
+          tile_range(P, s, t, &start, &len);
+          f4 x[kSlots];
+          key_tile(P, e, start, len, x);
+          capture_tile(P, s, t, start, len, x, d0 << 20, &P.recap_cnt[s], s_w, &s_base);
+          __syncthreads();
+        } else {
+          hist_tile(P, e, s, t, d0 << 20, 1, h);
+        }
+      });
+}
+
+// Re-captured segments: their runs placed and chunks listed (one workgroup per segment, in
+// list order); full path: the second digit, then the histogram of the last 9 bits.
+__global__ __launch_bounds__(kThreads) void k_fb_hist2(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t s_tmp[kWaves], s_out[3], s_act;
+  const uint32_t np = *P.pend_count;
+  if (np == 0) return;   // uniform
+  for (uint32_t i = blockIdx.x; i < np; i += gridDim.x) {
+    const int s = (int)P.pend_list[i];
+    if (P.mode[s] != kModeRecap) continue;   // uniform
+    const uint32_t c = P.recap_cnt[s];
+    if (threadIdx.x == 0) P.sel_cnt[s] = c;
+    seg_runs(P, s, c, s_tmp, &s_act);
+    __syncthreads();
+  }
+  uint32_t pfx = 0;
+  bool ok = false;
+  for_pending_tiles(
+      P, [&](int s) { return P.mode[s] == kModeFull; },
+      [&](int s, bool owner) {
+        uint32_t d, above, bin;
+        const uint32_t kk = P.kk1[s];
+        ok = find_digit(seg_hist(P, s, 1), kk, s_tmp, s_out, &d, &above, &bin);
+        pfx = P.pfx1[s] | (d << 9);
+        if (owner && threadIdx.x == 0) {
+          if (!ok) atomicOr(P.err, 1u);
+          P.pfx2[s] = pfx;
+          P.kk2[s] = ok ? kk - above : 0u;
+        }
+      },
+      [&](int s, int64_t t) {
+        if (ok) hist_tile(P, e, s, t, pfx, 2, h);
+      });
+}
+
+// Keys above and equal to kth in one tile-shaped block (block sums).  Contains barriers.
 __device__ __forceinline__ void count_block(const f4 (&x)[kSlots], int len, uint32_t kth,
                                             uint32_t* s_tmp, uint32_t* gt_out,
                                             uint32_t* eq_out) {
@@ -593,116 +500,120 @@ __device__ __forceinline__ void count_block(const f4 (&x)[kSlots], int len, uint
       gt += (ok && key > kth) ? 1u : 0u;
       eq += (ok && key == kth) ? 1u : 0u;
     }
-  const uint32_t tg = block_sum<kThreads>(gt, s_tmp);
-  const uint32_t te = block_sum<kThreads>(eq, s_tmp);
-  if (threadIdx.x == 0) {
-    *gt_out = tg;
-    *eq_out = te;
-  }
+  *gt_out = block_sum<kThreads>(gt, s_tmp);
+  *eq_out = block_sum<kThreads>(eq, s_tmp);
 }
 
-__device__ __forceinline__ void count_cand_chunk(const DevPlan& P, int64_t ch, uint32_t* s_tmp) {
-  const int s = P.chunk_seg[ch];
-  if (!has_candidates(P.mode[s])) return;
-  const int64_t c = P.cand_cnt[s];
-  const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
-  if (j0 >= c) return;
-  const int len = (int)min((int64_t)kChunk, c - j0);
-  f4 x[kSlots];
-  load_tile(P.sort_val + P.cand_base[s] + j0, len, x);
-  count_block(x, len, P.kth[s], s_tmp, &P.chunk_gt[ch], &P.chunk_eq[ch]);
+// Full path: the last digit gives the k-th key and the ties to take; then the keys above and
+// at it per tile, and each tile's largest key (the int8 scale).  The owner lists the segment.
+__global__ __launch_bounds__(kThreads) void k_fb_count(DevPlan P, const float* __restrict__ e) {
+  __shared__ uint32_t s_tmp[kWaves], s_out[3];
+  uint32_t kth = 0;
+  bool ok = false;
+  for_pending_tiles(
+      P, [&](int s) { return P.mode[s] == kModeFull; },
+      [&](int s, bool owner) {
+        uint32_t d, above, bin;
+        const uint32_t kk = P.kk2[s];
+        ok = find_digit(seg_hist(P, s, 2), kk, s_tmp, s_out, &d, &above, &bin);
+        kth = P.pfx2[s] | d;
+        if (owner && threadIdx.x == 0) {
+          if (!ok) atomicOr(P.err, 1u);
+          P.kth[s] = kth;
+          P.ties[s] = ok ? kk - above : 0u;
+          P.full_list[atomicAdd(P.full_count, 1u)] = (uint32_t)s;
+        }
+      },
+      [&](int s, int64_t t) {
+        if (!ok) return;   // uniform
+        int64_t start;
+        int len;
+        tile_range(P, s, t, &start, &len);
+        f4 x[kSlots];
+        key_tile(P, e, start, len, x);
+        uint32_t gt, eq;
+        count_block(x, len, kth, s_tmp, &gt, &eq);
+        uint32_t mx = 0;
+        const int pb = slot_base();
+#pragma unroll
+        for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (pb + v * 256 + c < len) mx = max(mx, mag_key(x[v][c]));
+        mx = block_max<kThreads>(mx, s_tmp);
+        if (threadIdx.x == 0) {
+          P.tile_gt[t] = gt;
+          P.tile_eq[t] = eq;
+          P.tile_max[t] = mx;
+        }
+      });
 }
 
-__device__ __forceinline__ void count_full_tiles(const DevPlan& P, const float* __restrict__ e,
-                                                 int fb, uint32_t* s_tmp) {
-  const uint32_t nf = *P.full_count;
-  for (uint32_t li = 0; li < nf; ++li) {
-    const int s = (int)P.full_list[li];
-    const uint32_t kth = P.kth[s];
-    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
-      int64_t start;
-      int len;
-      tile_range(P, s, t, &start, &len);
-      f4 x[kSlots];
-      key_tile(P, e, start, len, x);
-      count_block(x, len, kth, s_tmp, &P.tile_gt[t], &P.tile_eq[t]);
-      uint32_t mx = 0;
-      const int pb = slot_base();
+// ---------------------------------------------------------------------------- cold start
+// A plan's first call has no k-th key to start from.  Rather than capture nothing and
+// re-capture every large segment from two extra passes over it, the call first forms acc on
+// about 64 evenly spaced tiles of each such segment (exactly as the streaming pass will, but
+// without storing it), histograms the first key digit, and sets the capture threshold
+// GC_SAMPLE_MARGIN digits below the sample's estimate of the k-th key.  A wrong estimate only
+// costs the usual re-capture: the candidates are checked for completeness as on every call.
+template <bool kMomentum>
+__global__ __launch_bounds__(kThreads) void k_sample_hist(DevPlan P, const float* __restrict__ g,
+                                                         const float* __restrict__ e,
+                                                         const float* __restrict__ u, float m) {
+  __shared__ uint32_t h[kHistBins];
+  const int64_t t = P.sample_tile[blockIdx.x];
+  const int4 desc = P.tile_desc[t];
+  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+  const int len = desc.z, s = desc.w;
+  const float gf = grad_scale(P, s);
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+  f4 gv[kSlots], acc[kSlots], uv[kSlots];
+  load_tile(g + start, len, gv);
+  load_tile(e + start, len, acc);
+  if (kMomentum) load_tile(u + start, len, uv);
+  __syncthreads();
+  const int pb = slot_base();
 #pragma unroll
-      for (int v = 0; v < kSlots; ++v)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (pb + v * 256 + c < len) mx = max(mx, mag_key(x[v][c]));
-      mx = block_max<kThreads>(mx, s_tmp);
-      if (threadIdx.x == 0) P.tile_max[t] = mx;
+  for (int v = 0; v < kSlots; ++v) {
+    f4 x = gv[v] * gf;
+    if (kMomentum) {
+      const f4 mu = m * uv[v];
+      x = mu + x;
     }
+    acc[v] = acc[v] + x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (pb + v * 256 + c < len) atomicAdd(&h[mag_key(acc[v][c]) >> 20], 1u);
   }
+  __syncthreads();
+  hist_flush(h, seg_hist(P, s, 0));
 }
 
-// Workgroups [0, n_chunk_blocks) count the active candidate chunks; the last kFullBlocks the
-// tiles of the segments on the full path (one launch for both).
-__global__ __launch_bounds__(kThreads) void k_count(DevPlan P, const float* __restrict__ e) {
+// Per sampled segment still without an estimate: the first-digit bucket d that holds the
+// sample's ceil(k * sample / n)-th largest key; the threshold is the floor of bucket
+// d - GC_SAMPLE_MARGIN.  The sample's histogram is cleared afterwards (the fallback kernels of
+// the same call may need the segment's histogram).
+__global__ __launch_bounds__(kThreads) void k_sample_decide(DevPlan P) {
   __shared__ uint32_t s_tmp[kWaves];
-  if (blockIdx.x < (uint32_t)P.n_chunk_blocks) {
-    const uint32_t na = *P.act_count;
-    for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks)
-      count_cand_chunk(P, P.act_chunk[i], s_tmp);
-  } else {
-    count_full_tiles(P, e, (int)(blockIdx.x - P.n_chunk_blocks), s_tmp);
-  }
-}
-
-// --------------------------------------------------------------------------------- scan
-// Per segment, over its chunks (candidates) or tiles (full path) in index order: ties
-// before each item, then kept entries before each item (ties taken: the first `ties`).
-__global__ __launch_bounds__(1024) void k_scan(DevPlan P, float* __restrict__ scales) {
-  __shared__ uint32_t s_tmp[16];
+  __shared__ uint32_t s_out[3];
   const int s = blockIdx.x;
-  const uint32_t mode = P.mode[s];
-  if (mode == kModeSkip) {
-    if (scales && threadIdx.x == 0) scales[s] = 0.0f;  // fused int8: no kept values
-    return;
+  const int64_t ns = P.sample_elems[s];
+  if (ns == 0) return;
+  uint32_t* h = seg_hist(P, s, 0);
+  if (P.thr[s] == kNoCapture) {
+    const int64_t n = P.seg_off[s + 1] - P.seg_off[s];
+    const int64_t k = P.k[s];
+    const uint32_t kk = (uint32_t)max((int64_t)1, (k * ns + n - 1) / n);
+    uint32_t d, above, bin;
+    const bool ok = find_digit(h, kk, s_tmp, s_out, &d, &above, &bin);
+    if (threadIdx.x == 0 && ok)
+      P.thr[s] = d > (uint32_t)GC_SAMPLE_MARGIN ? (d - (uint32_t)GC_SAMPLE_MARGIN) << 20 : 0u;
   }
-  const uint32_t r = P.ties[s];
-  int64_t base, n;
-  const uint32_t *GT, *EQ, *MX;
-  uint32_t *EQB, *SELB;
-  if (has_candidates(mode)) {
-    base = P.chunk_base[s];
-    n = ((int64_t)P.cand_cnt[s] + kChunk - 1) / kChunk;
-    GT = P.chunk_gt; EQ = P.chunk_eq; EQB = P.chunk_eq_base; SELB = P.chunk_sel_base;
-    MX = P.chunk_max;
-  } else {
-    base = P.tile_base[s];
-    n = P.tile_base[s + 1] - base;
-    GT = P.tile_gt; EQ = P.tile_eq; EQB = P.tile_eq_base; SELB = P.tile_sel_base;
-    MX = P.tile_max;
-  }
-  uint32_t carry_eq = 0, carry_sel = 0, mx = 0;
-  for (int64_t ib = 0; ib < n; ib += 1024) {
-    const int64_t i = ib + threadIdx.x;
-    const bool ok = i < n;
-    const uint32_t gt = ok ? GT[base + i] : 0u, eq = ok ? EQ[base + i] : 0u;
-    if (scales && ok) mx = max(mx, MX[base + i]);
-    uint32_t tot_eq, tot_sel;
-    const uint32_t eqb = carry_eq + block_excl_scan<1024>(eq, s_tmp, &tot_eq);
-    const uint32_t take = eqb < r ? min(eq, r - eqb) : 0u;
-    const uint32_t selb = carry_sel + block_excl_scan<1024>(gt + take, s_tmp, &tot_sel);
-    if (ok) {
-      EQB[base + i] = eqb;
-      SELB[base + i] = selb;
-    }
-    carry_eq += tot_eq;
-    carry_sel += tot_sel;
-  }
-  if (threadIdx.x == 0 && carry_sel != P.k[s]) atomicOr(P.err, 2u);
-  if (scales) {  // fused int8: scale = fl(absmax / 127); the largest |acc| is always kept
-    mx = block_max<1024>(mx, s_tmp);
-    if (threadIdx.x == 0) scales[s] = __uint_as_float(mx) / 127.0f;
-  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
 }
 
-// --------------------------------------------------------------------------------- emit
+// ------------------------------------------------------------------------------ emission
 // Ordered compaction of one tile-shaped block: keep key > kth, and key == kth while the tie
 // rank (eq_base + rank among the block's ties) stays below r.  slot_idx(v) gives the
 // segment-local indices of this lane's slot v (loaded only for slots that keep something).
@@ -713,7 +624,7 @@ struct EmitOut {              // where kept entries go
   float* vals;               // kept values, or null (fused int8 call without values)
   int32_t* idx;
   int8_t* codes;             // fused int8: codes, or null
-  const float* scales;       // fused int8: per-segment scales (written by k_scan)
+  const float* scales;       // fused int8: per-segment scales (written by the select)
   float scale;
   uint32_t seed_lo, seed_hi, step_lo;
   uint32_t* err;
@@ -722,6 +633,11 @@ struct EmitOut {              // where kept entries go
   const float* vsrc_scale;   // Random-k reading g itself: the gradient scale, or null
   float vmul, gmul;
   __device__ float scales_of(int s) const { return scales[s]; }
+  __device__ void set_segment(int s) {
+    if (codes) scale = scales_of(s);
+    if (rk_scale) vmul = rk_scale[s];
+    if (vsrc_scale) gmul = vsrc_scale[s];
+  }
 };
 
 template <typename SlotIdx>
@@ -812,11 +728,16 @@ __device__ __forceinline__ void emit_block(const f4 (&x)[kSlots], int len, SlotI
   }
 }
 
+__device__ __forceinline__ bool has_candidates(uint32_t mode) {
+  return mode == kModeCand || mode == kModeRecap;
+}
+
+// One chunk of a segment's candidates, in ascending index order (the select put them there).
 __device__ __forceinline__ void emit_cand_chunk(const DevPlan& P, EmitOut o, int64_t ch,
                                                 uint32_t* s_w) {
   const int s = P.chunk_seg[ch];
   if (!has_candidates(P.mode[s])) return;
-  const int64_t c = P.cand_cnt[s];
+  const int64_t c = P.sel_cnt[s];
   const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
   if (j0 >= c) return;
   const int len = (int)min((int64_t)kChunk, c - j0);
@@ -835,44 +756,59 @@ __device__ __forceinline__ void emit_cand_chunk(const DevPlan& P, EmitOut o, int
     }
     return r;
   };
-  if (o.codes) o.scale = o.scales_of(s);
-  if (o.rk_scale) o.vmul = o.rk_scale[s];
-  if (o.vsrc_scale) o.gmul = o.vsrc_scale[s];
+  o.set_segment(s);
   emit_block(x, len, slot_idx, P.kth[s], P.ties[s], P.chunk_eq_base[ch], P.chunk_eq[ch],
              P.out_off[s] + P.chunk_sel_base[ch], P.out_off[s + 1], P.seg_off[s],
              (int32_t)(P.seg_off[s + 1] - P.seg_off[s]), s_w, o);
 }
 
-__device__ __forceinline__ void emit_full_tiles(const DevPlan& P, EmitOut o, int fb,
+// Ordered emission of one tile of a segment selected over its elements (the full path, or a
+// small segment in the select kernel): the tile's keys come from e (or the Random-k keys).
+__device__ __forceinline__ void emit_seg_tile(const DevPlan& P, const EmitOut& o, int s,
+                                              int64_t t, uint32_t kth, uint32_t r,
+                                              uint32_t eq_base, uint32_t eq_cnt,
+                                              uint32_t sel_base, const f4 (&x)[kSlots],
+                                              uint32_t* s_w) {
+  int64_t start;
+  int len;
+  const int64_t s0 = P.seg_off[s];
+  const int64_t st = s0 + (t - P.tile_base[s]) * (int64_t)kTile;
+  const int64_t rem = P.seg_off[s + 1] - st;
+  start = st;
+  len = rem < kTile ? (int)rem : kTile;
+  const int32_t lb = (int32_t)(start - s0) + slot_base();
+  auto slot_idx = [&](int v) {
+    const int32_t b0 = lb + v * 256;
+    return i4{b0, b0 + 1, b0 + 2, b0 + 3};
+  };
+  emit_block(x, len, slot_idx, kth, r, eq_base, eq_cnt, P.out_off[s] + sel_base,
+             P.out_off[s + 1], s0, (int32_t)(P.seg_off[s + 1] - s0), s_w, o);
+}
+
+__device__ __forceinline__ void emit_full_tiles(const DevPlan& P, EmitOut o, int fb, int nfb,
                                                 uint32_t* s_w) {
   const uint32_t nf = *P.full_count;
   for (uint32_t li = 0; li < nf; ++li) {
     const int s = (int)P.full_list[li];
     const uint32_t kth = P.kth[s], r = P.ties[s];
-    const int64_t s0 = P.seg_off[s];
-    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += kFullBlocks) {
+    o.set_segment(s);
+    for (int64_t t = P.tile_base[s] + fb; t < P.tile_base[s + 1]; t += nfb) {
       int64_t start;
       int len;
-      tile_range(P, s, t, &start, &len);
+      const int64_t st = P.seg_off[s] + (t - P.tile_base[s]) * (int64_t)kTile;
+      const int64_t rem = P.seg_off[s + 1] - st;
+      start = st;
+      len = rem < kTile ? (int)rem : kTile;
       f4 x[kSlots];
       key_tile(P, o.e, start, len, x);
-      const int32_t lb = (int32_t)(start - s0) + slot_base();
-      auto slot_idx = [&](int v) {
-        const int32_t b0 = lb + v * 256;
-        return i4{b0, b0 + 1, b0 + 2, b0 + 3};
-      };
-      if (o.codes) o.scale = o.scales_of(s);
-      if (o.rk_scale) o.vmul = o.rk_scale[s];
-      if (o.vsrc_scale) o.gmul = o.vsrc_scale[s];
-      emit_block(x, len, slot_idx, kth, r, P.tile_eq_base[t], P.tile_eq[t],
-                 P.out_off[s] + P.tile_sel_base[t], P.out_off[s + 1], s0,
-                 (int32_t)(P.seg_off[s + 1] - s0), s_w, o);
+      emit_seg_tile(P, o, s, t, kth, r, P.tile_eq_base[t], P.tile_eq[t], P.tile_sel_base[t], x,
+                    s_w);
     }
   }
 }
 
-// Workgroups [0, n_chunk_blocks) emit the active candidate chunks; the last kFullBlocks the
-// tiles of the segments on the full path (one launch for both).
+// Workgroups [0, n_chunk_blocks) emit the active candidate chunks; the rest the tiles of the
+// segments on the full path (one launch for both).
 __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, EmitOut o) {
   __shared__ uint32_t s_w[kWaves];
   if (blockIdx.x < (uint32_t)P.n_chunk_blocks) {
@@ -880,128 +816,570 @@ __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, EmitOut o) {
     for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks)
       emit_cand_chunk(P, o, P.act_chunk[i], s_w);
   } else {
-    emit_full_tiles(P, o, (int)(blockIdx.x - P.n_chunk_blocks), s_w);
+    emit_full_tiles(P, o, (int)(blockIdx.x - P.n_chunk_blocks),
+                    (int)(gridDim.x - P.n_chunk_blocks), s_w);
   }
 }
 
-// ---------------------------------------------------------------------------- cold start
-// A plan's first call has no k-th key to start from.  Rather than capture nothing and
-// re-capture every large segment from two extra passes over it, the call first forms acc on
-// about 64 evenly spaced tiles of each such segment (exactly as the streaming pass will, but
-// without storing it), histograms the first key digit, and sets the capture threshold
-// GC_SAMPLE_MARGIN digits below the sample's estimate of the k-th key.  A wrong estimate only costs the usual
-// re-capture: the candidates are checked for completeness as on every call.
-__global__ __launch_bounds__(kThreads) void k_sample_zero(DevPlan P) {
-  const int s = blockIdx.x;
-  if (P.sample_elems[s] == 0) return;
-  uint32_t* h = P.hist + (size_t)s * 3 * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+// ------------------------------------------------------------------------------- select
+// The keys in [lo, hi] hold the k-th largest key of the segment as their kk-th largest; cnt
+// of them (when known).
+struct KeyRange {
+  uint32_t lo, hi, kk, cnt;
+};
+
+// Histogram bins of 2^sh keys from lo.  With `window` (magnitudes above a capture threshold,
+// densest just above it) the bins span at most 2^24 keys (two binades) and the top bin also
+// takes every key above them; otherwise they span the whole range.
+__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi, bool window) {
+  uint64_t w = (uint64_t)hi - lo + 1;
+  if (window && w > ((uint64_t)1 << 24)) w = (uint64_t)1 << 24;
+  int sh = 0;
+  while (((w - 1) >> sh) >= (uint64_t)kHistBins) ++sh;
+  return sh;
 }
 
-template <bool kMomentum>
-__global__ __launch_bounds__(kThreads) void k_sample_hist(DevPlan P, const float* __restrict__ g,
-                                                         const float* __restrict__ e,
-                                                         const float* __restrict__ u, float m) {
-  __shared__ uint32_t h[kHistBins];
-  const int64_t t = P.sample_tile[blockIdx.x];
-  const int4 desc = P.tile_desc[t];
-  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
-  const int len = desc.z, s = desc.w;
-  const float gf = grad_scale(P, s);
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
-  f4 gv[kSlots], acc[kSlots], uv[kSlots];
-  load_tile(g + start, len, gv);
-  load_tile(e + start, len, acc);
-  if (kMomentum) load_tile(u + start, len, uv);
-  __syncthreads();
-  const int pb = slot_base();
-#pragma unroll
-  for (int v = 0; v < kSlots; ++v) {
-    f4 x = gv[v] * gf;
-    if (kMomentum) {
-      const f4 mu = m * uv[v];
-      x = mu + x;
-    }
-    acc[v] = acc[v] + x;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (pb + v * 256 + c < len) atomicAdd(&h[mag_key(acc[v][c]) >> 20], 1u);
-  }
-  __syncthreads();
-  hist_flush(h, P.hist + (size_t)s * 3 * kHistBins);
+__device__ __forceinline__ uint32_t range_bin(uint32_t key, uint32_t lo, int sh) {
+  return min((key - lo) >> sh, (uint32_t)(kHistBins - 1));
 }
 
-// Per sampled segment still without an estimate: the first-digit bucket d that holds the
-// sample's ceil(k * sample / n)-th largest key; the threshold is the floor of bucket
-// d - GC_SAMPLE_MARGIN.
-__global__ __launch_bounds__(kThreads) void k_sample_decide(DevPlan P) {
-  __shared__ uint32_t s_tmp[kWaves];
-  __shared__ uint32_t s_out[3];
-  const int s = blockIdx.x;
-  const int64_t ns = P.sample_elems[s];
-  if (ns == 0 || P.thr[s] != kNoCapture) return;
-  const int64_t n = P.seg_off[s + 1] - P.seg_off[s];
-  const int64_t k = P.k[s];
-  const uint32_t kk = (uint32_t)max((int64_t)1, (k * ns + n - 1) / n);
+// Narrow r to the bin of h that holds its kk-th largest key.  Contains barriers.
+__device__ bool range_step(const uint32_t* h, KeyRange& r, int sh, uint32_t* s_tmp,
+                           uint32_t* s_out) {
   uint32_t d, above, bin;
-  const bool ok = find_digit(P.hist + (size_t)s * 3 * kHistBins, kk, s_tmp, s_out, &d, &above,
-                             &bin);
-  if (threadIdx.x == 0 && ok)
-    P.thr[s] = d > (uint32_t)GC_SAMPLE_MARGIN ? (d - (uint32_t)GC_SAMPLE_MARGIN) << 20 : 0u;
+  if (!find_digit(h, r.kk, s_tmp, s_out, &d, &above, &bin)) return false;
+  const uint64_t nlo = (uint64_t)r.lo + ((uint64_t)d << sh);
+  const uint64_t top = nlo + ((uint64_t)1 << sh) - 1;
+  r.hi = (d == (uint32_t)(kHistBins - 1) || top > r.hi) ? r.hi : (uint32_t)top;
+  r.lo = (uint32_t)nlo;
+  r.kk -= above;
+  r.cnt = bin;
+  return true;
 }
 
-// ----------------------------------------------------------------------------- finalize
-// Threshold for the next call: beta * |kth|, where the margin beta follows the last calls:
-// lowered after too few candidates, raised after an overflow or far more than needed, and
-// kept in [0.25, GC_BETA_MAX]; a cap near 1 suits a residual that still grows, whose next
-// k-th key lies above the last one.
-// Segments that capture everything (small) or nothing (k = 0) keep their setting.
-__global__ __launch_bounds__(kThreads) void k_finalize(DevPlan P) {
-  const int s = blockIdx.x * kThreads + threadIdx.x;
-  if (s >= P.n_seg) return;
-  const uint32_t init = P.thr_init[s], mode = P.mode[s];
-  uint32_t next = init;
-  if (init == kNoCapture && mode != kModeSkip && !(P.flags & (kFlagForceFull | kFlagNoEstimate))) {
-    float b = P.beta[s];
-    const uint32_t why = P.why[s];
-    if (why == kWhyMiss) {
-      b = fmaxf(b * 0.85f, 0.25f);
-    } else if (why == kWhyOverflow) {
-      b = fminf(b * 1.05f, GC_BETA_MAX);
-    } else if (mode == kModeCand) {
-      const float rho = (float)P.cand_cnt[s] / (float)P.k[s];
-      if (rho > GC_RHO_HIGH) b = fminf(b * 1.03f, GC_BETA_MAX);
-      else if (rho < GC_RHO_LOW) b = fmaxf(b * 0.97f, 0.25f);
+// Histogram of the keys in [lo, hi] of a key source (each(f) calls f(key, position) for every
+// key, each thread a share).  Contains barriers.
+template <typename Each>
+__device__ void range_hist(Each each, uint32_t lo, uint32_t hi, int sh, uint32_t* h) {
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+  __syncthreads();
+  each([&](uint32_t key, uint32_t) {
+    if (key >= lo && key <= hi) atomicAdd(&h[range_bin(key, lo, sh)], 1u);
+  });
+  __syncthreads();
+}
+
+// Narrow r with histogram passes over the source until it holds one key value or at most
+// kListCap keys.  The first pass may use the window (see range_shift).
+template <typename Each>
+__device__ bool narrow_range(Each each, KeyRange& r, bool window, uint32_t* h, uint32_t* s_tmp,
+                             uint32_t* s_out) {
+  bool first = true;
+  for (int it = 0; r.hi > r.lo && r.cnt > (uint32_t)kListCap; ++it) {
+    if (it == 8) return false;
+    const int sh = range_shift(r.lo, r.hi, window && first);
+    range_hist(each, r.lo, r.hi, sh, h);
+    if (!range_step(h, r, sh, s_tmp, s_out)) return false;
+    first = false;
+  }
+  return true;
+}
+
+// The exact k-th key inside r from the n keys of the LDS list (every key of the source that
+// lies in r).  On return r.lo == r.hi is the key and r.kk the ties to take.
+__device__ bool list_select(const uint32_t* lkey, uint32_t n, KeyRange& r, uint32_t* h,
+                            uint32_t* s_tmp, uint32_t* s_out) {
+  for (int it = 0; r.hi > r.lo; ++it) {
+    if (it == 4) return false;
+    const int sh = range_shift(r.lo, r.hi, false);
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
+      const uint32_t key = lkey[i];
+      if (key >= r.lo && key <= r.hi) atomicAdd(&h[range_bin(key, r.lo, sh)], 1u);
     }
-    P.beta[s] = b;
-    next = mag_key(b * __uint_as_float(P.kth[s]));
+    __syncthreads();
+    if (!range_step(h, r, sh, s_tmp, s_out)) return false;
   }
-  P.thr[s] = next;
+  return true;
 }
 
-// Threshold calls: the capture floor for the next call, by the rule of k_finalize applied to
-// this call's k (so it tracks the k-th largest kept key while the cap binds and falls below
-// key(|tau|), where it has no effect, while it does not).
-__global__ __launch_bounds__(kThreads) void k_finalize_thr(DevPlan P) {
-  const int s = blockIdx.x * kThreads + threadIdx.x;
-  if (s >= P.n_seg) return;
-  const uint32_t mode = P.mode[s];
-  if (P.thr_init[s] != kNoCapture || mode == kModeSkip ||
-      (P.flags & (kFlagForceFull | kFlagNoEstimate)))
-    return;   // small segments capture everything; k = 0 keeps its floor
-  float b = P.beta_est[s];
-  const uint32_t why = P.why[s];
-  if (why == kWhyMiss) {
-    b = fmaxf(b * 0.85f, 0.25f);
-  } else if (why == kWhyOverflow) {
-    b = fminf(b * 1.05f, GC_BETA_MAX);
-  } else if (mode == kModeCand) {
-    const float rho = (float)P.cand_cnt[s] / (float)P.k_call[s];
-    if (rho > GC_RHO_HIGH) b = fminf(b * 1.03f, GC_BETA_MAX);
-    else if (rho < GC_RHO_LOW) b = fmaxf(b * 0.97f, 0.25f);
+// LDS of the finish kernel.
+struct SelLds {
+  uint32_t h[kHistBins];
+  uint32_t lkey[kListCap];
+  uint32_t cgt[kFinishChunks];   // per output chunk of a window: near keys above kth
+  uint32_t ceq[kFinishChunks];   // and at kth
+  uint32_t tmp[kWaves];
+  uint32_t out[3];
+  uint32_t w[kWaves];
+  uint32_t n_list;
+};
+
+// The segment's key range after the candidates' windowed histogram (k_scatter): the bin that
+// holds its k-th key.  Histogram bins of 2^sh keys from the capture floor lo (window: at most
+// two binades above it, the top bin taking everything above).  Contains barriers.
+__device__ __forceinline__ bool cand_range(const DevPlan& P, int s, uint32_t k, KeyRange* r,
+                                           uint32_t* s_tmp, uint32_t* s_out) {
+  const uint32_t lo = P.thr_lo[s];
+  const bool window = P.keys == kKeysMagnitude && lo > 0;
+  const int sh = range_shift(lo, 0x7FFFFFFFu, window);
+  *r = KeyRange{lo, 0x7FFFFFFFu, k, P.sel_cnt[s]};
+  return range_step(seg_hist(P, s, 1), *r, sh, s_tmp, s_out);
+}
+
+// ------------------------------------------------------------------------------ scatter
+// Candidates into ascending index order (tile t's run goes to run_dst[t]), the windowed
+// histogram of their keys (seg_hist slot 1) and each chunk's largest key.  One chunk of the
+// call's list of active chunks; contains barriers.
+__device__ void scatter_chunk(const DevPlan& P, int64_t ch, uint32_t* h, uint32_t* s_m) {
+  const int s = P.chunk_seg[ch];
+  const int64_t c = P.sel_cnt[s];
+  const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+  if (j0 >= c) return;   // uniform (not expected: only filled chunks are listed)
+  const uint32_t lo = P.thr_lo[s];
+  const bool window = P.keys == kKeysMagnitude && lo > 0;
+  const int sh = range_shift(lo, 0x7FFFFFFFu, window);
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
+  const int len = (int)min((int64_t)kChunk, c - j0);
+  const int64_t cb = P.cand_base[s], tb = P.tile_base[s];
+  const int32_t n_s = (int32_t)(P.seg_off[s + 1] - P.seg_off[s]);
+  constexpr int kPer = kChunk / kThreads;
+  int32_t ix[kPer];
+  float vx[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int p = r * kThreads + threadIdx.x;
+    ix[r] = p < len ? P.cand_idx[cb + j0 + p] : 0;
+    vx[r] = p < len ? P.cand_val[cb + j0 + p] : 0.0f;
   }
-  P.beta_est[s] = b;
-  P.thr_est[s] = mag_key(b * __uint_as_float(P.kth[s]));
+  uint32_t rd[kPer], ro[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t t = tb + (ix[r] >= 0 && ix[r] < n_s ? ix[r] / kTile : 0);
+    rd[r] = P.run_dst[t];
+    ro[r] = P.run_off[t];
+  }
+  __syncthreads();   // h cleared
+  uint32_t mx = 0, bad = 0;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int p = r * kThreads + threadIdx.x;
+    if (p < len) {
+      const uint32_t key = mag_key(vx[r]);
+      const uint32_t dst = rd[r] + ((uint32_t)(j0 + p) - ro[r]);
+      if (ix[r] >= 0 && ix[r] < n_s && dst < (uint32_t)c && key >= lo) {
+        P.sort_val[cb + dst] = vx[r];
+        P.sort_idx[cb + dst] = ix[r];
+        atomicAdd(&h[range_bin(key, lo, sh)], 1u);
+        mx = max(mx, key);
+      } else {
+        bad = 1;
+      }
+    }
+  }
+  if (bad) atomicOr(P.err, 8u);
+  mx = block_max<kThreads>(mx, s_m);
+  if (threadIdx.x == 0) P.chunk_max[ch] = mx;
+  hist_flush(h, seg_hist(P, s, 1));
+}
+
+__global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t s_m[kWaves];
+  const uint32_t na = *P.act_count;
+  for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks) {
+    scatter_chunk(P, P.act_chunk[i], h, s_m);
+    __syncthreads();   // the next chunk reuses h
+  }
+}
+
+// ------------------------------------------------------------------------------ collect
+// Per chunk of ordered candidates: the keys above the range that holds the segment's k-th
+// key (chunk_gt), and the keys inside it appended to the segment's near list (key bits in the
+// free unordered candidate region, ordered position beside them).  The range comes from the
+// windowed histogram, derived again by each workgroup for the segments of its chunks.
+__global__ __launch_bounds__(kThreads) void k_collect(DevPlan P) {
+  __shared__ uint32_t s_tmp[kWaves], s_out[3], s_w[kWaves], s_base;
+  const uint32_t na = *P.act_count;
+  int cur = -1;
+  KeyRange r{0u, 0u, 0u, 0u};
+  bool ok = false;
+  for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks) {
+    const int64_t ch = P.act_chunk[i];
+    const int s = P.chunk_seg[ch];
+    if (s != cur) {   // uniform
+      ok = cand_range(P, s, call_k(P, s), &r, s_tmp, s_out);
+      cur = s;
+      if (!ok && threadIdx.x == 0) atomicOr(P.err, 1u);
+    }
+    const int64_t c = P.sel_cnt[s];
+    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+    if (!ok || j0 >= c) continue;   // uniform
+    const int len = (int)min((int64_t)kChunk, c - j0);
+    const int64_t cb = P.cand_base[s];
+    f4 x[kSlots];
+    load_tile(P.sort_val + cb + j0, len, x);
+    const int pb = slot_base();
+    uint32_t near[kSlots], gt = 0;
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      uint32_t b = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t key = mag_key(x[v][q]);
+        const bool in = pb + v * 256 + q < len;
+        gt += (in && key > r.hi) ? 1u : 0u;
+        b |= (in && key >= r.lo && key <= r.hi) ? (1u << q) : 0u;
+      }
+      near[v] = b;
+    }
+    uint32_t woff[kSlots];
+    const uint32_t total = tile_rank(near, woff, s_w);
+    gt = block_sum<kThreads>(gt, s_tmp);
+    if (threadIdx.x == 0) {
+      P.chunk_gt[ch] = gt;
+      s_base = total ? atomicAdd(&P.near_cnt[s], total) : 0u;
+    }
+    __syncthreads();
+    const uint32_t base = s_base;
+    float* nk = P.cand_val + cb;
+    int32_t* np = P.cand_idx + cb;
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v) {
+      uint32_t q = base + woff[v];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        if ((near[v] >> cc) & 1u) {
+          nk[q] = x[v][cc];
+          np[q] = (int32_t)(j0 + pb + v * 256 + cc);
+          ++q;
+        }
+    }
+    __syncthreads();   // s_base is rewritten for the next chunk
+  }
+}
+
+// Near-list source: f(key, j) for the n entries at v (keys stored as float bits).
+struct NearKeys {
+  const float* v;
+  uint32_t n;
+  template <typename F>
+  __device__ __forceinline__ void operator()(F f) const {
+    for (uint32_t j = threadIdx.x; j < n; j += kThreads) f(mag_key(v[j]), j);
+  }
+};
+
+// Candidate segment after k_collect: the exact k-th key and ties from its near list (in LDS
+// when small enough, else narrowed first by histogram passes over it), the near keys added to
+// their chunks' counts, and the per-chunk offsets of the ordered emission.  Returns the
+// largest key in *mx.  Contains barriers.
+__device__ void finish_cands(const DevPlan& P, int s, uint32_t k, SelLds& L, uint32_t* kth_out,
+                             uint32_t* ties_out, uint32_t* mx_out) {
+  const uint32_t c = P.sel_cnt[s];
+  const int64_t cb = P.cand_base[s], ch0 = P.chunk_base[s];
+  KeyRange r;
+  bool ok = cand_range(P, s, k, &r, L.tmp, L.out);
+  const uint32_t n_near = P.near_cnt[s];
+  const NearKeys near{P.cand_val + cb, n_near};
+  const int32_t* npos = P.cand_idx + cb;
+  if (ok && n_near != r.cnt) ok = false;   // the list holds exactly the bin's keys
+  if (ok) ok = narrow_range(near, r, false, L.h, L.tmp, L.out);
+  if (threadIdx.x == 0) L.n_list = 0;
+  __syncthreads();
+  uint32_t bad = ok ? 0u : 1u;
+  if (ok && r.hi > r.lo) {
+    near([&](uint32_t key, uint32_t j) {
+      if (key >= r.lo && key <= r.hi) {
+        const uint32_t p = atomicAdd(&L.n_list, 1u);
+        if (p < (uint32_t)kListCap) L.lkey[p] = key;
+        else bad = 1;
+      }
+    });
+    bad = block_max<kThreads>(bad, L.tmp);
+    if (!bad && !list_select(L.lkey, min(L.n_list, (uint32_t)kListCap), r, L.h, L.tmp, L.out))
+      bad = 1;
+  }
+  const uint32_t kth = r.lo, ties = r.kk;
+  // per output chunk: the keys above kth (k_collect's count above the range plus the near
+  // keys above kth) and at kth (near keys only), counted in LDS for windows of kFinishChunks
+  // chunks; then ties before each chunk and kept entries before it (the first `ties` kept)
+  const uint32_t nch = (c + kChunk - 1) / kChunk;
+  uint32_t ce = 0, cs = 0, mx = 0;
+  for (uint32_t w0 = 0; w0 < nch; w0 += kFinishChunks) {
+    const uint32_t wn = min(nch - w0, (uint32_t)kFinishChunks);
+    for (uint32_t i = threadIdx.x; i < wn; i += kThreads) {
+      L.cgt[i] = 0;
+      L.ceq[i] = 0;
+    }
+    __syncthreads();
+    if (!bad) {
+      near([&](uint32_t key, uint32_t j) {
+        const uint32_t ch = (uint32_t)npos[j] / kChunk;
+        if (ch < w0 || ch >= w0 + wn) return;
+        if (key > kth) atomicAdd(&L.cgt[ch - w0], 1u);
+        else if (key == kth) atomicAdd(&L.ceq[ch - w0], 1u);
+      });
+    }
+    __syncthreads();
+    for (uint32_t i0 = 0; i0 < wn; i0 += kThreads) {
+      const uint32_t i = i0 + threadIdx.x;
+      const bool in = i < wn;
+      const int64_t ch = ch0 + w0 + i;
+      const uint32_t eq = in ? L.ceq[i] : 0u;
+      const uint32_t gt = in ? P.chunk_gt[ch] + L.cgt[i] : 0u;
+      if (in) mx = max(mx, P.chunk_max[ch]);
+      uint32_t te, ts;
+      const uint32_t eqb = ce + block_excl_scan<kThreads>(eq, L.tmp, &te);
+      const uint32_t take = eqb < ties ? min(eq, ties - eqb) : 0u;
+      const uint32_t selb = cs + block_excl_scan<kThreads>(gt + take, L.tmp, &ts);
+      if (in) {
+        P.chunk_eq[ch] = eq;
+        P.chunk_eq_base[ch] = eqb;
+        P.chunk_sel_base[ch] = selb;
+      }
+      ce += te;
+      cs += ts;
+    }
+    __syncthreads();   // the counters are cleared for the next window
+  }
+  if (threadIdx.x == 0) {
+    if (bad) atomicOr(P.err, 16u);
+    if (cs != k) atomicOr(P.err, 2u);
+  }
+  *kth_out = kth;
+  *ties_out = ties;
+  *mx_out = block_max<kThreads>(mx, L.tmp);
+}
+
+// Full path: the per-tile counts of the keys above and at kth (fb_count) scanned in tile order
+// into the tiles' ordered-emission offsets; returns the largest key.  Contains barriers.
+__device__ uint32_t select_full_scan(const DevPlan& P, int s, uint32_t k, uint32_t ties,
+                                     SelLds& L) {
+  const int64_t t0 = P.tile_base[s], t1 = P.tile_base[s + 1];
+  uint32_t ce = 0, cs = 0, mx = 0;
+  for (int64_t tb = t0; tb < t1; tb += kThreads) {
+    const int64_t t = tb + threadIdx.x;
+    const bool in = t < t1;
+    const uint32_t gt = in ? P.tile_gt[t] : 0u, eq = in ? P.tile_eq[t] : 0u;
+    if (in) mx = max(mx, P.tile_max[t]);
+    uint32_t te, ts;
+    const uint32_t eqb = ce + block_excl_scan<kThreads>(eq, L.tmp, &te);
+    const uint32_t take = eqb < ties ? min(eq, ties - eqb) : 0u;
+    const uint32_t selb = cs + block_excl_scan<kThreads>(gt + take, L.tmp, &ts);
+    if (in) {
+      P.tile_eq_base[t] = eqb;
+      P.tile_sel_base[t] = selb;
+    }
+    ce += te;
+    cs += ts;
+  }
+  if (threadIdx.x == 0 && cs != k) atomicOr(P.err, 2u);
+  return block_max<kThreads>(mx, L.tmp);
+}
+
+// Small segment (at most kSmallTiles tiles): selected whole from its residual (or Random-k
+// keys), every key loaded once into registers, and emitted in index order, tile by tile.
+// Returns kth, ties and the largest key.  Contains barriers.
+__device__ void select_small(const DevPlan& P, const float* e, const EmitOut& o, int s,
+                             uint32_t k, SelLds& L, uint32_t* kth_out, uint32_t* ties_out,
+                             uint32_t* mx_out) {
+  const int64_t t0 = P.tile_base[s];
+  const int nt = (int)(P.tile_base[s + 1] - t0);
+  const int64_t s0 = P.seg_off[s];
+  const uint32_t n = (uint32_t)(P.seg_off[s + 1] - s0);
+  const int pb = slot_base();
+  f4 x[kSmallTiles][kSlots];
+  int len[kSmallTiles];
+#pragma unroll
+  for (int j = 0; j < kSmallTiles; ++j) {
+    len[j] = 0;
+    if (j < nt) {
+      int64_t start;
+      tile_range(P, s, t0 + j, &start, &len[j]);
+      key_tile(P, e, start, len[j], x[j]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < kSlots; ++v) x[j][v] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
+  auto keys = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < kSmallTiles; ++j)
+#pragma unroll
+      for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (pb + v * 256 + c < len[j])
+            f(mag_key(x[j][v][c]), (uint32_t)(j * kTile + pb + v * 256 + c));
+  };
+  KeyRange r{0u, 0x7FFFFFFFu, k, n};
+  bool ok = narrow_range(keys, r, false, L.h, L.tmp, L.out);
+  uint32_t mx = 0;
+  if (threadIdx.x == 0) L.n_list = 0;
+  __syncthreads();
+  const bool narrow = r.hi > r.lo;
+  uint32_t bad = ok ? 0u : 1u;
+  if (ok) {
+    keys([&](uint32_t key, uint32_t) {
+      mx = max(mx, key);
+      if (narrow && key >= r.lo && key <= r.hi) {
+        const uint32_t p = atomicAdd(&L.n_list, 1u);
+        if (p < (uint32_t)kListCap) L.lkey[p] = key;
+        else bad = 1;
+      }
+    });
+  }
+  mx = block_max<kThreads>(mx, L.tmp);
+  bad = block_max<kThreads>(bad, L.tmp);
+  if (!bad && narrow && !list_select(L.lkey, min(L.n_list, (uint32_t)kListCap), r, L.h, L.tmp,
+                                     L.out))
+    bad = 1;
+  const uint32_t kth = r.lo, ties = r.kk;
+  if (!bad) {
+    EmitOut os = o;
+    if (os.codes) os.scale = __uint_as_float(mx) / 127.0f;
+    if (os.rk_scale) os.vmul = os.rk_scale[s];
+    if (os.vsrc_scale) os.gmul = os.vsrc_scale[s];
+    uint32_t eqb = 0, kept = 0;
+#pragma unroll
+    for (int j = 0; j < kSmallTiles; ++j) {
+      if (j >= nt) break;   // uniform
+      uint32_t gt, eq;
+      count_block(x[j], len[j], kth, L.tmp, &gt, &eq);
+      emit_seg_tile(P, os, s, t0 + j, kth, ties, eqb, eq, kept, x[j], L.w);
+      kept += gt + (eqb < ties ? min(eq, ties - eqb) : 0u);
+      eqb += eq;
+    }
+    if (threadIdx.x == 0 && kept != k) atomicOr(P.err, 2u);
+  } else if (threadIdx.x == 0) {
+    atomicOr(P.err, 16u);
+  }
+  *kth_out = kth;
+  *ties_out = ties;
+  *mx_out = mx;
+}
+
+// One workgroup per segment after the streaming pass: the segment's path this call.  k = 0:
+// nothing (its counters cleared).  Small: selected and emitted here, whole, from its residual
+// (it needs no fallback).  Candidates complete: the places of its runs, its chunks listed,
+// its capture floor.  Otherwise: listed as pending for the fallback kernels.
+__global__ __launch_bounds__(kThreads) void k_list(DevPlan P, const float* __restrict__ e,
+                                                  EmitOut o) {
+  __shared__ SelLds L;
+  __shared__ uint32_t s_act;
+  const int s = blockIdx.x;
+  const uint32_t k = call_k(P, s);
+  uint32_t mode = kModeCand;
+  if (k == 0) mode = kModeSkip;
+  else if (P.seg_flags[s] & kSegSmall) mode = kModeSmall;
+  else if (seg_pending(P, s)) mode = kModePending;
+  if (mode == kModeSmall) {
+    uint32_t kth, ties, mx;
+    select_small(P, e, o, s, k, L, &kth, &ties, &mx);
+    if (threadIdx.x == 0) {
+      P.mode[s] = kModeSmall;
+      if (P.scales) P.scales[s] = __uint_as_float(mx) / 127.0f;
+      P.kth[s] = kth;
+      P.ties[s] = ties;
+    }
+    return;
+  }
+  if (mode != kModeCand) {
+    if (threadIdx.x == 0) {
+      P.mode[s] = mode;
+      if (mode == kModePending) P.pend_list[atomicAdd(P.pend_count, 1u)] = (uint32_t)s;
+    }
+    return;
+  }
+  const uint32_t c = P.cand_cnt[s];
+  if (threadIdx.x == 0) {
+    P.mode[s] = kModeCand;
+    P.sel_cnt[s] = c;
+    P.thr_lo[s] = capture_thr(P, s);
+  }
+  seg_runs(P, s, c, L.tmp, &s_act);
+}
+
+// One workgroup per segment, last before the emission: the segment's exact k-th key and ties
+// (candidate path: from its near list; full path: from fb_count), the offsets of its ordered
+// emission, the int8 scale, the threshold call's count and padding, the call's statistics,
+// the next capture threshold, and the per-call counters and histograms cleared for the next
+// call.
+__global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __restrict__ e,
+                                                    EmitOut o) {
+  __shared__ SelLds L;
+  const int s = blockIdx.x;
+  const uint32_t k = call_k(P, s);
+  const uint32_t mode = P.mode[s];
+  const bool pend = mode == kModeRecap || mode == kModeFull;
+  const uint32_t thr_used = capture_thr(P, s);
+  const uint32_t c_cap = P.cand_cnt[s];
+  uint32_t kth = 0, ties = 0, mx = 0, c_sel = 0;
+  if (mode == kModeSmall) {   // selected and emitted by k_list
+    kth = P.kth[s];
+    ties = P.ties[s];
+  } else if (mode == kModeCand || mode == kModeRecap) {
+    c_sel = P.sel_cnt[s];
+    finish_cands(P, s, k, L, &kth, &ties, &mx);
+  } else if (mode == kModeFull) {
+    kth = P.kth[s];
+    ties = P.ties[s];
+    mx = select_full_scan(P, s, k, ties, L);
+  }
+  // threshold call: the count, and the unused slots padded with (+0, -1)
+  if (P.codec == kCodecThreshold) {
+    const int64_t a = P.out_off[s] + k, b = P.out_off[s + 1];
+    for (int64_t j = a + threadIdx.x; j < b; j += kThreads) {
+      o.vals[j] = 0.0f;
+      o.idx[j] = -1;
+    }
+  }
+  // histograms used by this call, cleared for the next one: the candidates' windowed one
+  // (slot 1) and, for a pending segment, the fallback's three
+  if (mode == kModeCand || pend) {
+    uint32_t* h = seg_hist(P, s, pend ? 0 : 1);
+    const int nb = (pend ? 3 : 1) * kHistBins;
+    for (int i = threadIdx.x; i < nb; i += kThreads) h[i] = 0;
+  }
+  if (threadIdx.x != 0) return;
+  if (P.out_count) P.out_count[s] = (int32_t)k;
+  if (P.scales && mode != kModeSmall) P.scales[s] = k ? __uint_as_float(mx) / 127.0f : 0.0f;
+  P.sel_cnt[s] = c_sel;
+  P.kth[s] = kth;
+  P.ties[s] = ties;
+  // next capture threshold: beta * |kth|, the margin beta steered by the last calls: lowered
+  // after too few candidates, raised after an overflow or far more than needed, kept in
+  // [0.25, GC_BETA_MAX] (a cap near 1 suits a residual that still grows, whose next k-th key
+  // lies above the last one).  Segments that capture everything or nothing keep their setting.
+  const bool steer = mode != kModeSmall && k > 0 && P.thr_init[s] == kNoCapture &&
+                     !(P.flags & (kFlagForceFull | kFlagNoEstimate));
+  if (P.codec == kCodecTopk || P.codec == kCodecThreshold) {
+    float* beta = P.codec == kCodecTopk ? P.beta : P.beta_est;
+    if (steer) {
+      float b = beta[s];
+      if (pend) {
+        if (thr_used != kNoCapture) {
+          if (c_cap < k) b = fmaxf(b * 0.85f, 0.25f);                // missed
+          else b = fminf(b * 1.05f, GC_BETA_MAX);                     // overflowed
+        }
+      } else {
+        const float rho = (float)c_cap / (float)k;
+        if (rho > GC_RHO_HIGH) b = fminf(b * 1.03f, GC_BETA_MAX);
+        else if (rho < GC_RHO_LOW) b = fmaxf(b * 0.97f, 0.25f);
+      }
+      beta[s] = b;
+      const uint32_t next = mag_key(b * __uint_as_float(kth));
+      if (P.codec == kCodecTopk) P.thr[s] = next;
+      else P.thr_est[s] = next;
+    } else if (P.codec == kCodecTopk) {
+      P.thr[s] = P.thr_init[s];
+    }
+  }
+  P.cand_cnt[s] = 0;
+  P.recap_cnt[s] = 0;
+  P.tau_cnt[s] = 0;
+  P.near_cnt[s] = 0;
 }
 
 // -------------------------------------------------------------------------------- Random-k
@@ -1023,6 +1401,7 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
   const int len = desc.z, s = desc.w;
   const uint32_t thr = P.thr[s];  // kNoCapture: this segment takes the exact fallback
   const float gf = kScale ? P.gscale[s] : 1.0f;
+  reset_call_lists(P);
   f4 key[kSlots];
   if (kEF && len == kTile && (start & 3) == 0) {
     // whole aligned tile: issue the loads, draw the keys while they are in flight
@@ -1061,7 +1440,7 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
     if (thr != kNoCapture) rand_key_tile(P, start, len, key);
   }
   if (thr == kNoCapture) return;  // uniform
-  capture_tile(P, s, t, start, len, key, thr, s_w, &s_base);
+  capture_tile(P, s, t, start, len, key, thr, &P.cand_cnt[s], s_w, &s_base);
 }
 
 // Random-k without error feedback or momentum reads nothing in its pass: it only draws keys
@@ -1168,6 +1547,7 @@ __global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
   __shared__ int32_t s_idx[kRkWaves][kRkStage];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kRkWaves + w;
+  reset_call_lists(P);
   if (t >= P.n_tiles) return;   // wave-uniform
   const int4 desc = P.tile_desc[t];
   const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
@@ -1180,56 +1560,45 @@ __global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
     rk_tile<false>(P, t, start, len, s, thr, lane, s_key[w], s_idx[w]);
 }
 
-// Threshold call: slots past the segment's kept entries get value +0 and index -1.
-__global__ __launch_bounds__(kThreads) void k_pad_out(OutPlan O, const uint32_t* __restrict__ k_call,
-                                                      float* __restrict__ vals,
-                                                      int32_t* __restrict__ idx) {
-  const int64_t ch = blockIdx.x;
-  const int s = O.out_chunk_seg[ch];
-  const int64_t j0 = O.out_off[s] + (ch - O.out_chunk_base[s]) * (int64_t)kOutChunk;
-  const int64_t j1 = min(j0 + kOutChunk, O.out_off[s + 1]);
-  const int64_t keep_end = O.out_off[s] + k_call[s];
-  for (int64_t j = max(j0, keep_end) + threadIdx.x; j < j1; j += kThreads) {
-    vals[j] = 0.0f;
-    idx[j] = -1;
+// Everything after the streaming pass: the per-segment list, the fallback kernels (they end
+// at once unless a segment's capture was incomplete), the candidates ordered and ranked, the
+// per-segment finish, and the ordered emission.  e holds acc (magnitude keys);
+// Random-k keys are drawn again where needed.
+void select_emit(const DevPlan& P, const float* e, const EmitOut& o, hipStream_t st) {
+  const int64_t nt = P.n_tiles > 0 ? P.n_tiles : 1;
+  const unsigned fb = (unsigned)(nt < kFallbackBlocks ? nt : kFallbackBlocks);
+  k_list<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P, e, o);
+  k_fb_hist<<<fb, kThreads, 0, st>>>(P, e);
+  k_fb_capture<<<fb, kThreads, 0, st>>>(P, e);
+  k_fb_hist2<<<fb, kThreads, 0, st>>>(P, e);
+  k_fb_count<<<fb, kThreads, 0, st>>>(P, e);
+  if (P.n_chunk_blocks > 0) {
+    k_scatter<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
+    k_collect<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
   }
-}
-
-// Everything after the streaming pass: select (candidates, re-capture or the exact full
-// path), ordered count/scan, emit.  e holds acc (magnitude keys); scales: fused int8 or null.
-void select_emit(const DevPlan& P, const float* e, const EmitOut& o, float* scales,
-                 hipStream_t st) {
-  k_select_init<<<P.n_seg, kThreads, 0, st>>>(P);
-  k_recap_hist<<<kFullBlocks, kThreads, 0, st>>>(P, e);
-  k_recap_decide<<<P.n_seg, kThreads, 0, st>>>(P);
-  k_recapture<<<kFullBlocks, kThreads, 0, st>>>(P, e);
-  k_runs<<<P.n_seg, 1024, 0, st>>>(P);
-  if (P.n_chunk_blocks > 0) k_scatter<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
-  k_find<<<P.n_seg, kThreads, 0, st>>>(P, 0);
-  const unsigned mixed = (unsigned)(P.n_chunk_blocks + kFullBlocks);
-  for (int pass = 1; pass < 3; ++pass) {
-    k_hist<<<mixed, kThreads, 0, st>>>(P, e, pass);
-    k_find<<<P.n_seg, kThreads, 0, st>>>(P, pass);
-  }
-  k_count<<<mixed, kThreads, 0, st>>>(P, e);
-  k_scan<<<P.n_seg, 1024, 0, st>>>(P, scales);
-  k_emit<<<mixed, kThreads, 0, st>>>(P, o);
+  k_finish<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P, e, o);
+  const unsigned nfull = (unsigned)(nt < kFullBlocks ? nt : kFullBlocks);
+  k_emit<<<(unsigned)P.n_chunk_blocks + nfull, kThreads, 0, st>>>(P, o);
 }
 
 }  // namespace
 
-hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u, float m,
+hipError_t launch_compress(const DevPlan& P0, const float* g, float* e, float* u, float m,
                            float* out_vals, int32_t* out_idx, const Int8Args& q8, bool cold,
                            hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  if (P.n_seg == 0) return hipSuccess;
-  k_prep<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
+  if (P0.n_seg == 0) return hipSuccess;
+  DevPlan P = P0;
+  P.codec = kCodecTopk;
+  P.keys = kKeysMagnitude;
+  P.tau = nullptr;
+  P.out_count = nullptr;
+  P.scales = q8.enabled ? q8.scales : nullptr;
   if (cold && P.n_sample > 0) {
-    k_sample_zero<<<P.n_seg, kThreads, 0, st>>>(P);
     if (u)
       k_sample_hist<true><<<(unsigned)P.n_sample, kThreads, 0, st>>>(P, g, e, u, m);
     else
       k_sample_hist<false><<<(unsigned)P.n_sample, kThreads, 0, st>>>(P, g, e, nullptr, m);
-    k_sample_decide<<<P.n_seg, kThreads, 0, st>>>(P);
+    k_sample_decide<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P);
   }
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (P.n_tiles > 0) {
@@ -1254,73 +1623,71 @@ hipError_t launch_compress(const DevPlan& P, const float* g, float* e, float* u,
   o.seed_hi = q8.seed_hi;
   o.step_lo = q8.step_lo;
   o.err = P.err;
-  select_emit(P, e, o, q8.enabled ? q8.scales : nullptr, st);
-  k_finalize<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
+  select_emit(P, e, o, st);
   return hipGetLastError();
 }
 
-hipError_t launch_threshold(const DevPlan& P, const OutPlan& O, const float* g, float* e,
-                            float* u, float m, const float* tau, float* out_vals,
-                            int32_t* out_idx, int32_t* out_count, hipStream_t st,
-                            hipEvent_t ev_begin, hipEvent_t ev_end) {
-  if (P.n_seg == 0) return hipSuccess;
-  DevPlan Q = P;
-  Q.k = P.k_call;
-  Q.thr = P.thr_call;
-  Q.keys = kKeysMagnitude;
-  k_prep_call<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, tau);
+hipError_t launch_threshold(const DevPlan& P0, const float* g, float* e, float* u, float m,
+                            const float* tau, float* out_vals, int32_t* out_idx,
+                            int32_t* out_count, hipStream_t st, hipEvent_t ev_begin,
+                            hipEvent_t ev_end) {
+  if (P0.n_seg == 0) return hipSuccess;
+  DevPlan P = P0;
+  P.codec = kCodecThreshold;
+  P.keys = kKeysMagnitude;
+  P.tau = tau;
+  P.out_count = out_count;
+  P.scales = nullptr;
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (P.n_tiles > 0) {
     const unsigned nt = (unsigned)P.n_tiles;
     if (P.gscale) {
-      if (u) k_ef_capture<true, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
-      else k_ef_capture<false, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+      if (u) k_ef_capture<true, true, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
+      else k_ef_capture<false, true, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
     } else {
-      if (u) k_ef_capture<true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
-      else k_ef_capture<false, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
+      if (u) k_ef_capture<true, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
+      else k_ef_capture<false, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
     }
   }
   if (ev_end) (void)hipEventRecord(ev_end, st);
-  k_thresh_k<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, out_count);
   EmitOut o{};
   o.e = e;
   o.u = (u && (P.flags & kFlagMomentumMask)) ? u : nullptr;
   o.vals = out_vals;
   o.idx = out_idx;
   o.err = P.err;
-  select_emit(Q, e, o, nullptr, st);
-  if (O.n_out_chunks > 0)
-    k_pad_out<<<(unsigned)O.n_out_chunks, kThreads, 0, st>>>(O, P.k_call, out_vals, out_idx);
-  k_finalize_thr<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P);
+  select_emit(P, e, o, st);
   return hipGetLastError();
 }
 
-hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, float m,
+hipError_t launch_randk(const DevPlan& P0, const float* g, float* e, float* u, float m,
                         uint64_t seed, uint64_t step, float* out_vals, int32_t* out_idx,
                         hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  if (P.n_seg == 0) return hipSuccess;
-  DevPlan Q = P;
-  Q.k = P.k_call;
-  Q.thr = P.thr_call;
-  Q.keys = kKeysRandom;
-  Q.seed_lo = (uint32_t)seed;
-  Q.seed_hi = (uint32_t)(seed >> 32);
-  Q.step_lo = (uint32_t)step;
-  k_prep_call<<<blocks_for(P.n_seg, kThreads), kThreads, 0, st>>>(P, nullptr);
+  if (P0.n_seg == 0) return hipSuccess;
+  DevPlan P = P0;
+  P.codec = kCodecRandk;
+  P.thr = const_cast<uint32_t*>(P0.thr_rand);   // read only in a Random-k call
+  P.keys = kKeysRandom;
+  P.tau = nullptr;
+  P.out_count = nullptr;
+  P.scales = nullptr;
+  P.seed_lo = (uint32_t)seed;
+  P.seed_hi = (uint32_t)(seed >> 32);
+  P.step_lo = (uint32_t)step;
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (P.n_tiles > 0) {
     const unsigned nt = (unsigned)P.n_tiles;
     if (P.gscale) {
-      if (e && u) k_randk_capture<true, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
-      else if (e) k_randk_capture<false, true, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
-      else if (u) k_randk_capture<true, false, true><<<nt, kThreads, 0, st>>>(Q, g, nullptr, u, m);
+      if (e && u) k_randk_capture<true, true, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
+      else if (e) k_randk_capture<false, true, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
+      else if (u) k_randk_capture<true, false, true><<<nt, kThreads, 0, st>>>(P, g, nullptr, u, m);
       // neither: the capture reads no g (the emit applies the scale to the gathered values)
-      else k_randk_keys<<<blocks_for(P.n_tiles, kRkWaves), kRkWaves * 64, 0, st>>>(Q);
+      else k_randk_keys<<<blocks_for(P.n_tiles, kRkWaves), kRkWaves * 64, 0, st>>>(P);
     } else {
-      if (e && u) k_randk_capture<true, true><<<nt, kThreads, 0, st>>>(Q, g, e, u, m);
-      else if (e) k_randk_capture<false, true><<<nt, kThreads, 0, st>>>(Q, g, e, nullptr, m);
-      else if (u) k_randk_capture<true, false><<<nt, kThreads, 0, st>>>(Q, g, nullptr, u, m);
-      else k_randk_keys<<<blocks_for(P.n_tiles, kRkWaves), kRkWaves * 64, 0, st>>>(Q);
+      if (e && u) k_randk_capture<true, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
+      else if (e) k_randk_capture<false, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
+      else if (u) k_randk_capture<true, false><<<nt, kThreads, 0, st>>>(P, g, nullptr, u, m);
+      else k_randk_keys<<<blocks_for(P.n_tiles, kRkWaves), kRkWaves * 64, 0, st>>>(P);
     }
   }
   if (ev_end) (void)hipEventRecord(ev_end, st);
@@ -1333,7 +1700,7 @@ hipError_t launch_randk(const DevPlan& P, const float* g, float* e, float* u, fl
   o.vsrc = e ? e : (u ? u : g);
   o.vsrc_scale = (!e && !u) ? P.gscale : nullptr;
   o.rk_scale = e ? nullptr : P.rk_scale;
-  select_emit(Q, e, o, nullptr, st);
+  select_emit(P, e, o, st);
   return hipGetLastError();
 }
 

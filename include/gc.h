@@ -94,9 +94,9 @@ int gc_layout(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const dou
  * The plan keeps a per-segment threshold estimate between calls; it only decides how much
  * work a call does, never what it returns.  Its single device allocation holds about 25 KB
  * per segment (three 2048-bin histograms and per-segment state), about 60 B per 8192-element
- * tile, and 16 B per candidate slot (max(16 k_s, 65536) slots per segment, n_s for segments
- * of at most 65536 elements): about 1.8 GB for a 6.7e9-element, 291-segment gradient at
- * k = 0.1%.
+ * tile, and 16 B per candidate slot (min(n_s, max(16 k_s, 65536)) slots per segment, none for
+ * segments of at most 16384 elements, which are selected whole): about 1.8 GB for a
+ * 6.7e9-element, 291-segment gradient at k = 0.1%.
  * Errors: GC_ERR_INVALID_ARG (any check above), GC_ERR_OOM (the workspace does not fit),
  * GC_ERR_UNSUPPORTED (2^31 or more tiles, candidate chunks or int8 output chunks, or more
  * than 4 * (2^32 - 1) candidate slots in all: the kernels' 32-bit grid and slot counts;
@@ -373,9 +373,11 @@ int gc_plan_reset_estimate(gc_plan* plan, void* stream);
  * Diagnostics of the last compress call (synchronises `stream`).  Host arrays of n_seg, any
  * may be NULL: mode[s] (0 = k is 0; 1 = selected among the candidates captured at the
  * estimated threshold; 2 = exact radix select over the whole segment; 3 = candidates
- * re-captured after a histogram of the whole segment), candidates[s] (entries captured),
- * kth_key[s] (the k-th largest key bits(acc) & 0x7FFFFFFF), ties_taken[s] (entries kept
- * at exactly that key).
+ * re-captured after a histogram of the whole segment; 5 = a segment of at most 16384
+ * elements, selected whole by one workgroup), candidates[s] (entries the select ran over:
+ * those captured in modes 1 and 3, else 0), kth_key[s] (the k-th largest key
+ * bits(acc) & 0x7FFFFFFF), ties_taken[s] (entries kept at exactly that key).  Returns
+ * GC_ERR_HIP when the call's kernels raised their internal consistency flag.
  */
 int gc_plan_last_stats(gc_plan* plan, uint32_t* mode, uint32_t* candidates, uint32_t* kth_key,
                        uint32_t* ties_taken, void* stream);

@@ -61,7 +61,8 @@ def test_many_steps(name, iters, momentum):
         plan.compress(g, e, vals, idx, u=u, momentum=momentum or 0.0)
         torch.cuda.synchronize()
         st = plan.last_stats()
-        off_cand.append(int((st["mode"] != gca.MODE_CANDIDATES).sum()))
+        off_cand.append(int(((st["mode"] != gca.MODE_CANDIDATES) &
+                             (st["mode"] != gca.MODE_SMALL) & (st["mode"] != gca.MODE_SKIP)).sum()))
         _props(off, plan, acc, e, vals, idx)
         del acc, x
         for s in sample:
