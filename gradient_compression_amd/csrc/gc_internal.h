@@ -28,10 +28,10 @@ namespace gc {
 #endif
 // Band of candidates-per-k that the threshold estimate steers toward (one step per call).
 #ifndef GC_RHO_LOW
-#define GC_RHO_LOW 1.5f
+#define GC_RHO_LOW 1.25f
 #endif
 #ifndef GC_RHO_HIGH
-#define GC_RHO_HIGH 4.0f
+#define GC_RHO_HIGH 2.25f
 #endif
 #ifndef GC_NT_ZERO_E        // the scattered residual zeroing of kept entries non-temporal
 #define GC_NT_ZERO_E 1
@@ -40,7 +40,7 @@ namespace gc {
 #define GC_SAMPLE_MARGIN 2  // estimate of the k-th key (a digit is a factor of 2^(1/8))
 #endif
 #ifndef GC_BETA_MAX         // largest margin: next threshold <= GC_BETA_MAX * |k-th key|
-#define GC_BETA_MAX 0.98f
+#define GC_BETA_MAX 0.995f
 #endif
 // First margin of the threshold estimate (next threshold = beta * |k-th largest|), on a fresh
 // plan and after an estimate reset.
@@ -56,13 +56,13 @@ constexpr int kTile = kWaves * kWaveSpan;
 // Candidate buffers are processed in chunks laid out exactly like tiles.
 constexpr int kChunk = kTile;
 // Workgroups that serve the exact full-segment path, striding over listed segments.
-constexpr int kFullBlocks = 1024;
+constexpr int kFullBlocks = 256;
 // Most workgroups that walk the candidate chunks of a call (the chunks that hold candidates
 // are listed per call; a plan has chunks for its full capacity, mostly unused).
 constexpr int kChunkBlocks = 1024;
 // Workgroups of the fallback kernels (histograms, re-capture and counts over the tiles of the
 // segments whose captured candidates were not complete).
-constexpr int kFallbackBlocks = 1024;
+constexpr int kFallbackBlocks = 256;
 // Output chunks for the int8 and decompression kernels.
 constexpr int kOutChunk = 4096;
 constexpr int kHistBins = 2048;

@@ -291,9 +291,12 @@ __device__ void hist_tile(const DevPlan& P, const float* __restrict__ e, int s, 
   __syncthreads();
 }
 
-// Digit of the k-th largest key in a histogram (descending scan): d and the count above it.
-// s_tmp: __shared__ uint32_t[kWaves]; s_out: __shared__ uint32_t[3].  Contains barriers.
-__device__ bool find_digit(const uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
+// Digit of the k-th largest key in a histogram of kHistBins bins (descending scan): the bin d
+// that holds it, the count above it and the bin's count.  kClear: each thread zeroes the bins
+// it read, leaving the histogram clear for the next pass.  s_tmp: __shared__
+// uint32_t[kWaves]; s_out: __shared__ uint32_t[3].  Contains barriers: call from every thread.
+template <bool kClear = false>
+__device__ bool find_digit(uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
                            uint32_t* d_out, uint32_t* above_out, uint32_t* bin_out) {
   constexpr int kPer = kHistBins / kThreads;
   uint32_t loc[kPer];
@@ -302,6 +305,10 @@ __device__ bool find_digit(const uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uin
   for (int j = 0; j < kPer; ++j) {
     loc[j] = gh[kHistBins - 1 - (threadIdx.x * kPer + j)];
     sum += loc[j];
+  }
+  if (kClear) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) gh[kHistBins - 1 - (threadIdx.x * kPer + j)] = 0;
   }
   if (threadIdx.x == 0) {
     s_out[0] = 0xFFFFFFFFu;
@@ -807,20 +814,6 @@ __device__ __forceinline__ void emit_full_tiles(const DevPlan& P, EmitOut o, int
   }
 }
 
-// Workgroups [0, n_chunk_blocks) emit the active candidate chunks; the rest the tiles of the
-// segments on the full path (one launch for both).
-__global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, EmitOut o) {
-  __shared__ uint32_t s_w[kWaves];
-  if (blockIdx.x < (uint32_t)P.n_chunk_blocks) {
-    const uint32_t na = *P.act_count;
-    for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks)
-      emit_cand_chunk(P, o, P.act_chunk[i], s_w);
-  } else {
-    emit_full_tiles(P, o, (int)(blockIdx.x - P.n_chunk_blocks),
-                    (int)(gridDim.x - P.n_chunk_blocks), s_w);
-  }
-}
-
 // ------------------------------------------------------------------------------- select
 // The keys in [lo, hi] hold the k-th largest key of the segment as their kk-th largest; cnt
 // of them (when known).
@@ -843,11 +836,12 @@ __device__ __forceinline__ uint32_t range_bin(uint32_t key, uint32_t lo, int sh)
   return min((key - lo) >> sh, (uint32_t)(kHistBins - 1));
 }
 
-// Narrow r to the bin of h that holds its kk-th largest key.  Contains barriers.
-__device__ bool range_step(const uint32_t* h, KeyRange& r, int sh, uint32_t* s_tmp,
-                           uint32_t* s_out) {
+// Narrow r to the bin of h that holds its kk-th largest key (kClear: h zeroed for the next
+// pass).  Contains barriers.
+template <bool kClear = false>
+__device__ bool range_step(uint32_t* h, KeyRange& r, int sh, uint32_t* s_tmp, uint32_t* s_out) {
   uint32_t d, above, bin;
-  if (!find_digit(h, r.kk, s_tmp, s_out, &d, &above, &bin)) return false;
+  if (!find_digit<kClear>(h, r.kk, s_tmp, s_out, &d, &above, &bin)) return false;
   const uint64_t nlo = (uint64_t)r.lo + ((uint64_t)d << sh);
   const uint64_t top = nlo + ((uint64_t)1 << sh) - 1;
   r.hi = (d == (uint32_t)(kHistBins - 1) || top > r.hi) ? r.hi : (uint32_t)top;
@@ -857,20 +851,15 @@ __device__ bool range_step(const uint32_t* h, KeyRange& r, int sh, uint32_t* s_t
   return true;
 }
 
-// Histogram of the keys in [lo, hi] of a key source (each(f) calls f(key, position) for every
-// key, each thread a share).  Contains barriers.
-template <typename Each>
-__device__ void range_hist(Each each, uint32_t lo, uint32_t hi, int sh, uint32_t* h) {
+__device__ __forceinline__ void lds_clear_hist(uint32_t* h) {
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
-  __syncthreads();
-  each([&](uint32_t key, uint32_t) {
-    if (key >= lo && key <= hi) atomicAdd(&h[range_bin(key, lo, sh)], 1u);
-  });
   __syncthreads();
 }
 
-// Narrow r with histogram passes over the source until it holds one key value or at most
-// kListCap keys.  The first pass may use the window (see range_shift).
+// Narrow r with histogram passes over a key source (each(f) calls f(key, position) for every
+// key, each thread a share) until it holds one key value or at most kListCap keys.  The first
+// pass may use the window (see range_shift).  h (LDS) is zero on entry and on a true return.
+// Contains barriers.
 template <typename Each>
 __device__ bool narrow_range(Each each, KeyRange& r, bool window, uint32_t* h, uint32_t* s_tmp,
                              uint32_t* s_out) {
@@ -878,28 +867,31 @@ __device__ bool narrow_range(Each each, KeyRange& r, bool window, uint32_t* h, u
   for (int it = 0; r.hi > r.lo && r.cnt > (uint32_t)kListCap; ++it) {
     if (it == 8) return false;
     const int sh = range_shift(r.lo, r.hi, window && first);
-    range_hist(each, r.lo, r.hi, sh, h);
-    if (!range_step(h, r, sh, s_tmp, s_out)) return false;
+    const uint32_t lo = r.lo, hi = r.hi;
+    each([&](uint32_t key, uint32_t) {
+      if (key >= lo && key <= hi) atomicAdd(&h[range_bin(key, lo, sh)], 1u);
+    });
+    __syncthreads();
+    if (!range_step<true>(h, r, sh, s_tmp, s_out)) return false;
     first = false;
   }
   return true;
 }
 
 // The exact k-th key inside r from the n keys of the LDS list (every key of the source that
-// lies in r).  On return r.lo == r.hi is the key and r.kk the ties to take.
+// lies in r).  On return r.lo == r.hi is the key and r.kk the ties to take.  h (LDS) is zero on
+// entry and on a true return.
 __device__ bool list_select(const uint32_t* lkey, uint32_t n, KeyRange& r, uint32_t* h,
                             uint32_t* s_tmp, uint32_t* s_out) {
   for (int it = 0; r.hi > r.lo; ++it) {
     if (it == 4) return false;
     const int sh = range_shift(r.lo, r.hi, false);
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0;
-    __syncthreads();
     for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
       const uint32_t key = lkey[i];
       if (key >= r.lo && key <= r.hi) atomicAdd(&h[range_bin(key, r.lo, sh)], 1u);
     }
     __syncthreads();
-    if (!range_step(h, r, sh, s_tmp, s_out)) return false;
+    if (!range_step<true>(h, r, sh, s_tmp, s_out)) return false;
   }
   return true;
 }
@@ -1079,19 +1071,27 @@ __device__ void finish_cands(const DevPlan& P, int s, uint32_t k, SelLds& L, uin
   const uint32_t c = P.sel_cnt[s];
   const int64_t cb = P.cand_base[s], ch0 = P.chunk_base[s];
   KeyRange r;
-  bool ok = cand_range(P, s, k, &r, L.tmp, L.out);
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) L.h[i] = 0;
+  if (threadIdx.x == 0) L.n_list = 0;
+  bool ok = cand_range(P, s, k, &r, L.tmp, L.out);   // (its barriers order the clears)
   const uint32_t n_near = P.near_cnt[s];
   const NearKeys near{P.cand_val + cb, n_near};
   const int32_t* npos = P.cand_idx + cb;
   if (ok && n_near != r.cnt) ok = false;   // the list holds exactly the bin's keys
   if (ok) ok = narrow_range(near, r, false, L.h, L.tmp, L.out);
-  if (threadIdx.x == 0) L.n_list = 0;
-  __syncthreads();
   uint32_t bad = ok ? 0u : 1u;
   if (ok && r.hi > r.lo) {
-    near([&](uint32_t key, uint32_t j) {
-      if (key >= r.lo && key <= r.hi) {
-        const uint32_t p = atomicAdd(&L.n_list, 1u);
+    // the keys inside r into the LDS list: one slot reservation per wave and step
+    near([&](uint32_t key, uint32_t) {
+      const bool in = key >= r.lo && key <= r.hi;
+      const uint64_t m = __ballot(in);
+      if (m == 0) return;
+      const int lead = __ffsll((unsigned long long)m) - 1;
+      uint32_t base = 0;
+      if (lane_id() == lead) base = atomicAdd(&L.n_list, (uint32_t)__popcll(m));
+      base = __shfl(base, lead, 64);
+      if (in) {
+        const uint32_t p = base + lanes_below(m);
         if (p < (uint32_t)kListCap) L.lkey[p] = key;
         else bad = 1;
       }
@@ -1178,16 +1178,40 @@ __device__ uint32_t select_full_scan(const DevPlan& P, int s, uint32_t k, uint32
   return block_max<kThreads>(mx, L.tmp);
 }
 
+// Sums over a block of N values per thread at once (one pair of barriers); scratch: LDS of
+// N * kWaves words.
+template <int N>
+__device__ __forceinline__ void block_sums(uint32_t (&v)[N], uint32_t* scratch) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v[i] += __shfl_xor(v[i], d, 64);
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) scratch[i * kWaves + wave_id()] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += scratch[i * kWaves + w];
+    v[i] = t;
+  }
+  __syncthreads();
+}
+
 // Small segment (at most kSmallTiles tiles): selected whole from its residual (or Random-k
-// keys), every key loaded once into registers, and emitted in index order, tile by tile.
-// Returns kth, ties and the largest key.  Contains barriers.
+// keys), every key loaded once into registers: the exact k-th key by a radix select over the
+// registers (digits of 11, 11 and 9 bits, as the full path), then the segment emitted in index
+// order, tile by tile.  Returns kth, ties and the largest key (when an int8 scale needs it).
+// Contains barriers.
 __device__ void select_small(const DevPlan& P, const float* e, const EmitOut& o, int s,
                              uint32_t k, SelLds& L, uint32_t* kth_out, uint32_t* ties_out,
                              uint32_t* mx_out) {
+  static_assert(kTile < 65536, "a tile's counts are packed in 16 bits");
   const int64_t t0 = P.tile_base[s];
   const int nt = (int)(P.tile_base[s + 1] - t0);
-  const int64_t s0 = P.seg_off[s];
-  const uint32_t n = (uint32_t)(P.seg_off[s + 1] - s0);
   const int pb = slot_base();
   f4 x[kSmallTiles][kSlots];
   int len[kSmallTiles];
@@ -1203,50 +1227,61 @@ __device__ void select_small(const DevPlan& P, const float* e, const EmitOut& o,
       for (int v = 0; v < kSlots; ++v) x[j][v] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
-  auto keys = [&](auto f) {
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) L.h[i] = 0;
+  __syncthreads();
+  uint32_t prefix = 0, kk = k;
+  bool ok = true;
+  for (int pass = 0; pass < 3; ++pass) {
+#pragma unroll
+    for (int j = 0; j < kSmallTiles; ++j) hist_add(L.h, x[j], len[j], prefix, pass);
+    __syncthreads();
+    uint32_t d, above, bin;
+    if (!find_digit<true>(L.h, kk, L.tmp, L.out, &d, &above, &bin)) {   // uniform
+      ok = false;
+      break;
+    }
+    prefix |= d << digit_shift(pass);
+    kk -= above;
+  }
+  const uint32_t kth = prefix, ties = kk;
+  uint32_t mx = 0;
+  if (P.scales || o.codes) {   // uniform
 #pragma unroll
     for (int j = 0; j < kSmallTiles; ++j)
 #pragma unroll
       for (int v = 0; v < kSlots; ++v)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (pb + v * 256 + c < len[j])
-            f(mag_key(x[j][v][c]), (uint32_t)(j * kTile + pb + v * 256 + c));
-  };
-  KeyRange r{0u, 0x7FFFFFFFu, k, n};
-  bool ok = narrow_range(keys, r, false, L.h, L.tmp, L.out);
-  uint32_t mx = 0;
-  if (threadIdx.x == 0) L.n_list = 0;
-  __syncthreads();
-  const bool narrow = r.hi > r.lo;
-  uint32_t bad = ok ? 0u : 1u;
-  if (ok) {
-    keys([&](uint32_t key, uint32_t) {
-      mx = max(mx, key);
-      if (narrow && key >= r.lo && key <= r.hi) {
-        const uint32_t p = atomicAdd(&L.n_list, 1u);
-        if (p < (uint32_t)kListCap) L.lkey[p] = key;
-        else bad = 1;
-      }
-    });
+          if (pb + v * 256 + c < len[j]) mx = max(mx, mag_key(x[j][v][c]));
+    mx = block_max<kThreads>(mx, L.tmp);
   }
-  mx = block_max<kThreads>(mx, L.tmp);
-  bad = block_max<kThreads>(bad, L.tmp);
-  if (!bad && narrow && !list_select(L.lkey, min(L.n_list, (uint32_t)kListCap), r, L.h, L.tmp,
-                                     L.out))
-    bad = 1;
-  const uint32_t kth = r.lo, ties = r.kk;
-  if (!bad) {
+  if (ok) {
     EmitOut os = o;
     if (os.codes) os.scale = __uint_as_float(mx) / 127.0f;
     if (os.rk_scale) os.vmul = os.rk_scale[s];
     if (os.vsrc_scale) os.gmul = os.vsrc_scale[s];
+    // per tile: the keys above kth (low half) and at it (high half), all tiles in one reduction
+    uint32_t cnt[kSmallTiles];
+#pragma unroll
+    for (int j = 0; j < kSmallTiles; ++j) {
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t key = mag_key(x[j][v][c]);
+          const bool in = pb + v * 256 + c < len[j];
+          gt += (in && key > kth) ? 1u : 0u;
+          eq += (in && key == kth) ? 1u : 0u;
+        }
+      cnt[j] = gt | (eq << 16);
+    }
+    block_sums<kSmallTiles>(cnt, L.lkey);
     uint32_t eqb = 0, kept = 0;
 #pragma unroll
     for (int j = 0; j < kSmallTiles; ++j) {
       if (j >= nt) break;   // uniform
-      uint32_t gt, eq;
-      count_block(x[j], len[j], kth, L.tmp, &gt, &eq);
+      const uint32_t gt = cnt[j] & 0xFFFFu, eq = cnt[j] >> 16;
       emit_seg_tile(P, os, s, t0 + j, kth, ties, eqb, eq, kept, x[j], L.w);
       kept += gt + (eqb < ties ? min(eq, ties - eqb) : 0u);
       eqb += eq;
@@ -1261,12 +1296,11 @@ __device__ void select_small(const DevPlan& P, const float* e, const EmitOut& o,
 }
 
 // One workgroup per segment after the streaming pass: the segment's path this call.  k = 0:
-// nothing (its counters cleared).  Small: selected and emitted here, whole, from its residual
+// nothing (its counters cleared).  Small: selected and emitted whole by the emission kernel
 // (it needs no fallback).  Candidates complete: the places of its runs, its chunks listed,
 // its capture floor.  Otherwise: listed as pending for the fallback kernels.
-__global__ __launch_bounds__(kThreads) void k_list(DevPlan P, const float* __restrict__ e,
-                                                  EmitOut o) {
-  __shared__ SelLds L;
+__global__ __launch_bounds__(kThreads) void k_list(DevPlan P) {
+  __shared__ uint32_t s_tmp[kWaves];
   __shared__ uint32_t s_act;
   const int s = blockIdx.x;
   const uint32_t k = call_k(P, s);
@@ -1274,17 +1308,6 @@ __global__ __launch_bounds__(kThreads) void k_list(DevPlan P, const float* __res
   if (k == 0) mode = kModeSkip;
   else if (P.seg_flags[s] & kSegSmall) mode = kModeSmall;
   else if (seg_pending(P, s)) mode = kModePending;
-  if (mode == kModeSmall) {
-    uint32_t kth, ties, mx;
-    select_small(P, e, o, s, k, L, &kth, &ties, &mx);
-    if (threadIdx.x == 0) {
-      P.mode[s] = kModeSmall;
-      if (P.scales) P.scales[s] = __uint_as_float(mx) / 127.0f;
-      P.kth[s] = kth;
-      P.ties[s] = ties;
-    }
-    return;
-  }
   if (mode != kModeCand) {
     if (threadIdx.x == 0) {
       P.mode[s] = mode;
@@ -1298,7 +1321,7 @@ __global__ __launch_bounds__(kThreads) void k_list(DevPlan P, const float* __res
     P.sel_cnt[s] = c;
     P.thr_lo[s] = capture_thr(P, s);
   }
-  seg_runs(P, s, c, L.tmp, &s_act);
+  seg_runs(P, s, c, s_tmp, &s_act);
 }
 
 // One workgroup per segment, last before the emission: the segment's exact k-th key and ties
@@ -1316,10 +1339,7 @@ __global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __r
   const uint32_t thr_used = capture_thr(P, s);
   const uint32_t c_cap = P.cand_cnt[s];
   uint32_t kth = 0, ties = 0, mx = 0, c_sel = 0;
-  if (mode == kModeSmall) {   // selected and emitted by k_list
-    kth = P.kth[s];
-    ties = P.ties[s];
-  } else if (mode == kModeCand || mode == kModeRecap) {
+  if (mode == kModeCand || mode == kModeRecap) {
     c_sel = P.sel_cnt[s];
     finish_cands(P, s, k, L, &kth, &ties, &mx);
   } else if (mode == kModeFull) {
@@ -1346,8 +1366,10 @@ __global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __r
   if (P.out_count) P.out_count[s] = (int32_t)k;
   if (P.scales && mode != kModeSmall) P.scales[s] = k ? __uint_as_float(mx) / 127.0f : 0.0f;
   P.sel_cnt[s] = c_sel;
-  P.kth[s] = kth;
-  P.ties[s] = ties;
+  if (mode != kModeSmall) {   // a small segment's are written by its select in k_emit
+    P.kth[s] = kth;
+    P.ties[s] = ties;
+  }
   // next capture threshold: beta * |kth|, the margin beta steered by the last calls: lowered
   // after too few candidates, raised after an overflow or far more than needed, kept in
   // [0.25, GC_BETA_MAX] (a cap near 1 suits a residual that still grows, whose next k-th key
@@ -1378,8 +1400,40 @@ __global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __r
   }
   P.cand_cnt[s] = 0;
   P.recap_cnt[s] = 0;
-  P.tau_cnt[s] = 0;
+  if (mode != kModeSmall) P.tau_cnt[s] = 0;   // a small segment's k is read by its select later
   P.near_cnt[s] = 0;
+}
+
+// The last kernel of a call.  Workgroups [0, n_seg): a small segment each (selected and
+// emitted whole, from its residual, alongside the rest: no other kernel waits for it); then
+// n_chunk_blocks over the active candidate chunks; the rest over the tiles of the segments on
+// the full path.
+__global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, const float* __restrict__ e,
+                                                  EmitOut o) {
+  __shared__ SelLds L;
+  const uint32_t b = blockIdx.x;
+  if (b < (uint32_t)P.n_seg) {
+    const int s = (int)b;
+    if (P.mode[s] != kModeSmall) return;   // uniform
+    uint32_t kth, ties, mx;
+    select_small(P, e, o, s, call_k(P, s), L, &kth, &ties, &mx);
+    if (threadIdx.x == 0) {
+      if (P.scales) P.scales[s] = __uint_as_float(mx) / 127.0f;
+      P.kth[s] = kth;
+      P.ties[s] = ties;
+      P.tau_cnt[s] = 0;   // the threshold call's count, read above, cleared for the next call
+    }
+    return;
+  }
+  const uint32_t c0 = b - (uint32_t)P.n_seg;
+  if (c0 < (uint32_t)P.n_chunk_blocks) {
+    const uint32_t na = *P.act_count;
+    for (uint32_t i = c0; i < na; i += (uint32_t)P.n_chunk_blocks)
+      emit_cand_chunk(P, o, P.act_chunk[i], L.w);
+  } else {
+    const uint32_t f0 = c0 - (uint32_t)P.n_chunk_blocks;
+    emit_full_tiles(P, o, (int)f0, (int)(gridDim.x - P.n_seg - P.n_chunk_blocks), L.w);
+  }
 }
 
 // -------------------------------------------------------------------------------- Random-k
@@ -1562,12 +1616,12 @@ __global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
 
 // Everything after the streaming pass: the per-segment list, the fallback kernels (they end
 // at once unless a segment's capture was incomplete), the candidates ordered and ranked, the
-// per-segment finish, and the ordered emission.  e holds acc (magnitude keys);
-// Random-k keys are drawn again where needed.
+// per-segment finish, and the ordered emission with the small segments' selects beside it.
+// e holds acc (magnitude keys); Random-k keys are drawn again where needed.
 void select_emit(const DevPlan& P, const float* e, const EmitOut& o, hipStream_t st) {
   const int64_t nt = P.n_tiles > 0 ? P.n_tiles : 1;
   const unsigned fb = (unsigned)(nt < kFallbackBlocks ? nt : kFallbackBlocks);
-  k_list<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P, e, o);
+  k_list<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P);
   k_fb_hist<<<fb, kThreads, 0, st>>>(P, e);
   k_fb_capture<<<fb, kThreads, 0, st>>>(P, e);
   k_fb_hist2<<<fb, kThreads, 0, st>>>(P, e);
@@ -1578,7 +1632,7 @@ void select_emit(const DevPlan& P, const float* e, const EmitOut& o, hipStream_t
   }
   k_finish<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P, e, o);
   const unsigned nfull = (unsigned)(nt < kFullBlocks ? nt : kFullBlocks);
-  k_emit<<<(unsigned)P.n_chunk_blocks + nfull, kThreads, 0, st>>>(P, o);
+  k_emit<<<(unsigned)(P.n_seg + P.n_chunk_blocks) + nfull, kThreads, 0, st>>>(P, e, o);
 }
 
 }  // namespace
