@@ -275,7 +275,7 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   d.flags = (int32_t)flags;
   d.n_tiles = n_tiles;
   d.n_chunks = n_chunks;
-  d.n_chunk_blocks = (int32_t)std::min<int64_t>(n_chunks, gc::kChunkBlocks);
+  d.n_chunk_blocks = gc::chunk_walkers(n_chunks);
   int64_t *d_seg_off, *d_tile_base, *d_chunk_base, *d_out_off, *d_cand_base, *d_out_chunk_base;
   int32_t *d_tile_seg, *d_chunk_seg, *d_out_chunk_seg;
   int4* d_tile_desc;
@@ -1111,7 +1111,7 @@ int gc_topk_ef_compress_noalloc(const int64_t* seg_off, int32_t n_seg, const int
   d.flags = (int32_t)(flags | gc::kFlagNoEstimate);
   d.n_tiles = tiles;
   d.n_chunks = chunks;
-  d.n_chunk_blocks = (int32_t)std::min<int64_t>(chunks, gc::kChunkBlocks);
+  d.n_chunk_blocks = gc::chunk_walkers(chunks);
   d.keys = gc::kKeysMagnitude;
   d.n_sample = 0;
   d.sample_tile = nullptr;

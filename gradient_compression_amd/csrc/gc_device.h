@@ -146,6 +146,42 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total
   return before + x - v;
 }
 
+// Exclusive scans of two uint32 per thread at once (one pair of barriers); *ta and *tb get the
+// sums.  s_a, s_b: __shared__ uint32_t[NT / 64] each.  Contains barriers.
+template <int NT>
+__device__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_t* s_a, uint32_t* s_b,
+                                 uint32_t* ea, uint32_t* eb, uint32_t* ta, uint32_t* tb) {
+  const int lane = lane_id(), w = wave_id();
+  uint32_t x = a, y = b;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t px = __shfl_up(x, d, 64), py = __shfl_up(y, d, 64);
+    if (lane >= d) {
+      x += px;
+      y += py;
+    }
+  }
+  if (lane == 63) {
+    s_a[w] = x;
+    s_b[w] = y;
+  }
+  __syncthreads();
+  uint32_t ba = 0, bb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t u = s_a[i], v = s_b[i];
+    ba += (i < w) ? u : 0u;
+    bb += (i < w) ? v : 0u;
+    sa += u;
+    sb += v;
+  }
+  __syncthreads();
+  *ea = ba + x - a;
+  *eb = bb + y - b;
+  *ta = sa;
+  *tb = sb;
+}
+
 // Largest value over a block of NT threads (valid in every thread).  s_tmp: [NT / 64].
 template <int NT>
 __device__ uint32_t block_max(uint32_t v, uint32_t* s_tmp) {

@@ -57,9 +57,16 @@ constexpr int kTile = kWaves * kWaveSpan;
 constexpr int kChunk = kTile;
 // Workgroups that serve the exact full-segment path, striding over listed segments.
 constexpr int kFullBlocks = 256;
-// Most workgroups that walk the candidate chunks of a call (the chunks that hold candidates
-// are listed per call; a plan has chunks for its full capacity, mostly unused).
+// Workgroups that walk the candidate chunks of a call.  A plan of at most kDirectChunks chunks
+// gets one walker per chunk (no list to read first); a larger one kChunkBlocks walkers over the
+// chunks that hold candidates, listed per call (a plan has chunks for its full capacity, mostly
+// unused).
 constexpr int kChunkBlocks = 1024;
+constexpr int kDirectChunks = 256;
+inline int32_t chunk_walkers(int64_t n_chunks) {
+  return (int32_t)(n_chunks <= kDirectChunks ? n_chunks
+                                             : (n_chunks < kChunkBlocks ? n_chunks : kChunkBlocks));
+}
 // Workgroups of the fallback kernels (histograms, re-capture and counts over the tiles of the
 // segments whose captured candidates were not complete).
 constexpr int kFallbackBlocks = 256;
@@ -111,7 +118,7 @@ struct DevPlan {
   int32_t flags;
   int64_t n_tiles;
   int64_t n_chunks;
-  int32_t n_chunk_blocks;      // min(n_chunks, kChunkBlocks): the chunk walkers of a launch
+  int32_t n_chunk_blocks;      // chunk_walkers(n_chunks): the chunk walkers of a launch
   int32_t codec;               // kCodec* of this call
   // host-built tables
   const int64_t* seg_off;      // [n_seg + 1]

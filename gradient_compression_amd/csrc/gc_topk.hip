@@ -291,25 +291,29 @@ __device__ void hist_tile(const DevPlan& P, const float* __restrict__ e, int s, 
   __syncthreads();
 }
 
-// Digit of the k-th largest key in a histogram of kHistBins bins (descending scan): the bin d
-// that holds it, the count above it and the bin's count.  kClear: each thread zeroes the bins
-// it read, leaving the histogram clear for the next pass.  s_tmp: __shared__
-// uint32_t[kWaves]; s_out: __shared__ uint32_t[3].  Contains barriers: call from every thread.
-template <bool kClear = false>
-__device__ bool find_digit(uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
-                           uint32_t* d_out, uint32_t* above_out, uint32_t* bin_out) {
+// This thread's share of a histogram's bins, in descending bin order.
+struct Bins {
+  uint32_t v[kHistBins / kThreads];
+};
+
+__device__ __forceinline__ Bins load_bins(const uint32_t* gh) {
+  Bins b;
+#pragma unroll
+  for (int j = 0; j < kHistBins / kThreads; ++j)
+    b.v[j] = gh[kHistBins - 1 - (threadIdx.x * (kHistBins / kThreads) + j)];
+  return b;
+}
+
+// Digit of the k-th largest key in a histogram of kHistBins bins (descending scan; each thread
+// holds its share, load_bins): the bin d that holds it, the count above it and the bin's
+// count.  s_tmp: __shared__ uint32_t[kWaves]; s_out: __shared__ uint32_t[3].  Contains
+// barriers: call from every thread.
+__device__ bool find_digit_in(const Bins& b, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
+                              uint32_t* d_out, uint32_t* above_out, uint32_t* bin_out) {
   constexpr int kPer = kHistBins / kThreads;
-  uint32_t loc[kPer];
   uint32_t sum = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    loc[j] = gh[kHistBins - 1 - (threadIdx.x * kPer + j)];
-    sum += loc[j];
-  }
-  if (kClear) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) gh[kHistBins - 1 - (threadIdx.x * kPer + j)] = 0;
-  }
+  for (int j = 0; j < kPer; ++j) sum += b.v[j];
   if (threadIdx.x == 0) {
     s_out[0] = 0xFFFFFFFFu;
     s_out[1] = 0;
@@ -319,12 +323,12 @@ __device__ bool find_digit(uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t*
   uint32_t acc = block_excl_scan<kThreads>(sum, s_tmp, &tot);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    if (acc < kk && acc + loc[j] >= kk) {
+    if (acc < kk && acc + b.v[j] >= kk) {
       s_out[0] = kHistBins - 1 - (threadIdx.x * kPer + j);
       s_out[1] = acc;
-      s_out[2] = loc[j];
+      s_out[2] = b.v[j];
     }
-    acc += loc[j];
+    acc += b.v[j];
   }
   __syncthreads();
   *d_out = s_out[0];
@@ -332,6 +336,20 @@ __device__ bool find_digit(uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t*
   *bin_out = s_out[2];
   __syncthreads();   // s_out may be written again by the next call
   return *d_out != 0xFFFFFFFFu;
+}
+
+// find_digit_in over the histogram at gh (LDS or global).  kClear: each thread zeroes the bins
+// it read, leaving the histogram clear for the next pass.  Contains barriers.
+template <bool kClear = false>
+__device__ bool find_digit(uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
+                           uint32_t* d_out, uint32_t* above_out, uint32_t* bin_out) {
+  const Bins b = load_bins(gh);
+  if (kClear) {
+#pragma unroll
+    for (int j = 0; j < kHistBins / kThreads; ++j)
+      gh[kHistBins - 1 - (threadIdx.x * (kHistBins / kThreads) + j)] = 0;
+  }
+  return find_digit_in(b, kk, s_tmp, s_out, d_out, above_out, bin_out);
 }
 
 // ---------------------------------------------------------------------- list and runs
@@ -739,11 +757,26 @@ __device__ __forceinline__ bool has_candidates(uint32_t mode) {
   return mode == kModeCand || mode == kModeRecap;
 }
 
+// The candidate chunks of the call for chunk walker w (uniform over its workgroup), as
+// f(chunk, listed): with a walker per chunk of the plan, walker w takes chunk w whatever its
+// segment's state (listed false: f checks it); otherwise the call's list of the chunks of
+// candidate segments (listed true), strided over the walkers.
+template <typename F>
+__device__ __forceinline__ void for_active_chunks(const DevPlan& P, uint32_t w, F f) {
+  if ((int64_t)P.n_chunk_blocks >= P.n_chunks) {
+    if ((int64_t)w < P.n_chunks) f((int64_t)w, false);
+    return;
+  }
+  const uint32_t na = *P.act_count;
+  for (uint32_t i = w; i < na; i += (uint32_t)P.n_chunk_blocks)
+    f((int64_t)P.act_chunk[i], true);
+}
+
 // One chunk of a segment's candidates, in ascending index order (the select put them there).
 __device__ __forceinline__ void emit_cand_chunk(const DevPlan& P, EmitOut o, int64_t ch,
-                                                uint32_t* s_w) {
+                                                bool listed, uint32_t* s_w) {
   const int s = P.chunk_seg[ch];
-  if (!has_candidates(P.mode[s])) return;
+  if (!listed && !has_candidates(P.mode[s])) return;
   const int64_t c = P.sel_cnt[s];
   const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
   if (j0 >= c) return;
@@ -836,12 +869,12 @@ __device__ __forceinline__ uint32_t range_bin(uint32_t key, uint32_t lo, int sh)
   return min((key - lo) >> sh, (uint32_t)(kHistBins - 1));
 }
 
-// Narrow r to the bin of h that holds its kk-th largest key (kClear: h zeroed for the next
-// pass).  Contains barriers.
-template <bool kClear = false>
-__device__ bool range_step(uint32_t* h, KeyRange& r, int sh, uint32_t* s_tmp, uint32_t* s_out) {
+// Narrow r to the bin that holds its kk-th largest key, from this thread's share of the
+// histogram's bins.  Contains barriers.
+__device__ bool range_step_in(const Bins& b, KeyRange& r, int sh, uint32_t* s_tmp,
+                              uint32_t* s_out) {
   uint32_t d, above, bin;
-  if (!find_digit<kClear>(h, r.kk, s_tmp, s_out, &d, &above, &bin)) return false;
+  if (!find_digit_in(b, r.kk, s_tmp, s_out, &d, &above, &bin)) return false;
   const uint64_t nlo = (uint64_t)r.lo + ((uint64_t)d << sh);
   const uint64_t top = nlo + ((uint64_t)1 << sh) - 1;
   r.hi = (d == (uint32_t)(kHistBins - 1) || top > r.hi) ? r.hi : (uint32_t)top;
@@ -849,6 +882,19 @@ __device__ bool range_step(uint32_t* h, KeyRange& r, int sh, uint32_t* s_tmp, ui
   r.kk -= above;
   r.cnt = bin;
   return true;
+}
+
+// range_step_in over the histogram at h (kClear: h zeroed for the next pass).  Contains
+// barriers.
+template <bool kClear = false>
+__device__ bool range_step(uint32_t* h, KeyRange& r, int sh, uint32_t* s_tmp, uint32_t* s_out) {
+  const Bins b = load_bins(h);
+  if (kClear) {
+#pragma unroll
+    for (int j = 0; j < kHistBins / kThreads; ++j)
+      h[kHistBins - 1 - (threadIdx.x * (kHistBins / kThreads) + j)] = 0;
+  }
+  return range_step_in(b, r, sh, s_tmp, s_out);
 }
 
 __device__ __forceinline__ void lds_clear_hist(uint32_t* h) {
@@ -897,9 +943,10 @@ __device__ bool list_select(const uint32_t* lkey, uint32_t n, KeyRange& r, uint3
 }
 
 // LDS of the finish kernel.
-struct SelLds {
+struct alignas(16) SelLds {
   uint32_t h[kHistBins];
   uint32_t lkey[kListCap];
+  uint32_t lch[kListCap];        // a near list held whole: each entry's output chunk
   uint32_t cgt[kFinishChunks];   // per output chunk of a window: near keys above kth
   uint32_t ceq[kFinishChunks];   // and at kth
   uint32_t tmp[kWaves];
@@ -911,24 +958,85 @@ struct SelLds {
 // The segment's key range after the candidates' windowed histogram (k_scatter): the bin that
 // holds its k-th key.  Histogram bins of 2^sh keys from the capture floor lo (window: at most
 // two binades above it, the top bin taking everything above).  Contains barriers.
-__device__ __forceinline__ bool cand_range(const DevPlan& P, int s, uint32_t k, KeyRange* r,
-                                           uint32_t* s_tmp, uint32_t* s_out) {
+__device__ __forceinline__ bool cand_range_in(const DevPlan& P, int s, uint32_t k,
+                                              const Bins& b, KeyRange* r, uint32_t* s_tmp,
+                                              uint32_t* s_out) {
   const uint32_t lo = P.thr_lo[s];
   const bool window = P.keys == kKeysMagnitude && lo > 0;
   const int sh = range_shift(lo, 0x7FFFFFFFu, window);
   *r = KeyRange{lo, 0x7FFFFFFFu, k, P.sel_cnt[s]};
-  return range_step(seg_hist(P, s, 1), *r, sh, s_tmp, s_out);
+  return range_step_in(b, *r, sh, s_tmp, s_out);
+}
+
+__device__ __forceinline__ bool cand_range(const DevPlan& P, int s, uint32_t k, KeyRange* r,
+                                           uint32_t* s_tmp, uint32_t* s_out) {
+  return cand_range_in(P, s, k, load_bins(seg_hist(P, s, 1)), r, s_tmp, s_out);
+}
+
+// Most keys that rank_select takes (it compares each key with every other).
+constexpr uint32_t kRankMax = 256;
+
+// The kk-th largest of the n <= kRankMax keys of an LDS list (16-byte aligned), by counting:
+// q threads per key (q a power of two, q * n <= kThreads), each comparing it with its own
+// contiguous part of the list, so that its count of keys above it and at it is exact.  On
+// return r is that one key and r.kk the ties to take.  s_out: LDS uint32_t[3].  Contains
+// barriers.
+__device__ bool rank_select(const uint32_t* lkey, uint32_t n, KeyRange& r, uint32_t* s_out) {
+  uint32_t q = 1;
+  while (q < 64 && q * 2 * n <= (uint32_t)kThreads) q *= 2;
+  const uint32_t j = threadIdx.x / q, part = threadIdx.x % q, kk = r.kk;
+  const uint32_t per = ((n + q - 1) / q + 3) & ~3u;   // whole 16-byte groups per part
+  if (threadIdx.x == 0) s_out[2] = 0;
+  __syncthreads();
+  const uint32_t kj = j < n ? lkey[j] : 0u;
+  uint32_t gt = 0, eq = 0;
+  if (j < n) {
+    const uint32_t i0 = part * per, i1 = min(n, i0 + per);
+    uint32_t i = i0;
+#pragma unroll 4
+    for (; i + 4 <= i1; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lkey + i);
+      gt += (v.x > kj ? 1u : 0u) + (v.y > kj ? 1u : 0u) + (v.z > kj ? 1u : 0u) +
+            (v.w > kj ? 1u : 0u);
+      eq += (v.x == kj ? 1u : 0u) + (v.y == kj ? 1u : 0u) + (v.z == kj ? 1u : 0u) +
+            (v.w == kj ? 1u : 0u);
+    }
+    for (; i < i1; ++i) {
+      const uint32_t ki = lkey[i];
+      gt += ki > kj ? 1u : 0u;
+      eq += ki == kj ? 1u : 0u;
+    }
+  }
+  for (uint32_t d = 1; d < q; d <<= 1) {
+    gt += __shfl_xor(gt, (int)d, 64);
+    eq += __shfl_xor(eq, (int)d, 64);
+  }
+  if (j < n && part == 0 && gt < kk && kk <= gt + eq) {   // every such thread holds the same key
+    s_out[0] = kj;
+    s_out[1] = kk - gt;
+    s_out[2] = 1;
+  }
+  __syncthreads();
+  const bool found = s_out[2] != 0;
+  if (found) {
+    r.lo = r.hi = s_out[0];
+    r.kk = s_out[1];
+  }
+  __syncthreads();
+  return found;
 }
 
 // ------------------------------------------------------------------------------ scatter
 // Candidates into ascending index order (tile t's run goes to run_dst[t]), the windowed
 // histogram of their keys (seg_hist slot 1) and each chunk's largest key.  One chunk of the
 // call's list of active chunks; contains barriers.
-__device__ void scatter_chunk(const DevPlan& P, int64_t ch, uint32_t* h, uint32_t* s_m) {
+__device__ void scatter_chunk(const DevPlan& P, int64_t ch, bool listed, uint32_t* h,
+                              uint32_t* s_m) {
   const int s = P.chunk_seg[ch];
+  if (!listed && !has_candidates(P.mode[s])) return;   // uniform
   const int64_t c = P.sel_cnt[s];
   const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
-  if (j0 >= c) return;   // uniform (not expected: only filled chunks are listed)
+  if (j0 >= c) return;   // uniform: a chunk past the segment's candidates
   const uint32_t lo = P.thr_lo[s];
   const bool window = P.keys == kKeysMagnitude && lo > 0;
   const int sh = range_shift(lo, 0x7FFFFFFFu, window);
@@ -979,11 +1087,10 @@ __device__ void scatter_chunk(const DevPlan& P, int64_t ch, uint32_t* h, uint32_
 __global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t s_m[kWaves];
-  const uint32_t na = *P.act_count;
-  for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks) {
-    scatter_chunk(P, P.act_chunk[i], h, s_m);
+  for_active_chunks(P, blockIdx.x, [&](int64_t ch, bool listed) {
+    scatter_chunk(P, ch, listed, h, s_m);
     __syncthreads();   // the next chunk reuses h
-  }
+  });
 }
 
 // ------------------------------------------------------------------------------ collect
@@ -993,21 +1100,21 @@ __global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
 // windowed histogram, derived again by each workgroup for the segments of its chunks.
 __global__ __launch_bounds__(kThreads) void k_collect(DevPlan P) {
   __shared__ uint32_t s_tmp[kWaves], s_out[3], s_w[kWaves], s_base;
-  const uint32_t na = *P.act_count;
   int cur = -1;
   KeyRange r{0u, 0u, 0u, 0u};
   bool ok = false;
-  for (uint32_t i = blockIdx.x; i < na; i += (uint32_t)P.n_chunk_blocks) {
-    const int64_t ch = P.act_chunk[i];
+  for_active_chunks(P, blockIdx.x, [&](int64_t ch, bool listed) {
     const int s = P.chunk_seg[ch];
+    if (!listed && !has_candidates(P.mode[s])) return;   // uniform
+    const int64_t c = P.sel_cnt[s];
+    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
+    if (j0 >= c) return;   // uniform
     if (s != cur) {   // uniform
       ok = cand_range(P, s, call_k(P, s), &r, s_tmp, s_out);
       cur = s;
       if (!ok && threadIdx.x == 0) atomicOr(P.err, 1u);
     }
-    const int64_t c = P.sel_cnt[s];
-    const int64_t j0 = (ch - P.chunk_base[s]) * (int64_t)kChunk;
-    if (!ok || j0 >= c) continue;   // uniform
+    if (!ok) return;   // uniform
     const int len = (int)min((int64_t)kChunk, c - j0);
     const int64_t cb = P.cand_base[s];
     f4 x[kSlots];
@@ -1049,7 +1156,7 @@ __global__ __launch_bounds__(kThreads) void k_collect(DevPlan P) {
         }
     }
     __syncthreads();   // s_base is rewritten for the next chunk
-  }
+  });
 }
 
 // Near-list source: f(key, j) for the n entries at v (keys stored as float bits).
@@ -1068,44 +1175,70 @@ struct NearKeys {
 // largest key in *mx.  Contains barriers.
 __device__ void finish_cands(const DevPlan& P, int s, uint32_t k, SelLds& L, uint32_t* kth_out,
                              uint32_t* ties_out, uint32_t* mx_out) {
-  const uint32_t c = P.sel_cnt[s];
+  // loads that do not wait on one another first: the windowed histogram, the counts, and the
+  // first chunks' counts above the range and largest keys
+  const Bins hb = load_bins(seg_hist(P, s, 1));
+  const uint32_t c = P.sel_cnt[s], n_near = P.near_cnt[s];
   const int64_t cb = P.cand_base[s], ch0 = P.chunk_base[s];
-  KeyRange r;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) L.h[i] = 0;
-  if (threadIdx.x == 0) L.n_list = 0;
-  bool ok = cand_range(P, s, k, &r, L.tmp, L.out);   // (its barriers order the clears)
-  const uint32_t n_near = P.near_cnt[s];
+  const uint32_t nch = (c + kChunk - 1) / kChunk;
+  uint32_t gt0 = 0, mx0 = 0;
+  if (threadIdx.x < nch) {
+    gt0 = P.chunk_gt[ch0 + threadIdx.x];
+    mx0 = P.chunk_max[ch0 + threadIdx.x];
+  }
   const NearKeys near{P.cand_val + cb, n_near};
   const int32_t* npos = P.cand_idx + cb;
+  // a near list that fits in LDS is read once: every entry's key and output chunk
+  const bool in_lds = n_near <= (uint32_t)kListCap;
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) L.h[i] = 0;
+  if (threadIdx.x == 0) L.n_list = 0;
+  if (in_lds) {
+    for (uint32_t j = threadIdx.x; j < n_near; j += kThreads) {
+      L.lkey[j] = mag_key(near.v[j]);
+      L.lch[j] = (uint32_t)npos[j] / kChunk;
+    }
+  }
+  KeyRange r;
+  bool ok = cand_range_in(P, s, k, hb, &r, L.tmp, L.out);   // (its barriers order the above)
   if (ok && n_near != r.cnt) ok = false;   // the list holds exactly the bin's keys
-  if (ok) ok = narrow_range(near, r, false, L.h, L.tmp, L.out);
   uint32_t bad = ok ? 0u : 1u;
-  if (ok && r.hi > r.lo) {
-    // the keys inside r into the LDS list: one slot reservation per wave and step
-    near([&](uint32_t key, uint32_t) {
-      const bool in = key >= r.lo && key <= r.hi;
-      const uint64_t m = __ballot(in);
-      if (m == 0) return;
-      const int lead = __ffsll((unsigned long long)m) - 1;
-      uint32_t base = 0;
-      if (lane_id() == lead) base = atomicAdd(&L.n_list, (uint32_t)__popcll(m));
-      base = __shfl(base, lead, 64);
-      if (in) {
-        const uint32_t p = base + lanes_below(m);
-        if (p < (uint32_t)kListCap) L.lkey[p] = key;
-        else bad = 1;
-      }
-    });
-    bad = block_max<kThreads>(bad, L.tmp);
-    if (!bad && !list_select(L.lkey, min(L.n_list, (uint32_t)kListCap), r, L.h, L.tmp, L.out))
-      bad = 1;
+  if (in_lds) {
+    if (ok && r.hi > r.lo) {
+      const bool found = n_near <= kRankMax
+                             ? rank_select(L.lkey, n_near, r, L.out)
+                             : list_select(L.lkey, n_near, r, L.h, L.tmp, L.out);
+      if (!found) bad = 1;
+    }
+  } else {
+    if (ok) ok = narrow_range(near, r, false, L.h, L.tmp, L.out);
+    bad = ok ? 0u : 1u;
+    if (ok && r.hi > r.lo) {
+      // the keys inside r into the LDS list: one slot reservation per wave and step
+      near([&](uint32_t key, uint32_t) {
+        const bool in = key >= r.lo && key <= r.hi;
+        const uint64_t m = __ballot(in);
+        if (m == 0) return;
+        const int lead = __ffsll((unsigned long long)m) - 1;
+        uint32_t base = 0;
+        if (lane_id() == lead) base = atomicAdd(&L.n_list, (uint32_t)__popcll(m));
+        base = __shfl(base, lead, 64);
+        if (in) {
+          const uint32_t p = base + lanes_below(m);
+          if (p < (uint32_t)kListCap) L.lkey[p] = key;
+          else bad = 1;
+        }
+      });
+      bad = block_max<kThreads>(bad, L.tmp);
+      if (!bad && !list_select(L.lkey, min(L.n_list, (uint32_t)kListCap), r, L.h, L.tmp, L.out))
+        bad = 1;
+    }
   }
   const uint32_t kth = r.lo, ties = r.kk;
   // per output chunk: the keys above kth (k_collect's count above the range plus the near
   // keys above kth) and at kth (near keys only), counted in LDS for windows of kFinishChunks
-  // chunks; then ties before each chunk and kept entries before it (the first `ties` kept)
-  const uint32_t nch = (c + kChunk - 1) / kChunk;
-  uint32_t ce = 0, cs = 0, mx = 0;
+  // chunks; then the ties before each chunk and the kept entries before it: the keys above
+  // kth before it plus the first `ties` of the ties before it
+  uint32_t ce = 0, cg = 0, mx = 0;
   for (uint32_t w0 = 0; w0 < nch; w0 += kFinishChunks) {
     const uint32_t wn = min(nch - w0, (uint32_t)kFinishChunks);
     for (uint32_t i = threadIdx.x; i < wn; i += kThreads) {
@@ -1113,39 +1246,45 @@ __device__ void finish_cands(const DevPlan& P, int s, uint32_t k, SelLds& L, uin
       L.ceq[i] = 0;
     }
     __syncthreads();
-    if (!bad) {
-      near([&](uint32_t key, uint32_t j) {
-        const uint32_t ch = (uint32_t)npos[j] / kChunk;
-        if (ch < w0 || ch >= w0 + wn) return;
-        if (key > kth) atomicAdd(&L.cgt[ch - w0], 1u);
-        else if (key == kth) atomicAdd(&L.ceq[ch - w0], 1u);
-      });
+    auto count = [&](uint32_t key, uint32_t ch) {
+      if (ch < w0 || ch >= w0 + wn) return;
+      if (key > kth) atomicAdd(&L.cgt[ch - w0], 1u);
+      else if (key == kth) atomicAdd(&L.ceq[ch - w0], 1u);
+    };
+    if (!bad && in_lds) {
+      for (uint32_t j = threadIdx.x; j < n_near; j += kThreads) count(L.lkey[j], L.lch[j]);
+    } else if (!bad) {
+      near([&](uint32_t key, uint32_t j) { count(key, (uint32_t)npos[j] / kChunk); });
     }
     __syncthreads();
     for (uint32_t i0 = 0; i0 < wn; i0 += kThreads) {
       const uint32_t i = i0 + threadIdx.x;
       const bool in = i < wn;
       const int64_t ch = ch0 + w0 + i;
-      const uint32_t eq = in ? L.ceq[i] : 0u;
-      const uint32_t gt = in ? P.chunk_gt[ch] + L.cgt[i] : 0u;
-      if (in) mx = max(mx, P.chunk_max[ch]);
-      uint32_t te, ts;
-      const uint32_t eqb = ce + block_excl_scan<kThreads>(eq, L.tmp, &te);
-      const uint32_t take = eqb < ties ? min(eq, ties - eqb) : 0u;
-      const uint32_t selb = cs + block_excl_scan<kThreads>(gt + take, L.tmp, &ts);
+      const bool first = w0 + i0 == 0;   // uniform: the chunks loaded up front
+      uint32_t eq = 0, gt = 0;
+      if (in) {
+        eq = L.ceq[i];
+        gt = (first ? gt0 : P.chunk_gt[ch]) + L.cgt[i];
+        mx = max(mx, first ? mx0 : P.chunk_max[ch]);
+      }
+      uint32_t eqb, gtb, te, tg;
+      block_excl_scan2<kThreads>(eq, gt, L.tmp, L.w, &eqb, &gtb, &te, &tg);
+      eqb += ce;
+      gtb += cg;
       if (in) {
         P.chunk_eq[ch] = eq;
         P.chunk_eq_base[ch] = eqb;
-        P.chunk_sel_base[ch] = selb;
+        P.chunk_sel_base[ch] = gtb + min(eqb, ties);
       }
       ce += te;
-      cs += ts;
+      cg += tg;
     }
     __syncthreads();   // the counters are cleared for the next window
   }
   if (threadIdx.x == 0) {
     if (bad) atomicOr(P.err, 16u);
-    if (cs != k) atomicOr(P.err, 2u);
+    if (cg + min(ce, ties) != k) atomicOr(P.err, 2u);
   }
   *kth_out = kth;
   *ties_out = ties;
@@ -1157,24 +1296,24 @@ __device__ void finish_cands(const DevPlan& P, int s, uint32_t k, SelLds& L, uin
 __device__ uint32_t select_full_scan(const DevPlan& P, int s, uint32_t k, uint32_t ties,
                                      SelLds& L) {
   const int64_t t0 = P.tile_base[s], t1 = P.tile_base[s + 1];
-  uint32_t ce = 0, cs = 0, mx = 0;
+  uint32_t ce = 0, cg = 0, mx = 0;
   for (int64_t tb = t0; tb < t1; tb += kThreads) {
     const int64_t t = tb + threadIdx.x;
     const bool in = t < t1;
     const uint32_t gt = in ? P.tile_gt[t] : 0u, eq = in ? P.tile_eq[t] : 0u;
     if (in) mx = max(mx, P.tile_max[t]);
-    uint32_t te, ts;
-    const uint32_t eqb = ce + block_excl_scan<kThreads>(eq, L.tmp, &te);
-    const uint32_t take = eqb < ties ? min(eq, ties - eqb) : 0u;
-    const uint32_t selb = cs + block_excl_scan<kThreads>(gt + take, L.tmp, &ts);
-    if (in) {
+    uint32_t eqb, gtb, te, tg;
+    block_excl_scan2<kThreads>(eq, gt, L.tmp, L.w, &eqb, &gtb, &te, &tg);
+    eqb += ce;
+    gtb += cg;
+    if (in) {   // kept before the tile: its keys above kth and the first `ties` of its ties
       P.tile_eq_base[t] = eqb;
-      P.tile_sel_base[t] = selb;
+      P.tile_sel_base[t] = gtb + min(eqb, ties);
     }
     ce += te;
-    cs += ts;
+    cg += tg;
   }
-  if (threadIdx.x == 0 && cs != k) atomicOr(P.err, 2u);
+  if (threadIdx.x == 0 && cg + min(ce, ties) != k) atomicOr(P.err, 2u);
   return block_max<kThreads>(mx, L.tmp);
 }
 
@@ -1201,13 +1340,22 @@ __device__ __forceinline__ void block_sums(uint32_t (&v)[N], uint32_t* scratch) 
   __syncthreads();
 }
 
+// LDS of a small segment's select (in the emission kernel).
+struct SmallLds {
+  uint32_t h[kHistBins];
+  uint32_t sums[kSmallTiles * kWaves];
+  uint32_t tmp[kWaves];
+  uint32_t out[3];
+  uint32_t w[kWaves];
+};
+
 // Small segment (at most kSmallTiles tiles): selected whole from its residual (or Random-k
 // keys), every key loaded once into registers: the exact k-th key by a radix select over the
 // registers (digits of 11, 11 and 9 bits, as the full path), then the segment emitted in index
 // order, tile by tile.  Returns kth, ties and the largest key (when an int8 scale needs it).
 // Contains barriers.
 __device__ void select_small(const DevPlan& P, const float* e, const EmitOut& o, int s,
-                             uint32_t k, SelLds& L, uint32_t* kth_out, uint32_t* ties_out,
+                             uint32_t k, SmallLds& L, uint32_t* kth_out, uint32_t* ties_out,
                              uint32_t* mx_out) {
   static_assert(kTile < 65536, "a tile's counts are packed in 16 bits");
   const int64_t t0 = P.tile_base[s];
@@ -1276,7 +1424,7 @@ __device__ void select_small(const DevPlan& P, const float* e, const EmitOut& o,
         }
       cnt[j] = gt | (eq << 16);
     }
-    block_sums<kSmallTiles>(cnt, L.lkey);
+    block_sums<kSmallTiles>(cnt, L.sums);
     uint32_t eqb = 0, kept = 0;
 #pragma unroll
     for (int j = 0; j < kSmallTiles; ++j) {
@@ -1410,7 +1558,7 @@ __global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __r
 // the full path.
 __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, const float* __restrict__ e,
                                                   EmitOut o) {
-  __shared__ SelLds L;
+  __shared__ SmallLds L;
   const uint32_t b = blockIdx.x;
   if (b < (uint32_t)P.n_seg) {
     const int s = (int)b;
@@ -1427,9 +1575,9 @@ __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, const float* __res
   }
   const uint32_t c0 = b - (uint32_t)P.n_seg;
   if (c0 < (uint32_t)P.n_chunk_blocks) {
-    const uint32_t na = *P.act_count;
-    for (uint32_t i = c0; i < na; i += (uint32_t)P.n_chunk_blocks)
-      emit_cand_chunk(P, o, P.act_chunk[i], L.w);
+    for_active_chunks(P, c0, [&](int64_t ch, bool listed) {
+      emit_cand_chunk(P, o, ch, listed, L.w);
+    });
   } else {
     const uint32_t f0 = c0 - (uint32_t)P.n_chunk_blocks;
     emit_full_tiles(P, o, (int)f0, (int)(gridDim.x - P.n_seg - P.n_chunk_blocks), L.w);
