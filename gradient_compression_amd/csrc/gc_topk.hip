@@ -357,21 +357,32 @@ __device__ bool find_digit(uint32_t* gh, uint32_t kk, uint32_t* s_tmp, uint32_t*
 // over its tiles, four per thread), and the segment's candidate chunks appended to the call's
 // list of active chunks.  Contains barriers.
 __device__ void seg_runs(const DevPlan& P, int s, uint32_t c, uint32_t* s_tmp, uint32_t* s_act) {
+  // four tiles per thread and step (16 bytes a lane), four steps' loads issued together
+  constexpr int kQ = 4, kSteps = 4;
   const int64_t t0 = P.tile_base[s], t1 = P.tile_base[s + 1];
   uint32_t carry = 0;
-  for (int64_t tb = t0; tb < t1; tb += kThreads * 4) {
-    const int64_t tq = tb + (int64_t)threadIdx.x * 4;
-    uint32_t n[4];
+  for (int64_t tr = t0; tr < t1; tr += (int64_t)kThreads * kQ * kSteps) {
+    uint32_t n[kSteps][kQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) n[q] = tq + q < t1 ? P.run_cnt[tq + q] : 0u;
-    uint32_t tot;
-    uint32_t run = carry + block_excl_scan<kThreads>(n[0] + n[1] + n[2] + n[3], s_tmp, &tot);
+    for (int st = 0; st < kSteps; ++st) {
+      const int64_t tq = tr + (int64_t)st * kThreads * kQ + (int64_t)threadIdx.x * kQ;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (tq + q < t1) P.run_dst[tq + q] = run;
-      run += n[q];
+      for (int q = 0; q < kQ; ++q) n[st][q] = tq + q < t1 ? P.run_cnt[tq + q] : 0u;
     }
-    carry += tot;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int64_t tq = tr + (int64_t)st * kThreads * kQ + (int64_t)threadIdx.x * kQ;
+      if (tr + (int64_t)st * kThreads * kQ >= t1) break;   // uniform
+      uint32_t tot;
+      uint32_t run = carry + block_excl_scan<kThreads>(n[st][0] + n[st][1] + n[st][2] + n[st][3],
+                                                       s_tmp, &tot);
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        if (tq + q < t1) P.run_dst[tq + q] = run;
+        run += n[st][q];
+      }
+      carry += tot;
+    }
   }
   const uint32_t nch = (c + kChunk - 1) / kChunk;
   if (threadIdx.x == 0) {
@@ -1084,7 +1095,7 @@ __device__ void scatter_chunk(const DevPlan& P, int64_t ch, bool listed, uint32_
   hist_flush(h, seg_hist(P, s, 1));
 }
 
-__global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
+__global__ __launch_bounds__(kThreads, 8) void k_scatter(DevPlan P) {
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t s_m[kWaves];
   for_active_chunks(P, blockIdx.x, [&](int64_t ch, bool listed) {
@@ -1098,7 +1109,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P) {
 // key (chunk_gt), and the keys inside it appended to the segment's near list (key bits in the
 // free unordered candidate region, ordered position beside them).  The range comes from the
 // windowed histogram, derived again by each workgroup for the segments of its chunks.
-__global__ __launch_bounds__(kThreads) void k_collect(DevPlan P) {
+__global__ __launch_bounds__(kThreads, 8) void k_collect(DevPlan P) {
   __shared__ uint32_t s_tmp[kWaves], s_out[3], s_w[kWaves], s_base;
   int cur = -1;
   KeyRange r{0u, 0u, 0u, 0u};
