@@ -45,14 +45,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the code the Top-k streaming pass is built from (its source, the shared device
-    helpers and the plan layout): comments dropped and whitespace collapsed, so that only a
-    change of that code invalidates counters taken on it."""
+    """Hash of the code the Top-k streaming pass is built from (its source file, the capture
+    and device helpers it includes and the plan layout): comments dropped and whitespace
+    collapsed, so that only a change of that code invalidates counters taken on it."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "gradient_compression_amd", "csrc")
     code = []
-    for f in ("gc_topk.hip", "gc_device.h", "gc_internal.h"):
+    for f in ("gc_pass.hip", "gc_capture.h", "gc_device.h", "gc_internal.h"):
         text = open(os.path.join(csrc, f), encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
         text = re.sub(r"//[^\n]*", " ", text)                 # line comments

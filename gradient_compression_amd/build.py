@@ -17,8 +17,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgc.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("gc_topk.hip", "gc_codecs.hip", "gc_scatter.hip",
-                                                       "gc_api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("gc_pass.hip", "gc_topk.hip", "gc_codecs.hip",
+                                                       "gc_scatter.hip", "gc_api.hip")]
 ARCH = "gfx950"
 
 # Tile geometries besides the default (1024 threads x 2 slots, 8192-element tiles).  A tile is

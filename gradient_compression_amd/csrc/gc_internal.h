@@ -216,6 +216,11 @@ struct Int8Args {
   uint32_t seed_lo, seed_hi, step_lo;
 };
 
+// The streaming pass of a Top-k (count_tau false) or threshold (true) call (gc_pass.hip):
+// acc = e + (u = m u + g | g) written into e (and u), candidates captured per tile.
+void launch_ef_capture(const DevPlan& P, const float* g, float* e, float* u, float m,
+                       bool count_tau, hipStream_t st);
+
 // Launchers (gc_topk.hip, gc_codecs.hip, gc_scatter.hip).  Each returns the hipError_t of
 // its launches.
 // cold: the plan has no threshold estimate yet; a sample of tiles sets a first one.

@@ -1,10 +1,10 @@
-// gc_topk.hip -- gfx950 kernels of the error-feedback Top-k path, and the threshold and
-// Random-k sparsifiers that share its select and ordered emission.
+// gc_topk.hip -- gfx950 kernels of the error-feedback Top-k path after the streaming pass, and
+// the threshold and Random-k sparsifiers that share its select and ordered emission.
 //
 // Top-k call (one stream, no host round trip; ten launches on a warm plan):
-//   ef_capture  the streaming pass over g, e (and u): momentum, EF add, write acc into e,
-//               and capture every (acc, index) whose magnitude key reaches the segment's
-//               threshold, as one index-ordered run per tile            [HBM-bound]
+//   ef_capture  (gc_pass.hip) the streaming pass over g, e (and u): momentum, EF add, acc
+//               written into e, and every (acc, index) whose magnitude key reaches the
+//               segment's threshold captured, as one index-ordered run per tile [HBM-bound]
 //   list        per segment: its path (candidates complete, small, or pending), the places
 //               of its runs in index order, its candidate chunks listed
 //   fb_hist     \   only for pending segments (too few or too many candidates, or no
@@ -16,21 +16,22 @@
 //   collect     per chunk: keys above the bin that holds the k-th key, and the keys inside
 //               it appended to the segment's near list
 //   finish      one workgroup per segment: the exact k-th key from the near list (in LDS),
-//               the per-chunk offsets of the ordered emission; small segments are selected
-//               and emitted here whole, from the residual; the next threshold estimate
+//               the per-chunk offsets of the ordered emission, the next threshold estimate
 //   emit        order-preserving compaction: keys above the k-th, then the ties in index
-//               order; writes (value, index) and zeroes e (and u) where kept
+//               order; writes (value, index) and zeroes e (and u) where kept.  Small
+//               segments are selected and emitted whole by workgroups of the same launch.
 //
 // Threshold and Random-k calls run the same select and emit on a per-call copy of the plan
 // (their own k and capture threshold); Random-k ranks per-element Philox keys instead of
 // magnitudes.  The two-pass codecs are in gc_codecs.hip, the payload scatters (int8 stage,
-// decompression) in gc_scatter.hip, the shared device helpers in gc_device.h.
+// decompression) in gc_scatter.hip, the shared device helpers in gc_device.h and
+// gc_capture.h.
 //
 // The method is the Top-K with error feedback of "Communication Optimization > Gradient
 // Compression" (Top-K section equations); momentum correction per the "Gradient
 // Sparsification" glossary; the int8 stage per the "Gradient Compression" glossary
 // (Top-k then 8-bit) with stochastic rounding (QSGD paragraph) and one scale per layer.
-#include "gc_device.h"
+#include "gc_capture.h"
 
 #pragma clang fp contract(off)
 
@@ -55,17 +56,6 @@ __device__ __forceinline__ uint32_t call_k(const DevPlan& P, int s) {
   return P.codec == kCodecThreshold ? min(P.tau_cnt[s], k) : k;
 }
 
-// Capture threshold of segment s in this call: the Top-k estimate, the Random-k plan
-// threshold, or for a threshold call max(key(|tau|), floor), the floor being the estimate of
-// the k-th largest key kept from the last threshold calls (so the capture stays within its
-// capacity when more than k entries reach tau).  Small segments capture nothing.
-__device__ __forceinline__ uint32_t capture_thr(const DevPlan& P, int s) {
-  if (P.codec != kCodecThreshold) return P.thr[s];
-  if (P.seg_flags[s] & kSegSmall) return kNoCapture;
-  const uint32_t tk = mag_key(P.tau[s]), fl = P.thr_est[s];
-  return fl == kNoCapture ? tk : max(tk, fl);
-}
-
 // True when the streaming pass's capture does not hold segment s's k largest keys (fewer
 // than k candidates, more than the capacity, or no threshold yet), so the fallback kernels
 // re-capture it or select it over the whole segment.  Small segments and k = 0 never are.
@@ -76,171 +66,6 @@ __device__ __forceinline__ bool seg_pending(const DevPlan& P, int s) {
   if (P.flags & kFlagForceFull) return true;
   const uint32_t c = P.cand_cnt[s];
   return capture_thr(P, s) == kNoCapture || c < k || c > P.cand_cap[s];
-}
-
-// Tile t of segment s: first element and length.
-__device__ __forceinline__ void tile_range(const DevPlan& P, int s, int64_t t, int64_t* start,
-                                           int* len) {
-  const int64_t st = P.seg_off[s] + (t - P.tile_base[s]) * (int64_t)kTile;
-  const int64_t rem = P.seg_off[s + 1] - st;
-  *start = st;
-  *len = rem < kTile ? (int)rem : kTile;
-}
-
-// Capture, in index order, the elements of tile t (values acc in the tile layout) whose key
-// reaches thr: one atomic on the segment's counter (*count) reserves the tile's run; entries
-// past the capacity are counted but not stored (the segment then leaves the candidate path).
-__device__ __forceinline__ void capture_tile(const DevPlan& P, int s, int64_t t, int64_t start,
-                                             int len, const f4 (&acc)[kSlots], uint32_t thr,
-                                             uint32_t* count, uint32_t* s_w, uint32_t* s_base) {
-  const int pb = slot_base();
-  uint32_t bits[kSlots];
-#pragma unroll
-  for (int v = 0; v < kSlots; ++v) {
-    uint32_t b = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      b |= (pb + v * 256 + c < len && mag_key(acc[v][c]) >= thr) ? (1u << c) : 0u;
-    bits[v] = b;
-  }
-  uint32_t woff[kSlots];
-  const uint32_t total = tile_rank(bits, woff, s_w);
-  if (threadIdx.x == 0) {
-    const uint32_t base = total ? atomicAdd(count, total) : 0u;
-    P.run_off[t] = base;
-    P.run_cnt[t] = total;
-    *s_base = base;
-  }
-  __syncthreads();
-  if (total == 0) return;
-  const uint32_t base = *s_base, cap = P.cand_cap[s];
-  float* cv = P.cand_val + P.cand_base[s];
-  int32_t* ci = P.cand_idx + P.cand_base[s];
-  const int32_t lbase = (int32_t)(start - P.seg_off[s]) + pb;
-#pragma unroll
-  for (int v = 0; v < kSlots; ++v) {
-    const uint32_t b = bits[v];
-    if (!b) continue;
-    uint32_t q = base + woff[v];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if ((b >> c) & 1u) {
-        if (q < cap) {
-          cv[q] = acc[v][c];
-          ci[q] = lbase + v * 256 + c;
-        }
-        ++q;
-      }
-    }
-  }
-}
-
-// The call's lists and the error flag start empty: cleared by the first workgroup of the
-// streaming pass (the kernels that fill them run after it; the last call's readers have ended).
-__device__ __forceinline__ void reset_call_lists(const DevPlan& P) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    *P.pend_count = 0;
-    *P.act_count = 0;
-    *P.full_count = 0;
-    *P.err = 0;
-  }
-}
-
-// -------------------------------------------------------------------------- ef_capture
-// One tile per workgroup.  acc = e + (u = m*u + g | g) is written back into e; elements
-// whose key reaches the segment's threshold are captured (capture_tile).
-// kCountTau (threshold calls): also count the tile's keys >= key(|tau|) into tau_cnt.
-// kScale: the plan carries a gradient scale (a separate instantiation, so that the unscaled
-// pass has no dependent load of the factor in front of its stream).
-template <bool kMomentum, bool kCountTau = false, bool kScale = false>
-__global__ __launch_bounds__(kThreads) void k_ef_capture(DevPlan P, const float* __restrict__ g,
-                                                        float* __restrict__ e,
-                                                        float* __restrict__ u, float m) {
-  __shared__ uint32_t s_w[kWaves];
-  __shared__ uint32_t s_base;
-  __shared__ uint32_t s_tau[kWaves];
-#if GC_XCD_REMAP
-  // workgroups go round-robin to the 8 XCDs: give XCD x a contiguous range of tiles
-  const int64_t G = gridDim.x, per = G / 8, rem = G % 8, xcd = blockIdx.x % 8;
-  const int64_t t = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / 8;
-#else
-  const int64_t t = blockIdx.x;
-#endif
-  const int4 desc = P.tile_desc[t];  // one load: no dependent lookups before the stream
-  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
-  const int len = desc.z, s = desc.w;
-  const int pb = slot_base();
-  const float gf = kScale ? P.gscale[s] : 1.0f;
-  reset_call_lists(P);
-
-  f4 acc[kSlots];
-  if (len == kTile && (start & 3) == 0) {
-    const f4* g4 = reinterpret_cast<const f4*>(g + start);
-    f4* e4 = reinterpret_cast<f4*>(e + start);
-    f4* u4 = kMomentum ? reinterpret_cast<f4*>(u + start) : nullptr;
-    f4 gv[kSlots], uv[kSlots];
-#pragma unroll
-    for (int v = 0; v < kSlots; ++v) {
-      const int q = (pb + v * 256) >> 2;
-      gv[v] = GC_NT_LOAD_G ? __builtin_nontemporal_load(g4 + q) : g4[q];
-      acc[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(e4 + q) : e4[q];
-      if (kMomentum) uv[v] = GC_NT_LOAD_E ? __builtin_nontemporal_load(u4 + q) : u4[q];
-    }
-#pragma unroll
-    for (int v = 0; v < kSlots; ++v) {
-      const int q = (pb + v * 256) >> 2;
-      f4 x = gv[v] * gf;
-      if (kMomentum) {
-        const f4 mu = m * uv[v];
-        x = mu + x;
-        if (GC_NT_STORE_E) __builtin_nontemporal_store(x, u4 + q); else u4[q] = x;
-      }
-      acc[v] = acc[v] + x;
-      if (GC_NT_STORE_E) __builtin_nontemporal_store(acc[v], e4 + q); else e4[q] = acc[v];
-    }
-  } else {
-#pragma unroll
-    for (int v = 0; v < kSlots; ++v)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int p = pb + v * 256 + c;
-        float a = 0.0f;
-        if (p < len) {
-          const int64_t i = start + p;
-          float x = g[i] * gf;
-          if (kMomentum) {
-            const float mu = m * u[i];
-            x = mu + x;
-            u[i] = x;
-          }
-          a = e[i] + x;
-          e[i] = a;
-        }
-        acc[v][c] = a;
-      }
-  }
-  if (kCountTau) {
-    const uint32_t tk = mag_key(P.tau[s]);
-    uint32_t c = 0;
-#pragma unroll
-    for (int v = 0; v < kSlots; ++v)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        c += (pb + v * 256 + cc < len && mag_key(acc[v][cc]) >= tk) ? 1u : 0u;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
-    if (lane_id() == 0) s_tau[wave_id()] = c;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t tot = 0;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) tot += s_tau[i];
-      if (tot) atomicAdd(&P.tau_cnt[s], tot);
-    }
-  }
-  const uint32_t thr = kCountTau ? capture_thr(P, s) : P.thr[s];
-  if (thr == kNoCapture) return;  // uniform: nothing to capture (small, or not estimated yet)
-  capture_tile(P, s, t, start, len, acc, thr, &P.cand_cnt[s], s_w, &s_base);
 }
 
 // ------------------------------------------------------------------------ digit histograms
@@ -1814,16 +1639,7 @@ hipError_t launch_compress(const DevPlan& P0, const float* g, float* e, float* u
     k_sample_decide<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P);
   }
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
-  if (P.n_tiles > 0) {
-    const unsigned nt = (unsigned)P.n_tiles;
-    if (P.gscale) {
-      if (u) k_ef_capture<true, false, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
-      else k_ef_capture<false, false, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
-    } else {
-      if (u) k_ef_capture<true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
-      else k_ef_capture<false><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
-    }
-  }
+  launch_ef_capture(P, g, e, u, m, false, st);
   if (ev_end) (void)hipEventRecord(ev_end, st);
   EmitOut o{};
   o.e = e;
@@ -1852,16 +1668,8 @@ hipError_t launch_threshold(const DevPlan& P0, const float* g, float* e, float* 
   P.out_count = out_count;
   P.scales = nullptr;
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
-  if (P.n_tiles > 0) {
-    const unsigned nt = (unsigned)P.n_tiles;
-    if (P.gscale) {
-      if (u) k_ef_capture<true, true, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
-      else k_ef_capture<false, true, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
-    } else {
-      if (u) k_ef_capture<true, true><<<nt, kThreads, 0, st>>>(P, g, e, u, m);
-      else k_ef_capture<false, true><<<nt, kThreads, 0, st>>>(P, g, e, nullptr, m);
-    }
-  }
+  launch_ef_capture(P, g, e, u, m, true, st);
+
   if (ev_end) (void)hipEventRecord(ev_end, st);
   EmitOut o{};
   o.e = e;
