@@ -2,7 +2,7 @@
 // QSGD with s levels) and of local gradient clipping: a streaming pass for the per-segment
 // sum (|acc| or acc^2, in double), the per-segment scale, then a streaming pass that writes the
 // codes and the residual (or scales g).
-#include "gc_device.h"
+#include "gc_random.h"
 
 #pragma clang fp contract(off)
 

@@ -2,7 +2,7 @@
 // values (per-segment absmax, Philox stochastic rounding, quantisation error fed back),
 // decompression into a dense buffer, and the reference copy and y += x streams used to
 // calibrate bandwidth.
-#include "gc_device.h"
+#include "gc_random.h"
 
 #pragma clang fp contract(off)
 

@@ -32,6 +32,7 @@
 // Sparsification" glossary; the int8 stage per the "Gradient Compression" glossary
 // (Top-k then 8-bit) with stochastic rounding (QSGD paragraph) and one scale per layer.
 #include "gc_capture.h"
+#include "gc_random.h"
 
 #pragma clang fp contract(off)
 
@@ -1487,56 +1488,85 @@ __global__ __launch_bounds__(kThreads) void k_randk_capture(DevPlan P, const flo
 // of the tile layout dominate, so here one wave owns a whole tile: slot v (0 .. kTile/256 - 1)
 // of lane l holds the 4 elements from v * 256 + l * 4 (index order is slot, lane, element).
 // The wave draws its keys slot by slot, ranks the flagged ones with ballots as it goes and
-// stages the first kRkStage of them (key, tile offset) in its own LDS rows; then it reserves
-// the tile's run with one atomic and copies the staged entries out.  Entries past the staging
-// rows (dense segments) are drawn again from the per-slot flags.  No barrier anywhere.
+// stages the first kRkStage of them (key, tile offset) in its own LDS rows.  Then the
+// workgroup's kRkWaves tiles reserve their runs together, one atomic per segment they cover
+// (consecutive tiles, runs in tile order): with one atomic per tile, thousands of waves that
+// finish their tiles of one large segment at once contend on the segment's counter.  Each
+// wave then copies its staged entries out; entries past the staging rows (dense segments) are
+// drawn again from the per-slot flags.  One barrier pair per workgroup.
+// Tiles (waves) per workgroup: one reservation for four tiles took the 7B shape's key pass
+// from 5.1 to 2.9 ms; eight measured the same, sixteen slower (one workgroup per CU).
 constexpr int kRkWaves = 4;
 constexpr int kRkSlots = kTile / 256;
 constexpr int kRkStage = 256;
+// Slots whose keys a wave draws before it looks at their flags (independent Philox chains).
+constexpr int kRkGroup = 4;
+static_assert(8 % kRkGroup == 0, "groups of slots divide a word of eight");
 static_assert(kRkSlots % 8 == 0, "a tile must hold whole words of eight 256-element slots");
 
-template <bool kAligned>
-__device__ __forceinline__ void rk_tile(const DevPlan& P, int64_t t, int64_t start, int len,
-                                        int s, uint32_t thr, int lane, uint32_t* sk,
-                                        int32_t* si) {
-  uint32_t pk[kRkSlots / 8];   // flags, one nibble per slot (the word loop is unrolled)
-  uint32_t cnt = 0;            // wave-uniform: flagged entries so far
+// The keys of one tile: per-slot flags (key >= thr) into pk, one nibble per slot, the first
+// kRkStage flagged (key, tile offset) pairs into the wave's LDS rows in index order; returns
+// the tile's flagged count (wave-uniform).  kWhole: the tile holds kTile elements.
+template <bool kAligned, bool kWhole>
+__device__ __forceinline__ uint32_t rk_draw(const DevPlan& P, int64_t start, int len,
+                                            uint32_t thr, int lane, uint32_t* sk, int32_t* si,
+                                            uint32_t (&pk)[kRkSlots / 8]) {
+  uint32_t cnt = 0;   // wave-uniform: flagged entries so far
 #pragma unroll
   for (int wi = 0; wi < kRkSlots / 8; ++wi) {
     uint32_t word = 0;
-    for (int j = 0; j < 8; ++j) {
-      const int p0 = (wi * 8 + j) * 256 + lane * 4;
-      uint32_t k[4];
-      rand_key4<kAligned>(P, start + p0, k);
-      uint32_t nib = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) nib |= (p0 + c < len && k[c] >= thr) ? (1u << c) : 0u;
-      word |= nib << (4 * j);
-      if (!__ballot(nib != 0)) continue;   // uniform
-      const uint64_t m0 = __ballot(nib & 1u), m1 = __ballot(nib & 2u);
-      const uint64_t m2 = __ballot(nib & 4u), m3 = __ballot(nib & 8u);
-      uint32_t r = cnt + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
-      cnt += __popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3);
+    for (int j0 = 0; j0 < 8; j0 += kRkGroup) {
+      uint32_t k[kRkGroup][4];
+      uint32_t gw = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if ((nib >> c) & 1u) {
-          if (r < (uint32_t)kRkStage) {
-            sk[r] = k[c];
-            si[r] = p0 + c;
+      for (int jj = 0; jj < kRkGroup; ++jj) {
+        const int p0 = (wi * 8 + j0 + jj) * 256 + lane * 4;
+        rand_key4<kAligned>(P, start + p0, k[jj]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          gw |= ((kWhole || p0 + c < len) && k[jj][c] >= thr) ? (1u << (4 * jj + c)) : 0u;
+      }
+      word |= gw << (4 * j0);
+      if (!__ballot(gw != 0)) continue;   // uniform
+#pragma unroll
+      for (int jj = 0; jj < kRkGroup; ++jj) {
+        const uint32_t nib = (gw >> (4 * jj)) & 0xFu;
+        if (!__ballot(nib != 0)) continue;   // uniform
+        const int p0 = (wi * 8 + j0 + jj) * 256 + lane * 4;
+        const uint64_t m0 = __ballot(nib & 1u), m1 = __ballot(nib & 2u);
+        const uint64_t m2 = __ballot(nib & 4u), m3 = __ballot(nib & 8u);
+        uint32_t r = cnt + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) +
+                     lanes_below(m3);
+        cnt += __popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if ((nib >> c) & 1u) {
+            if (r < (uint32_t)kRkStage) {
+              sk[r] = k[jj][c];
+              si[r] = p0 + c;
+            }
+            ++r;
           }
-          ++r;
-        }
+      }
     }
     pk[wi] = word;
   }
-  uint32_t base = 0;
+  return cnt;
+}
+
+// Tile t's run at base: its run record, the staged entries copied out, and the entries past
+// the staging rows drawn again from the flags.
+template <bool kAligned>
+__device__ __forceinline__ void rk_write(const DevPlan& P, int64_t t, int64_t start, int s,
+                                         uint32_t base, uint32_t cnt, int lane,
+                                         const uint32_t* sk, const int32_t* si,
+                                         const uint32_t (&pk)[kRkSlots / 8]) {
   if (lane == 0) {
-    base = cnt ? atomicAdd(&P.cand_cnt[s], cnt) : 0u;
     P.run_off[t] = base;
     P.run_cnt[t] = cnt;
   }
   if (cnt == 0) return;   // uniform
-  base = __shfl(base, 0, 64);
   const uint32_t cap = P.cand_cap[s];
   float* cv = P.cand_val + P.cand_base[s];
   int32_t* ci = P.cand_idx + P.cand_base[s];
@@ -1583,19 +1613,58 @@ __device__ __forceinline__ void rk_tile(const DevPlan& P, int64_t t, int64_t sta
 __global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
   __shared__ uint32_t s_key[kRkWaves][kRkStage];
   __shared__ int32_t s_idx[kRkWaves][kRkStage];
+  __shared__ uint32_t s_cnt[kRkWaves], s_base[kRkWaves];
+  __shared__ int32_t s_seg[kRkWaves];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kRkWaves + w;
   reset_call_lists(P);
-  if (t >= P.n_tiles) return;   // wave-uniform
-  const int4 desc = P.tile_desc[t];
-  const int64_t start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
-  const int len = desc.z, s = desc.w;
-  const uint32_t thr = P.thr[s];
-  if (thr == kNoCapture) return;   // this segment takes the exact fallback
-  if ((start & 3) == 0)   // wave-uniform: every lane's four elements share one Philox block
-    rk_tile<true>(P, t, start, len, s, thr, lane, s_key[w], s_idx[w]);
+  int s = -1;   // -1: nothing to capture (past the last tile, or a segment without threshold)
+  int64_t start = 0;
+  uint32_t cnt = 0;
+  uint32_t pk[kRkSlots / 8];
+  if (t < P.n_tiles) {   // wave-uniform
+    const int4 desc = P.tile_desc[t];
+    start = (int64_t)(((uint64_t)(uint32_t)desc.y << 32) | (uint32_t)desc.x);
+    const int len = desc.z, sd = desc.w;
+    const uint32_t thr = P.thr[sd];
+    if (thr != kNoCapture) {   // else the segment takes the exact fallback
+      s = sd;
+      if ((start & 3) == 0 && len == kTile)   // a whole tile, one Philox block per lane
+        cnt = rk_draw<true, true>(P, start, len, thr, lane, s_key[w], s_idx[w], pk);
+      else if ((start & 3) == 0)
+        cnt = rk_draw<true, false>(P, start, len, thr, lane, s_key[w], s_idx[w], pk);
+      else
+        cnt = rk_draw<false, false>(P, start, len, thr, lane, s_key[w], s_idx[w], pk);
+    }
+  }
+  if (lane == 0) {
+    s_cnt[w] = cnt;
+    s_seg[w] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {   // one reservation per segment covered (its tiles are consecutive)
+    for (int i = 0; i < kRkWaves;) {
+      const int si = s_seg[i];
+      int j = i + 1;
+      while (j < kRkWaves && s_seg[j] == si) ++j;
+      if (si >= 0) {
+        uint32_t tot = 0;
+        for (int q = i; q < j; ++q) tot += s_cnt[q];
+        uint32_t b = tot ? atomicAdd(&P.cand_cnt[si], tot) : 0u;
+        for (int q = i; q < j; ++q) {
+          s_base[q] = b;
+          b += s_cnt[q];
+        }
+      }
+      i = j;
+    }
+  }
+  __syncthreads();
+  if (s < 0) return;   // wave-uniform
+  if ((start & 3) == 0)
+    rk_write<true>(P, t, start, s, s_base[w], cnt, lane, s_key[w], s_idx[w], pk);
   else
-    rk_tile<false>(P, t, start, len, s, thr, lane, s_key[w], s_idx[w]);
+    rk_write<false>(P, t, start, s, s_base[w], cnt, lane, s_key[w], s_idx[w], pk);
 }
 
 // Everything after the streaming pass: the per-segment list, the fallback kernels (they end
