@@ -23,6 +23,9 @@ GC_ERR_UNSUPPORTED = -4
 GC_MOMENTUM_MASK = 0x1
 GC_DEBUG_FORCE_FALLBACK = 0x100
 GC_DEBUG_NO_ESTIMATE = 0x200
+# Select with the chain of kernels over candidate chunks even where one workgroup per segment
+# would do (same results; tests).
+GC_DEBUG_CHAIN = 0x400
 
 MODE_SKIP, MODE_CANDIDATES, MODE_FULL, MODE_RECAPTURED, MODE_SMALL = 0, 1, 2, 3, 5
 # Segments of at most this many elements are selected whole by one workgroup (MODE_SMALL).
@@ -473,5 +476,5 @@ def read_f32(x, sink, stream=None):
 
 __all__ = ["Plan", "GCError", "lib", "status_string", "copy_f32", "add_f32", "read_f32", "layout",
            "topk_ef_compress_noalloc", "EXPORTS",
-           "GC_MOMENTUM_MASK", "GC_DEBUG_FORCE_FALLBACK", "GC_DEBUG_NO_ESTIMATE", "MODE_SKIP",
+           "GC_MOMENTUM_MASK", "GC_DEBUG_FORCE_FALLBACK", "GC_DEBUG_NO_ESTIMATE", "GC_DEBUG_CHAIN", "MODE_SKIP",
            "MODE_CANDIDATES", "MODE_FULL", "MODE_RECAPTURED", "MODE_SMALL", "SMALL_SEGMENT"]

@@ -276,6 +276,9 @@ int plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const d
   d.n_tiles = n_tiles;
   d.n_chunks = n_chunks;
   d.n_chunk_blocks = gc::chunk_walkers(n_chunks);
+  d.single = (flags & GC_DEBUG_CHAIN) ? 0 : 1;
+  for (int32_t s = 0; s < n_seg && d.single; ++s)
+    if (!gc::single_segment_ok(seg_off[s + 1] - seg_off[s], ks[s])) d.single = 0;
   int64_t *d_seg_off, *d_tile_base, *d_chunk_base, *d_out_off, *d_cand_base, *d_out_chunk_base;
   int32_t *d_tile_seg, *d_chunk_seg, *d_out_chunk_seg;
   int4* d_tile_desc;
@@ -440,7 +443,8 @@ int gc_plan_create(const int64_t* seg_off, int32_t n_seg, const int64_t* k, cons
   if (!out) return GC_ERR_INVALID_ARG;
   *out = nullptr;
   if (n_seg < 0 || !seg_off) return GC_ERR_INVALID_ARG;
-  if (flags & ~(uint32_t)(GC_MOMENTUM_MASK | GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE))
+  if (flags & ~(uint32_t)(GC_MOMENTUM_MASK | GC_DEBUG_FORCE_FALLBACK | GC_DEBUG_NO_ESTIMATE |
+                          GC_DEBUG_CHAIN))
     return GC_ERR_INVALID_ARG;
   try {
     return plan_create(seg_off, n_seg, k, ratio, flags, out);
@@ -1112,6 +1116,7 @@ int gc_topk_ef_compress_noalloc(const int64_t* seg_off, int32_t n_seg, const int
   d.n_tiles = tiles;
   d.n_chunks = chunks;
   d.n_chunk_blocks = gc::chunk_walkers(chunks);
+  d.single = 0;
   d.keys = gc::kKeysMagnitude;
   d.n_sample = 0;
   d.sample_tile = nullptr;

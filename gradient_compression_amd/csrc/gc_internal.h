@@ -85,6 +85,17 @@ constexpr int kListCap = 4096;
 // Output chunks whose counts the finish workgroup keeps in LDS at a time.
 constexpr int kFinishChunks = 1024;
 
+// Plans whose every segment is small, or has at most kSingleMaxElems elements and either
+// 4 k <= kChunk or at most kSingleWholeElems elements, are selected after the pass by one
+// workgroup per segment (k_single): its candidates, when complete and at most one chunk, in
+// LDS; otherwise a radix select over the whole segment streamed by that workgroup.
+constexpr int64_t kSingleMaxElems = (int64_t)1 << 22;
+constexpr int64_t kSingleWholeElems = 65536;
+inline bool single_segment_ok(int64_t n, int64_t k) {
+  return n <= kSmallSegment ||
+         (n <= kSingleMaxElems && (4 * k <= kChunk || n <= kSingleWholeElems));
+}
+
 constexpr uint32_t kNoCapture = 0xFFFFFFFFu;        // threshold above every key
 // Per-segment path of a call.  kModeCand: the candidates captured at the estimated threshold
 // hold the k largest.  kModeRecap: they did not, the segment's first-digit histogram was
@@ -100,6 +111,7 @@ constexpr uint32_t kSegSmall = 0x1;
 constexpr int32_t kFlagMomentumMask = 0x1;
 constexpr int32_t kFlagForceFull = 0x100;
 constexpr int32_t kFlagNoEstimate = 0x200;
+constexpr int32_t kFlagChain = 0x400;
 // What the select ranks: |acc| (Top-k, threshold) or a per-element Philox key (Random-k).
 // Random keys are 31-bit and travel through the candidate buffers as float bit patterns, so
 // the select kernels read both kinds through the same magnitude-key view.
@@ -119,6 +131,7 @@ struct DevPlan {
   int64_t n_tiles;
   int64_t n_chunks;
   int32_t n_chunk_blocks;      // chunk_walkers(n_chunks): the chunk walkers of a launch
+  int32_t single;              // one workgroup per segment selects after the pass (k_single)
   int32_t codec;               // kCodec* of this call
   // host-built tables
   const int64_t* seg_off;      // [n_seg + 1]

@@ -134,7 +134,7 @@ __device__ __forceinline__ Bins load_bins(const uint32_t* gh) {
 // holds its share, load_bins): the bin d that holds it, the count above it and the bin's
 // count.  s_tmp: __shared__ uint32_t[kWaves]; s_out: __shared__ uint32_t[3].  Contains
 // barriers: call from every thread.
-__device__ bool find_digit_in(const Bins& b, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
+__device__ __forceinline__ bool find_digit_in(const Bins& b, uint32_t kk, uint32_t* s_tmp, uint32_t* s_out,
                               uint32_t* d_out, uint32_t* above_out, uint32_t* bin_out) {
   constexpr int kPer = kHistBins / kThreads;
   uint32_t sum = 0;
@@ -708,7 +708,7 @@ __device__ __forceinline__ uint32_t range_bin(uint32_t key, uint32_t lo, int sh)
 
 // Narrow r to the bin that holds its kk-th largest key, from this thread's share of the
 // histogram's bins.  Contains barriers.
-__device__ bool range_step_in(const Bins& b, KeyRange& r, int sh, uint32_t* s_tmp,
+__device__ __forceinline__ bool range_step_in(const Bins& b, KeyRange& r, int sh, uint32_t* s_tmp,
                               uint32_t* s_out) {
   uint32_t d, above, bin;
   if (!find_digit_in(b, r.kk, s_tmp, s_out, &d, &above, &bin)) return false;
@@ -1191,9 +1191,10 @@ struct SmallLds {
 // registers (digits of 11, 11 and 9 bits, as the full path), then the segment emitted in index
 // order, tile by tile.  Returns kth, ties and the largest key (when an int8 scale needs it).
 // Contains barriers.
-__device__ void select_small(const DevPlan& P, const float* e, const EmitOut& o, int s,
-                             uint32_t k, SmallLds& L, uint32_t* kth_out, uint32_t* ties_out,
-                             uint32_t* mx_out) {
+__device__ __forceinline__ void select_small(const DevPlan& P, const float* e,
+                                             const EmitOut& o, int s, uint32_t k, SmallLds& L,
+                                             uint32_t* kth_out, uint32_t* ties_out,
+                                             uint32_t* mx_out) {
   static_assert(kTile < 65536, "a tile's counts are packed in 16 bits");
   const int64_t t0 = P.tile_base[s];
   const int nt = (int)(P.tile_base[s + 1] - t0);
@@ -1309,30 +1310,18 @@ __global__ __launch_bounds__(kThreads) void k_list(DevPlan P) {
   seg_runs(P, s, c, s_tmp, &s_act);
 }
 
-// One workgroup per segment, last before the emission: the segment's exact k-th key and ties
-// (candidate path: from its near list; full path: from fb_count), the offsets of its ordered
-// emission, the int8 scale, the threshold call's count and padding, the call's statistics,
-// the next capture threshold, and the per-call counters and histograms cleared for the next
-// call.
-__global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __restrict__ e,
-                                                    EmitOut o) {
-  __shared__ SelLds L;
-  const int s = blockIdx.x;
-  const uint32_t k = call_k(P, s);
-  const uint32_t mode = P.mode[s];
-  const bool pend = mode == kModeRecap || mode == kModeFull;
-  const uint32_t thr_used = capture_thr(P, s);
-  const uint32_t c_cap = P.cand_cnt[s];
-  uint32_t kth = 0, ties = 0, mx = 0, c_sel = 0;
-  if (mode == kModeCand || mode == kModeRecap) {
-    c_sel = P.sel_cnt[s];
-    finish_cands(P, s, k, L, &kth, &ties, &mx);
-  } else if (mode == kModeFull) {
-    kth = P.kth[s];
-    ties = P.ties[s];
-    mx = select_full_scan(P, s, k, ties, L);
-  }
-  // threshold call: the count, and the unused slots padded with (+0, -1)
+// Last per-segment step of a call (every thread of the workgroup): the threshold call's
+// count and its unused slots padded with (+0, -1); the statistics; the next capture threshold
+// (beta * |kth|, the margin beta steered by the last calls: lowered after too few candidates,
+// raised after an overflow or far more than needed, kept in [0.25, GC_BETA_MAX]; segments that
+// capture everything or nothing keep their setting); the per-call counters cleared.  pend: the
+// capture was incomplete; c_cap: candidates the pass captured; c_sel: candidates the select
+// ran over.  A small segment's kth, ties and scale are written by its select.
+__device__ __forceinline__ void finalize_segment(const DevPlan& P, const EmitOut& o, int s,
+                                                 uint32_t k, uint32_t mode, bool pend,
+                                                 uint32_t thr_used, uint32_t c_cap,
+                                                 uint32_t c_sel, uint32_t kth, uint32_t ties,
+                                                 uint32_t mx) {
   if (P.codec == kCodecThreshold) {
     const int64_t a = P.out_off[s] + k, b = P.out_off[s + 1];
     for (int64_t j = a + threadIdx.x; j < b; j += kThreads) {
@@ -1340,25 +1329,14 @@ __global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __r
       o.idx[j] = -1;
     }
   }
-  // histograms used by this call, cleared for the next one: the candidates' windowed one
-  // (slot 1) and, for a pending segment, the fallback's three
-  if (mode == kModeCand || pend) {
-    uint32_t* h = seg_hist(P, s, pend ? 0 : 1);
-    const int nb = (pend ? 3 : 1) * kHistBins;
-    for (int i = threadIdx.x; i < nb; i += kThreads) h[i] = 0;
-  }
   if (threadIdx.x != 0) return;
   if (P.out_count) P.out_count[s] = (int32_t)k;
   if (P.scales && mode != kModeSmall) P.scales[s] = k ? __uint_as_float(mx) / 127.0f : 0.0f;
   P.sel_cnt[s] = c_sel;
-  if (mode != kModeSmall) {   // a small segment's are written by its select in k_emit
+  if (mode != kModeSmall) {
     P.kth[s] = kth;
     P.ties[s] = ties;
   }
-  // next capture threshold: beta * |kth|, the margin beta steered by the last calls: lowered
-  // after too few candidates, raised after an overflow or far more than needed, kept in
-  // [0.25, GC_BETA_MAX] (a cap near 1 suits a residual that still grows, whose next k-th key
-  // lies above the last one).  Segments that capture everything or nothing keep their setting.
   const bool steer = mode != kModeSmall && k > 0 && P.thr_init[s] == kNoCapture &&
                      !(P.flags & (kFlagForceFull | kFlagNoEstimate));
   if (P.codec == kCodecTopk || P.codec == kCodecThreshold) {
@@ -1387,6 +1365,39 @@ __global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __r
   P.recap_cnt[s] = 0;
   if (mode != kModeSmall) P.tau_cnt[s] = 0;   // a small segment's k is read by its select later
   P.near_cnt[s] = 0;
+}
+
+// One workgroup per segment, last before the emission: the segment's exact k-th key and ties
+// (candidate path: from its near list; full path: from fb_count), the offsets of its ordered
+// emission, the int8 scale, the threshold call's count and padding, the call's statistics,
+// the next capture threshold, and the per-call counters and histograms cleared for the next
+// call.
+__global__ __launch_bounds__(kThreads) void k_finish(DevPlan P, const float* __restrict__ e,
+                                                    EmitOut o) {
+  __shared__ SelLds L;
+  const int s = blockIdx.x;
+  const uint32_t k = call_k(P, s);
+  const uint32_t mode = P.mode[s];
+  const bool pend = mode == kModeRecap || mode == kModeFull;
+  const uint32_t thr_used = capture_thr(P, s);
+  const uint32_t c_cap = P.cand_cnt[s];
+  uint32_t kth = 0, ties = 0, mx = 0, c_sel = 0;
+  if (mode == kModeCand || mode == kModeRecap) {
+    c_sel = P.sel_cnt[s];
+    finish_cands(P, s, k, L, &kth, &ties, &mx);
+  } else if (mode == kModeFull) {
+    kth = P.kth[s];
+    ties = P.ties[s];
+    mx = select_full_scan(P, s, k, ties, L);
+  }
+  // histograms used by this call, cleared for the next one: the candidates' windowed one
+  // (slot 1) and, for a pending segment, the fallback's three
+  if (mode == kModeCand || pend) {
+    uint32_t* h = seg_hist(P, s, pend ? 0 : 1);
+    const int nb = (pend ? 3 : 1) * kHistBins;
+    for (int i = threadIdx.x; i < nb; i += kThreads) h[i] = 0;
+  }
+  finalize_segment(P, o, s, k, mode, pend, thr_used, c_cap, c_sel, kth, ties, mx);
 }
 
 // The last kernel of a call.  Workgroups [0, n_seg): a small segment each (selected and
@@ -1419,6 +1430,238 @@ __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, const float* __res
     const uint32_t f0 = c0 - (uint32_t)P.n_chunk_blocks;
     emit_full_tiles(P, o, (int)f0, (int)(gridDim.x - P.n_seg - P.n_chunk_blocks), L.w);
   }
+}
+
+// ----------------------------------------------------------------- one workgroup per segment
+// A plan whose segments are all modest (single_segment_ok) is selected after the streaming
+// pass by this kernel alone, one workgroup per segment, instead of the chain of kernels over
+// candidate chunks (whose launches, not bytes, set such a call's time):
+//  * a small segment: select_small, from its residual;
+//  * candidates complete (k <= count <= capacity) and at most one chunk: the runs placed in
+//    index order in LDS, the exact k-th key by a radix select over them in registers, and the
+//    chunk emitted in order;
+//  * candidates complete but more than one chunk: the radix select over the candidate buffer
+//    (in any order), then the segment's tiles emitted in order from its residual;
+//  * otherwise (a miss, an overflow, no estimate yet): a radix select streamed over the
+//    segment's residual (three passes), then its tiles emitted in order.
+// Then the segment's finish.
+constexpr int kSingleTiles = (int)((kSingleMaxElems + kTile - 1) / kTile);
+
+struct alignas(16) SingleLds {
+  float val[kChunk];             // the candidates in index order
+  int32_t idx[kChunk];
+  uint32_t rdst[kSingleTiles];   // per tile: the index-ordered place of its run
+  uint32_t roff[kSingleTiles];   // per tile: the run's offset in the candidate buffer
+  SmallLds sm;
+};
+
+// The k-th largest key of a key source by a radix select, digits of 11, 11 and 9 bits, each
+// LDS histogram (zero on entry and on return) cleared by its digit search; *ties: the entries
+// to take at exactly the k-th key.  each(f) calls f(key) for the source's keys, each thread a
+// share.  False when the source holds fewer than k keys.  Contains barriers.
+template <typename Each>
+__device__ __forceinline__ bool radix_select(Each each, uint32_t k, SmallLds& L,
+                                             uint32_t* kth, uint32_t* ties) {
+  uint32_t prefix = 0, kk = k;
+  for (int pass = 0; pass < 3; ++pass) {
+    const uint32_t pm = prefix_mask(pass), dm = digit_mask(pass);
+    const int sh = digit_shift(pass);
+    each([&](uint32_t key) {
+      if ((key & pm) == prefix) atomicAdd(&L.h[(key >> sh) & dm], 1u);
+    });
+    __syncthreads();
+    uint32_t d, above, bin;
+    if (!find_digit<true>(L.h, kk, L.tmp, L.out, &d, &above, &bin)) return false;
+    prefix |= d << sh;
+    kk -= above;
+  }
+  *kth = prefix;
+  *ties = kk;
+  return true;
+}
+
+__global__ __launch_bounds__(kThreads) void k_single(DevPlan P, const float* __restrict__ e,
+                                                    EmitOut o) {
+  __shared__ SingleLds L;
+  const int s = blockIdx.x;
+  const uint32_t k = call_k(P, s);
+  const int64_t s0 = P.seg_off[s];
+  const int32_t n_s = (int32_t)(P.seg_off[s + 1] - s0);
+  const int64_t t0 = P.tile_base[s];
+  const int nt = (int)(P.tile_base[s + 1] - t0);
+  const uint32_t thr_used = capture_thr(P, s);
+  const uint32_t c = P.cand_cnt[s];
+  const int pb = slot_base();
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) L.sm.h[i] = 0;
+  __syncthreads();
+  if (k == 0) {   // uniform
+    if (threadIdx.x == 0) P.mode[s] = kModeSkip;
+    finalize_segment(P, o, s, 0u, kModeSkip, false, thr_used, c, 0u, 0u, 0u, 0u);
+    return;
+  }
+  if (P.seg_flags[s] & kSegSmall) {   // uniform
+    uint32_t kth, ties, mx;
+    select_small(P, e, o, s, k, L.sm, &kth, &ties, &mx);
+    if (threadIdx.x == 0) {
+      P.mode[s] = kModeSmall;
+      if (P.scales) P.scales[s] = __uint_as_float(mx) / 127.0f;
+      P.kth[s] = kth;
+      P.ties[s] = ties;
+    }
+    __syncthreads();   // every thread has read k (the threshold call's count) before it is reset
+    finalize_segment(P, o, s, k, kModeSmall, false, thr_used, c, 0u, kth, ties, mx);
+    if (threadIdx.x == 0) P.tau_cnt[s] = 0;
+    return;
+  }
+  EmitOut os = o;
+  if (os.rk_scale) os.vmul = os.rk_scale[s];
+  if (os.vsrc_scale) os.gmul = os.vsrc_scale[s];
+  const bool want_mx = P.scales || os.codes;
+  const bool pend = seg_pending(P, s);
+  uint32_t kth = 0, ties = 0, mx = 0, c_sel = 0, mode;
+  uint32_t bad = 0;
+  if (!pend && c <= (uint32_t)kChunk) {   // uniform
+    mode = kModeCand;
+    c_sel = c;
+    // the runs' places in index order: an exclusive scan of the run sizes over the tiles
+    const int64_t cb = P.cand_base[s];
+    uint32_t carry = 0;
+    for (int tb = 0; tb < nt; tb += kThreads) {
+      const int lt = tb + (int)threadIdx.x;
+      const uint32_t n = lt < nt ? P.run_cnt[t0 + lt] : 0u;
+      uint32_t tot;
+      const uint32_t d = carry + block_excl_scan<kThreads>(n, L.sm.tmp, &tot);
+      if (lt < nt) {
+        L.rdst[lt] = d;
+        L.roff[lt] = P.run_off[t0 + lt];
+      }
+      carry += tot;
+    }
+    __syncthreads();
+    if (carry != c) bad = 1;
+    for (uint32_t j = threadIdx.x; j < c; j += kThreads) {
+      const float v = P.cand_val[cb + j];
+      const int32_t ix = P.cand_idx[cb + j];
+      const int lt = ix >= 0 && ix < n_s ? ix / kTile : -1;
+      uint32_t dst = (uint32_t)kChunk;
+      if (lt >= 0 && lt < nt && j >= L.roff[lt]) dst = L.rdst[lt] + (j - L.roff[lt]);
+      if (dst < c) {
+        L.val[dst] = v;
+        L.idx[dst] = ix;
+      } else {
+        bad = 1;
+      }
+    }
+    bad = block_max<kThreads>(bad, L.sm.tmp);   // (its barriers order the LDS writes above)
+    f4 x[kSlots];
+#pragma unroll
+    for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p = pb + v * 256 + q;
+        x[v][q] = p < (int)c ? L.val[p] : 0.0f;
+      }
+    auto keys = [&](auto f) {
+#pragma unroll
+      for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (pb + v * 256 + q < (int)c) f(mag_key(x[v][q]));
+    };
+    const bool ok = !bad && radix_select(keys, k, L.sm, &kth, &ties);
+    if (want_mx) {   // uniform
+      keys([&](uint32_t key) { mx = max(mx, key); });
+      mx = block_max<kThreads>(mx, L.sm.tmp);
+    }
+    if (ok) {   // uniform
+      if (os.codes) os.scale = __uint_as_float(mx) / 127.0f;
+      uint32_t gt, eq;
+      count_block(x, (int)c, kth, L.sm.tmp, &gt, &eq);
+      auto slot_idx = [&](int v) {
+        i4 r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int p = pb + v * 256 + q;
+          r[q] = p < (int)c ? L.idx[p] : 0;
+        }
+        return r;
+      };
+      emit_block(x, (int)c, slot_idx, kth, ties, 0u, eq, P.out_off[s], P.out_off[s + 1], s0,
+                 n_s, L.sm.w, os);
+      if (threadIdx.x == 0 && gt + min(eq, ties) != k) atomicOr(P.err, 2u);
+    } else {
+      bad = 1;
+    }
+  } else {
+    // the k-th key from the candidates when they are complete (more than one chunk: read
+    // from the candidate buffer, in any order), else from a radix select streamed over the
+    // segment's residual; then the segment's tiles emitted in order
+    mode = pend ? kModeFull : kModeCand;
+    c_sel = pend ? 0u : c;
+    const int64_t cb = P.cand_base[s];
+    auto cand_keys = [&](auto f) {
+      for (uint32_t j = threadIdx.x; j < c; j += kThreads) f(mag_key(P.cand_val[cb + j]));
+    };
+    auto seg_keys = [&](auto f) {   // two tiles' loads in flight at a time
+      for (int j = 0; j < nt; j += 2) {
+        int64_t st0, st1 = 0;
+        int len0, len1 = 0;
+        tile_range(P, s, t0 + j, &st0, &len0);
+        if (j + 1 < nt) tile_range(P, s, t0 + j + 1, &st1, &len1);
+        f4 x0[kSlots], x1[kSlots];
+        key_tile(P, e, st0, len0, x0);
+        key_tile(P, e, st1, len1, x1);
+#pragma unroll
+        for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (pb + v * 256 + q < len0) f(mag_key(x0[v][q]));
+            if (pb + v * 256 + q < len1) f(mag_key(x1[v][q]));
+          }
+      }
+    };
+    bool ok;
+    if (pend) {   // uniform
+      ok = radix_select(seg_keys, k, L.sm, &kth, &ties);
+      if (want_mx) seg_keys([&](uint32_t key) { mx = max(mx, key); });
+    } else {
+      ok = radix_select(cand_keys, k, L.sm, &kth, &ties);
+      if (want_mx) cand_keys([&](uint32_t key) { mx = max(mx, key); });   // the largest is one
+    }
+    if (want_mx) mx = block_max<kThreads>(mx, L.sm.tmp);
+    if (ok) {   // uniform
+      if (os.codes) os.scale = __uint_as_float(mx) / 127.0f;
+      uint32_t eqb = 0, kept = 0;
+      f4 xn[kSlots];   // the next tile's keys, loaded while this one is emitted
+      int64_t stn;
+      int lenn;
+      tile_range(P, s, t0, &stn, &lenn);
+      key_tile(P, e, stn, lenn, xn);
+      for (int j = 0; j < nt; ++j) {
+        f4 x[kSlots];
+#pragma unroll
+        for (int v = 0; v < kSlots; ++v) x[v] = xn[v];
+        const int len = lenn;
+        if (j + 1 < nt) {
+          tile_range(P, s, t0 + j + 1, &stn, &lenn);
+          key_tile(P, e, stn, lenn, xn);
+        }
+        uint32_t gt, eq;
+        count_block(x, len, kth, L.sm.tmp, &gt, &eq);
+        emit_seg_tile(P, os, s, t0 + j, kth, ties, eqb, eq, kept, x, L.sm.w);
+        kept += gt + (eqb < ties ? min(eq, ties - eqb) : 0u);
+        eqb += eq;
+      }
+      if (threadIdx.x == 0 && kept != k) atomicOr(P.err, 2u);
+    } else {
+      bad = 1;
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (bad) atomicOr(P.err, 16u);
+    P.mode[s] = mode;
+  }
+  finalize_segment(P, o, s, k, mode, pend, thr_used, c, c_sel, kth, ties, mx);
 }
 
 // -------------------------------------------------------------------------------- Random-k
@@ -1672,6 +1915,10 @@ __global__ __launch_bounds__(kRkWaves * 64) void k_randk_keys(DevPlan P) {
 // per-segment finish, and the ordered emission with the small segments' selects beside it.
 // e holds acc (magnitude keys); Random-k keys are drawn again where needed.
 void select_emit(const DevPlan& P, const float* e, const EmitOut& o, hipStream_t st) {
+  if (P.single) {
+    k_single<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P, e, o);
+    return;
+  }
   const int64_t nt = P.n_tiles > 0 ? P.n_tiles : 1;
   const unsigned fb = (unsigned)(nt < kFallbackBlocks ? nt : kFallbackBlocks);
   k_list<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P);

@@ -66,6 +66,9 @@ typedef enum {
 #define GC_DEBUG_NO_ESTIMATE 0x200u    /* keep no threshold between calls: every call
                                           re-captures candidates from a histogram of the
                                           whole segment (same results, slower; tests) */
+#define GC_DEBUG_CHAIN 0x400u          /* select with the chain of kernels over candidate
+                                          chunks even where one workgroup per segment would
+                                          do (same results; tests) */
 
 typedef struct gc_plan gc_plan;
 
@@ -89,7 +92,8 @@ int gc_layout(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const dou
  *   ratio   : host double[n_seg] in [0, 1]; k[s] = min(n_s, ceil(n_s * ratio[s])) computed in
  *             exact parts-per-billion (0.1% of 2^20 gives 1049); or NULL when k is given.
  *             Exactly one of k and ratio must be non-NULL.
- *   flags   : any of GC_MOMENTUM_MASK, GC_DEBUG_FORCE_FALLBACK, GC_DEBUG_NO_ESTIMATE, or 0.
+ *   flags   : any of GC_MOMENTUM_MASK, GC_DEBUG_FORCE_FALLBACK, GC_DEBUG_NO_ESTIMATE,
+ *             GC_DEBUG_CHAIN, or 0.
  *   out     : receives the plan.
  * The plan keeps a per-segment threshold estimate between calls; it only decides how much
  * work a call does, never what it returns.  Its single device allocation holds about 25 KB

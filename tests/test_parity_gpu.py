@@ -133,19 +133,33 @@ def test_thousands_of_segments_full_path():
                flags=gca.GC_DEBUG_FORCE_FALLBACK, label="800 segments, full path")
 
 
-def test_no_estimate_recaptures_every_call():
-    sizes = [300000, 20000, 8192 * 9 + 5]
+# These plans are modest enough for the one-workgroup-per-segment select; GC_DEBUG_CHAIN runs
+# the chain of kernels instead.  Both must give the oracle's results; their paths differ: an
+# incomplete capture is re-captured by the chain's fallback kernels (MODE_RECAPTURED) and
+# selected over the whole segment by the segment's workgroup (MODE_FULL).
+PATHS = pytest.mark.parametrize("chain", [True, False], ids=["chain", "single"])
+
+
+def _fallback_mode(chain):
+    return gca.MODE_RECAPTURED if chain else gca.MODE_FULL
+
+
+@PATHS
+def test_no_estimate_recaptures_every_call(chain):
+    sizes = [200000, 20000, 8192 * 9 + 5]   # every segment allows the one-workgroup select
     seen = []
     run_parity(sizes, t_grads(sum(sizes), 3, seed=19), ratio=0.01,
-               flags=gca.GC_DEBUG_NO_ESTIMATE, label="no estimate",
+               flags=gca.GC_DEBUG_NO_ESTIMATE | (gca.GC_DEBUG_CHAIN if chain else 0),
+               label=f"no estimate chain={chain}",
                check_stats=lambda t, st: seen.append(st["mode"].tolist()))
-    # no threshold is kept: every large segment re-captures from its histogram on every call
-    # (a small one is selected whole, as always)
-    want = [gca.MODE_SMALL if n <= gca.SMALL_SEGMENT else gca.MODE_RECAPTURED for n in sizes]
+    # no threshold is kept: every large segment takes the fallback on every call (a small one
+    # is selected whole, as always)
+    want = [gca.MODE_SMALL if n <= gca.SMALL_SEGMENT else _fallback_mode(chain) for n in sizes]
     assert all(m == want for m in seen), seen
 
 
-def test_estimate_miss_and_overflow_fall_back():
+@PATHS
+def test_estimate_miss_and_overflow_fall_back(chain):
     """acc far smaller than at the last call (the threshold is too high: fewer than k
     candidates) and then far larger (more candidates than the capacity) must still give
     exact results, through the full-segment path."""
@@ -162,13 +176,50 @@ def test_estimate_miss_and_overflow_fall_back():
         return noise
 
     seen = []
-    run_parity(sizes, (6, grad), ratio=0.001, label="miss/overflow",
+    run_parity(sizes, (6, grad), ratio=0.001, flags=gca.GC_DEBUG_CHAIN if chain else 0,
+               label=f"miss/overflow chain={chain}",
                check_stats=lambda t, st: seen.append(st["mode"].tolist()))
     log(f"modes: {seen}")
     assert seen[0] == [gca.MODE_CANDIDATES] * 2        # fresh plan: the sampled estimate
     assert seen[1] == [gca.MODE_CANDIDATES] * 2
-    assert seen[2] == [gca.MODE_RECAPTURED] * 2        # too few candidates
-    assert seen[4] == [gca.MODE_RECAPTURED] * 2        # too many candidates
+    assert seen[2] == [_fallback_mode(chain)] * 2      # too few candidates
+    assert seen[4] == [_fallback_mode(chain)] * 2      # too many candidates
+
+
+# Segment sizes per ratio that every segment of the plan allows the one-workgroup select for
+# (at most 2^22 elements, and 4 k <= 8192 or at most 65536 elements; small ones always).
+SINGLE_SIZES = {0.001: [1 << 20, 300007, 16384, 65536 + 17, 9000],
+                0.01: [200000, 50000, 16384, 65536 + 17, 9000],
+                0.1: [65536, 20000, 16385, 60000, 9000]}
+
+
+@pytest.mark.parametrize("ratio", sorted(SINGLE_SIZES))
+def test_single_and_chain_agree(ratio):
+    """The same plan selected by one workgroup per segment and by the chain of kernels:
+    bit-identical outputs and state on every step (ties, ragged tiles, small segments, and at
+    10% segments captured whole, more candidates than one chunk)."""
+    sizes = SINGLE_SIZES[ratio]
+    n = sum(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    rng = np.random.default_rng(23)
+    grads = [(np.round(rng.standard_t(3, n) * 8.0) / 8.0 * 1e-3).astype(np.float32)
+             for _ in range(4)]
+    plans = [gca.Plan(off, ratio=ratio), gca.Plan(off, ratio=ratio, flags=gca.GC_DEBUG_CHAIN)]
+    es = [torch.zeros(n, device="cuda") for _ in plans]
+    outs = [(torch.empty(plans[0].total_k, device="cuda"),
+             torch.empty(plans[0].total_k, dtype=torch.int32, device="cuda")) for _ in plans]
+    for t, g in enumerate(grads):
+        gd = torch.from_numpy(g).cuda()
+        for p, e, (v, i) in zip(plans, es, outs):
+            p.compress(gd, e, v, i)
+        torch.cuda.synchronize()
+        modes = [p.last_stats()["mode"].tolist() for p in plans]
+        log(f"[single/chain ratio={ratio}] step {t}: modes {modes}")
+        assert_bitwise(outs[0][1], outs[1][1].cpu().numpy(), f"step {t} idx")
+        assert_bitwise(outs[0][0], outs[1][0].cpu().numpy(), f"step {t} vals")
+        assert_bitwise(es[0], es[1].cpu().numpy(), f"step {t} residual")
+    for p in plans:
+        p.close()
 
 
 def test_warm_and_cold_plans_agree():

@@ -33,9 +33,14 @@ def _config(seed):
     return sizes, ks, flags, momentum, mask, codec, scale, rng
 
 
+@pytest.mark.parametrize("chain", [False, True], ids=["single", "chain"])
 @pytest.mark.parametrize("seed", range(20))
-def test_random_configuration(seed):
+def test_random_configuration(seed, chain):
+    """chain: the chain of kernels over candidate chunks even where one workgroup per segment
+    would select (most of these plans are small enough for that)."""
     sizes, ks, flags, momentum, mask, codec, scale, rng = _config(seed)
+    if chain:
+        flags |= gca.GC_DEBUG_CHAIN
     if codec == "int8":
         momentum, mask = None, False
     log(f"[random {seed}] {codec} sizes={sizes} k={ks} flags={flags:#x} momentum={momentum} "

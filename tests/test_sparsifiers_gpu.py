@@ -268,14 +268,19 @@ def test_randk_k_edges():
     run_randk(sizes, [1, 0, 8192, 1, 100000], _grads(sum(sizes), 2, 14), label="edges")
 
 
+@pytest.mark.parametrize("chain", [True, False], ids=["chain", "single"])
 @pytest.mark.parametrize("flag", [gca.GC_DEBUG_FORCE_FALLBACK, gca.GC_DEBUG_NO_ESTIMATE],
                          ids=["forced-full", "recapture"])
-def test_randk_fallbacks(flag):
+def test_randk_fallbacks(flag, chain):
+    """Both fallbacks, through the chain of kernels (re-capture or full path) and through the
+    one-workgroup-per-segment select (always the whole segment)."""
     sizes = [300001, 70003, 1001]
-    plan = run_randk(sizes, [300, 100, 10], _grads(sum(sizes), 2, 15), flags=flag,
-                     label=f"flag{flag:#x}")
+    plan = run_randk(sizes, [300, 100, 10], _grads(sum(sizes), 2, 15),
+                     flags=flag | (gca.GC_DEBUG_CHAIN if chain else 0),
+                     label=f"flag{flag:#x} chain={chain}")
     st = plan.last_stats()
-    want = gca.MODE_FULL if flag == gca.GC_DEBUG_FORCE_FALLBACK else gca.MODE_RECAPTURED
+    recap = flag != gca.GC_DEBUG_FORCE_FALLBACK and chain
+    want = gca.MODE_RECAPTURED if recap else gca.MODE_FULL
     assert st["mode"][0] == want, st["mode"]
 
 
