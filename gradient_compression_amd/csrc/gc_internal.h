@@ -87,8 +87,8 @@ constexpr int kFinishChunks = 1024;
 
 // Plans whose every segment is small, or has at most kSingleMaxElems elements and either
 // 4 k <= kChunk or at most kSingleWholeElems elements, are selected after the pass by one
-// workgroup per segment (k_single): its candidates, when complete and at most one chunk, in
-// LDS; otherwise a radix select over the whole segment streamed by that workgroup.
+// workgroup per segment (k_single): its candidates, when complete, selected and emitted in
+// index order; otherwise a radix select over the whole segment streamed by that workgroup.
 constexpr int64_t kSingleMaxElems = (int64_t)1 << 22;
 constexpr int64_t kSingleWholeElems = 65536;
 inline bool single_segment_ok(int64_t n, int64_t k) {

@@ -1437,21 +1437,21 @@ __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, const float* __res
 // pass by this kernel alone, one workgroup per segment, instead of the chain of kernels over
 // candidate chunks (whose launches, not bytes, set such a call's time):
 //  * a small segment: select_small, from its residual;
-//  * candidates complete (k <= count <= capacity) and at most one chunk: the runs placed in
-//    index order in LDS, the exact k-th key by a radix select over them in registers, and the
-//    chunk emitted in order;
-//  * candidates complete but more than one chunk: the radix select over the candidate buffer
-//    (in any order), then the segment's tiles emitted in order from its residual;
+//  * candidates complete (k <= count <= capacity): the tiles' runs placed in index order by a
+//    scan in LDS.  At most one chunk of them is placed in LDS in that order and selected in
+//    registers; more are selected from the candidate buffer (in any order) and gathered a
+//    chunk at a time in index order, each place's run found by bisection over the scan.
+//    Then emitted in order;
 //  * otherwise (a miss, an overflow, no estimate yet): a radix select streamed over the
 //    segment's residual (three passes), then its tiles emitted in order.
 // Then the segment's finish.
 constexpr int kSingleTiles = (int)((kSingleMaxElems + kTile - 1) / kTile);
 
 struct alignas(16) SingleLds {
-  float val[kChunk];             // the candidates in index order
+  float val[kChunk];                 // at most one chunk of candidates in index order
   int32_t idx[kChunk];
-  uint32_t rdst[kSingleTiles];   // per tile: the index-ordered place of its run
-  uint32_t roff[kSingleTiles];   // per tile: the run's offset in the candidate buffer
+  uint32_t rdst[kSingleTiles + 1];   // per tile: the index-ordered place of its run (then c)
+  uint32_t roff[kSingleTiles];       // per tile: the run's offset in the candidate buffer
   SmallLds sm;
 };
 
@@ -1520,7 +1520,7 @@ __global__ __launch_bounds__(kThreads) void k_single(DevPlan P, const float* __r
   const bool pend = seg_pending(P, s);
   uint32_t kth = 0, ties = 0, mx = 0, c_sel = 0, mode;
   uint32_t bad = 0;
-  if (!pend && c <= (uint32_t)kChunk) {   // uniform
+  if (!pend) {   // uniform
     mode = kModeCand;
     c_sel = c;
     // the runs' places in index order: an exclusive scan of the run sizes over the tiles
@@ -1537,71 +1537,135 @@ __global__ __launch_bounds__(kThreads) void k_single(DevPlan P, const float* __r
       }
       carry += tot;
     }
+    if (threadIdx.x == 0) L.rdst[nt] = carry;
     __syncthreads();
-    if (carry != c) bad = 1;
-    for (uint32_t j = threadIdx.x; j < c; j += kThreads) {
-      const float v = P.cand_val[cb + j];
-      const int32_t ix = P.cand_idx[cb + j];
-      const int lt = ix >= 0 && ix < n_s ? ix / kTile : -1;
-      uint32_t dst = (uint32_t)kChunk;
-      if (lt >= 0 && lt < nt && j >= L.roff[lt]) dst = L.rdst[lt] + (j - L.roff[lt]);
-      if (dst < c) {
-        L.val[dst] = v;
-        L.idx[dst] = ix;
-      } else {
-        bad = 1;
-      }
-    }
-    bad = block_max<kThreads>(bad, L.sm.tmp);   // (its barriers order the LDS writes above)
+    // the candidates at index-ordered places base + p of a tile-shaped block: each place's
+    // run found by bisection over the scan (rdst[t] <= place < rdst[t + 1]); a place outside
+    // the buffer's c entries, or an index outside its run's tile, marks the call bad
     f4 x[kSlots];
+    i4 ix[kSlots];
+    auto gather = [&](uint32_t base, int len) {
+      uint32_t b = 0;
 #pragma unroll
-    for (int v = 0; v < kSlots; ++v)
+      for (int v = 0; v < kSlots; ++v)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int p = pb + v * 256 + q;
-        x[v][q] = p < (int)c ? L.val[p] : 0.0f;
-      }
-    auto keys = [&](auto f) {
+        for (int q = 0; q < 4; ++q) {
+          const int p = pb + v * 256 + q;
+          float val = 0.0f;
+          int32_t id = 0;
+          if (p < len) {
+            const uint32_t pos = base + (uint32_t)p;
+            int lo = 0, hi = nt;
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (L.rdst[mid] <= pos) lo = mid; else hi = mid;
+            }
+            const uint32_t off = L.roff[lo] + (pos - L.rdst[lo]);
+            if (off < c) {
+              val = P.cand_val[cb + off];
+              id = P.cand_idx[cb + off];
+            }
+            if (off >= c || id < lo * kTile || id >= min((lo + 1) * kTile, n_s)) {
+              b = 1;
+              id = 0;
+            }
+          }
+          x[v][q] = val;
+          ix[v][q] = id;
+        }
+      return block_max<kThreads>(b, L.sm.tmp);
+    };
+    // the keys: one chunk from registers, more read from the candidate buffer in any order
+    auto reg_keys = [&](auto f) {
 #pragma unroll
       for (int v = 0; v < kSlots; ++v)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (pb + v * 256 + q < (int)c) f(mag_key(x[v][q]));
     };
-    const bool ok = !bad && radix_select(keys, k, L.sm, &kth, &ties);
-    if (want_mx) {   // uniform
-      keys([&](uint32_t key) { mx = max(mx, key); });
-      mx = block_max<kThreads>(mx, L.sm.tmp);
-    }
-    if (ok) {   // uniform
-      if (os.codes) os.scale = __uint_as_float(mx) / 127.0f;
-      uint32_t gt, eq;
-      count_block(x, (int)c, kth, L.sm.tmp, &gt, &eq);
-      auto slot_idx = [&](int v) {
-        i4 r;
+    auto buf_keys = [&](auto f) {
+      for (uint32_t base = 0; base < c; base += (uint32_t)kChunk) {
+        const int len = (int)min((uint32_t)kChunk, c - base);
+        f4 y[kSlots];
+        load_tile(P.cand_val + cb + base, len, y);
+#pragma unroll
+        for (int v = 0; v < kSlots; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (pb + v * 256 + q < len) f(mag_key(y[v][q]));
+      }
+    };
+    bad = carry != c;   // uniform
+    const bool one = c <= (uint32_t)kChunk;
+    if (!bad && one) {   // uniform: placed in LDS, each candidate at its run's place
+      for (uint32_t j = threadIdx.x; j < c; j += kThreads) {
+        const float v = P.cand_val[cb + j];
+        const int32_t id = P.cand_idx[cb + j];
+        const int lt = id >= 0 && id < n_s ? id / kTile : -1;
+        uint32_t dst = (uint32_t)kChunk;
+        if (lt >= 0 && lt < nt && j >= L.roff[lt]) dst = L.rdst[lt] + (j - L.roff[lt]);
+        if (dst < c) {
+          L.val[dst] = v;
+          L.idx[dst] = id;
+        } else {
+          bad = 1;
+        }
+      }
+      bad = block_max<kThreads>(bad, L.sm.tmp);   // (its barriers order the LDS writes above)
+#pragma unroll
+      for (int v = 0; v < kSlots; ++v)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int p = pb + v * 256 + q;
-          r[q] = p < (int)c ? L.idx[p] : 0;
+          x[v][q] = p < (int)c ? L.val[p] : 0.0f;
         }
-        return r;
-      };
-      emit_block(x, (int)c, slot_idx, kth, ties, 0u, eq, P.out_off[s], P.out_off[s + 1], s0,
-                 n_s, L.sm.w, os);
-      if (threadIdx.x == 0 && gt + min(eq, ties) != k) atomicOr(P.err, 2u);
+    }
+    bool ok = false;
+    if (!bad) {   // uniform
+      if (one) {
+        ok = radix_select(reg_keys, k, L.sm, &kth, &ties);
+        if (want_mx) reg_keys([&](uint32_t key) { mx = max(mx, key); });
+      } else {
+        ok = radix_select(buf_keys, k, L.sm, &kth, &ties);
+        if (want_mx) buf_keys([&](uint32_t key) { mx = max(mx, key); });
+      }
+      if (want_mx) mx = block_max<kThreads>(mx, L.sm.tmp);
+    }
+    if (ok) {   // uniform
+      if (os.codes) os.scale = __uint_as_float(mx) / 127.0f;
+      // emitted a chunk at a time in index order, the ties kept counted across chunks
+      uint32_t eqb = 0, kept = 0;
+      for (uint32_t base = 0; base < c; base += (uint32_t)kChunk) {
+        const int len = (int)min((uint32_t)kChunk, c - base);
+        if (!one && gather(base, len)) {   // uniform
+          bad = 1;
+          break;
+        }
+        auto slot_idx = [&](int v) {
+          if (!one) return ix[v];
+          i4 r;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int p = pb + v * 256 + q;
+            r[q] = p < (int)c ? L.idx[p] : 0;
+          }
+          return r;
+        };
+        uint32_t gt, eq;
+        count_block(x, len, kth, L.sm.tmp, &gt, &eq);
+        emit_block(x, len, slot_idx, kth, ties, eqb, eq, P.out_off[s] + kept, P.out_off[s + 1],
+                   s0, n_s, L.sm.w, os);
+        kept += gt + (eqb < ties ? min(eq, ties - eqb) : 0u);
+        eqb += eq;
+      }
+      if (threadIdx.x == 0 && !bad && kept != k) atomicOr(P.err, 2u);
     } else {
       bad = 1;
     }
   } else {
-    // the k-th key from the candidates when they are complete (more than one chunk: read
-    // from the candidate buffer, in any order), else from a radix select streamed over the
-    // segment's residual; then the segment's tiles emitted in order
-    mode = pend ? kModeFull : kModeCand;
-    c_sel = pend ? 0u : c;
-    const int64_t cb = P.cand_base[s];
-    auto cand_keys = [&](auto f) {
-      for (uint32_t j = threadIdx.x; j < c; j += kThreads) f(mag_key(P.cand_val[cb + j]));
-    };
+    // no complete candidates: a radix select streamed over the segment's residual, then its
+    // tiles emitted in order
+    mode = kModeFull;
     auto seg_keys = [&](auto f) {   // two tiles' loads in flight at a time
       for (int j = 0; j < nt; j += 2) {
         int64_t st0, st1 = 0;
@@ -1620,15 +1684,11 @@ __global__ __launch_bounds__(kThreads) void k_single(DevPlan P, const float* __r
           }
       }
     };
-    bool ok;
-    if (pend) {   // uniform
-      ok = radix_select(seg_keys, k, L.sm, &kth, &ties);
-      if (want_mx) seg_keys([&](uint32_t key) { mx = max(mx, key); });
-    } else {
-      ok = radix_select(cand_keys, k, L.sm, &kth, &ties);
-      if (want_mx) cand_keys([&](uint32_t key) { mx = max(mx, key); });   // the largest is one
+    const bool ok = radix_select(seg_keys, k, L.sm, &kth, &ties);
+    if (want_mx) {   // uniform
+      seg_keys([&](uint32_t key) { mx = max(mx, key); });
+      mx = block_max<kThreads>(mx, L.sm.tmp);
     }
-    if (want_mx) mx = block_max<kThreads>(mx, L.sm.tmp);
     if (ok) {   // uniform
       if (os.codes) os.scale = __uint_as_float(mx) / 127.0f;
       uint32_t eqb = 0, kept = 0;

@@ -142,3 +142,37 @@ def test_capture_all_segments_with_ties():
     for modes, cands in seen:
         assert modes == [gca.MODE_CANDIDATES] * 2
         assert cands == sizes
+
+
+@pytest.mark.parametrize("grid", [False, True], ids=["distinct", "ties"])
+@pytest.mark.parametrize("chain", [False, True], ids=["single", "chain"])
+def test_many_complete_candidates(chain, grid):
+    """One 2^20-element segment with k = 1000 (a plan the single-workgroup select takes): a
+    first call with 3000 magnitudes near 1 sets the threshold just below 1, then 30000
+    magnitudes in [0.996, 0.9999] (on a grid of 64 values with ties) are all captured, so
+    the complete candidates span four chunks of 8192, gathered and emitted a chunk at a
+    time in index order."""
+    rng = np.random.default_rng(606)
+    k = 1000
+    targets = [_cluster(rng, N, 3000)]
+    for _ in range(3):
+        a = rng.normal(0.0, 1e-3, N)
+        pos = rng.choice(N, 30000, replace=False)
+        if grid:
+            mag = 0.996 + rng.integers(0, 64, pos.size) * (0.0039 / 64)
+        else:
+            mag = rng.uniform(0.996, 0.9999, pos.size)
+        a[pos] = mag * rng.choice([-1.0, 1.0], pos.size)
+        targets.append(a)
+    seen = []
+    run_parity([N], _target_grads(targets), k=[k], label=f"many-cands chain={chain}",
+               flags=gca.GC_DEBUG_CHAIN if chain else 0,
+               check_stats=lambda t, st: seen.append((st["mode"].tolist(),
+                                                      st["candidates"].tolist(),
+                                                      st["ties"].tolist())))
+    log(f"modes/candidates/ties: {seen}")
+    for modes, cands, _ in seen[1:]:
+        assert modes == [gca.MODE_CANDIDATES]
+        assert cands[0] > 3 * 8192
+    if grid:
+        assert any(t[0] > 1 for _, _, t in seen[1:]), "the grid gave no ties at the k-th key"
