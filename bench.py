@@ -126,6 +126,10 @@ def run_step(plan, wl, codec, g, e, u, outs, t):
 
 
 def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
+    """(ms per step, ms per streaming pass, passes timed, first call ms): warmup steps (the
+    first one timed alone), then `steps` timed steps with no event between them, then as many
+    again with events around each pass and after each step for the pass time and the median
+    step (time_steps.median_ms)."""
     import torch
 
     def step(t):
@@ -142,17 +146,28 @@ def time_steps(plan, wl, gbufs, e, u, outs, steps, warmup, codec="topk"):
     torch.cuda.synchronize()
     cold_ms = cold[0].elapsed_time(cold[1]) if warmup > 0 else None
     plan.timing()                       # drop the warm-up events
+    # the timed steps: nothing between them but the steps (an event record per step costs a
+    # few microseconds of GPU time, which shows on the small shapes)
+    ends = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ends[0].record()
+    for t in range(warmup, warmup + steps):
+        step(t)
+    ends[1].record()
+    torch.cuda.synchronize()
+    total_ms = ends[0].elapsed_time(ends[1])
+    # the same number of steps again with events: the streaming pass's own time (the library's
+    # events on the stream it launches on, around each pass) and the median step (an event
+    # after every step)
     plan.set_timing(True)
-    # an event after every step: the total is first to last, the median comes from the gaps
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     marks[0].record()
-    for j, t in enumerate(range(warmup, warmup + steps)):
+    for j, t in enumerate(range(warmup + steps, warmup + 2 * steps)):
         step(t)
         marks[j + 1].record()
     torch.cuda.synchronize()
     plan.set_timing(False)
-    total_ms = marks[0].elapsed_time(marks[-1])
     per_step = [marks[j].elapsed_time(marks[j + 1]) for j in range(steps)]
     time_steps.median_ms = float(np.median(per_step)) if per_step else None
     k1_ms, launches = plan.timing()
