@@ -1,18 +1,21 @@
 // gc_topk.hip -- gfx950 kernels of the error-feedback Top-k path after the streaming pass, and
 // the threshold and Random-k sparsifiers that share its select and ordered emission.
 //
-// Top-k call (one stream, no host round trip; ten launches on a warm plan):
+// Top-k call (one stream, no host round trip; eight launches on a warm plan, two when every
+// segment is modest: the pass, then k_single):
 //   ef_capture  (gc_pass.hip) the streaming pass over g, e (and u): momentum, EF add, acc
 //               written into e, and every (acc, index) whose magnitude key reaches the
 //               segment's threshold captured, as one index-ordered run per tile [HBM-bound]
 //   list        per segment: its path (candidates complete, small, or pending), the places
-//               of its runs in index order, its candidate chunks listed
+//               of its runs in index order, its candidate chunks listed.  Its other
+//               workgroups run fb_hist:
 //   fb_hist     \   only for pending segments (too few or too many candidates, or no
 //   fb_capture   |  threshold yet); they end at once when none is pending: first-digit
 //   fb_hist2     |  histogram of e, then a re-capture at the exact bucket floor, or (a bucket
 //   fb_count    /   larger than the capacity) the radix select over the whole segment
 //   scatter     candidates into ascending index order; a histogram of their keys in bins
-//               that start at the capture threshold (two binades wide)
+//               that start at the capture threshold (two binades wide).  Its other
+//               workgroups run fb_count
 //   collect     per chunk: keys above the bin that holds the k-th key, and the keys inside
 //               it appended to the segment's near list
 //   finish      one workgroup per segment: the exact k-th key from the near list (in LDS),
@@ -221,26 +224,28 @@ __device__ void seg_runs(const DevPlan& P, int s, uint32_t c, uint32_t* s_tmp, u
 }
 
 // ------------------------------------------------------------------------------- fallback
-// The tiles of the listed pending segments for which pick(s) holds, in list order, dealt to
-// the workgroups of the launch in turn (picked tile j goes to workgroup j mod G).  For each
-// picked segment that has tiles here, seg_fn(s, owner) runs first (owner: this workgroup has
-// the segment's first tile, so exactly one workgroup is the owner), then tile_fn(s, t) for
-// each of its tiles here.  With no pending segment the kernel ends at once.  The picks, the
+// The tiles of the pending segments for which pick(s) holds, in list order, dealt to the w of
+// G workgroups in turn (picked tile j goes to workgroup j mod G).  The list is the call's
+// pending list, or with kFromPlan the plan's segments in ascending order for which
+// seg_pending holds (for a workgroup that runs beside the list's own kernel).  For each picked
+// segment that has tiles here, seg_fn(s, owner) runs first (owner: this workgroup has the
+// segment's first tile, so exactly one workgroup is the owner), then tile_fn(s, t) for each of
+// its tiles here.  With no pending segment the function returns at once.  The picks, the
 // segment loop and the tile loop are uniform over the workgroup, so both functions may
 // contain barriers.
-template <typename Pick, typename SegFn, typename TileFn>
-__device__ void for_pending_tiles(const DevPlan& P, Pick pick, SegFn seg_fn, TileFn tile_fn) {
+template <bool kFromPlan = false, typename Pick, typename SegFn, typename TileFn>
+__device__ void for_pending_tiles(const DevPlan& P, uint32_t w, uint32_t G, Pick pick,
+                                  SegFn seg_fn, TileFn tile_fn) {
   __shared__ uint32_t s_seg[kThreads];
   __shared__ uint32_t s_first[kThreads];
   __shared__ uint32_t s_tmp[kWaves];
-  const uint32_t np = *P.pend_count;
+  const uint32_t np = kFromPlan ? (uint32_t)P.n_seg : *P.pend_count;
   if (np == 0) return;   // uniform
-  const uint32_t G = gridDim.x, w = blockIdx.x;
   uint64_t rot = 0;   // picked tiles of the segments before this chunk of the list
   for (uint32_t c0 = 0; c0 < np; c0 += kThreads) {
     const uint32_t i = c0 + threadIdx.x;
-    const int s = i < np ? (int)P.pend_list[i] : -1;
-    const bool p = s >= 0 && pick(s);
+    const int s = i < np ? (kFromPlan ? (int)i : (int)P.pend_list[i]) : -1;
+    const bool p = s >= 0 && (!kFromPlan || seg_pending(P, s)) && pick(s);
     const uint32_t nt = p ? (uint32_t)(P.tile_base[s + 1] - P.tile_base[s]) : 0u;
     uint32_t m, tt;
     const uint32_t at = block_excl_scan<kThreads>(p ? 1u : 0u, s_tmp, &m);
@@ -263,11 +268,12 @@ __device__ void for_pending_tiles(const DevPlan& P, Pick pick, SegFn seg_fn, Til
   }
 }
 
-// First-digit histogram of e over the pending segments.
-__global__ __launch_bounds__(kThreads) void k_fb_hist(DevPlan P, const float* __restrict__ e) {
+// First-digit histogram of e over the pending segments, by workgroup w of G (run beside the
+// list kernel, so the pending segments are found from the plan's state).
+__device__ void fb_hist(const DevPlan& P, const float* __restrict__ e, uint32_t w, uint32_t G) {
   __shared__ uint32_t h[kHistBins];
-  for_pending_tiles(
-      P, [&](int) { return true; }, [&](int, bool) {},
+  for_pending_tiles<true>(
+      P, w, G, [&](int) { return true; }, [&](int, bool) {},
       [&](int s, int64_t t) { hist_tile(P, e, s, t, 0u, 0, h); });
 }
 
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_fb_capture(DevPlan P, const float*
   uint32_t d0 = 0, kk = 0;
   bool ok = false, fits = false;
   for_pending_tiles(
-      P, [&](int) { return true; },
+      P, blockIdx.x, gridDim.x, [&](int) { return true; },
       [&](int s, bool owner) {
         const uint32_t k = call_k(P, s);
         uint32_t above, bin;
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void k_fb_hist2(DevPlan P, const float* _
   uint32_t pfx = 0;
   bool ok = false;
   for_pending_tiles(
-      P, [&](int s) { return P.mode[s] == kModeFull; },
+      P, blockIdx.x, gridDim.x, [&](int s) { return P.mode[s] == kModeFull; },
       [&](int s, bool owner) {
         uint32_t d, above, bin;
         const uint32_t kk = P.kk1[s];
@@ -367,13 +373,14 @@ __device__ __forceinline__ void count_block(const f4 (&x)[kSlots], int len, uint
 }
 
 // Full path: the last digit gives the k-th key and the ties to take; then the keys above and
-// at it per tile, and each tile's largest key (the int8 scale).  The owner lists the segment.
-__global__ __launch_bounds__(kThreads) void k_fb_count(DevPlan P, const float* __restrict__ e) {
+// at it per tile, and each tile's largest key (the int8 scale), by workgroup w of G.  The
+// owner lists the segment.
+__device__ void fb_count(const DevPlan& P, const float* __restrict__ e, uint32_t w, uint32_t G) {
   __shared__ uint32_t s_tmp[kWaves], s_out[3];
   uint32_t kth = 0;
   bool ok = false;
   for_pending_tiles(
-      P, [&](int s) { return P.mode[s] == kModeFull; },
+      P, w, G, [&](int s) { return P.mode[s] == kModeFull; },
       [&](int s, bool owner) {
         uint32_t d, above, bin;
         const uint32_t kk = P.kk2[s];
@@ -740,14 +747,14 @@ __device__ __forceinline__ void lds_clear_hist(uint32_t* h) {
 }
 
 // Narrow r with histogram passes over a key source (each(f) calls f(key, position) for every
-// key, each thread a share) until it holds one key value or at most kListCap keys.  The first
+// key, each thread a share) until it holds one key value or at most cap keys.  The first
 // pass may use the window (see range_shift).  h (LDS) is zero on entry and on a true return.
 // Contains barriers.
 template <typename Each>
 __device__ bool narrow_range(Each each, KeyRange& r, bool window, uint32_t* h, uint32_t* s_tmp,
-                             uint32_t* s_out) {
+                             uint32_t* s_out, uint32_t cap = kListCap) {
   bool first = true;
-  for (int it = 0; r.hi > r.lo && r.cnt > (uint32_t)kListCap; ++it) {
+  for (int it = 0; r.hi > r.lo && r.cnt > cap; ++it) {
     if (it == 8) return false;
     const int sh = range_shift(r.lo, r.hi, window && first);
     const uint32_t lo = r.lo, hi = r.hi;
@@ -921,9 +928,16 @@ __device__ void scatter_chunk(const DevPlan& P, int64_t ch, bool listed, uint32_
   hist_flush(h, seg_hist(P, s, 1));
 }
 
-__global__ __launch_bounds__(kThreads, 8) void k_scatter(DevPlan P) {
+// Workgroups [0, n_chunk_blocks) scatter the active candidate chunks; the rest run the full
+// path's count (its segments are not among the chunks').
+__global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P, const float* __restrict__ e) {
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t s_m[kWaves];
+  const uint32_t nb = (uint32_t)P.n_chunk_blocks;
+  if (blockIdx.x >= nb) {   // uniform
+    fb_count(P, e, blockIdx.x - nb, gridDim.x - nb);
+    return;
+  }
   for_active_chunks(P, blockIdx.x, [&](int64_t ch, bool listed) {
     scatter_chunk(P, ch, listed, h, s_m);
     __syncthreads();   // the next chunk reuses h
@@ -1281,13 +1295,18 @@ __device__ __forceinline__ void select_small(const DevPlan& P, const float* e,
   *mx_out = mx;
 }
 
-// One workgroup per segment after the streaming pass: the segment's path this call.  k = 0:
-// nothing (its counters cleared).  Small: selected and emitted whole by the emission kernel
-// (it needs no fallback).  Candidates complete: the places of its runs, its chunks listed,
-// its capture floor.  Otherwise: listed as pending for the fallback kernels.
-__global__ __launch_bounds__(kThreads) void k_list(DevPlan P) {
+// First after the streaming pass.  Workgroups [0, n_seg): one per segment, the segment's path
+// this call.  k = 0: nothing (its counters cleared).  Small: selected and emitted whole by the
+// emission kernel (it needs no fallback).  Candidates complete: the places of its runs, its
+// chunks listed, its capture floor.  Otherwise: listed as pending for the fallback kernels.
+// The rest: the first-digit histogram of the pending segments.
+__global__ __launch_bounds__(kThreads) void k_list(DevPlan P, const float* __restrict__ e) {
   __shared__ uint32_t s_tmp[kWaves];
   __shared__ uint32_t s_act;
+  if (blockIdx.x >= (uint32_t)P.n_seg) {   // uniform
+    fb_hist(P, e, blockIdx.x - (uint32_t)P.n_seg, gridDim.x - (uint32_t)P.n_seg);
+    return;
+  }
   const int s = blockIdx.x;
   const uint32_t k = call_k(P, s);
   uint32_t mode = kModeCand;
@@ -1438,22 +1457,25 @@ __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, const float* __res
 // candidate chunks (whose launches, not bytes, set such a call's time):
 //  * a small segment: select_small, from its residual;
 //  * candidates complete (k <= count <= capacity): the tiles' runs placed in index order by a
-//    scan in LDS.  At most one chunk of them is placed in LDS in that order and selected in
-//    registers; more are selected from the candidate buffer (in any order) and gathered a
-//    chunk at a time in index order, each place's run found by bisection over the scan.
-//    Then emitted in order;
+//    scan in LDS; the exact k-th key by window_select over the candidates (held in registers
+//    when they fit one chunk, placed there in index order through LDS; else read from the
+//    candidate buffer in any order); then emitted in order, more than one chunk gathered a
+//    chunk at a time, each place's run found by bisection over the scan;
 //  * otherwise (a miss, an overflow, no estimate yet): a radix select streamed over the
 //    segment's residual (three passes), then its tiles emitted in order.
 // Then the segment's finish.
 constexpr int kSingleTiles = (int)((kSingleMaxElems + kTile - 1) / kTile);
 
 struct alignas(16) SingleLds {
-  float val[kChunk];                 // at most one chunk of candidates in index order
-  int32_t idx[kChunk];
+  float val[kChunk];                 // at most one chunk of candidates in index order (then
+  int32_t idx[kChunk];               // val holds the select's list of keys)
   uint32_t rdst[kSingleTiles + 1];   // per tile: the index-ordered place of its run (then c)
   uint32_t roff[kSingleTiles];       // per tile: the run's offset in the candidate buffer
+  uint32_t n_list;
   SmallLds sm;
 };
+// Keys the single workgroup's select ranks in its list (held in the value slots).
+constexpr uint32_t kSingleList = (uint32_t)kChunk < kListCap ? (uint32_t)kChunk : kListCap;
 
 // The k-th largest key of a key source by a radix select, digits of 11, 11 and 9 bits, each
 // LDS histogram (zero on entry and on return) cleared by its digit search; *ties: the entries
@@ -1477,6 +1499,62 @@ __device__ __forceinline__ bool radix_select(Each each, uint32_t k, SmallLds& L,
   }
   *kth = prefix;
   *ties = kk;
+  return true;
+}
+
+// The exact k-th key (and the ties to take) of a segment's complete candidates, every key at
+// or above the capture floor lo, as the chain selects them but in one workgroup: the windowed
+// histogram of the keys (bins of 2^13 keys from lo over two binades, the top bin open; plain
+// bins over [lo, top] for Random-k keys) picks the bin that holds the k-th key; the bin's keys
+// are narrowed by further histogram passes while more than kSingleList, then gathered into
+// the LDS list lkey and ranked there.  each(f) calls f(key) for every candidate, each thread a
+// share; *mx: this thread's largest key.  L.sm.h is zero on entry and on a true return.
+// Contains barriers.
+template <typename Each>
+__device__ __forceinline__ bool window_select(Each each, uint32_t lo, bool window, uint32_t k,
+                                              uint32_t c, SingleLds& L, uint32_t* lkey,
+                                              uint32_t* kth, uint32_t* ties, uint32_t* mx) {
+  uint32_t* h = L.sm.h;
+  const int sh = range_shift(lo, 0x7FFFFFFFu, window);
+  uint32_t m = 0;
+  each([&](uint32_t key) {
+    m = max(m, key);
+    if (key >= lo) atomicAdd(&h[range_bin(key, lo, sh)], 1u);
+  });
+  *mx = m;
+  if (threadIdx.x == 0) L.n_list = 0;
+  __syncthreads();
+  KeyRange r{lo, 0x7FFFFFFFu, k, c};
+  if (!range_step<true>(h, r, sh, L.sm.tmp, L.sm.out)) return false;
+  if (r.hi > r.lo) {
+    auto each_at = [&](auto f) { each([&](uint32_t key) { f(key, 0u); }); };
+    if (!narrow_range(each_at, r, false, h, L.sm.tmp, L.sm.out, kSingleList)) return false;
+  }
+  if (r.hi > r.lo) {   // uniform
+    // the keys inside r into the list: one slot reservation per wave and step
+    uint32_t bad = 0;
+    each([&](uint32_t key) {
+      const bool in = key >= r.lo && key <= r.hi;
+      const uint64_t b = __ballot(in);
+      if (b == 0) return;
+      const int lead = __ffsll((unsigned long long)b) - 1;
+      uint32_t base = 0;
+      if (lane_id() == lead) base = atomicAdd(&L.n_list, (uint32_t)__popcll(b));
+      base = __shfl(base, lead, 64);
+      if (in) {
+        const uint32_t p = base + lanes_below(b);
+        if (p < kSingleList) lkey[p] = key;
+        else bad = 1;
+      }
+    });
+    if (block_max<kThreads>(bad, L.sm.tmp)) return false;   // (its barriers order the list)
+    const uint32_t n = L.n_list;
+    if (!(n <= kRankMax ? rank_select(lkey, n, r, L.sm.out)
+                        : list_select(lkey, n, r, h, L.sm.tmp, L.sm.out)))
+      return false;
+  }
+  *kth = r.lo;
+  *ties = r.kk;
   return true;
 }
 
@@ -1622,13 +1700,10 @@ __global__ __launch_bounds__(kThreads) void k_single(DevPlan P, const float* __r
     }
     bool ok = false;
     if (!bad) {   // uniform
-      if (one) {
-        ok = radix_select(reg_keys, k, L.sm, &kth, &ties);
-        if (want_mx) reg_keys([&](uint32_t key) { mx = max(mx, key); });
-      } else {
-        ok = radix_select(buf_keys, k, L.sm, &kth, &ties);
-        if (want_mx) buf_keys([&](uint32_t key) { mx = max(mx, key); });
-      }
+      const bool window = P.keys == kKeysMagnitude && thr_used > 0;
+      uint32_t* lkey = reinterpret_cast<uint32_t*>(L.val);
+      ok = one ? window_select(reg_keys, thr_used, window, k, c, L, lkey, &kth, &ties, &mx)
+               : window_select(buf_keys, thr_used, window, k, c, L, lkey, &kth, &ties, &mx);
       if (want_mx) mx = block_max<kThreads>(mx, L.sm.tmp);
     }
     if (ok) {   // uniform
@@ -1981,15 +2056,11 @@ void select_emit(const DevPlan& P, const float* e, const EmitOut& o, hipStream_t
   }
   const int64_t nt = P.n_tiles > 0 ? P.n_tiles : 1;
   const unsigned fb = (unsigned)(nt < kFallbackBlocks ? nt : kFallbackBlocks);
-  k_list<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P);
-  k_fb_hist<<<fb, kThreads, 0, st>>>(P, e);
+  k_list<<<(unsigned)P.n_seg + fb, kThreads, 0, st>>>(P, e);
   k_fb_capture<<<fb, kThreads, 0, st>>>(P, e);
   k_fb_hist2<<<fb, kThreads, 0, st>>>(P, e);
-  k_fb_count<<<fb, kThreads, 0, st>>>(P, e);
-  if (P.n_chunk_blocks > 0) {
-    k_scatter<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
-    k_collect<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
-  }
+  k_scatter<<<(unsigned)P.n_chunk_blocks + fb, kThreads, 0, st>>>(P, e);
+  if (P.n_chunk_blocks > 0) k_collect<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
   k_finish<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P, e, o);
   const unsigned nfull = (unsigned)(nt < kFullBlocks ? nt : kFullBlocks);
   k_emit<<<(unsigned)(P.n_seg + P.n_chunk_blocks) + nfull, kThreads, 0, st>>>(P, e, o);

@@ -84,8 +84,35 @@ def test_near_list_ties():
     assert any(t > 1 for _, ties in seen for t in ties), "the grid gave no ties at the k-th key"
 
 
+@pytest.mark.parametrize("grid", [False, True], ids=["distinct", "ties"])
+@pytest.mark.parametrize("chain", [False, True], ids=["single", "chain"])
+def test_near_list_classes_both_paths(chain, grid):
+    """Segments of 2^20 with k = 100, 1500 and 2000 (a plan the single-workgroup select
+    takes, or with GC_DEBUG_CHAIN the chain): near lists of about 200 keys (ranked), 3000
+    (LDS passes) and 40000 (narrowed first; on the single path the candidates span five
+    chunks and are read from the candidate buffer), optionally with the cluster on a grid of
+    256 magnitudes so that hundreds of entries tie at the k-th key."""
+    rng = np.random.default_rng(707)
+    ms, ks = [200, 3000, 40000], [100, 1500, 2000]
+    targets = [np.concatenate([_cluster(rng, N, m, grid=grid) for m in ms]) for _ in range(3)]
+    seen = []
+    run_parity([N] * 3, _target_grads(targets), k=ks,
+               label=f"near-classes chain={chain} grid={grid}",
+               flags=gca.GC_DEBUG_CHAIN if chain else 0,
+               check_stats=lambda t, st: seen.append((st["mode"].tolist(),
+                                                      st["candidates"].tolist(),
+                                                      st["ties"].tolist())))
+    log(f"modes/candidates/ties: {seen}")
+    for modes, cands, _ in seen[1:]:
+        assert modes == [gca.MODE_CANDIDATES] * 3
+        assert all(c >= m for c, m in zip(cands, ms))
+    if grid:
+        assert any(t > 1 for _, _, ties in seen for t in ties), "no ties at the k-th key"
+
+
+@pytest.mark.parametrize("chain", [False, True], ids=["single", "chain"])
 @pytest.mark.parametrize("m,k", [(200, 120), (600, 300)], ids=["ranked", "lds-passes"])
-def test_kth_key_in_the_open_top_bin(m, k):
+def test_kth_key_in_the_open_top_bin(m, k, chain):
     """The k-th key far above the capture floor: a call with m magnitudes near 1 sets the
     next floor near 1, then the same positions jump to 4..4000 (log-uniform, distinct), all of
     them in the histogram's top bin, which is open upwards.  The near list is then every
@@ -102,7 +129,8 @@ def test_kth_key_in_the_open_top_bin(m, k):
                 [-1.0, 1.0], m)
         targets.append(a)
     seen = []
-    run_parity([N], _target_grads(targets), k=[k], label=f"top-bin m={m}",
+    run_parity([N], _target_grads(targets), k=[k], label=f"top-bin m={m} chain={chain}",
+               flags=gca.GC_DEBUG_CHAIN if chain else 0,
                check_stats=lambda t, st: seen.append((st["mode"].tolist(),
                                                       st["candidates"].tolist())))
     log(f"modes/candidates: {seen}")
