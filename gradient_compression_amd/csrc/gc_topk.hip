@@ -1192,19 +1192,88 @@ __device__ __forceinline__ void block_sums(uint32_t (&v)[N], uint32_t* scratch) 
 }
 
 // LDS of a small segment's select (in the emission kernel).
-struct SmallLds {
+// The exact k-th key (and the ties to take) of a key source whose k-th key lies in [lo, hi]:
+// a histogram of the keys in [lo, hi] (bins of 2^sh keys from lo; with `window`, magnitudes
+// above a capture floor, bins of 2^13 keys over two binades, the top bin open) picks the bin
+// that holds the k-th key; the bin's keys are narrowed by further histogram passes while more
+// than L.cap, then gathered into the LDS list L.lkey and ranked there (by counting for at
+// most kRankMax keys).  each(f) calls f(key) for every key of the source, each thread a
+// share; *mx (if given): this thread's largest key.  False when [lo, hi] holds fewer than k
+// keys (or on a list past its capacity).  L.h is zero on entry and on a true return.
+// Contains barriers.
+struct NearLds {
+  uint32_t* h;        // kHistBins
+  uint32_t* tmp;      // kWaves
+  uint32_t* out;      // 3
+  uint32_t* n_list;
+  uint32_t* lkey;     // cap keys, 16-byte aligned
+  uint32_t cap;
+};
+
+template <typename Each>
+__device__ __forceinline__ bool near_select(Each each, uint32_t lo, uint32_t hi, bool window,
+                                            uint32_t k, const NearLds& L, uint32_t* kth,
+                                            uint32_t* ties, uint32_t* mx = nullptr) {
+  const int sh = range_shift(lo, hi, window);
+  uint32_t m = 0;
+  each([&](uint32_t key) {
+    m = max(m, key);
+    if (key >= lo && key <= hi) atomicAdd(&L.h[range_bin(key, lo, sh)], 1u);
+  });
+  if (mx) *mx = m;
+  if (threadIdx.x == 0) *L.n_list = 0;
+  __syncthreads();
+  KeyRange r{lo, hi, k, 0u};
+  if (!range_step<true>(L.h, r, sh, L.tmp, L.out)) return false;
+  if (r.hi > r.lo) {
+    auto each_at = [&](auto f) { each([&](uint32_t key) { f(key, 0u); }); };
+    if (!narrow_range(each_at, r, false, L.h, L.tmp, L.out, L.cap)) return false;
+  }
+  if (r.hi > r.lo) {   // uniform
+    // the keys inside r into the list: one slot reservation per wave and step
+    uint32_t bad = 0;
+    each([&](uint32_t key) {
+      const bool in = key >= r.lo && key <= r.hi;
+      const uint64_t b = __ballot(in);
+      if (b == 0) return;
+      const int lead = __ffsll((unsigned long long)b) - 1;
+      uint32_t base = 0;
+      if (lane_id() == lead) base = atomicAdd(L.n_list, (uint32_t)__popcll(b));
+      base = __shfl(base, lead, 64);
+      if (in) {
+        const uint32_t p = base + lanes_below(b);
+        if (p < L.cap) L.lkey[p] = key;
+        else bad = 1;
+      }
+    });
+    if (block_max<kThreads>(bad, L.tmp)) return false;   // (its barriers order the list)
+    const uint32_t n = *L.n_list;
+    if (!(n <= kRankMax ? rank_select(L.lkey, n, r, L.out)
+                        : list_select(L.lkey, n, r, L.h, L.tmp, L.out)))
+      return false;
+  }
+  *kth = r.lo;
+  *ties = r.kk;
+  return true;
+}
+
+struct alignas(16) SmallLds {
   uint32_t h[kHistBins];
+  uint32_t lkey[kRankMax];   // the select's near list
   uint32_t sums[kSmallTiles * kWaves];
   uint32_t tmp[kWaves];
   uint32_t out[3];
   uint32_t w[kWaves];
+  uint32_t n_list;
 };
 
 // Small segment (at most kSmallTiles tiles): selected whole from its residual (or Random-k
-// keys), every key loaded once into registers: the exact k-th key by a radix select over the
-// registers (digits of 11, 11 and 9 bits, as the full path), then the segment emitted in index
-// order, tile by tile.  Returns kth, ties and the largest key (when an int8 scale needs it).
-// Contains barriers.
+// keys), every key loaded once into registers.  The exact k-th key by near_select over the
+// eight binades below the segment's largest key (2048 bins of 2^15 keys: a radix digit of 11
+// bits would pile the bulk of the keys onto a few bins, serialising the LDS atomics), or, when
+// fewer than k keys lie there, by a radix select over the registers (digits of 11, 11 and 9
+// bits, as the full path); then the segment emitted in index order, tile by tile.  Returns
+// kth, ties and the largest key.  Contains barriers.
 __device__ __forceinline__ void select_small(const DevPlan& P, const float* e,
                                              const EmitOut& o, int s, uint32_t k, SmallLds& L,
                                              uint32_t* kth_out, uint32_t* ties_out,
@@ -1228,32 +1297,41 @@ __device__ __forceinline__ void select_small(const DevPlan& P, const float* e,
     }
   }
   for (int i = threadIdx.x; i < kHistBins; i += kThreads) L.h[i] = 0;
-  __syncthreads();
-  uint32_t prefix = 0, kk = k;
-  bool ok = true;
-  for (int pass = 0; pass < 3; ++pass) {
-#pragma unroll
-    for (int j = 0; j < kSmallTiles; ++j) hist_add(L.h, x[j], len[j], prefix, pass);
-    __syncthreads();
-    uint32_t d, above, bin;
-    if (!find_digit<true>(L.h, kk, L.tmp, L.out, &d, &above, &bin)) {   // uniform
-      ok = false;
-      break;
-    }
-    prefix |= d << digit_shift(pass);
-    kk -= above;
-  }
-  const uint32_t kth = prefix, ties = kk;
-  uint32_t mx = 0;
-  if (P.scales || o.codes) {   // uniform
+  auto keys = [&](auto f) {
 #pragma unroll
     for (int j = 0; j < kSmallTiles; ++j)
 #pragma unroll
       for (int v = 0; v < kSlots; ++v)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (pb + v * 256 + c < len[j]) mx = max(mx, mag_key(x[j][v][c]));
-    mx = block_max<kThreads>(mx, L.tmp);
+          if (pb + v * 256 + c < len[j]) f(mag_key(x[j][v][c]));
+  };
+  uint32_t mx = 0;
+  keys([&](uint32_t key) { mx = max(mx, key); });
+  mx = block_max<kThreads>(mx, L.tmp);   // (its barriers order the histogram's clearing)
+  constexpr uint32_t kSpan = (1u << 26) - 1;   // eight binades of keys
+  const NearLds nl{L.h, L.tmp, L.out, &L.n_list, L.lkey, kRankMax};
+  uint32_t kth = 0, ties = 0;
+  bool ok = k > 0 && near_select(keys, mx > kSpan ? mx - kSpan : 0u, mx, false, k, nl, &kth,
+                                 &ties);
+  if (!ok) {   // uniform: the k-th key lies further down
+    lds_clear_hist(L.h);
+    uint32_t prefix = 0, kk = k;
+    ok = true;
+    for (int pass = 0; pass < 3; ++pass) {
+#pragma unroll
+      for (int j = 0; j < kSmallTiles; ++j) hist_add(L.h, x[j], len[j], prefix, pass);
+      __syncthreads();
+      uint32_t d, above, bin;
+      if (!find_digit<true>(L.h, kk, L.tmp, L.out, &d, &above, &bin)) {   // uniform
+        ok = false;
+        break;
+      }
+      prefix |= d << digit_shift(pass);
+      kk -= above;
+    }
+    kth = prefix;
+    ties = kk;
   }
   if (ok) {
     EmitOut os = o;
@@ -1457,7 +1535,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(DevPlan P, const float* __res
 // candidate chunks (whose launches, not bytes, set such a call's time):
 //  * a small segment: select_small, from its residual;
 //  * candidates complete (k <= count <= capacity): the tiles' runs placed in index order by a
-//    scan in LDS; the exact k-th key by window_select over the candidates (held in registers
+//    scan in LDS; the exact k-th key by near_select over the candidates (held in registers
 //    when they fit one chunk, placed there in index order through LDS; else read from the
 //    candidate buffer in any order); then emitted in order, more than one chunk gathered a
 //    chunk at a time, each place's run found by bisection over the scan;
@@ -1499,62 +1577,6 @@ __device__ __forceinline__ bool radix_select(Each each, uint32_t k, SmallLds& L,
   }
   *kth = prefix;
   *ties = kk;
-  return true;
-}
-
-// The exact k-th key (and the ties to take) of a segment's complete candidates, every key at
-// or above the capture floor lo, as the chain selects them but in one workgroup: the windowed
-// histogram of the keys (bins of 2^13 keys from lo over two binades, the top bin open; plain
-// bins over [lo, top] for Random-k keys) picks the bin that holds the k-th key; the bin's keys
-// are narrowed by further histogram passes while more than kSingleList, then gathered into
-// the LDS list lkey and ranked there.  each(f) calls f(key) for every candidate, each thread a
-// share; *mx: this thread's largest key.  L.sm.h is zero on entry and on a true return.
-// Contains barriers.
-template <typename Each>
-__device__ __forceinline__ bool window_select(Each each, uint32_t lo, bool window, uint32_t k,
-                                              uint32_t c, SingleLds& L, uint32_t* lkey,
-                                              uint32_t* kth, uint32_t* ties, uint32_t* mx) {
-  uint32_t* h = L.sm.h;
-  const int sh = range_shift(lo, 0x7FFFFFFFu, window);
-  uint32_t m = 0;
-  each([&](uint32_t key) {
-    m = max(m, key);
-    if (key >= lo) atomicAdd(&h[range_bin(key, lo, sh)], 1u);
-  });
-  *mx = m;
-  if (threadIdx.x == 0) L.n_list = 0;
-  __syncthreads();
-  KeyRange r{lo, 0x7FFFFFFFu, k, c};
-  if (!range_step<true>(h, r, sh, L.sm.tmp, L.sm.out)) return false;
-  if (r.hi > r.lo) {
-    auto each_at = [&](auto f) { each([&](uint32_t key) { f(key, 0u); }); };
-    if (!narrow_range(each_at, r, false, h, L.sm.tmp, L.sm.out, kSingleList)) return false;
-  }
-  if (r.hi > r.lo) {   // uniform
-    // the keys inside r into the list: one slot reservation per wave and step
-    uint32_t bad = 0;
-    each([&](uint32_t key) {
-      const bool in = key >= r.lo && key <= r.hi;
-      const uint64_t b = __ballot(in);
-      if (b == 0) return;
-      const int lead = __ffsll((unsigned long long)b) - 1;
-      uint32_t base = 0;
-      if (lane_id() == lead) base = atomicAdd(&L.n_list, (uint32_t)__popcll(b));
-      base = __shfl(base, lead, 64);
-      if (in) {
-        const uint32_t p = base + lanes_below(b);
-        if (p < kSingleList) lkey[p] = key;
-        else bad = 1;
-      }
-    });
-    if (block_max<kThreads>(bad, L.sm.tmp)) return false;   // (its barriers order the list)
-    const uint32_t n = L.n_list;
-    if (!(n <= kRankMax ? rank_select(lkey, n, r, L.sm.out)
-                        : list_select(lkey, n, r, h, L.sm.tmp, L.sm.out)))
-      return false;
-  }
-  *kth = r.lo;
-  *ties = r.kk;
   return true;
 }
 
@@ -1700,10 +1722,12 @@ __global__ __launch_bounds__(kThreads) void k_single(DevPlan P, const float* __r
     }
     bool ok = false;
     if (!bad) {   // uniform
+      // the candidates' windowed histogram from the capture floor, as the chain's scatter
       const bool window = P.keys == kKeysMagnitude && thr_used > 0;
-      uint32_t* lkey = reinterpret_cast<uint32_t*>(L.val);
-      ok = one ? window_select(reg_keys, thr_used, window, k, c, L, lkey, &kth, &ties, &mx)
-               : window_select(buf_keys, thr_used, window, k, c, L, lkey, &kth, &ties, &mx);
+      const NearLds nl{L.sm.h, L.sm.tmp, L.sm.out, &L.n_list,
+                       reinterpret_cast<uint32_t*>(L.val), kSingleList};
+      ok = one ? near_select(reg_keys, thr_used, 0x7FFFFFFFu, window, k, nl, &kth, &ties, &mx)
+               : near_select(buf_keys, thr_used, 0x7FFFFFFFu, window, k, nl, &kth, &ties, &mx);
       if (want_mx) mx = block_max<kThreads>(mx, L.sm.tmp);
     }
     if (ok) {   // uniform
