@@ -1,7 +1,7 @@
 // gc_topk.hip -- gfx950 kernels of the error-feedback Top-k path after the streaming pass, and
 // the threshold and Random-k sparsifiers that share its select and ordered emission.
 //
-// Top-k call (one stream, no host round trip; eight launches on a warm plan, two when every
+// Top-k call (one stream, no host round trip; nine launches on a warm plan, two when every
 // segment is modest: the pass, then k_single):
 //   ef_capture  (gc_pass.hip) the streaming pass over g, e (and u): momentum, EF add, acc
 //               written into e, and every (acc, index) whose magnitude key reaches the
@@ -14,8 +14,7 @@
 //   fb_hist2     |  histogram of e, then a re-capture at the exact bucket floor, or (a bucket
 //   fb_count    /   larger than the capacity) the radix select over the whole segment
 //   scatter     candidates into ascending index order; a histogram of their keys in bins
-//               that start at the capture threshold (two binades wide).  Its other
-//               workgroups run fb_count
+//               that start at the capture threshold (two binades wide)
 //   collect     per chunk: keys above the bin that holds the k-th key, and the keys inside
 //               it appended to the segment's near list
 //   finish      one workgroup per segment: the exact k-th key from the near list (in LDS),
@@ -373,14 +372,14 @@ __device__ __forceinline__ void count_block(const f4 (&x)[kSlots], int len, uint
 }
 
 // Full path: the last digit gives the k-th key and the ties to take; then the keys above and
-// at it per tile, and each tile's largest key (the int8 scale), by workgroup w of G.  The
-// owner lists the segment.
-__device__ void fb_count(const DevPlan& P, const float* __restrict__ e, uint32_t w, uint32_t G) {
+// at it per tile, and each tile's largest key (the int8 scale).  The owner lists the segment.
+// (Its registers would halve the scatter's occupancy were it run in that launch.)
+__global__ __launch_bounds__(kThreads) void k_fb_count(DevPlan P, const float* __restrict__ e) {
   __shared__ uint32_t s_tmp[kWaves], s_out[3];
   uint32_t kth = 0;
   bool ok = false;
   for_pending_tiles(
-      P, w, G, [&](int s) { return P.mode[s] == kModeFull; },
+      P, blockIdx.x, gridDim.x, [&](int s) { return P.mode[s] == kModeFull; },
       [&](int s, bool owner) {
         uint32_t d, above, bin;
         const uint32_t kk = P.kk2[s];
@@ -928,16 +927,9 @@ __device__ void scatter_chunk(const DevPlan& P, int64_t ch, bool listed, uint32_
   hist_flush(h, seg_hist(P, s, 1));
 }
 
-// Workgroups [0, n_chunk_blocks) scatter the active candidate chunks; the rest run the full
-// path's count (its segments are not among the chunks').
-__global__ __launch_bounds__(kThreads) void k_scatter(DevPlan P, const float* __restrict__ e) {
+__global__ __launch_bounds__(kThreads, 8) void k_scatter(DevPlan P) {
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t s_m[kWaves];
-  const uint32_t nb = (uint32_t)P.n_chunk_blocks;
-  if (blockIdx.x >= nb) {   // uniform
-    fb_count(P, e, blockIdx.x - nb, gridDim.x - nb);
-    return;
-  }
   for_active_chunks(P, blockIdx.x, [&](int64_t ch, bool listed) {
     scatter_chunk(P, ch, listed, h, s_m);
     __syncthreads();   // the next chunk reuses h
@@ -2083,8 +2075,11 @@ void select_emit(const DevPlan& P, const float* e, const EmitOut& o, hipStream_t
   k_list<<<(unsigned)P.n_seg + fb, kThreads, 0, st>>>(P, e);
   k_fb_capture<<<fb, kThreads, 0, st>>>(P, e);
   k_fb_hist2<<<fb, kThreads, 0, st>>>(P, e);
-  k_scatter<<<(unsigned)P.n_chunk_blocks + fb, kThreads, 0, st>>>(P, e);
-  if (P.n_chunk_blocks > 0) k_collect<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
+  k_fb_count<<<fb, kThreads, 0, st>>>(P, e);
+  if (P.n_chunk_blocks > 0) {
+    k_scatter<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
+    k_collect<<<(unsigned)P.n_chunk_blocks, kThreads, 0, st>>>(P);
+  }
   k_finish<<<(unsigned)P.n_seg, kThreads, 0, st>>>(P, e, o);
   const unsigned nfull = (unsigned)(nt < kFullBlocks ? nt : kFullBlocks);
   k_emit<<<(unsigned)(P.n_seg + P.n_chunk_blocks) + nfull, kThreads, 0, st>>>(P, e, o);
