@@ -34,7 +34,7 @@ def _config(seed):
 
 
 @pytest.mark.parametrize("chain", [False, True], ids=["single", "chain"])
-@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("seed", range(100))
 def test_random_configuration(seed, chain):
     """chain: the chain of kernels over candidate chunks even where one workgroup per segment
     would select (most of these plans are small enough for that)."""
