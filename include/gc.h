@@ -96,7 +96,11 @@ int gc_layout(const int64_t* seg_off, int32_t n_seg, const int64_t* k, const dou
  *             GC_DEBUG_CHAIN, or 0.
  *   out     : receives the plan.
  * The plan keeps a per-segment threshold estimate between calls; it only decides how much
- * work a call does, never what it returns.  Its single device allocation holds about 25 KB
+ * work a call does, never what it returns.  Where every segment is modest (at most 4M
+ * elements with 4 k[s] <= 8192, or at most 65536 elements, at the default tile geometry) a
+ * call selects with one workgroup per segment after its streaming pass; otherwise with a
+ * chain of kernels over the candidate chunks; the results are the same.  Its single device
+ * allocation holds about 25 KB
  * per segment (three 2048-bin histograms and per-segment state), about 60 B per 8192-element
  * tile, and 16 B per candidate slot (min(n_s, max(16 k_s, 65536)) slots per segment, none for
  * segments of at most 16384 elements, which are selected whole): about 1.8 GB for a
