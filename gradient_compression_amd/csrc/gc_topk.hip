@@ -1900,7 +1900,9 @@ static_assert(kRkSlots % 8 == 0, "a tile must hold whole words of eight 256-elem
 
 // The keys of one tile: per-slot flags (key >= thr) into pk, one nibble per slot, the first
 // kRkStage flagged (key, tile offset) pairs into the wave's LDS rows in index order; returns
-// the tile's flagged count (wave-uniform).  kWhole: the tile holds kTile elements.
+// the tile's flagged count (wave-uniform).  kWhole: the tile holds kTile elements.  A slot
+// where no lane holds two flagged keys (nearly all of them at the usual densities) is ranked
+// by one prefix count over the lanes; otherwise by one per element position.
 template <bool kAligned, bool kWhole>
 __device__ __forceinline__ uint32_t rk_draw(const DevPlan& P, int64_t start, int len,
                                             uint32_t thr, int lane, uint32_t* sk, int32_t* si,
@@ -1926,8 +1928,19 @@ __device__ __forceinline__ uint32_t rk_draw(const DevPlan& P, int64_t start, int
 #pragma unroll
       for (int jj = 0; jj < kRkGroup; ++jj) {
         const uint32_t nib = (gw >> (4 * jj)) & 0xFu;
-        if (!__ballot(nib != 0)) continue;   // uniform
+        const uint64_t any = __ballot(nib != 0);
+        if (!any) continue;   // uniform
         const int p0 = (wi * 8 + j0 + jj) * 256 + lane * 4;
+        if (!__ballot((nib & (nib - 1u)) != 0)) {   // uniform: at most one flagged key a lane
+          const uint32_t r = cnt + lanes_below(any);
+          cnt += __popcll(any);
+          if (nib && r < (uint32_t)kRkStage) {   // the lane's one flagged key, chosen by its bit
+            sk[r] = (nib & 1u) ? k[jj][0] : (nib & 2u) ? k[jj][1] : (nib & 4u) ? k[jj][2]
+                                                                               : k[jj][3];
+            si[r] = p0 + (int)__builtin_ctz(nib);
+          }
+          continue;
+        }
         const uint64_t m0 = __ballot(nib & 1u), m1 = __ballot(nib & 2u);
         const uint64_t m2 = __ballot(nib & 4u), m3 = __ballot(nib & 8u);
         uint32_t r = cnt + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) +
