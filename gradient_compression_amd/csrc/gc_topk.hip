@@ -1615,8 +1615,22 @@ __global__ __launch_bounds__(kThreads) void k_single(DevPlan P, const float* __r
   if (!pend) {   // uniform
     mode = kModeCand;
     c_sel = c;
-    // the runs' places in index order: an exclusive scan of the run sizes over the tiles
     const int64_t cb = P.cand_base[s];
+    const bool one = c <= (uint32_t)kChunk;
+    // one chunk of candidates: their loads issued before the scan below (they do not wait on
+    // it), placed after it
+    constexpr int kPer = kChunk / kThreads;
+    float cv[kPer];
+    int32_t ci[kPer];
+    if (one) {   // uniform
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const uint32_t j = threadIdx.x + (uint32_t)(q * kThreads);
+        cv[q] = j < c ? P.cand_val[cb + j] : 0.0f;
+        ci[q] = j < c ? P.cand_idx[cb + j] : -1;
+      }
+    }
+    // the runs' places in index order: an exclusive scan of the run sizes over the tiles
     uint32_t carry = 0;
     for (int tb = 0; tb < nt; tb += kThreads) {
       const int lt = tb + (int)threadIdx.x;
@@ -1688,11 +1702,13 @@ __global__ __launch_bounds__(kThreads) void k_single(DevPlan P, const float* __r
       }
     };
     bad = carry != c;   // uniform
-    const bool one = c <= (uint32_t)kChunk;
     if (!bad && one) {   // uniform: placed in LDS, each candidate at its run's place
-      for (uint32_t j = threadIdx.x; j < c; j += kThreads) {
-        const float v = P.cand_val[cb + j];
-        const int32_t id = P.cand_idx[cb + j];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const uint32_t j = threadIdx.x + (uint32_t)(q * kThreads);
+        if (j >= c) break;
+        const float v = cv[q];
+        const int32_t id = ci[q];
         const int lt = id >= 0 && id < n_s ? id / kTile : -1;
         uint32_t dst = (uint32_t)kChunk;
         if (lt >= 0 && lt < nt && j >= L.roff[lt]) dst = L.rdst[lt] + (j - L.roff[lt]);
