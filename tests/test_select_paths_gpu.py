@@ -204,3 +204,45 @@ def test_many_complete_candidates(chain, grid):
         assert cands[0] > 3 * 8192
     if grid:
         assert any(t[0] > 1 for _, _, t in seen[1:]), "the grid gave no ties at the k-th key"
+
+
+@pytest.mark.parametrize("k", [2048, 2049], ids=["single-4k-8192", "chain-4k-8196"])
+def test_single_rule_limit_at_4m_elements(k):
+    """A segment of 2^22 elements (the largest one workgroup selects: 512 tiles, its LDS run
+    tables full) with k at the rule's limit (4k = 8192, one chunk) and one past it (the chain):
+    a first call with 3k magnitudes near 1 sets the threshold just below 1, then 12k magnitudes
+    in [0.996, 0.9999] are all captured (candidates over several chunks, gathered across all
+    512 tiles on the single path), against the oracle on every call."""
+    n = 1 << 22
+    rng = np.random.default_rng(808)
+    targets = [_cluster(rng, n, 3 * k)]
+    for _ in range(2):
+        a = rng.normal(0.0, 1e-3, n)
+        pos = rng.choice(n, 12 * k, replace=False)
+        a[pos] = rng.uniform(0.996, 0.9999, pos.size) * rng.choice([-1.0, 1.0], pos.size)
+        targets.append(a)
+    seen = []
+    run_parity([n], _target_grads(targets), k=[k], label=f"4M k={k}",
+               check_stats=lambda t, st: seen.append((st["mode"].tolist(),
+                                                      st["candidates"].tolist())))
+    log(f"modes/candidates: {seen}")
+    for modes, cands in seen[1:]:
+        assert modes == [gca.MODE_CANDIDATES]
+        assert cands[0] > 8192
+
+
+@pytest.mark.parametrize("n", [65536, 65537], ids=["single-whole", "chain"])
+def test_single_rule_limit_at_65536_elements(n):
+    """k = 10% of a 65536-element segment (the largest a workgroup selects whatever its k; every
+    element captured, eight chunks of candidates) and of 65537 (the chain), with ties from
+    integer-valued gradients."""
+    rng = np.random.default_rng(909)
+    grads = [rng.integers(-8, 9, n).astype(np.float32) for _ in range(3)]
+    seen = []
+    run_parity([n], grads, ratio=0.1, label=f"whole n={n}",
+               check_stats=lambda t, st: seen.append((st["mode"].tolist(),
+                                                      st["candidates"].tolist())))
+    log(f"modes/candidates: {seen}")
+    for modes, cands in seen:
+        assert modes == [gca.MODE_CANDIDATES]
+        assert cands == [n]
