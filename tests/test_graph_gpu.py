@@ -17,6 +17,9 @@ from tests.gpu_helpers import assert_bitwise, log
 pytestmark = pytest.mark.gpu
 
 SIZES = [1001, 70003, 8192 * 3 + 5, 300001, 4097]
+# at k = 1% this plan selects with the chain (its 300001-element segment is past the
+# one-workgroup rule); this one with one workgroup per segment
+SINGLE_SIZES = [1001, 70003, 8192 * 3 + 5, 200000, 4097]
 
 
 def _grads(n, iters, seed):
@@ -24,9 +27,10 @@ def _grads(n, iters, seed):
     return [(rng.standard_t(3.0, n)).astype(np.float32) for _ in range(iters)]
 
 
+@pytest.mark.parametrize("sizes", [SIZES, SINGLE_SIZES], ids=["chain", "single"])
 @pytest.mark.parametrize("momentum", [None, 0.9], ids=["plain", "momentum"])
-def test_topk_compress_graph_replays(momentum):
-    off = np.concatenate([[0], np.cumsum(SIZES)]).astype(np.int64)
+def test_topk_compress_graph_replays(momentum, sizes):
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     n = int(off[-1])
     plan = gca.Plan(off, ratio=0.01, flags=gca.GC_MOMENTUM_MASK if momentum else 0)
     dev = torch.device("cuda")
