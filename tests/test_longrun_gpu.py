@@ -1,5 +1,6 @@
 """Many error-feedback steps on one plan: the threshold estimate must settle (few segments
-leave the candidate path once warm) while every step stays exact.  Sampled segments (the
+leave the candidate path once warm) while every step stays exact.  The single 1M tensor's plan
+selects with one workgroup per segment, the others with the chain.  Sampled segments (the
 smallest, the largest up to 5M elements and a spread between) are stepped through the oracle
 every iteration;
 every segment is checked by the properties that fix the Top-k result."""
@@ -35,7 +36,9 @@ def _props(off, plan, acc, e, vals, idx):
         assert torch.equal(res.view(torch.int32), e[a:b].view(torch.int32)), f"residual {s}"
 
 
-@pytest.mark.parametrize("name,iters,momentum", [("c2_resnet50", 40, None),
+@pytest.mark.parametrize("name,iters,momentum", [("c1_single_1m", 60, None),
+                                                 ("c1_single_1m", 40, 0.9),
+                                                 ("c2_resnet50", 40, None),
                                                  ("c3_bert_large", 20, 0.9)])
 def test_many_steps(name, iters, momentum):
     wl = workload(name)
