@@ -480,3 +480,38 @@ def test_calibration_kernels_match_torch():
     assert torch.equal(dst.view(torch.int32), x.view(torch.int32))
     with pytest.raises(gca.GCError):          # x and y overlap
         gca.add_f32(y[:100], y[52:152])
+
+
+def test_two_plans_on_two_streams_concurrently():
+    """Two plans (one that selects with one workgroup per segment, one on the chain) called
+    alternately on two streams with no synchronisation between their calls: each keeps its own
+    state, and every call is bit-exact against the oracle."""
+    rng = np.random.default_rng(1212)
+    cases = [([300007, 20000, 9000], 0.001), ([400003, 70001, 5000], 0.01)]
+    dev = torch.device("cuda")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for sizes, ratio in cases:
+        off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+        n = int(off[-1])
+        plan = gca.Plan(off, ratio=ratio)
+        grads = [(rng.standard_t(3, n) * 1e-3).astype(np.float32) for _ in range(4)]
+        runs.append(dict(off=off, plan=plan, grads=grads,
+                         g=[torch.from_numpy(x).to(dev) for x in grads],
+                         e=torch.zeros(n, device=dev), e_h=np.zeros(n, np.float32),
+                         vals=[torch.empty(plan.total_k, device=dev) for _ in grads],
+                         idx=[torch.empty(plan.total_k, dtype=torch.int32, device=dev)
+                              for _ in grads]))
+    torch.cuda.synchronize()
+    for t in range(4):
+        for r, st in zip(runs, streams):
+            with torch.cuda.stream(st):
+                r["plan"].compress(r["g"][t], r["e"], r["vals"][t], r["idx"][t])
+    torch.cuda.synchronize()
+    for j, r in enumerate(runs):
+        for t in range(4):
+            hv, hi = oracle.topk_ef(r["grads"][t], r["e_h"], r["off"], r["plan"].k)
+            assert_bitwise(r["idx"][t], hi, f"plan {j} call {t} idx")
+            assert_bitwise(r["vals"][t], hv, f"plan {j} call {t} vals")
+        assert_bitwise(r["e"], r["e_h"], f"plan {j} residual")
+        r["plan"].close()
